@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for ONNX MatMul workloads.
+
+This module only draws random numbers and stores them in the element type;
+it holds none of the matrix-product arithmetic.  Both the GPU path (tests,
+benchmark) and the CPU oracle consume exactly the bit patterns it returns.
+
+Recipe: numpy ``default_rng`` (PCG64) seeded with ``[seed, product, operand]``
+draws float32 values in fixed chunks of ``CHUNK`` elements; uniform(lo, hi)
+is ``lo + (hi - lo) * U[0,1)``, normal(0, s) is ``s * N(0,1)``; "int" draws
+integers uniformly from {-2, ..., 2}.  The float32 values are then rounded to
+the element type: FLOAT16 by numpy's float32->float16 conversion, BFLOAT16 by
+torch's float32->bfloat16 conversion (both round to nearest, ties to even).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+FLOAT, FLOAT16, BFLOAT16 = 1, 10, 16
+DTYPE_NAMES = {FLOAT: "fp32", FLOAT16: "fp16", BFLOAT16: "bf16"}
+ELEM_SIZE = {FLOAT: 4, FLOAT16: 2, BFLOAT16: 2}
+CHUNK = 1 << 24
+
+
+def _draw(rng: np.random.Generator, n: int, dist: Tuple) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    kind = dist[0]
+    for s in range(0, n, CHUNK):
+        e = min(n, s + CHUNK)
+        if kind == "uniform":
+            lo, hi = dist[1], dist[2]
+            out[s:e] = rng.random(e - s, dtype=np.float32)
+            out[s:e] *= np.float32(hi - lo)
+            out[s:e] += np.float32(lo)
+        elif kind == "normal":
+            out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+            out[s:e] *= np.float32(dist[1])
+        elif kind == "int":
+            out[s:e] = rng.integers(-2, 3, e - s).astype(np.float32)
+        else:
+            raise ValueError(f"unknown distribution {dist}")
+    return out
+
+
+def to_storage(x32: np.ndarray, dtype: int) -> np.ndarray:
+    """float32 values -> element storage (float32, or uint16 bit patterns)."""
+    if dtype == FLOAT:
+        return x32
+    if dtype == FLOAT16:
+        return x32.astype(np.float16).view(np.uint16)
+    if dtype == BFLOAT16:
+        import torch
+
+        out = np.empty(x32.shape, dtype=np.uint16)
+        flat_in = x32.reshape(-1)
+        flat_out = out.reshape(-1)
+        for s in range(0, flat_in.size, CHUNK):
+            e = min(flat_in.size, s + CHUNK)
+            t = torch.from_numpy(flat_in[s:e]).to(torch.bfloat16)
+            flat_out[s:e] = t.view(torch.int16).numpy().view(np.uint16)
+        return out
+    raise ValueError(f"dtype {dtype}")
+
+
+def generate(shape: Sequence[int], dtype: int, dist: Tuple, seed: Sequence[int]) -> np.ndarray:
+    """Storage array (float32, or uint16 bits for 16-bit types) of ``shape``."""
+    n = int(np.prod(shape, dtype=np.int64)) if len(shape) else 1
+    rng = np.random.default_rng(list(seed))
+    return to_storage(_draw(rng, n, dist), dtype).reshape(tuple(shape))
+
+
+def as_torch(storage: np.ndarray, dtype: int):
+    """CPU torch tensor viewing the same bits with the element type."""
+    import torch
+
+    if dtype == FLOAT:
+        return torch.from_numpy(np.ascontiguousarray(storage))
+    t = torch.from_numpy(np.ascontiguousarray(storage).view(np.int16))
+    return t.view(torch.float16 if dtype == FLOAT16 else torch.bfloat16)
+
+
+def from_torch(t) -> np.ndarray:
+    """Storage array of a (CPU or device) torch tensor."""
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclass
+class Product:
+    """One MatMul: shapes, element type, value distribution and seed."""
+
+    name: str
+    a_shape: Tuple[int, ...]
+    b_shape: Tuple[int, ...]
+    dtype: int
+    dist: Tuple
+    seed: int
+    index: int = 0
+
+    @property
+    def K(self) -> int:
+        return int(self.a_shape[-1])
+
+    def make(self, dist: Tuple = None) -> Tuple[np.ndarray, np.ndarray]:
+        d = dist if dist is not None else self.dist
+        a = generate(self.a_shape, self.dtype, d, [self.seed, self.index, 0])
+        b = generate(self.b_shape, self.dtype, d, [self.seed, self.index, 1])
+        return a, b
+
+
+@dataclass
+class Workload:
+    name: str
+    products: List[Product] = field(default_factory=list)
+
+
+def _normal_over_sqrt_k(k: int) -> Tuple:
+    return ("normal", 1.0 / math.sqrt(k))
+
+
+def _workloads() -> dict:
+    w = {}
+    u1 = ("uniform", -1.0, 1.0)
+    w["fp32_tiny_broadcast"] = Workload("fp32_tiny_broadcast", [
+        Product("fp32_4x64x96_by_96x80", (4, 64, 96), (96, 80), FLOAT, u1, 1, 0),
+        Product("fp32_vec96_by_96x80", (96,), (96, 80), FLOAT, u1, 1, 1),
+        Product("fp32_4x64x96_by_vec96", (4, 64, 96), (96,), FLOAT, u1, 1, 2),
+    ])
+    w["fp32_square_and_batched_broadcast"] = Workload("fp32_square_and_batched_broadcast", [
+        Product("fp32_1024_square", (1024, 1024), (1024, 1024), FLOAT, _normal_over_sqrt_k(1024), 2, 0),
+        Product("fp32_8x1x512x512_by_1x6x512x512", (8, 1, 512, 512), (1, 6, 512, 512), FLOAT,
+                _normal_over_sqrt_k(512), 2, 1),
+    ])
+    w["bf16_transformer_projection"] = Workload("bf16_transformer_projection", [
+        Product("bf16_16x512x4096_by_4096x11008", (16, 512, 4096), (4096, 11008), BFLOAT16,
+                ("normal", 0.02), 3, 0),
+    ])
+    u5 = ("uniform", -0.5, 0.5)
+    w["fp16_decode_skinny"] = Workload("fp16_decode_skinny", [
+        Product("fp16_gemv_32x1x4096_by_32x4096x4096", (32, 1, 4096), (32, 4096, 4096), FLOAT16, u5, 4, 0),
+        Product("fp16_skinny_n_8192x4096_by_4096x8", (8192, 4096), (4096, 8), FLOAT16, u5, 4, 1),
+    ])
+    w["longk_and_attention"] = Workload("longk_and_attention", [
+        Product("fp32_splitk_64x131072_by_131072x64", (64, 131072), (131072, 64), FLOAT,
+                _normal_over_sqrt_k(131072), 5, 0),
+        Product("bf16_qk_4x32x2048x128_by_4x32x128x2048", (4, 32, 2048, 128), (4, 32, 128, 2048), BFLOAT16,
+                _normal_over_sqrt_k(128), 5, 1),
+        Product("bf16_pv_4x32x2048x2048_by_4x32x2048x128", (4, 32, 2048, 2048), (4, 32, 2048, 128), BFLOAT16,
+                _normal_over_sqrt_k(2048), 5, 2),
+    ])
+    return w
+
+
+WORKLOADS = _workloads()
+
+
+def all_products() -> List[Product]:
+    return [p for w in WORKLOADS.values() for p in w.products]

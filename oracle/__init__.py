@@ -1,0 +1,167 @@
+"""CPU oracle for ONNX MatMul -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it and
+shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64 accumulation over an
+explicit broadcast index walk); this module only builds it with gcc and
+marshals numpy arrays through ctypes.  ``compare.py`` holds the comparator
+that applies the parity tolerances.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+# ONNX TensorProto type codes.
+FLOAT, FLOAT16, DOUBLE, BFLOAT16 = 1, 10, 11, 16
+
+STATUS = {
+    0: "ok",
+    1: "rank",
+    2: "negative dimension",
+    3: "inner dimension mismatch",
+    4: "batch dimensions not broadcastable",
+    5: "unknown dtype",
+    6: "allocation failed",
+}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"oracle status {code}: {STATUS.get(code, '?')}")
+        self.code = code
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so with gcc (always recompiles)."""
+    cmd = [
+        "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+        "-Wall", "-Wextra", SRC, "-o", LIB + ".tmp", "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.oracle_output_shape.argtypes = [i64p, ctypes.c_int, i64p, ctypes.c_int, i64p,
+                                          ctypes.POINTER(ctypes.c_int)]
+        L.oracle_matmul.argtypes = [ctypes.c_int, ctypes.c_void_p, i64p, ctypes.c_int,
+                                    ctypes.c_void_p, i64p, ctypes.c_int, ctypes.c_void_p]
+        L.oracle_matmul_at.argtypes = [ctypes.c_int, ctypes.c_void_p, i64p, ctypes.c_int,
+                                       ctypes.c_void_p, i64p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_void_p]
+        L.oracle_narrow_array.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p]
+        L.oracle_decode_array.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p]
+        L.oracle_narrow_f16.argtypes = [ctypes.c_double]
+        L.oracle_narrow_f16.restype = ctypes.c_uint16
+        L.oracle_narrow_bf16.argtypes = [ctypes.c_double]
+        L.oracle_narrow_bf16.restype = ctypes.c_uint16
+        L.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+        L.oracle_decode_f16.restype = ctypes.c_double
+        L.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        L.oracle_decode_bf16.restype = ctypes.c_double
+        L.oracle_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _shape_arr(shape):
+    arr = (ctypes.c_int64 * max(1, len(shape)))(*[int(d) for d in shape])
+    return arr
+
+
+def _storage(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Contiguous raw storage: float32, float64, or uint16 bit patterns."""
+    want = {FLOAT: np.float32, DOUBLE: np.float64, FLOAT16: np.uint16, BFLOAT16: np.uint16}[dtype]
+    if x.dtype == np.float16 and dtype == FLOAT16:
+        x = x.view(np.uint16)
+    if x.dtype != want:
+        raise TypeError(f"storage for dtype {dtype} must be {want}, got {x.dtype}")
+    return np.ascontiguousarray(x)
+
+
+def output_shape(a_shape, b_shape):
+    """Output shape of MatMul(A, B); raises OracleError on invalid shapes."""
+    out = (ctypes.c_int64 * (max(len(a_shape), len(b_shape)) + 1))()
+    rank = ctypes.c_int(0)
+    st = lib().oracle_output_shape(_shape_arr(a_shape), len(a_shape), _shape_arr(b_shape),
+                                   len(b_shape), out, ctypes.byref(rank))
+    if st:
+        raise OracleError(st)
+    return tuple(out[i] for i in range(rank.value))
+
+
+def matmul(a: np.ndarray, b: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact-to-fp64 MatMul of stored tensors ``a`` and ``b`` (raw storage:
+    float32 / float64 arrays, or uint16 bit patterns for FLOAT16/BFLOAT16).
+    Returns a float64 array of the output shape."""
+    a = _storage(a, dtype)
+    b = _storage(b, dtype)
+    shape = output_shape(a.shape, b.shape)
+    y = np.empty(int(np.prod(shape, dtype=np.int64)), dtype=np.float64)
+    st = lib().oracle_matmul(dtype, a.ctypes.data, _shape_arr(a.shape), a.ndim, b.ctypes.data,
+                             _shape_arr(b.shape), b.ndim, y.ctypes.data)
+    if st:
+        raise OracleError(st)
+    return y.reshape(shape)
+
+
+def matmul_at(a: np.ndarray, b: np.ndarray, dtype: int, flat_idx) -> np.ndarray:
+    """Selected outputs (flat row-major indices into the output) as float64."""
+    a = _storage(a, dtype)
+    b = _storage(b, dtype)
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    out = np.empty(idx.size, dtype=np.float64)
+    st = lib().oracle_matmul_at(dtype, a.ctypes.data, _shape_arr(a.shape), a.ndim,
+                                b.ctypes.data, _shape_arr(b.shape), b.ndim, idx.ctypes.data,
+                                idx.size, out.ctypes.data)
+    if st:
+        raise OracleError(st)
+    return out
+
+
+def narrow(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Round float64 values to the storage of ``dtype`` (nearest, ties to even).
+    Returns float32 / float64 arrays, or uint16 bit patterns for 16-bit types."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out_dt = {FLOAT: np.float32, DOUBLE: np.float64, FLOAT16: np.uint16, BFLOAT16: np.uint16}[dtype]
+    out = np.empty(x.shape, dtype=out_dt)
+    st = lib().oracle_narrow_array(dtype, x.ctypes.data, x.size, out.ctypes.data)
+    if st:
+        raise OracleError(st)
+    return out
+
+
+def decode(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact float64 values of stored elements."""
+    bits = _storage(np.asarray(bits), dtype)
+    out = np.empty(bits.shape, dtype=np.float64)
+    st = lib().oracle_decode_array(dtype, bits.ctypes.data, bits.size, out.ctypes.data)
+    if st:
+        raise OracleError(st)
+    return out
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())

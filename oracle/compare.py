@@ -1,0 +1,115 @@
+"""Parity comparator -- TEST INFRASTRUCTURE ONLY (part of the oracle).
+
+Tolerances (readings of the parity rule for this operator; the pages fix FP32
+accumulation with final narrowing, page "MatMul Kernel Design", section
+"Types and algorithm selection"):
+
+* FLOAT output: ``max |y - o| <= 1e-4 * sqrt(K) * max|A| * max|B|`` where
+  ``o`` is the fp64 oracle value and the maxima run over the whole stored A
+  and B.
+* FLOAT16 / BFLOAT16 output: each element is within 2 units in the last place
+  of ``narrow(o)`` (ulp distance measured on the monotone ordering of the
+  16-bit patterns), or -- for results so close to zero that the output ulp is
+  finer than FP32 accumulation noise -- meets the FLOAT rule above.  The
+  number of elements that pass only through the second clause is reported.
+* Exact mode (small-integer-valued inputs): ``y == narrow(o)`` bit for bit.
+* NaN matches only NaN; an infinity matches only the same infinity.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import BFLOAT16, DOUBLE, FLOAT, FLOAT16, decode, narrow
+
+
+def fp32_tolerance(K: int, amax: float, bmax: float) -> float:
+    return 1e-4 * math.sqrt(max(int(K), 0)) * float(amax) * float(bmax)
+
+
+def abs_max(x: np.ndarray, dtype: int) -> float:
+    """max |x| over stored values (0 for an empty tensor)."""
+    if x.size == 0:
+        return 0.0
+    v = decode(x, dtype) if dtype in (FLOAT16, BFLOAT16) else np.asarray(x, dtype=np.float64)
+    return float(np.max(np.abs(v)))
+
+
+def _key16(bits: np.ndarray) -> np.ndarray:
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def ulp_distance16(y_bits: np.ndarray, r_bits: np.ndarray) -> np.ndarray:
+    return np.abs(_key16(y_bits) - _key16(r_bits))
+
+
+@dataclass
+class Report:
+    ok: bool
+    n: int
+    max_abs_err: float
+    tolerance: float
+    max_ulp: int = 0
+    n_fp32_clause: int = 0
+    n_bad: int = 0
+    detail: str = ""
+
+    def __str__(self) -> str:
+        return (f"ok={self.ok} n={self.n} max_abs_err={self.max_abs_err:.3e} tol={self.tolerance:.3e} "
+                f"max_ulp={self.max_ulp} fp32_clause={self.n_fp32_clause} bad={self.n_bad} {self.detail}")
+
+
+def _special_mismatch(yv: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """Elements where NaN/Inf status differs between result and oracle."""
+    nan_bad = np.isnan(yv) != np.isnan(o)
+    inf_o = np.isinf(o)
+    inf_y = np.isinf(yv)
+    inf_bad = (inf_o | inf_y) & ~(np.isnan(yv) | np.isnan(o)) & ~((inf_o & inf_y) & (np.sign(yv) == np.sign(o)))
+    return nan_bad | inf_bad
+
+
+def check(y: np.ndarray, o: np.ndarray, dtype: int, K: int, amax: float, bmax: float,
+          exact: bool = False) -> Report:
+    """Compare stored results ``y`` (float32 array, or uint16 bit patterns) with
+    fp64 oracle values ``o`` of the same shape."""
+    o = np.asarray(o, dtype=np.float64).reshape(-1)
+    y = np.asarray(y).reshape(-1)
+    if y.size != o.size:
+        return Report(False, int(y.size), math.inf, 0.0, detail=f"size {y.size} != {o.size}")
+    tol = fp32_tolerance(K, amax, bmax)
+    if y.size == 0:
+        return Report(True, 0, 0.0, tol)
+    if dtype in (FLOAT16, BFLOAT16):
+        y_bits = y.view(np.uint16) if y.dtype != np.uint16 else y
+        yv = decode(y_bits, dtype)
+        ref = narrow(o, dtype)
+        special = _special_mismatch(yv, o)
+        finite = np.isfinite(yv) & np.isfinite(o)
+        err = np.where(finite, np.abs(yv - o), 0.0)
+        if exact:
+            bad = (y_bits != ref) & ~(np.isnan(yv) & np.isnan(o))
+            return Report(not bad.any(), int(y.size), float(err.max()), 0.0, n_bad=int(bad.sum()),
+                          detail="exact")
+        ulp = np.where(finite, ulp_distance16(y_bits, ref), 0)
+        ulp_ok = ulp <= 2
+        tol_ok = err <= tol
+        bad = special | ~(ulp_ok | tol_ok)
+        return Report(not bad.any(), int(y.size), float(err.max()), tol, max_ulp=int(ulp.max()),
+                      n_fp32_clause=int((~ulp_ok & tol_ok).sum()), n_bad=int(bad.sum()))
+    if dtype == FLOAT or dtype == DOUBLE:
+        yv = y.astype(np.float64)
+        special = _special_mismatch(yv, o)
+        finite = np.isfinite(yv) & np.isfinite(o)
+        err = np.where(finite, np.abs(yv - o), 0.0)
+        if exact:
+            ref = narrow(o, dtype)
+            bad = (y != ref) & ~(np.isnan(yv) & np.isnan(o))
+            return Report(not bad.any(), int(y.size), float(err.max()), 0.0, n_bad=int(bad.sum()),
+                          detail="exact")
+        bad = special | (err > tol)
+        return Report(not bad.any(), int(y.size), float(err.max()), tol, n_bad=int(bad.sum()))
+    raise ValueError(f"dtype {dtype}")

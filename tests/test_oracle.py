@@ -1,0 +1,343 @@
+"""Pins for the CPU oracle: checks against facts fixed outside the oracle
+(shape rules printed in the pages, numpy's independent matmul, closed forms,
+exact integer arithmetic, identity/permutation products, IEEE narrowing as
+implemented by numpy and torch, and a hand-derived BF16 table)."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import BFLOAT16, DOUBLE, FLOAT, FLOAT16
+from oracle.compare import check, fp32_tolerance, ulp_distance16
+from onnx_broadcast_matmul_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _parse_shape(s):
+    s = s.strip()
+    if s == "()":
+        return ()
+    return tuple(int(x) for x in s.split(","))
+
+
+def _golden_shape_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "shape_rules.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            a, b, out, src = [x.strip() for x in line.split("|")]
+            cases.append((_parse_shape(a), _parse_shape(b), None if out == "ERROR" else _parse_shape(out), src))
+    return cases
+
+
+@pytest.mark.parametrize("a,b,out,src", _golden_shape_cases())
+def test_golden_shape_rules(a, b, out, src):
+    if out is None:
+        with pytest.raises(oracle.OracleError):
+            oracle.output_shape(a, b)
+    else:
+        assert oracle.output_shape(a, b) == out, src
+
+
+def _all_shapes(max_rank=4, dims=(0, 1, 2, 3)):
+    for r in range(1, max_rank + 1):
+        for shp in itertools.product(dims, repeat=r):
+            yield shp
+
+
+def test_output_shape_matches_numpy_exhaustive():
+    """Every pair of shapes of rank 1..4 with dims in {0,1,2,3}: the oracle's
+    output shape (or its refusal) equals numpy.matmul's."""
+    shapes = list(_all_shapes())
+    zeros = {s: np.zeros(s, dtype=np.float64) for s in shapes}
+    n_err = 0
+    for sa in shapes:
+        for sb in shapes:
+            try:
+                want = np.matmul(zeros[sa], zeros[sb]).shape
+            except ValueError:
+                want = None
+            try:
+                got = oracle.output_shape(sa, sb)
+            except oracle.OracleError as e:
+                assert e.code in (3, 4)
+                got = None
+            assert got == want, (sa, sb, got, want)
+            n_err += got is None
+    assert n_err > 1000  # the grid exercises refusals too
+
+
+def test_shape_errors():
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.output_shape((), (3, 4))
+    assert e.value.code == 1
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.output_shape((2, -1), (3, 4))
+    assert e.value.code == 2
+
+
+def _closed_form(bidx, m, n, K):
+    # sum_k (bidx + m + 10k) (k + 100n) with S1 = sum k, S2 = sum k^2, k = 0..K-1
+    S1 = K * (K - 1) // 2
+    S2 = (K - 1) * K * (2 * K - 1) // 6
+    c = bidx + m
+    return c * S1 + 100 * n * c * K + 10 * S2 + 1000 * n * S1
+
+
+@pytest.mark.parametrize("dtype", [FLOAT, DOUBLE])
+def test_closed_form_batched_broadcast(dtype):
+    """A[b,m,k] = b + m + 10k, B[k,n] = k + 100n broadcast over b.  A
+    transposed operand, a dropped term or a wrong batch offset changes the
+    closed form."""
+    Bt, M, N, K = 3, 5, 4, 7
+    npdt = np.float32 if dtype == FLOAT else np.float64
+    b_, m_, k_ = np.meshgrid(np.arange(Bt), np.arange(M), np.arange(K), indexing="ij")
+    A = (b_ + m_ + 10 * k_).astype(npdt)
+    k2, n2 = np.meshgrid(np.arange(K), np.arange(N), indexing="ij")
+    B = (k2 + 100 * n2).astype(npdt)
+    Y = oracle.matmul(A, B, dtype)
+    assert Y.shape == (Bt, M, N)
+    for b in range(Bt):
+        for m in range(M):
+            for n in range(N):
+                assert Y[b, m, n] == _closed_form(b, m, n, K)
+
+
+def test_closed_form_16bit():
+    """Same closed form with values small enough to be exact in FP16 and BF16."""
+    M, N, K = 3, 2, 4
+    m_, k_ = np.meshgrid(np.arange(M), np.arange(K), indexing="ij")
+    A = (m_ + 10 * k_).astype(np.float32)  # <= 32
+    k2, n2 = np.meshgrid(np.arange(K), np.arange(N), indexing="ij")
+    B = (k2 + 100 * n2).astype(np.float32)  # <= 103: exact in fp16, not all in bf16
+    Bb = (k2 + 8 * n2).astype(np.float32)    # <= 11: exact in bf16
+    Y = oracle.matmul(synth.to_storage(A, FLOAT16), synth.to_storage(B, FLOAT16), FLOAT16)
+    for m in range(M):
+        for n in range(N):
+            assert Y[m, n] == _closed_form(0, m, n, K)
+    Y = oracle.matmul(synth.to_storage(A, BFLOAT16), synth.to_storage(Bb, BFLOAT16), BFLOAT16)
+    S1, S2 = K * (K - 1) // 2, (K - 1) * K * (2 * K - 1) // 6
+    for m in range(M):
+        for n in range(N):
+            assert Y[m, n] == m * S1 + 8 * n * m * K + 10 * S2 + 80 * n * S1
+
+
+def test_hand_enumerated_2x2():
+    A = np.array([[1.0, 2.0], [3.0, 4.0]], dtype=np.float32)
+    B = np.array([[5.0, 6.0], [7.0, 8.0]], dtype=np.float32)
+    # [[1*5+2*7, 1*6+2*8], [3*5+4*7, 3*6+4*8]]
+    assert oracle.matmul(A, B, FLOAT).tolist() == [[19.0, 22.0], [43.0, 50.0]]
+    # B rank one: A @ [5, 7] = [19, 43]; A rank one: [1, 2] @ B = [19, 22]
+    assert oracle.matmul(A, np.array([5.0, 7.0], np.float32), FLOAT).tolist() == [19.0, 43.0]
+    assert oracle.matmul(np.array([1.0, 2.0], np.float32), B, FLOAT).tolist() == [19.0, 22.0]
+    assert oracle.matmul(np.array([1.0, 2.0], np.float32), np.array([5.0, 7.0], np.float32), FLOAT).shape == ()
+    assert float(oracle.matmul(np.array([1.0, 2.0], np.float32), np.array([5.0, 7.0], np.float32), FLOAT)) == 19.0
+
+
+@pytest.mark.parametrize("sa,sb", [
+    ((5, 7), (7, 3)), ((2, 5, 7), (7, 3)), ((7,), (2, 7, 3)), ((2, 1, 5, 7), (3, 7, 4)),
+    ((4, 6), (6,)), ((1, 3, 2, 9), (4, 1, 9, 2)), ((3, 0, 4), (4, 2)), ((2, 3, 0), (0, 4)),
+])
+def test_matches_numpy_float64(sa, sb):
+    """numpy.matmul in float64 is an independent implementation of the same
+    definition; results agree to well below the fp64 summation bound."""
+    rng = np.random.default_rng(7)
+    A = rng.standard_normal(sa)
+    B = rng.standard_normal(sb)
+    Y = oracle.matmul(A, B, DOUBLE)
+    R = np.matmul(A, B)
+    assert Y.shape == R.shape
+    bound = 1e-12 * (np.matmul(np.abs(A), np.abs(B)) + 1e-300)
+    assert np.all(np.abs(Y - R) <= bound)
+
+
+def test_identity_and_permutation_exact():
+    rng = np.random.default_rng(11)
+    A = rng.standard_normal((2, 6, 9)).astype(np.float32)
+    I9 = np.eye(9, dtype=np.float32)
+    assert np.array_equal(oracle.matmul(A, I9, FLOAT), A.astype(np.float64))
+    I6 = np.eye(6, dtype=np.float32)
+    assert np.array_equal(oracle.matmul(I6, A, FLOAT), A.astype(np.float64))
+    perm = rng.permutation(6)
+    P = np.eye(6, dtype=np.float32)[perm]
+    assert np.array_equal(oracle.matmul(P, A, FLOAT), A[:, perm, :].astype(np.float64))
+    Bh = synth.to_storage(rng.standard_normal((5, 4)).astype(np.float32), BFLOAT16)
+    Ph = synth.to_storage(np.eye(5, dtype=np.float32)[rng.permutation(5)], BFLOAT16)
+    Yh = oracle.matmul(Ph, Bh, BFLOAT16)
+    assert np.array_equal(Yh, oracle.decode(Bh, BFLOAT16)[np.argmax(oracle.decode(Ph, BFLOAT16), axis=1)])
+
+
+@pytest.mark.parametrize("dtype", [FLOAT, FLOAT16, BFLOAT16])
+def test_small_integer_exact(dtype):
+    """Integer-valued inputs: the fp64 sum is exact and equals int64 matmul."""
+    rng = np.random.default_rng(3)
+    Ai = rng.integers(-2, 3, (3, 1, 13, 37))
+    Bi = rng.integers(-2, 3, (4, 37, 11))
+    A = synth.to_storage(Ai.astype(np.float32), dtype)
+    B = synth.to_storage(Bi.astype(np.float32), dtype)
+    Y = oracle.matmul(A, B, dtype)
+    assert np.array_equal(Y, np.matmul(Ai, Bi).astype(np.float64))
+
+
+def test_broadcast_equals_explicit_repeat():
+    rng = np.random.default_rng(5)
+    A = synth.to_storage(rng.standard_normal((3, 1, 8, 10)).astype(np.float32), BFLOAT16)
+    B = synth.to_storage(rng.standard_normal((1, 4, 10, 6)).astype(np.float32), BFLOAT16)
+    Ar = np.ascontiguousarray(np.broadcast_to(A, (3, 4, 8, 10)))
+    Br = np.ascontiguousarray(np.broadcast_to(B, (3, 4, 10, 6)))
+    assert np.array_equal(oracle.matmul(A, B, BFLOAT16), oracle.matmul(Ar, Br, BFLOAT16))
+    A2 = rng.standard_normal((5, 10)).astype(np.float32)
+    B2 = rng.standard_normal((2, 3, 10, 4)).astype(np.float32)
+    A2r = np.ascontiguousarray(np.broadcast_to(A2, (2, 3, 5, 10)))
+    assert np.array_equal(oracle.matmul(A2, B2, FLOAT), oracle.matmul(A2r, B2, FLOAT))
+
+
+def test_rank1_equals_promoted():
+    rng = np.random.default_rng(9)
+    a = rng.standard_normal(12).astype(np.float32)
+    B = rng.standard_normal((3, 12, 5)).astype(np.float32)
+    assert np.array_equal(oracle.matmul(a, B, FLOAT), oracle.matmul(a[None, :], B, FLOAT)[:, 0, :])
+    A = rng.standard_normal((2, 4, 12)).astype(np.float32)
+    b = rng.standard_normal(12).astype(np.float32)
+    assert np.array_equal(oracle.matmul(A, b, FLOAT), oracle.matmul(A, b[:, None], FLOAT)[..., 0])
+
+
+def test_matmul_at_equals_full():
+    rng = np.random.default_rng(21)
+    A = synth.to_storage(rng.standard_normal((2, 1, 7, 33)).astype(np.float32), FLOAT16)
+    B = synth.to_storage(rng.standard_normal((3, 33, 5)).astype(np.float32), FLOAT16)
+    full = oracle.matmul(A, B, FLOAT16).reshape(-1)
+    idx = rng.choice(full.size, 40, replace=False)
+    assert np.array_equal(oracle.matmul_at(A, B, FLOAT16, idx), full[idx])
+
+
+# ---------------------------------------------------------------- decoding
+
+def test_decode_f16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint16)
+    got = oracle.decode(bits, FLOAT16)
+    want = bits.view(np.float16).astype(np.float64)
+    both_nan = np.isnan(got) & np.isnan(want)
+    assert np.all(both_nan | (got == want))
+    assert np.array_equal(np.signbit(got[~both_nan]), np.signbit(want[~both_nan]))
+
+
+def test_decode_bf16_all_patterns():
+    torch = pytest.importorskip("torch")
+    bits = np.arange(65536, dtype=np.uint16)
+    got = oracle.decode(bits, BFLOAT16)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    both_nan = np.isnan(got) & np.isnan(want)
+    assert np.all(both_nan | (got == want))
+    # independent closed form: BF16 is the top half of an FP32 pattern
+    want2 = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    both_nan2 = np.isnan(got) & np.isnan(want2)
+    assert np.all(both_nan2 | (got == want2))
+
+
+# ---------------------------------------------------------------- narrowing
+
+def _edge_doubles():
+    vals = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 65536.0, 1e6, -1e6,
+            2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -25, 2.0 ** -14,
+            2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -40,
+            math.inf, -math.inf, 1e-300, -1e-300, 0.1, 1 / 3]
+    return np.array(vals, dtype=np.float64)
+
+
+def test_narrow_f16_matches_numpy():
+    rng = np.random.default_rng(1)
+    mags = rng.uniform(-30, 17, 1_000_000)
+    x = np.concatenate([_edge_doubles(), np.sign(rng.standard_normal(mags.size)) * 2.0 ** mags])
+    got = oracle.narrow(x, FLOAT16)
+    want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+    assert oracle.narrow(np.array([math.nan]), FLOAT16)[0] & 0x7E00 == 0x7E00
+
+
+BF16_TABLE = [
+    # value, expected bits -- derived by hand from the BF16 format (1 sign,
+    # 8 exponent, 7 fraction bits), round to nearest, ties to even.
+    (1.0, 0x3F80),
+    (1 + 2.0 ** -8, 0x3F80),             # halfway between 0x3F80 and 0x3F81 -> even
+    (1 + 3 * 2.0 ** -8, 0x3F82),         # halfway between 0x3F81 and 0x3F82 -> even
+    (1 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),  # just above the tie
+    (-1.5, 0xBFC0),
+    (3.0, 0x4040),
+    (0.1, 0x3DCD),
+    ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),   # largest finite
+    ((2 - 2.0 ** -8) * 2.0 ** 127, 0x7F80),   # tie with 2^128, odd mantissa -> rounds up to inf
+    ((2 - 2.0 ** -8 - 2.0 ** -20) * 2.0 ** 127, 0x7F7F),
+    (1e39, 0x7F80), (-1e39, 0xFF80),
+    (math.inf, 0x7F80), (-math.inf, 0xFF80),
+    (0.0, 0x0000), (-0.0, 0x8000),
+    (2.0 ** -133, 0x0001),                   # smallest subnormal
+    (2.0 ** -134, 0x0000),                   # tie with 0 -> even (0)
+    (1.5 * 2.0 ** -134, 0x0001),
+    (3 * 2.0 ** -134, 0x0002),               # tie between 1 and 2 units -> 2
+    (2.0 ** -126, 0x0080),                   # smallest normal
+    (2.0 ** -126 - 2.0 ** -134, 0x0080),     # halfway below smallest normal: 0x7F odd -> 0x80
+]
+
+
+@pytest.mark.parametrize("x,bits", BF16_TABLE)
+def test_narrow_bf16_table(x, bits):
+    assert int(oracle.narrow(np.array([x]), BFLOAT16)[0]) == bits
+
+
+def test_narrow_bf16_nan():
+    r = int(oracle.narrow(np.array([math.nan]), BFLOAT16)[0])
+    assert (r & 0x7F80) == 0x7F80 and (r & 0x7F) != 0
+
+
+def test_narrow_bf16_matches_torch_on_float32_values():
+    """For values exactly representable in FP32, narrowing from double and
+    torch's FP32->BF16 rounding see the same number: results must agree."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(2)
+    bits32 = rng.integers(0, 2 ** 32, 1_000_000, dtype=np.uint64).astype(np.uint32)
+    x32 = bits32.view(np.float32)
+    x32 = x32[np.isfinite(x32)]
+    got = oracle.narrow(x32.astype(np.float64), BFLOAT16)
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- comparator
+
+def test_comparator_ulp_rules():
+    o = np.array([1.0, 2.0, -3.0, 1e-3], dtype=np.float64)
+    ref = oracle.narrow(o, BFLOAT16)
+    r = check(ref, o, BFLOAT16, K=16, amax=1.0, bmax=1.0)
+    assert r.ok and r.max_ulp == 0
+    two = ref.copy()
+    two[0] += 2
+    assert check(two, o, BFLOAT16, K=16, amax=1e-9, bmax=1e-9).ok
+    three = ref.copy()
+    three[1] += 3
+    assert not check(three, o, BFLOAT16, K=16, amax=1e-9, bmax=1e-9).ok
+    # 3 ulp off but within the FP32 rule: accepted through the second clause
+    r = check(three, o, BFLOAT16, K=1_000_000, amax=100.0, bmax=100.0)
+    assert r.ok and r.n_fp32_clause == 1
+    nan = ref.copy()
+    nan[2] = 0x7FC0
+    assert not check(nan, o, BFLOAT16, K=16, amax=1e9, bmax=1e9).ok
+    assert ulp_distance16(np.array([0x8000], np.uint16), np.array([0x0000], np.uint16))[0] == 0
+    assert ulp_distance16(np.array([0x8001], np.uint16), np.array([0x0001], np.uint16))[0] == 2
+
+
+def test_comparator_fp32_rule():
+    o = np.array([1.0, -2.0])
+    K, amax, bmax = 100, 2.0, 3.0
+    tol = fp32_tolerance(K, amax, bmax)
+    assert tol == pytest.approx(1e-4 * 10 * 6)
+    y = (o + 0.9 * tol).astype(np.float32)
+    assert check(y, o, FLOAT, K, amax, bmax).ok
+    y = (o + 1.5 * tol).astype(np.float32)
+    assert not check(y, o, FLOAT, K, amax, bmax).ok
+    assert check(o.astype(np.float32), o, FLOAT, K, amax, bmax, exact=True).ok
