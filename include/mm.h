@@ -1,0 +1,186 @@
+/*
+ * mm.h -- C ABI of the MI355X (gfx950) ONNX MatMul library (libmm.so).
+ *
+ * The operation is ONNX MatMul as described on the page "MatMul Kernel
+ * Design" (sections "Shape and plan model", "Types and algorithm selection",
+ * "Scheduling and invariants") and on the page "Gemm and MatMul Performance
+ * Roadmap" (sections "Target computation algorithm", "Planning once, computing
+ * many times", "Parallel execution", "Phase 4: complete MatMul"):
+ *
+ *   Y[i, m, n] = sum_k A[iA(i), m, k] * B[iB(i), k, n]
+ *
+ * with a rank-one A ([K], used as [1, K]) or B ([K], used as [K, 1]) promoted
+ * for the product and its axis removed from the output, and the leading batch
+ * dimensions broadcast NumPy style (right-aligned, 1 stretches, otherwise
+ * equal).  Inputs and output share one element type; FLOAT16 and BFLOAT16
+ * products accumulate in FP32 and are narrowed once, at the end, with
+ * round-to-nearest-even.
+ *
+ * Usage: create a plan once per (A shape, B shape, type); execute it any
+ * number of times on device buffers; destroy it.  Plan creation touches no
+ * GPU.  Every shape/type error is reported by plan creation, before compute.
+ *
+ * Layout: A, B and Y are dense, contiguous, row-major device tensors with the
+ * ONNX shapes given at plan creation (Y has the plan's output shape).
+ * Broadcast operands are read in place through zero batch strides; nothing is
+ * copied or widened.
+ *
+ * Ownership: the caller owns A, B and Y and keeps them alive until the work
+ * enqueued on the stream has completed.  The plan owns its metadata and, for
+ * the split-K algorithm, an FP32 workspace on the device of the first
+ * execution (allocated by that first mm_execute, freed by mm_plan_destroy).
+ * Because of that workspace, executions of one split-K plan must not overlap
+ * on different streams; use one plan per stream.
+ *
+ * Threading: plans are immutable after creation apart from the lazily
+ * allocated workspace, which is guarded; mm_last_error() is per thread.
+ */
+#ifndef MM_H
+#define MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Maximum number of broadcast batch dimensions; inputs may have rank up to
+ * MM_MAX_BATCH_DIMS + 2. */
+#define MM_MAX_BATCH_DIMS 8
+#define MM_MAX_RANK (MM_MAX_BATCH_DIMS + 2)
+
+/* Element types: the ONNX TensorProto codes.  DOUBLE is recognised and
+ * rejected with MM_ERR_DTYPE (not supported by this library yet). */
+typedef enum mm_dtype {
+    MM_FLOAT = 1,
+    MM_FLOAT16 = 10,
+    MM_DOUBLE = 11,
+    MM_BFLOAT16 = 16
+} mm_dtype;
+
+typedef enum mm_status {
+    MM_OK = 0,
+    MM_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+    MM_ERR_RANK = 2,         /* rank 0, or rank above MM_MAX_RANK */
+    MM_ERR_NEG_DIM = 3,      /* a dimension is negative (dynamic) */
+    MM_ERR_K_MISMATCH = 4,   /* A's last dim differs from B's second-to-last */
+    MM_ERR_BROADCAST = 5,    /* batch dimensions cannot be broadcast */
+    MM_ERR_DTYPE = 6,        /* unsupported or unknown element type */
+    MM_ERR_BAD_OPTION = 7,   /* invalid mm_plan_options field */
+    MM_ERR_TOO_LARGE = 8,    /* a size exceeds what the kernels index */
+    MM_ERR_ALLOC = 9,        /* host or device allocation failed */
+    MM_ERR_HIP = 10          /* a HIP runtime call failed (see mm_last_error) */
+} mm_status;
+
+/* Algorithms (page "Gemm and MatMul Performance Roadmap", section "Target
+ * computation algorithm", the shape-to-algorithm table; page "MatMul Kernel
+ * Design", section "Types and algorithm selection"). */
+typedef enum mm_algo {
+    MM_ALGO_AUTO = 0,      /* let the plan choose (only valid as an option) */
+    MM_ALGO_EMPTY = 1,     /* output has no element: nothing is launched */
+    MM_ALGO_ZERO_FILL = 2, /* K == 0: the output is filled with zeros */
+    MM_ALGO_DIRECT = 3,    /* tiny products: one thread per output */
+    MM_ALGO_SKINNY_M = 4,  /* small M (GEMV): B streamed once along N */
+    MM_ALGO_SKINNY_N = 5,  /* small N: A streamed once along K */
+    MM_ALGO_SPLIT_K = 6,   /* tiny output, long K: FP32 partials + ordered reduce */
+    MM_ALGO_GENERAL = 7    /* tiled MFMA GEMM with LDS double buffering */
+} mm_algo;
+
+typedef struct mm_plan_s *mm_plan_t;
+
+/* Overrides for tests and tuning.  Zero-initialise for defaults. */
+typedef struct mm_plan_options {
+    int32_t force_algo; /* MM_ALGO_AUTO, or one of DIRECT..GENERAL; ignored
+                           (EMPTY / ZERO_FILL kept) when the output is empty
+                           or K == 0 */
+    int32_t tile;       /* 0 = plan's choice; k >= 1 selects entry k-1 of the
+                           GENERAL/SPLIT_K tile table for the element type
+                           (see mm_tile_config) */
+    int32_t split_k;    /* 0 = plan's choice; >= 1 number of K partitions for
+                           SPLIT_K (clamped so every partition is non-empty) */
+    int32_t reserved;   /* must be 0 */
+} mm_plan_options;
+
+/* Everything the plan resolved, for inspection and tests. */
+typedef struct mm_plan_info {
+    int32_t dtype;
+    int32_t algo;             /* mm_algo actually selected */
+    int64_t M, N, K;          /* promoted matrix sizes of one product */
+    int64_t batch;            /* independent products launched (after collapse/fold) */
+    int64_t kernel_m;         /* rows per product seen by the kernels (batch*M when folded) */
+    int32_t folded;           /* 1 if A's batch was folded into M (B shared by every batch) */
+    int32_t batch_rank;       /* number of collapsed batch dimensions */
+    int64_t batch_dims[MM_MAX_BATCH_DIMS];
+    int64_t a_batch_strides[MM_MAX_BATCH_DIMS]; /* elements; 0 = broadcast */
+    int64_t b_batch_strides[MM_MAX_BATCH_DIMS]; /* elements; 0 = broadcast */
+    int32_t tile;             /* tile table entry + 1 (0 if not a tiled algorithm) */
+    int32_t split_k;          /* K partitions (1 unless SPLIT_K) */
+    int64_t k_chunk;          /* K elements per partition */
+    int64_t workspace_bytes;  /* FP32 workspace the plan needs on the device */
+    double flops;             /* 2 * batch * M * N * K of the un-folded problem */
+    double min_bytes;         /* element size * (numel A + numel B + numel Y) */
+} mm_plan_info;
+
+/* Create a plan for Y = MatMul(A, B) with A of shape a_shape[0..a_rank) and
+ * B of shape b_shape[0..b_rank), all of type `dtype`.  Validates ranks
+ * (1..MM_MAX_RANK), dimensions (>= 0), the inner dimension, batch
+ * broadcasting and the type; resolves the output shape, collapsed batch
+ * strides and the algorithm.  Host only: no GPU call.  On error *out is set
+ * to NULL and a status is returned (details: mm_last_error()). */
+mm_status mm_plan_create(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank,
+                         int dtype, mm_plan_t *out);
+
+/* As mm_plan_create, with overrides (NULL = defaults). */
+mm_status mm_plan_create_ex(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank,
+                            int dtype, const mm_plan_options *opt, mm_plan_t *out);
+
+/* Release a plan and its device workspace.  NULL is ignored.  The caller
+ * must make sure no enqueued execution of the plan is still running. */
+void mm_plan_destroy(mm_plan_t plan);
+
+/* Enqueue Y = MatMul(A, B) on `stream` (a hipStream_t; NULL = the null
+ * stream of the current device).  A, B, Y are device pointers to tensors of
+ * the planned shapes and type.  Returns after enqueueing; results are ready
+ * when the stream reaches this point.  Empty output: nothing is launched and
+ * the pointers may be NULL.  K == 0: A and B are not read (may be NULL) and Y
+ * is filled with zeros.  Otherwise NULL A, B or Y gives MM_ERR_NULL_ARG.
+ * Pointers need no particular alignment (16-byte aligned buffers take the
+ * vectorized kernels).  MM_ERR_HIP reports a failed launch or allocation. */
+mm_status mm_execute(mm_plan_t plan, const void *A, const void *B, void *Y, void *stream);
+
+/* Output shape: writes up to MM_MAX_RANK entries to `shape` and the rank to
+ * *rank (0 when both inputs are rank one). */
+mm_status mm_plan_output_shape(mm_plan_t plan, int64_t *shape, int *rank);
+
+/* Number of output elements (the Y buffer must hold this many), or -1 for a
+ * NULL plan. */
+int64_t mm_plan_output_numel(mm_plan_t plan);
+
+/* Selected algorithm (an mm_algo value), or -1 for a NULL plan. */
+int mm_plan_algo(mm_plan_t plan);
+
+/* Device workspace bytes the plan uses (0 unless SPLIT_K). */
+size_t mm_plan_workspace_bytes(mm_plan_t plan);
+
+/* Fill *info with everything the plan resolved. */
+mm_status mm_plan_get_info(mm_plan_t plan, mm_plan_info *info);
+
+/* Tile table of the tiled kernels for `dtype`: number of entries. */
+int mm_tile_count(int dtype);
+
+/* Entry `index` (0-based) of the tile table: block rows, block columns and
+ * K elements per LDS stage.  MM_ERR_BAD_OPTION for an invalid index. */
+mm_status mm_tile_config(int dtype, int index, int *block_m, int *block_n, int *block_k);
+
+/* Static description of a status code. */
+const char *mm_status_string(mm_status status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *mm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MM_H */

@@ -1,0 +1,258 @@
+"""ctypes binding of libmm.so (argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+``include/mm.h``; this module converts shapes and torch tensors to the plain
+pointers and sizes the ABI takes, and raises on error statuses.  There is no
+fallback: if ``libmm.so`` is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmm.so")
+
+FLOAT, FLOAT16, DOUBLE, BFLOAT16 = 1, 10, 11, 16
+MAX_BATCH_DIMS = 8
+MAX_RANK = MAX_BATCH_DIMS + 2
+
+ALGO_AUTO, ALGO_EMPTY, ALGO_ZERO_FILL, ALGO_DIRECT = 0, 1, 2, 3
+ALGO_SKINNY_M, ALGO_SKINNY_N, ALGO_SPLIT_K, ALGO_GENERAL = 4, 5, 6, 7
+ALGO_NAMES = {0: "auto", 1: "empty", 2: "zero_fill", 3: "direct", 4: "skinny_m", 5: "skinny_n",
+              6: "split_k", 7: "general"}
+
+ERR_NULL_ARG, ERR_RANK, ERR_NEG_DIM, ERR_K_MISMATCH, ERR_BROADCAST = 1, 2, 3, 4, 5
+ERR_DTYPE, ERR_BAD_OPTION, ERR_TOO_LARGE, ERR_ALLOC, ERR_HIP = 6, 7, 8, 9, 10
+
+
+class MMError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"mm status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class PlanOptions(ctypes.Structure):
+    _fields_ = [("force_algo", ctypes.c_int32), ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("algo", ctypes.c_int32),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("batch", ctypes.c_int64), ("kernel_m", ctypes.c_int64),
+        ("folded", ctypes.c_int32), ("batch_rank", ctypes.c_int32),
+        ("batch_dims", ctypes.c_int64 * MAX_BATCH_DIMS),
+        ("a_batch_strides", ctypes.c_int64 * MAX_BATCH_DIMS),
+        ("b_batch_strides", ctypes.c_int64 * MAX_BATCH_DIMS),
+        ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
+        ("k_chunk", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+        ("flops", ctypes.c_double), ("min_bytes", ctypes.c_double),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmm.so (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python -m onnx_broadcast_matmul_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        vp = ctypes.c_void_p
+        L.mm_plan_create.argtypes = [i64p, ctypes.c_int, i64p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
+        L.mm_plan_create.restype = ctypes.c_int
+        L.mm_plan_create_ex.argtypes = [i64p, ctypes.c_int, i64p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(PlanOptions), ctypes.POINTER(vp)]
+        L.mm_plan_create_ex.restype = ctypes.c_int
+        L.mm_plan_destroy.argtypes = [vp]
+        L.mm_plan_destroy.restype = None
+        L.mm_execute.argtypes = [vp, vp, vp, vp, vp]
+        L.mm_execute.restype = ctypes.c_int
+        L.mm_plan_output_shape.argtypes = [vp, i64p, ctypes.POINTER(ctypes.c_int)]
+        L.mm_plan_output_shape.restype = ctypes.c_int
+        L.mm_plan_output_numel.argtypes = [vp]
+        L.mm_plan_output_numel.restype = ctypes.c_int64
+        L.mm_plan_algo.argtypes = [vp]
+        L.mm_plan_algo.restype = ctypes.c_int
+        L.mm_plan_workspace_bytes.argtypes = [vp]
+        L.mm_plan_workspace_bytes.restype = ctypes.c_size_t
+        L.mm_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+        L.mm_plan_get_info.restype = ctypes.c_int
+        L.mm_tile_count.argtypes = [ctypes.c_int]
+        L.mm_tile_count.restype = ctypes.c_int
+        L.mm_tile_config.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+        L.mm_tile_config.restype = ctypes.c_int
+        L.mm_status_string.argtypes = [ctypes.c_int]
+        L.mm_status_string.restype = ctypes.c_char_p
+        L.mm_last_error.argtypes = []
+        L.mm_last_error.restype = ctypes.c_char_p
+        _lib = L
+        return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        detail = (L.mm_last_error() or b"").decode() or L.mm_status_string(status).decode()
+        raise MMError(status, detail)
+
+
+def _shape(shape: Sequence[int]):
+    return (ctypes.c_int64 * max(1, len(shape)))(*[int(d) for d in shape])
+
+
+def torch_dtype_code(dt) -> int:
+    import torch
+
+    codes = {torch.float32: FLOAT, torch.float16: FLOAT16, torch.bfloat16: BFLOAT16, torch.float64: DOUBLE}
+    if dt not in codes:
+        raise TypeError(f"unsupported tensor dtype {dt}")
+    return codes[dt]
+
+
+def torch_dtype(code: int):
+    import torch
+
+    return {FLOAT: torch.float32, FLOAT16: torch.float16, BFLOAT16: torch.bfloat16, DOUBLE: torch.float64}[code]
+
+
+def tile_configs(dtype: int):
+    L = lib()
+    out = []
+    for i in range(L.mm_tile_count(dtype)):
+        bm, bn, bk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _check(L.mm_tile_config(dtype, i, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(bk)))
+        out.append((bm.value, bn.value, bk.value))
+    return out
+
+
+class Plan:
+    """mm_plan_create / mm_execute / mm_plan_destroy for one (A shape, B shape, dtype)."""
+
+    def __init__(self, a_shape: Sequence[int], b_shape: Sequence[int], dtype: int, force_algo: int = 0,
+                 tile: int = 0, split_k: int = 0):
+        L = lib()
+        self._handle = ctypes.c_void_p()
+        self.a_shape = tuple(int(d) for d in a_shape)
+        self.b_shape = tuple(int(d) for d in b_shape)
+        self.dtype = int(dtype)
+        if force_algo or tile or split_k:
+            opt = PlanOptions(force_algo, tile, split_k, 0)
+            st = L.mm_plan_create_ex(_shape(self.a_shape), len(self.a_shape), _shape(self.b_shape),
+                                     len(self.b_shape), self.dtype, ctypes.byref(opt), ctypes.byref(self._handle))
+        else:
+            st = L.mm_plan_create(_shape(self.a_shape), len(self.a_shape), _shape(self.b_shape),
+                                  len(self.b_shape), self.dtype, ctypes.byref(self._handle))
+        _check(st)
+        self._lock = threading.Lock()
+
+    def close(self) -> None:
+        """mm_plan_destroy (the caller makes sure no execution is in flight)."""
+        h = getattr(self, "_handle", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.mm_plan_destroy(h)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._handle
+
+    @property
+    def output_shape(self) -> Tuple[int, ...]:
+        shp = (ctypes.c_int64 * MAX_RANK)()
+        rank = ctypes.c_int()
+        _check(lib().mm_plan_output_shape(self._handle, shp, ctypes.byref(rank)))
+        return tuple(shp[i] for i in range(rank.value))
+
+    @property
+    def output_numel(self) -> int:
+        return int(lib().mm_plan_output_numel(self._handle))
+
+    @property
+    def algo(self) -> int:
+        return int(lib().mm_plan_algo(self._handle))
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(lib().mm_plan_workspace_bytes(self._handle))
+
+    def info(self) -> dict:
+        inf = PlanInfo()
+        _check(lib().mm_plan_get_info(self._handle, ctypes.byref(inf)))
+        nb = inf.batch_rank
+        return {
+            "dtype": inf.dtype, "algo": inf.algo, "algo_name": ALGO_NAMES.get(inf.algo, "?"),
+            "M": inf.M, "N": inf.N, "K": inf.K, "batch": inf.batch, "kernel_m": inf.kernel_m,
+            "folded": bool(inf.folded), "batch_dims": tuple(inf.batch_dims[:nb]),
+            "a_batch_strides": tuple(inf.a_batch_strides[:nb]), "b_batch_strides": tuple(inf.b_batch_strides[:nb]),
+            "tile": inf.tile, "split_k": inf.split_k, "k_chunk": inf.k_chunk,
+            "workspace_bytes": inf.workspace_bytes, "flops": inf.flops, "min_bytes": inf.min_bytes,
+        }
+
+    def execute_ptr(self, A: int, B: int, Y: int, stream: int = 0) -> None:
+        """mm_execute on raw device pointers and a raw hipStream_t."""
+        _check(lib().mm_execute(self._handle, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(Y),
+                                ctypes.c_void_p(stream)))
+
+    def execute(self, A, B, Y, stream=None) -> None:
+        """mm_execute on torch device tensors; ``stream`` is a torch.cuda.Stream
+        (default: the current stream of Y's device)."""
+        import torch
+
+        want = torch_dtype(self.dtype)
+        for name, t, shape in (("A", A, self.a_shape), ("B", B, self.b_shape), ("Y", Y, self.output_shape)):
+            if t.dtype != want:
+                raise TypeError(f"{name} has dtype {t.dtype}, plan expects {want}")
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {tuple(shape)}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if t.numel() and not t.is_cuda:
+                raise ValueError(f"{name} must be a device tensor")
+        if stream is None:
+            stream = torch.cuda.current_stream(Y.device)
+        with self._lock:
+            self.execute_ptr(A.data_ptr(), B.data_ptr(), Y.data_ptr(), stream.cuda_stream)
+
+
+_plan_cache = {}
+_plan_cache_lock = threading.Lock()
+
+
+def matmul(A, B, out=None, stream=None):
+    """Y = MatMul(A, B) (ONNX semantics) on ``stream`` (default: the current
+    stream of A's device).  Plans are cached per (shapes, dtype, stream), so a
+    plan's split-K workspace is never shared by two streams."""
+    import torch
+
+    code = torch_dtype_code(A.dtype)
+    if B.dtype != A.dtype:
+        raise TypeError(f"mixed input types {A.dtype} and {B.dtype}")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    key = (tuple(A.shape), tuple(B.shape), code, A.device.index, stream.cuda_stream)
+    with _plan_cache_lock:
+        plan = _plan_cache.get(key)
+        if plan is None:
+            plan = Plan(A.shape, B.shape, code)
+            _plan_cache[key] = plan
+    if out is None:
+        out = torch.empty(plan.output_shape, dtype=A.dtype, device=A.device)
+    plan.execute(A, B, out, stream)
+    return out

@@ -1,0 +1,86 @@
+// device.h -- device-side helpers shared by the HIP kernels: element
+// conversions, the FP32 -> 16-bit narrowing epilogue, batch decoding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace mm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// FP32 -> BF16, round to nearest, ties to even; NaN stays a (quiet) NaN with
+// its sign, values beyond the largest finite BF16 round to infinity.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// FP32 -> FP16 with the hardware conversion (IEEE round to nearest even,
+// overflow to infinity, subnormals kept).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    _Float16 h = (_Float16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// Element traits by ONNX type code.
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<MM_FLOAT> {
+    using S = float;
+    static constexpr int kVE = 4;  // elements per 16 bytes
+    __device__ static __forceinline__ float to_f32(S x) { return x; }
+    __device__ static __forceinline__ S from_f32(float x) { return x; }
+};
+
+template <>
+struct Elem<MM_FLOAT16> {
+    using S = uint16_t;
+    static constexpr int kVE = 8;
+    __device__ static __forceinline__ float to_f32(S x) { return f16_to_f32(x); }
+    __device__ static __forceinline__ S from_f32(float x) { return f32_to_f16(x); }
+};
+
+template <>
+struct Elem<MM_BFLOAT16> {
+    using S = uint16_t;
+    static constexpr int kVE = 8;
+    __device__ static __forceinline__ float to_f32(S x) { return bf16_to_f32(x); }
+    __device__ static __forceinline__ S from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// Element offsets of the A and B matrices used by output batch `b`.
+__device__ __forceinline__ void batch_offsets(const BatchDesc &bd, int64_t b, int64_t &oa, int64_t &ob) {
+    oa = 0;
+    ob = 0;
+    for (int d = bd.nb - 1; d >= 0; --d) {
+        int64_t n = bd.dim[d];
+        int64_t i = b % n;
+        b /= n;
+        oa += i * bd.sa[d];
+        ob += i * bd.sb[d];
+    }
+}
+
+// Workgroups are dealt to the XCDs round-robin by their linear id.  Remap so
+// that each XCD receives a contiguous range of logical tile ids (neighbouring
+// tiles then share that XCD's L2).  Bijective on [0, n).
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
+    const int64_t per = n / kNumXCDs, rem = n % kNumXCDs;
+    const int64_t xcd = bid % kNumXCDs, local = bid / kNumXCDs;
+    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+}  // namespace mm

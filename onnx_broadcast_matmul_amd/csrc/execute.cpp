@@ -1,0 +1,112 @@
+// execute.cpp -- mm_execute / mm_plan_destroy: turn a plan into kernel
+// launches on the caller's stream.
+#include <string.h>
+
+#include "internal.h"
+#include "plan.h"
+
+using namespace mm;
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static mm_status hip_fail(hipError_t e, const char *what) {
+    return fail(MM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Split-K workspace: allocated once, on the device of the first execution.
+static mm_status ensure_workspace(mm_plan_s *p) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(p->ws_mutex);
+    if (p->ws) {
+        if (p->ws_device != dev)
+            return fail(MM_ERR_HIP, "plan workspace lives on device %d; executing on device %d needs its own plan",
+                        p->ws_device, dev);
+        return MM_OK;
+    }
+    void *ptr = nullptr;
+    e = hipMalloc(&ptr, (size_t)p->workspace_bytes);
+    if (e != hipSuccess) return fail(MM_ERR_ALLOC, "hipMalloc of %lld workspace bytes: %s",
+                                     (long long)p->workspace_bytes, hipGetErrorString(e));
+    p->ws = ptr;
+    p->ws_device = dev;
+    return MM_OK;
+}
+
+extern "C" {
+
+mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *stream) {
+    clear_error();
+    if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
+    if (p->algo == MM_ALGO_EMPTY) return MM_OK;
+    if (!Y) return fail(MM_ERR_NULL_ARG, "Y is NULL for a non-empty output");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (p->algo == MM_ALGO_ZERO_FILL) {
+        e = launch_fill_zero(p->dtype, Y, p->out_numel, s);
+        return e == hipSuccess ? MM_OK : hip_fail(e, "zero-fill launch");
+    }
+    if (!A || !B) return fail(MM_ERR_NULL_ARG, "A or B is NULL");
+
+    KArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = A;
+    a.B = B;
+    a.Y = Y;
+    a.W = nullptr;
+    a.M = p->kernel_m;
+    a.N = p->N;
+    a.K = p->K;
+    a.batch = p->batch;
+    a.kchunk = p->kchunk;
+    a.split = p->split;
+    a.bd = p->bd;
+
+    const int64_t es = elem_size(p->dtype);
+    Align al;
+    al.a = aligned16(A) && (p->K * es) % 16 == 0;
+    al.b = aligned16(B) && (p->N * es) % 16 == 0;
+    al.y = aligned16(Y) && (p->N * es) % 16 == 0;
+
+    switch (p->algo) {
+    case MM_ALGO_DIRECT:
+        e = launch_direct(p->dtype, a, s);
+        break;
+    case MM_ALGO_SKINNY_M:
+        e = launch_skinny_m(p->dtype, al, a, s);
+        break;
+    case MM_ALGO_SKINNY_N:
+        e = launch_skinny_n(p->dtype, al, a, s);
+        break;
+    case MM_ALGO_GENERAL:
+        e = launch_general(p->dtype, p->tile, al, false, a, s);
+        break;
+    case MM_ALGO_SPLIT_K: {
+        mm_status st = ensure_workspace(p);
+        if (st != MM_OK) return st;
+        a.W = (float *)p->ws;
+        e = launch_general(p->dtype, p->tile, al, true, a, s);
+        if (e == hipSuccess) e = launch_splitk_reduce(p->dtype, a, s);
+        break;
+    }
+    default:
+        return fail(MM_ERR_BAD_OPTION, "plan has no executable algorithm (%d)", p->algo);
+    }
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    return MM_OK;
+}
+
+void mm_plan_destroy(mm_plan_t p) {
+    if (!p) return;
+    if (p->ws) {
+        int cur = -1;
+        bool have_cur = hipGetDevice(&cur) == hipSuccess;
+        if (hipSetDevice(p->ws_device) == hipSuccess) (void)hipFree(p->ws);
+        if (have_cur) (void)hipSetDevice(cur);
+        p->ws = nullptr;
+    }
+    delete p;
+}
+
+}  // extern "C"

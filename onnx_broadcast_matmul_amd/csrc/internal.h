@@ -1,0 +1,72 @@
+// internal.h -- structures shared by the host plan layer and the HIP kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "mm.h"
+
+namespace mm {
+
+// Number of compute units the selector plans for (MI355X: 256 CUs in 8 XCDs).
+constexpr int kNumCUs = 256;
+constexpr int kNumXCDs = 8;
+
+// Collapsed batch description: output batch index b is unravelled row-major
+// over dim[0..nb); each operand's matrix starts at sum_d i_d * stride_d
+// elements.  A zero stride reads the same matrix for every index along that
+// dimension (broadcast without a copy).
+struct BatchDesc {
+    int32_t nb;
+    int32_t pad_;
+    int64_t dim[MM_MAX_BATCH_DIMS];
+    int64_t sa[MM_MAX_BATCH_DIMS];
+    int64_t sb[MM_MAX_BATCH_DIMS];
+};
+
+// Arguments of every kernel (passed by value).  M is the number of rows of
+// one product as the kernels see it (batch*M when A's batch is folded into
+// the rows).  Y is dense [batch][M][N]; W is the split-K workspace
+// [split][batch][M][N] in FP32.
+struct KArgs {
+    const void *A;
+    const void *B;
+    void *Y;
+    float *W;
+    int64_t M, N, K;
+    int64_t batch;
+    int64_t kchunk;
+    int32_t split;
+    int32_t pad_;
+    BatchDesc bd;
+};
+
+// Which operands allow 16-byte vector access: the base pointer is 16-byte
+// aligned and every row starts on a 16-byte boundary (A: K elements per row;
+// B and Y: N elements per row).
+struct Align {
+    bool a, b, y;
+};
+
+// Tile table entry of the tiled (MFMA) kernels.
+struct TileCfg {
+    int bm, bn;  // block tile
+    int wm, wn;  // wave tile (4 waves per block)
+};
+
+// Number of tile table entries and the entries, per element type.
+int tile_count(int dtype);
+const TileCfg *tile_entry(int dtype, int index);
+
+// Kernel launchers (defined in the .hip files).  All return hipSuccess or
+// the launch error.  `al` selects the 16-byte vectorized kernel variants
+// where the operands they stream allow it.
+hipError_t launch_direct(int dtype, const KArgs &a, hipStream_t s);
+hipError_t launch_fill_zero(int dtype, void *Y, int64_t n, hipStream_t s);
+hipError_t launch_general(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);
+hipError_t launch_splitk_reduce(int dtype, const KArgs &a, hipStream_t s);
+hipError_t launch_skinny_m(int dtype, const Align &al, const KArgs &a, hipStream_t s);
+hipError_t launch_skinny_n(int dtype, const Align &al, const KArgs &a, hipStream_t s);
+
+}  // namespace mm

@@ -1,0 +1,413 @@
+// plan.cpp -- host-side MatMul plan: shape resolution, broadcast strides,
+// batch collapsing/folding and algorithm selection.  No GPU call happens
+// here, so the whole layer is testable on a machine without a GPU.
+//
+// Page "MatMul Kernel Design", section "Shape and plan model": the plan
+// resolves the complete output shape before execution (rank-one promotion and
+// squeeze, multidirectional batch broadcasting, precomputed batch strides
+// with zeros for broadcast dimensions, empty outputs that read nothing).
+// Page "Gemm and MatMul Performance Roadmap", section "Phase 4: complete
+// MatMul": collapse contiguous batch dimensions, dispatch independent batches
+// together, dedicated kernels for M == 1 / N == 1.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "internal.h"
+#include "plan.h"
+#include "tiles.h"
+
+namespace mm {
+
+static thread_local std::string g_last_error;
+
+mm_status fail(mm_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int tile_count(int dtype) {
+    if (dtype == MM_FLOAT) return kNumTiles32;
+    if (dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) return kNumTiles16;
+    return 0;
+}
+
+const TileCfg *tile_entry(int dtype, int index) {
+    if (index < 0 || index >= tile_count(dtype)) return nullptr;
+    return dtype == MM_FLOAT ? &kTiles32[index] : &kTiles16[index];
+}
+
+int elem_size(int dtype) { return dtype == MM_FLOAT ? 4 : 2; }
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Relative per-CU throughput of a tile entry (bigger tiles reuse each LDS
+// byte more often); used only to rank entries against each other.
+static double tile_quality(int dtype, int index) {
+    static const double q16[kNumTiles16] = {1.0, 0.92, 0.8, 0.6, 0.45};
+    static const double q32[kNumTiles32] = {1.0, 0.9, 0.8};
+    return dtype == MM_FLOAT ? q32[index] : q16[index];
+}
+
+// Estimated useful fraction of the machine for a tile entry: wave
+// quantization over the CUs, tile padding at the edges, and tile quality.
+static double tile_score(int dtype, int index, int64_t batch, int64_t M, int64_t N) {
+    const TileCfg *t = tile_entry(dtype, index);
+    int64_t tm = cdiv(M, t->bm), tn = cdiv(N, t->bn);
+    double tiles = (double)batch * (double)tm * (double)tn;
+    double waves = ceil(tiles / kNumCUs);
+    double occ = tiles / (waves * kNumCUs);
+    double pad = ((double)M * (double)N) / ((double)(tm * t->bm) * (double)(tn * t->bn));
+    return occ * pad * tile_quality(dtype, index);
+}
+
+static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N) {
+    int best = 0;
+    double best_s = -1.0;
+    for (int i = 0; i < tile_count(dtype); ++i) {
+        double s = tile_score(dtype, i, batch, M, N);
+        if (s > best_s + 1e-9) {
+            best_s = s;
+            best = i;
+        }
+    }
+    return best;
+}
+
+// Smallest-padding tile for split-K (its output is tiny by construction).
+static int choose_split_tile(int dtype, int64_t M, int64_t N) {
+    int best = 0;
+    double best_pad = -1.0;
+    for (int i = 0; i < tile_count(dtype); ++i) {
+        const TileCfg *t = tile_entry(dtype, i);
+        double pad = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
+        if (pad > best_pad + 1e-9) {
+            best_pad = pad;
+            best = i;
+        }
+    }
+    return best;
+}
+
+// Resolve shapes, strides, collapse and fold into `p`.
+static mm_status resolve(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank,
+                         mm_plan_s *p) {
+    if (a_rank < 1 || b_rank < 1)
+        return fail(MM_ERR_RANK, "input rank must be >= 1 (got A rank %d, B rank %d)", a_rank, b_rank);
+    if (a_rank > MM_MAX_RANK || b_rank > MM_MAX_RANK)
+        return fail(MM_ERR_RANK, "input rank must be <= %d (got A rank %d, B rank %d)", MM_MAX_RANK,
+                    a_rank, b_rank);
+    for (int i = 0; i < a_rank; ++i)
+        if (a_shape[i] < 0) return fail(MM_ERR_NEG_DIM, "A dimension %d is negative (%lld)", i, (long long)a_shape[i]);
+    for (int i = 0; i < b_rank; ++i)
+        if (b_shape[i] < 0) return fail(MM_ERR_NEG_DIM, "B dimension %d is negative (%lld)", i, (long long)b_shape[i]);
+
+    p->a_rank = a_rank;
+    p->b_rank = b_rank;
+    memcpy(p->a_shape, a_shape, sizeof(int64_t) * a_rank);
+    memcpy(p->b_shape, b_shape, sizeof(int64_t) * b_rank);
+
+    // Rank-one promotion: A [K] -> [1, K]; B [K] -> [K, 1].
+    const bool a_vec = a_rank == 1, b_vec = b_rank == 1;
+    const int64_t M = a_vec ? 1 : a_shape[a_rank - 2];
+    const int64_t Ka = a_shape[a_rank - 1];
+    const int64_t Kb = b_vec ? b_shape[0] : b_shape[b_rank - 2];
+    const int64_t N = b_vec ? 1 : b_shape[b_rank - 1];
+    if (Ka != Kb)
+        return fail(MM_ERR_K_MISMATCH, "inner dimensions differ: A has K=%lld, B has K=%lld", (long long)Ka,
+                    (long long)Kb);
+    const int64_t K = Ka;
+    const int abr = a_vec ? 0 : a_rank - 2;  // batch ranks
+    const int bbr = b_vec ? 0 : b_rank - 2;
+    const int r = std::max(abr, bbr);
+    if (r > MM_MAX_BATCH_DIMS)
+        return fail(MM_ERR_RANK, "at most %d batch dimensions are supported", MM_MAX_BATCH_DIMS);
+
+    // Right-aligned broadcast of the batch dimensions, with dense row-major
+    // strides (in elements) of each operand, zero where it broadcasts.
+    int64_t da[MM_MAX_BATCH_DIMS], db[MM_MAX_BATCH_DIMS], dout[MM_MAX_BATCH_DIMS];
+    for (int d = 0; d < r; ++d) {
+        int ai = d - (r - abr), bi = d - (r - bbr);
+        da[d] = ai >= 0 ? a_shape[ai] : 1;
+        db[d] = bi >= 0 ? b_shape[bi] : 1;
+        if (da[d] == db[d]) dout[d] = da[d];
+        else if (da[d] == 1) dout[d] = db[d];
+        else if (db[d] == 1) dout[d] = da[d];
+        else
+            return fail(MM_ERR_BROADCAST, "batch dimension %d cannot be broadcast: A has %lld, B has %lld", d,
+                        (long long)da[d], (long long)db[d]);
+    }
+    int64_t sa[MM_MAX_BATCH_DIMS], sb[MM_MAX_BATCH_DIMS];
+    {
+        int64_t ma = M * K, mb = K * N;  // element stride of the innermost batch dim
+        for (int d = r - 1; d >= 0; --d) {
+            sa[d] = da[d] == 1 ? 0 : ma;
+            sb[d] = db[d] == 1 ? 0 : mb;
+            ma *= da[d];
+            mb *= db[d];
+        }
+    }
+
+    // Output shape: batch ++ [M unless A was rank one] ++ [N unless B was].
+    p->out_rank = 0;
+    int64_t batch = 1;
+    for (int d = 0; d < r; ++d) {
+        p->out_shape[p->out_rank++] = dout[d];
+        batch *= dout[d];
+    }
+    if (!a_vec) p->out_shape[p->out_rank++] = M;
+    if (!b_vec) p->out_shape[p->out_rank++] = N;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->out_numel = batch * M * N;
+    p->total_batch = batch;
+
+    // Collapse: drop size-1 dims, then merge neighbours whose strides stay
+    // linear for both operands.
+    BatchDesc bd;
+    memset(&bd, 0, sizeof(bd));
+    for (int d = 0; d < r; ++d) {
+        if (dout[d] == 1) continue;
+        if (bd.nb > 0) {
+            int q = bd.nb - 1;
+            // merging the new dim d into q: q's stride must equal stride_d * dim_d
+            if (bd.sa[q] == sa[d] * dout[d] && bd.sb[q] == sb[d] * dout[d]) {
+                bd.dim[q] *= dout[d];
+                bd.sa[q] = sa[d];
+                bd.sb[q] = sb[d];
+                continue;
+            }
+        }
+        bd.dim[bd.nb] = dout[d];
+        bd.sa[bd.nb] = sa[d];
+        bd.sb[bd.nb] = sb[d];
+        bd.nb++;
+    }
+    // Fold: B shared by every batch (all its strides zero) and A dense over
+    // the (single collapsed) batch dim -> one product with batch*M rows.
+    p->folded = 0;
+    p->kernel_m = M;
+    p->batch = batch;
+    if (bd.nb == 1 && bd.sb[0] == 0 && bd.sa[0] == M * K && batch > 1) {
+        p->folded = 1;
+        p->kernel_m = batch * M;
+        p->batch = 1;
+        bd.nb = 0;
+    }
+    if (batch == 0) bd.nb = 0;
+    p->bd = bd;
+    return MM_OK;
+}
+
+// Split count and chunk for SPLIT_K.
+static void plan_split(mm_plan_s *p, int requested) {
+    const int bk = stage_k(p->dtype);
+    const TileCfg *t = tile_entry(p->dtype, p->tile);
+    int64_t tiles = p->batch * cdiv(p->kernel_m, t->bm) * cdiv(p->N, t->bn);
+    int64_t kblocks = cdiv(p->K, bk);
+    int64_t s;
+    if (requested > 0) {
+        s = requested;
+    } else {
+        // Aim for about four workgroups per CU, with at least 512 K elements
+        // (eight LDS stages of FP32, or more of 16-bit) per partition.
+        int64_t want = cdiv(4 * (int64_t)kNumCUs, std::max<int64_t>(tiles, 1));
+        int64_t max_s = std::max<int64_t>(1, p->K / 512);
+        s = std::min(want, max_s);
+    }
+    s = std::max<int64_t>(1, std::min(s, kblocks));
+    int64_t chunk_blocks = cdiv(kblocks, s);
+    p->kchunk = chunk_blocks * bk;
+    p->split = (int32_t)cdiv(p->K, p->kchunk);
+    p->workspace_bytes = (int64_t)p->split * p->batch * p->kernel_m * p->N * (int64_t)sizeof(float);
+}
+
+static mm_status check_limits(const mm_plan_s *p) {
+    const int64_t lim = INT32_MAX;
+    if (p->kernel_m > lim || p->N > lim || p->K > lim || p->batch > lim)
+        return fail(MM_ERR_TOO_LARGE, "M, N, K and batch must each be below 2^31");
+    return MM_OK;
+}
+
+static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
+    const int64_t M = p->kernel_m, N = p->N, K = p->K;
+    p->tile = -1;
+    p->split = 1;
+    p->kchunk = K;
+    p->workspace_bytes = 0;
+    if (p->out_numel == 0) {
+        p->algo = MM_ALGO_EMPTY;
+        return MM_OK;
+    }
+    if (K == 0) {
+        p->algo = MM_ALGO_ZERO_FILL;
+        return MM_OK;
+    }
+    mm_status st = check_limits(p);
+    if (st != MM_OK) return st;
+
+    int algo = opt ? opt->force_algo : MM_ALGO_AUTO;
+    if (algo == MM_ALGO_AUTO) {
+        const double flops = 2.0 * (double)p->batch * M * N * K;
+        const TileCfg *big = tile_entry(p->dtype, 0);
+        const int64_t big_tiles = p->batch * cdiv(M, big->bm) * cdiv(N, big->bn);
+        const TileCfg *small = tile_entry(p->dtype, tile_count(p->dtype) - 1);
+        const int64_t small_tiles = p->batch * cdiv(M, small->bm) * cdiv(N, small->bn);
+        (void)big_tiles;
+        if (flops <= 16777216.0 && K <= 512) {
+            algo = MM_ALGO_DIRECT;  // tiny product with a short reduction: launch latency dominates
+        } else if (N < 16 && N <= M) {
+            algo = MM_ALGO_SKINNY_N;  // includes N == 1: never split-K
+        } else if (M < 16) {
+            algo = MM_ALGO_SKINNY_M;
+        } else if (small_tiles < kNumCUs / 2 && K >= 4096 && K >= 8 * std::max(M, N)) {
+            algo = MM_ALGO_SPLIT_K;  // tiles cannot fill the GPU; long K
+        } else {
+            algo = MM_ALGO_GENERAL;
+        }
+    }
+    if (algo < MM_ALGO_DIRECT || algo > MM_ALGO_GENERAL)
+        return fail(MM_ERR_BAD_OPTION, "force_algo %d is not a forcible algorithm", algo);
+    p->algo = algo;
+
+    if (algo == MM_ALGO_GENERAL || algo == MM_ALGO_SPLIT_K) {
+        int req = opt ? opt->tile : 0;
+        if (req < 0 || req > tile_count(p->dtype))
+            return fail(MM_ERR_BAD_OPTION, "tile %d out of range 0..%d", req, tile_count(p->dtype));
+        if (req > 0) p->tile = req - 1;
+        else if (algo == MM_ALGO_GENERAL) p->tile = choose_tile(p->dtype, p->batch, M, N);
+        else p->tile = choose_split_tile(p->dtype, M, N);
+        const TileCfg *t = tile_entry(p->dtype, p->tile);
+        const int64_t tiles = p->batch * cdiv(M, t->bm) * cdiv(N, t->bn);
+        if (algo == MM_ALGO_SPLIT_K) {
+            int sreq = opt ? opt->split_k : 0;
+            if (sreq < 0) return fail(MM_ERR_BAD_OPTION, "split_k %d is negative", sreq);
+            plan_split(p, sreq);
+        }
+        if (tiles * p->split > INT32_MAX)
+            return fail(MM_ERR_TOO_LARGE, "too many workgroups (%lld tiles x %d splits)", (long long)tiles,
+                        p->split);
+    }
+    return MM_OK;
+}
+
+}  // namespace mm
+
+using namespace mm;
+
+extern "C" {
+
+mm_status mm_plan_create_ex(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank,
+                            int dtype, const mm_plan_options *opt, mm_plan_t *out) {
+    clear_error();
+    if (!out) return fail(MM_ERR_NULL_ARG, "out is NULL");
+    *out = nullptr;
+    if ((!a_shape && a_rank > 0) || (!b_shape && b_rank > 0)) return fail(MM_ERR_NULL_ARG, "shape pointer is NULL");
+    if (dtype == MM_DOUBLE) return fail(MM_ERR_DTYPE, "DOUBLE is not supported yet");
+    if (dtype != MM_FLOAT && dtype != MM_FLOAT16 && dtype != MM_BFLOAT16)
+        return fail(MM_ERR_DTYPE, "unknown element type %d", dtype);
+    if (opt && opt->reserved != 0) return fail(MM_ERR_BAD_OPTION, "reserved option field must be 0");
+    mm_plan_s *p = new (std::nothrow) mm_plan_s();
+    if (!p) return fail(MM_ERR_ALLOC, "host allocation failed");
+    p->dtype = dtype;
+    mm_status st = resolve(a_shape, a_rank, b_shape, b_rank, p);
+    if (st == MM_OK) st = select_algo(p, opt);
+    if (st != MM_OK) {
+        delete p;
+        return st;
+    }
+    *out = p;
+    return MM_OK;
+}
+
+mm_status mm_plan_create(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank, int dtype,
+                         mm_plan_t *out) {
+    return mm_plan_create_ex(a_shape, a_rank, b_shape, b_rank, dtype, nullptr, out);
+}
+
+mm_status mm_plan_output_shape(mm_plan_t p, int64_t *shape, int *rank) {
+    if (!p || !rank || (!shape && p->out_rank > 0)) return fail(MM_ERR_NULL_ARG, "NULL argument");
+    for (int i = 0; i < p->out_rank; ++i) shape[i] = p->out_shape[i];
+    *rank = p->out_rank;
+    return MM_OK;
+}
+
+int64_t mm_plan_output_numel(mm_plan_t p) { return p ? p->out_numel : -1; }
+
+int mm_plan_algo(mm_plan_t p) { return p ? p->algo : -1; }
+
+size_t mm_plan_workspace_bytes(mm_plan_t p) { return p ? (size_t)p->workspace_bytes : 0; }
+
+mm_status mm_plan_get_info(mm_plan_t p, mm_plan_info *info) {
+    if (!p || !info) return fail(MM_ERR_NULL_ARG, "NULL argument");
+    memset(info, 0, sizeof(*info));
+    info->dtype = p->dtype;
+    info->algo = p->algo;
+    info->M = p->M;
+    info->N = p->N;
+    info->K = p->K;
+    info->batch = p->batch;
+    info->kernel_m = p->kernel_m;
+    info->folded = p->folded;
+    info->batch_rank = p->bd.nb;
+    for (int d = 0; d < p->bd.nb; ++d) {
+        info->batch_dims[d] = p->bd.dim[d];
+        info->a_batch_strides[d] = p->bd.sa[d];
+        info->b_batch_strides[d] = p->bd.sb[d];
+    }
+    info->tile = p->tile >= 0 ? p->tile + 1 : 0;
+    info->split_k = p->split;
+    info->k_chunk = p->kchunk;
+    info->workspace_bytes = p->workspace_bytes;
+    info->flops = 2.0 * (double)p->total_batch * (double)p->M * (double)p->N * (double)p->K;
+    int64_t na = 1, nb = 1;
+    for (int i = 0; i < p->a_rank; ++i) na *= p->a_shape[i];
+    for (int i = 0; i < p->b_rank; ++i) nb *= p->b_shape[i];
+    info->min_bytes = (double)elem_size(p->dtype) * ((double)na + (double)nb + (double)p->out_numel);
+    return MM_OK;
+}
+
+int mm_tile_count(int dtype) { return tile_count(dtype); }
+
+mm_status mm_tile_config(int dtype, int index, int *bm, int *bn, int *bk) {
+    const TileCfg *t = tile_entry(dtype, index);
+    if (!t) return fail(MM_ERR_BAD_OPTION, "no tile %d for dtype %d", index, dtype);
+    if (bm) *bm = t->bm;
+    if (bn) *bn = t->bn;
+    if (bk) *bk = stage_k(dtype);
+    return MM_OK;
+}
+
+const char *mm_status_string(mm_status s) {
+    switch (s) {
+    case MM_OK: return "ok";
+    case MM_ERR_NULL_ARG: return "null argument";
+    case MM_ERR_RANK: return "invalid rank";
+    case MM_ERR_NEG_DIM: return "negative dimension";
+    case MM_ERR_K_MISMATCH: return "inner dimension mismatch";
+    case MM_ERR_BROADCAST: return "batch dimensions not broadcastable";
+    case MM_ERR_DTYPE: return "unsupported element type";
+    case MM_ERR_BAD_OPTION: return "invalid option";
+    case MM_ERR_TOO_LARGE: return "size too large";
+    case MM_ERR_ALLOC: return "allocation failed";
+    case MM_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *mm_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// plan.h -- the plan object behind mm_plan_t.
+#pragma once
+
+#include <stdarg.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "internal.h"
+
+struct mm_plan_s {
+    int dtype = 0;
+    int a_rank = 0, b_rank = 0;
+    int64_t a_shape[MM_MAX_RANK] = {};
+    int64_t b_shape[MM_MAX_RANK] = {};
+    int out_rank = 0;
+    int64_t out_shape[MM_MAX_RANK] = {};
+    int64_t out_numel = 0;
+    int64_t M = 0, N = 0, K = 0;  // promoted sizes of one product
+    int64_t total_batch = 0;      // broadcast batch count before folding
+    int64_t batch = 0;            // products launched (1 when folded)
+    int64_t kernel_m = 0;         // rows per launched product
+    int folded = 0;
+    mm::BatchDesc bd = {};
+    int algo = MM_ALGO_EMPTY;
+    int tile = -1;  // tile table index (tiled algorithms)
+    int32_t split = 1;
+    int64_t kchunk = 0;
+    int64_t workspace_bytes = 0;
+
+    // Device workspace for split-K, allocated on first execution.
+    std::mutex ws_mutex;
+    void *ws = nullptr;
+    int ws_device = -1;
+};
+
+namespace mm {
+mm_status fail(mm_status st, const char *fmt, ...);
+void clear_error();
+int elem_size(int dtype);
+}  // namespace mm

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP kernels behind the C ABI against the fp64 CPU oracle.
+
+Tolerances (oracle/compare.py): FP32 max|y-o| <= 1e-4*sqrt(K)*max|A|*max|B|;
+FP16/BF16 within 2 ulp of the narrowed oracle value (or the FP32 rule for
+results near zero); bit-exact on small-integer-valued inputs.  Every
+algorithm is forced on every element type over shapes that span several
+tiles and ragged tails, plus broadcast, rank-one, empty, K == 0, unaligned
+and special-value cases, and the full-size workload products on sampled
+outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.compare import abs_max, check
+from onnx_broadcast_matmul_amd import binding as mm
+from onnx_broadcast_matmul_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+DTYPES = [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16]
+DT_IDS = {mm.FLOAT: "fp32", mm.FLOAT16: "fp16", mm.BFLOAT16: "bf16"}
+ALGOS = [mm.ALGO_DIRECT, mm.ALGO_SKINNY_M, mm.ALGO_SKINNY_N, mm.ALGO_SPLIT_K, mm.ALGO_GENERAL]
+U1 = ("uniform", -1.0, 1.0)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mm.lib()  # the native library must load: no fallback exists
+    return torch.device("cuda:0")
+
+
+def _sentinel(shape, dt, dev):
+    # NaN everywhere, so an output the kernels never write fails the check
+    return torch.full(shape, float("nan"), dtype=mm.torch_dtype(dt), device=dev)
+
+
+def run_plan(plan, a, b, dt, dev):
+    A = synth.as_torch(a, dt).to(dev)
+    B = synth.as_torch(b, dt).to(dev)
+    Y = _sentinel(plan.output_shape, dt, dev)
+    plan.execute(A, B, Y)
+    torch.cuda.synchronize()
+    return Y
+
+
+def parity(sa, sb, dt, dev, algo=0, tile=0, split=0, dist=U1, seed=0, exact=False):
+    a = synth.generate(sa, dt, dist, [seed, 0])
+    b = synth.generate(sb, dt, dist, [seed, 1])
+    plan = mm.Plan(sa, sb, dt, force_algo=algo, tile=tile, split_k=split)
+    if algo:
+        assert plan.algo == algo
+    Y = run_plan(plan, a, b, dt, dev)
+    o = oracle.matmul(a, b, dt)
+    assert tuple(Y.shape) == o.shape
+    rep = check(synth.from_torch(Y), o, dt, sa[-1], abs_max(a, dt), abs_max(b, dt), exact=exact)
+    assert rep.ok, f"{sa} x {sb} {DT_IDS[dt]} algo={mm.ALGO_NAMES[plan.algo]} tile={plan.info()['tile']}: {rep}"
+    return plan, Y, rep
+
+
+RAGGED = [
+    ((300, 520), (520, 200)),          # several tiles, ragged M/N tails, 16-byte rows
+    ((67, 77), (77, 19)),              # odd sizes: element-wise loads
+    ((2, 3, 33, 40), (40, 24)),        # batch folded into M (B shared)
+    ((3, 1, 17, 64), (2, 64, 48)),     # both operands broadcast
+    ((5, 130), (130, 3)),              # tiny N
+    ((2, 1, 1000), (2, 1000, 72)),     # M == 1 per batch, K tail vs 64-wide stages
+]
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+@pytest.mark.parametrize("sa,sb", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_forced_algorithms(sa, sb, dt, algo, dev):
+    parity(sa, sb, dt, dev, algo=algo)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+def test_every_tile(dt, dev):
+    for t in range(1, len(mm.tile_configs(dt)) + 1):
+        parity((300, 520), (520, 200), dt, dev, algo=mm.ALGO_GENERAL, tile=t, seed=t)
+        parity((2, 1, 96, 1000), (3, 1000, 72), dt, dev, algo=mm.ALGO_GENERAL, tile=t, seed=t)
+        parity((3, 250, 770), (770, 130), dt, dev, algo=mm.ALGO_SPLIT_K, tile=t, split=5, seed=t)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+def test_small_integer_bit_exact(dt, algo, dev):
+    parity((2, 130, 1000), (1000, 70), dt, dev, algo=algo, dist=("int",), exact=True)
+    parity((70, 333), (333, 9), dt, dev, algo=algo, dist=("int",), exact=True)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("algo", [0] + ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+def test_broadcast_equals_materialized(dt, algo, dev):
+    """Zero-stride broadcast reads give bitwise the same result as an
+    explicitly repeated batch under the same kernel."""
+    sa, sb = (3, 1, 64, 96), (1, 4, 96, 80)
+    a = synth.generate(sa, dt, U1, [7, 0])
+    b = synth.generate(sb, dt, U1, [7, 1])
+    ar = np.ascontiguousarray(np.broadcast_to(a, (3, 4, 64, 96)))
+    br = np.ascontiguousarray(np.broadcast_to(b, (3, 4, 96, 80)))
+    p1 = mm.Plan(sa, sb, dt, force_algo=algo)
+    p2 = mm.Plan(ar.shape, br.shape, dt, force_algo=p1.algo, tile=p1.info()["tile"])
+    y1 = synth.from_torch(run_plan(p1, a, b, dt, dev))
+    y2 = synth.from_torch(run_plan(p2, ar, br, dt, dev))
+    assert np.array_equal(y1.view(np.uint8), y2.view(np.uint8))
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+def test_rank_one(dt, dev):
+    K = 96
+    _, yv, _ = parity((K,), (K, 80), dt, dev)
+    assert tuple(yv.shape) == (80,)
+    _, ym, _ = parity((4, 64, K), (K,), dt, dev)
+    assert tuple(ym.shape) == (4, 64)
+    _, ys, _ = parity((K,), (K,), dt, dev)
+    assert tuple(ys.shape) == ()
+    _, yb, _ = parity((K,), (3, K, 40), dt, dev)
+    assert tuple(yb.shape) == (3, 40)
+    for algo in ALGOS:
+        a = synth.generate((K,), dt, U1, [3, 0])
+        b = synth.generate((K, 80), dt, U1, [3, 1])
+        y1 = synth.from_torch(run_plan(mm.Plan((K,), (K, 80), dt, force_algo=algo), a, b, dt, dev))
+        y2 = synth.from_torch(run_plan(mm.Plan((1, K), (K, 80), dt, force_algo=algo), a[None, :], b, dt, dev))
+        assert np.array_equal(y1.view(np.uint8), y2.reshape(-1).view(np.uint8))
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+def test_empty_and_zero_k(dt, dev):
+    for sa, sb in [((3, 0, 5), (5, 4)), ((0, 4, 5), (1, 5, 6)), ((4, 5), (5, 0))]:
+        plan = mm.Plan(sa, sb, dt)
+        assert plan.algo == mm.ALGO_EMPTY and plan.output_numel == 0
+        plan.execute_ptr(0, 0, 0)  # launches nothing, reads nothing
+    for sa, sb in [((3, 4, 0), (0, 5)), ((0,), (0, 7)), ((2, 1, 6, 0), (3, 0, 2))]:
+        plan = mm.Plan(sa, sb, dt)
+        assert plan.algo == mm.ALGO_ZERO_FILL
+        Y = _sentinel(plan.output_shape, dt, dev)
+        plan.execute_ptr(0, 0, Y.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.all(Y == 0).item()
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+def test_deterministic(dt, algo, dev):
+    sa, sb = (2, 200, 700), (700, 150)
+    a = synth.generate(sa, dt, U1, [11, 0])
+    b = synth.generate(sb, dt, U1, [11, 1])
+    plan = mm.Plan(sa, sb, dt, force_algo=algo)
+    y1 = synth.from_torch(run_plan(plan, a, b, dt, dev))
+    y2 = synth.from_torch(run_plan(plan, a, b, dt, dev))
+    assert np.array_equal(y1.view(np.uint8), y2.view(np.uint8))
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+def test_unaligned_pointers(dt, algo, dev):
+    """Operands that start one element past a 16-byte boundary take the
+    element-wise load paths."""
+    sa, sb = (96, 256), (256, 64)
+    a = synth.generate(sa, dt, U1, [13, 0])
+    b = synth.generate(sb, dt, U1, [13, 1])
+    plan = mm.Plan(sa, sb, dt, force_algo=algo)
+    A = torch.empty(a.size + 1, dtype=mm.torch_dtype(dt), device=dev)[1:].view(sa)
+    B = torch.empty(b.size + 1, dtype=mm.torch_dtype(dt), device=dev)[1:].view(sb)
+    A.copy_(synth.as_torch(a, dt).to(dev))
+    B.copy_(synth.as_torch(b, dt).to(dev))
+    Yb = torch.full((96 * 64 + 1,), float("nan"), dtype=mm.torch_dtype(dt), device=dev)
+    Y = Yb[1:].view(96, 64)
+    plan.execute(A, B, Y)
+    torch.cuda.synchronize()
+    rep = check(synth.from_torch(Y), oracle.matmul(a, b, dt), dt, 256, abs_max(a, dt), abs_max(b, dt))
+    assert rep.ok, str(rep)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+def test_special_values(dt, algo, dev):
+    """An infinity or NaN in A reaches exactly the outputs of its row, as in
+    the oracle (NaN stays NaN through the narrowing)."""
+    sa, sb = (40, 128), (128, 24)
+    a = synth.generate(sa, dt, U1, [17, 0])
+    b = synth.generate(sb, dt, U1, [17, 1])
+    inf_bits = {mm.FLOAT: np.float32(np.inf), mm.FLOAT16: np.uint16(0x7C00), mm.BFLOAT16: np.uint16(0x7F80)}[dt]
+    nan_bits = {mm.FLOAT: np.float32(np.nan), mm.FLOAT16: np.uint16(0x7E00), mm.BFLOAT16: np.uint16(0x7FC0)}[dt]
+    a[3, 5] = inf_bits
+    a[7, 9] = nan_bits
+    plan = mm.Plan(sa, sb, dt, force_algo=algo)
+    Y = run_plan(plan, a, b, dt, dev)
+    o = oracle.matmul(a, b, dt)
+    finite = np.isfinite(oracle.decode(a, dt) if dt != mm.FLOAT else a)
+    rep = check(synth.from_torch(Y), o, dt, 128, float(np.abs(oracle.decode(a, dt) if dt != mm.FLOAT else a)[finite].max()),
+                abs_max(b, dt))
+    assert rep.ok, str(rep)
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def _sample_indices(shape, n, rng):
+    total = int(np.prod(shape, dtype=np.int64)) if len(shape) else 1
+    idx = rng.choice(total, size=min(n, total), replace=False)
+    # always include the first and last elements (corners of the last tile)
+    return np.unique(np.concatenate([idx, [0, total - 1]]))
+
+
+@pytest.mark.parametrize("product", synth.all_products(), ids=lambda p: p.name)
+def test_workload_full_size(product, dev):
+    """Each workload product at full size in the configuration the benchmark
+    times (the plan's own choice), checked on sampled outputs against the
+    oracle and on every output for finiteness."""
+    print(f"\n[full-size] {product.name} {product.a_shape} x {product.b_shape}", flush=True)
+    a, b = product.make()
+    dt = product.dtype
+    plan = mm.Plan(product.a_shape, product.b_shape, dt)
+    Y = run_plan(plan, a, b, dt, dev)
+    y = synth.from_torch(Y)
+    assert torch.isfinite(Y.float()).all().item()
+    rng = np.random.default_rng(1234)
+    idx = _sample_indices(plan.output_shape, 3000, rng)
+    o = oracle.matmul_at(a, b, dt, idx)
+    rep = check(y.reshape(-1)[idx], o, dt, product.K, abs_max(a, dt), abs_max(b, dt))
+    print(f"[full-size] {product.name} algo={mm.ALGO_NAMES[plan.algo]} {rep}", flush=True)
+    assert rep.ok, str(rep)

@@ -1,0 +1,258 @@
+"""CPU tests of the C ABI: exported symbols, shape resolution against numpy,
+every error path, broadcast strides / collapse / fold, and the algorithm
+selector.  Plan creation makes no GPU call, so none of this needs a GPU."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+from onnx_broadcast_matmul_amd import binding as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not os.path.exists(mm.LIB_PATH):
+        from onnx_broadcast_matmul_amd import build
+
+        build.build()
+    return mm.lib()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "mm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(mm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    names = _declared_functions()
+    assert "mm_plan_create" in names and "mm_execute" in names and len(names) >= 13
+    lib = ctypes.CDLL(mm.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def _try_plan(sa, sb, dtype=mm.FLOAT, **kw):
+    try:
+        return mm.Plan(sa, sb, dtype, **kw), None
+    except mm.MMError as e:
+        return None, e.status
+
+
+def test_output_shapes_match_numpy_exhaustive():
+    dims = (0, 1, 2, 3)
+    shapes = [s for r in range(1, 5) for s in itertools.product(dims, repeat=r)]
+    zeros = {s: np.zeros(s, dtype=np.float32) for s in shapes}
+    for sa in shapes:
+        for sb in shapes:
+            try:
+                want = np.matmul(zeros[sa], zeros[sb]).shape
+            except ValueError:
+                want = None
+            plan, st = _try_plan(sa, sb)
+            if want is None:
+                assert plan is None and st in (mm.ERR_K_MISMATCH, mm.ERR_BROADCAST), (sa, sb, st)
+            else:
+                assert plan is not None, (sa, sb, st)
+                assert plan.output_shape == want, (sa, sb)
+                assert plan.output_numel == int(np.prod(want, dtype=np.int64))
+                n = plan.output_numel
+                assert plan.algo == (mm.ALGO_EMPTY if n == 0 else mm.ALGO_ZERO_FILL if sa[-1] == 0 else plan.algo)
+
+
+@pytest.mark.parametrize("sa,sb,dtype,status", [
+    ((), (3, 4), mm.FLOAT, mm.ERR_RANK),
+    ((3, 4), (), mm.FLOAT, mm.ERR_RANK),
+    ((1,) * 11, (1, 1), mm.FLOAT, mm.ERR_RANK),
+    ((2, -1), (3, 4), mm.FLOAT, mm.ERR_NEG_DIM),
+    ((2, 3), (3, -4), mm.FLOAT, mm.ERR_NEG_DIM),
+    ((2, 3), (4, 5), mm.FLOAT, mm.ERR_K_MISMATCH),
+    ((2, 2, 3), (3, 3, 4), mm.FLOAT, mm.ERR_BROADCAST),
+    ((0, 2, 3), (2, 3, 4), mm.FLOAT, mm.ERR_BROADCAST),
+    ((2, 3), (3, 4), mm.DOUBLE, mm.ERR_DTYPE),
+    ((2, 3), (3, 4), 7, mm.ERR_DTYPE),
+])
+def test_plan_errors(sa, sb, dtype, status):
+    plan, st = _try_plan(sa, sb, dtype)
+    assert plan is None and st == status
+    assert mm.lib().mm_last_error()
+
+
+def test_rank_limit_accepts_eight_batch_dims():
+    plan, st = _try_plan((2,) * 8 + (3, 4), (4, 5))
+    assert st is None and plan.output_shape == (2,) * 8 + (3, 5)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(force_algo=mm.ALGO_EMPTY), mm.ERR_BAD_OPTION),
+    (dict(force_algo=99), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_GENERAL, tile=99), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_SPLIT_K, split_k=-1), mm.ERR_BAD_OPTION),
+])
+def test_option_errors(kw, status):
+    plan, st = _try_plan((64, 64), (64, 64), mm.FLOAT, **kw)
+    assert plan is None and st == status
+
+
+def test_reserved_option_rejected():
+    L = mm.lib()
+    h = ctypes.c_void_p()
+    opt = mm.PlanOptions(0, 0, 0, 1)
+    st = L.mm_plan_create_ex(mm._shape((4, 4)), 2, mm._shape((4, 4)), 2, mm.FLOAT, ctypes.byref(opt),
+                             ctypes.byref(h))
+    assert st == mm.ERR_BAD_OPTION and not h.value
+
+
+def test_null_arguments():
+    L = mm.lib()
+    st = L.mm_plan_create(mm._shape((4, 4)), 2, mm._shape((4, 4)), 2, mm.FLOAT, None)
+    assert st == mm.ERR_NULL_ARG
+    assert L.mm_execute(None, None, None, None, None) == mm.ERR_NULL_ARG
+    assert L.mm_plan_output_numel(None) == -1
+    assert L.mm_plan_algo(None) == -1
+    L.mm_plan_destroy(None)  # NULL is ignored
+    shp = (ctypes.c_int64 * mm.MAX_RANK)()
+    rank = ctypes.c_int()
+    assert L.mm_plan_output_shape(None, shp, ctypes.byref(rank)) == mm.ERR_NULL_ARG
+
+
+def test_execute_without_gpu_paths():
+    """Empty outputs launch nothing (NULL pointers allowed); a non-empty
+    output with NULL pointers is refused before any GPU call."""
+    empty = mm.Plan((3, 0, 5), (5, 4), mm.FLOAT)
+    assert empty.algo == mm.ALGO_EMPTY
+    empty.execute_ptr(0, 0, 0)
+    zero_k = mm.Plan((3, 4, 0), (0, 5), mm.FLOAT)
+    assert zero_k.algo == mm.ALGO_ZERO_FILL
+    with pytest.raises(mm.MMError) as e:
+        zero_k.execute_ptr(0, 0, 0)
+    assert e.value.status == mm.ERR_NULL_ARG
+    p = mm.Plan((3, 4, 5), (5, 6), mm.FLOAT)
+    with pytest.raises(mm.MMError) as e:
+        p.execute_ptr(0, 0, 1 << 20)
+    assert e.value.status == mm.ERR_NULL_ARG
+
+
+def test_status_strings():
+    L = mm.lib()
+    for s in range(11):
+        assert L.mm_status_string(s)
+
+
+@pytest.mark.parametrize("sa,sb,dims,sa_str,sb_str,folded,kernel_m", [
+    ((8, 1, 512, 512), (1, 6, 512, 512), (8, 6), (262144, 0), (0, 262144), False, 512),
+    ((2, 3, 4, 5, 6), (6, 7), (), (), (), True, 120),
+    ((2, 1, 5, 6), (3, 6, 7), (2, 3), (30, 0), (0, 42), False, 5),
+    ((2, 3, 5, 6), (2, 3, 6, 7), (6,), (30,), (42,), False, 5),
+    ((1, 1, 5, 6), (6, 7), (), (), (), False, 5),
+    ((6,), (2, 3, 6, 7), (6,), (0,), (42,), False, 1),
+    ((4, 1, 2, 5, 6), (3, 2, 6, 7), (4, 3, 2), (60, 0, 30), (0, 84, 42), False, 5),
+    ((4, 3, 2, 5, 6), (1, 1, 6, 7), (), (), (), True, 120),
+    ((4, 1, 2, 5, 6), (1, 1, 6, 7), (), (), (), True, 40),
+    ((2, 5, 6), (6,), (), (), (), True, 10),
+    ((16, 512, 4096), (4096, 11008), (), (), (), True, 8192),
+])
+def test_strides_collapse_fold(sa, sb, dims, sa_str, sb_str, folded, kernel_m):
+    info = mm.Plan(sa, sb, mm.BFLOAT16).info()
+    assert info["batch_dims"] == dims
+    assert info["a_batch_strides"] == sa_str
+    assert info["b_batch_strides"] == sb_str
+    assert info["folded"] == folded
+    assert info["kernel_m"] == kernel_m
+
+
+def _plan_walk_matches_broadcast(sa, sb):
+    """The collapsed (dims, strides) must address exactly the matrices
+    numpy's broadcasting pairs up, in output batch order."""
+    info = mm.Plan(sa, sb, mm.FLOAT).info()
+    M, N, K = info["M"], info["N"], info["K"]
+    a_idx = np.arange(int(np.prod(sa)) // (M * K) if len(sa) > 1 else 1).reshape(sa[:-2] or (1,))
+    b_idx = np.arange(int(np.prod(sb)) // (K * N) if len(sb) > 1 else 1).reshape(sb[:-2] or (1,))
+    bshape = np.broadcast_shapes(a_idx.shape, b_idx.shape)
+    ea = np.broadcast_to(a_idx, bshape).reshape(-1) * M * K
+    eb = np.broadcast_to(b_idx, bshape).reshape(-1) * K * N
+    if info["folded"]:
+        assert np.all(eb == 0) and np.array_equal(ea, np.arange(ea.size) * M * K)
+        return
+    dims = info["batch_dims"]
+    oa, ob = [], []
+    for idx in itertools.product(*[range(d) for d in dims]):
+        oa.append(sum(i * s for i, s in zip(idx, info["a_batch_strides"])))
+        ob.append(sum(i * s for i, s in zip(idx, info["b_batch_strides"])))
+    if not dims:
+        oa, ob = [0], [0]
+    assert np.array_equal(np.array(oa), ea) and np.array_equal(np.array(ob), eb)
+
+
+def test_collapsed_walk_equals_numpy_broadcast():
+    dims = (1, 2, 3)
+    for ra in range(2, 5):
+        for rb in range(2, 5):
+            for ba in itertools.product(dims, repeat=ra - 2):
+                for bb in itertools.product(dims, repeat=rb - 2):
+                    try:
+                        np.broadcast_shapes(ba, bb)
+                    except ValueError:
+                        continue
+                    _plan_walk_matches_broadcast(ba + (2, 3), bb + (3, 4))
+
+
+SELECTOR_CASES = [
+    # workload products and the algorithm the selector must pick
+    ((4, 64, 96), (96, 80), mm.FLOAT, "direct"),
+    ((96,), (96, 80), mm.FLOAT, "direct"),
+    ((4, 64, 96), (96,), mm.FLOAT, "direct"),
+    ((1024, 1024), (1024, 1024), mm.FLOAT, "general"),
+    ((8, 1, 512, 512), (1, 6, 512, 512), mm.FLOAT, "general"),
+    ((16, 512, 4096), (4096, 11008), mm.BFLOAT16, "general"),
+    ((32, 1, 4096), (32, 4096, 4096), mm.FLOAT16, "skinny_m"),
+    ((8192, 4096), (4096, 8), mm.FLOAT16, "skinny_n"),
+    ((64, 131072), (131072, 64), mm.FLOAT, "split_k"),
+    ((4, 32, 2048, 128), (4, 32, 128, 2048), mm.BFLOAT16, "general"),
+    ((4, 32, 2048, 2048), (4, 32, 2048, 128), mm.BFLOAT16, "general"),
+    ((1024, 1024), (1024, 1), mm.FLOAT, "skinny_n"),       # N == 1 never goes to split-K
+    ((1, 1 << 20), (1 << 20, 1), mm.FLOAT, "skinny_n"),
+    ((3, 0, 5), (5, 4), mm.FLOAT, "empty"),
+    ((3, 4, 0), (0, 5), mm.FLOAT, "zero_fill"),
+]
+
+
+@pytest.mark.parametrize("sa,sb,dt,algo", SELECTOR_CASES)
+def test_selector(sa, sb, dt, algo):
+    assert mm.ALGO_NAMES[mm.Plan(sa, sb, dt).algo] == algo
+
+
+def test_tile_table():
+    t16 = mm.tile_configs(mm.BFLOAT16)
+    t32 = mm.tile_configs(mm.FLOAT)
+    assert t16 == mm.tile_configs(mm.FLOAT16)
+    assert all(bk == 64 for _, _, bk in t16) and all(bk == 32 for _, _, bk in t32)
+    assert (256, 256, 64) in t16
+    for dt, table in ((mm.BFLOAT16, t16), (mm.FLOAT, t32)):
+        for i in range(len(table)):
+            info = mm.Plan((300, 200), (200, 100), dt, force_algo=mm.ALGO_GENERAL, tile=i + 1).info()
+            assert info["tile"] == i + 1
+
+
+def test_split_plan():
+    info = mm.Plan((64, 1000), (1000, 64), mm.FLOAT, force_algo=mm.ALGO_SPLIT_K, split_k=3).info()
+    assert info["algo_name"] == "split_k"
+    assert info["k_chunk"] % 32 == 0 and info["split_k"] == 3
+    assert info["k_chunk"] * (info["split_k"] - 1) < 1000 <= info["k_chunk"] * info["split_k"]
+    assert info["workspace_bytes"] == 3 * 64 * 64 * 4
+    # more partitions than K stages: clamped so none is empty
+    info = mm.Plan((8, 100), (100, 8), mm.BFLOAT16, force_algo=mm.ALGO_SPLIT_K, split_k=50).info()
+    assert info["split_k"] == 2 and info["k_chunk"] == 64
+    auto = mm.Plan((64, 131072), (131072, 64), mm.FLOAT).info()
+    assert auto["split_k"] >= 2 and auto["k_chunk"] >= 512
+
+
+def test_info_flops_bytes():
+    info = mm.Plan((8, 1, 512, 512), (1, 6, 512, 512), mm.FLOAT).info()
+    assert info["flops"] == 2.0 * 48 * 512 ** 3
+    assert info["min_bytes"] == 4.0 * (8 * 512 * 512 + 6 * 512 * 512 + 48 * 512 * 512)
