@@ -1,0 +1,277 @@
+"""Benchmark of the MI355X ONNX MatMul library.
+
+One step = one pass of the headline workload (FP32 square [1024,1024]^2 plus
+the batch-broadcast [8,1,512,512] x [1,6,512,512]) through mm_execute, with
+inputs resident in HBM and rotated over enough copies that no step finds
+them in the 256 MB Infinity Cache.  The JSON line also carries:
+
+* ``roofline``: the dominant kernel's algorithmic FLOPs per launch divided by
+  its average launch time, measured with HIP events on the launch stream over
+  the timed region, against the FP32 MFMA peak;
+* ``cases``: every other workload product timed the same way (TFLOP/s,
+  HBM GB/s and the fraction of its own roofline);
+* ``cpu_baseline``: the fp64 CPU oracle timed on a bounded random sample of
+  the headline workload's outputs on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cases]
+       [--no-cpu] [--cpu-seconds S] [--only NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from onnx_broadcast_matmul_amd import binding as mm  # noqa: E402
+from onnx_broadcast_matmul_amd import synth  # noqa: E402
+
+HEADLINE = "fp32_square_and_batched_broadcast"
+# MI355X published peaks: HBM3E 8 TB/s; dense MFMA FP32 157.3 TFLOP/s,
+# FP16/BF16 2.5 PFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP/clk = 2516.6).
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {mm.FLOAT: 157.3, mm.FLOAT16: 2516.6, mm.BFLOAT16: 2516.6}
+ROTATE_BYTES = 1 << 30  # rotate input/output copies until a step touches >= 1 GiB
+MAX_COPIES = 16
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Case:
+    """One workload product on the device, with rotated buffer copies."""
+
+    def __init__(self, product: synth.Product, dev):
+        import torch
+
+        self.p = product
+        self.dt = product.dtype
+        self.plan = mm.Plan(product.a_shape, product.b_shape, self.dt)
+        self.info = self.plan.info()
+        a, b = product.make()
+        A = synth.as_torch(a, self.dt).to(dev)
+        B = synth.as_torch(b, self.dt).to(dev)
+        del a, b
+        tdt = mm.torch_dtype(self.dt)
+        self.bytes = self.info["min_bytes"]
+        self.flops = self.info["flops"]
+        self.copies = int(min(MAX_COPIES, max(1, math.ceil(ROTATE_BYTES / max(self.bytes, 1)))))
+        self.A = [A] + [A.clone() for _ in range(self.copies - 1)]
+        self.B = [B] + [B.clone() for _ in range(self.copies - 1)]
+        self.Y = [torch.empty(self.plan.output_shape, dtype=tdt, device=dev) for _ in range(self.copies)]
+        self.ptrs = [(self.A[i].data_ptr(), self.B[i].data_ptr(), self.Y[i].data_ptr()) for i in range(self.copies)]
+        self.bound = "hbm" if self.flops / self.bytes < MFMA_PEAK_TFLOPS[self.dt] * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+
+    def run(self, i: int, stream: int) -> None:
+        a, b, y = self.ptrs[i % self.copies]
+        self.plan.execute_ptr(a, b, y, stream)
+
+
+def time_cases(cases, steps: int, warmup: int):
+    """Run `steps` steps (each step: every case once), bracketed by device
+    synchronisation, with an event pair around every launch.  Returns the
+    step time in ms and per-case lists of launch durations in ms."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for w in range(warmup):
+        for c in cases:
+            c.run(w, sp)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for _ in cases]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(steps):
+        for ci, c in enumerate(cases):
+            ev[ci][k][0].record(stream)
+            c.run(warmup + k, sp)
+            ev[ci][k][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    ms = start.elapsed_time(end) / steps
+    per = [[e0.elapsed_time(e1) for e0, e1 in ev[ci]] for ci in range(len(cases))]
+    return ms, per, wall / steps
+
+
+def case_report(c: Case, durs_ms):
+    d = np.array(durs_ms)
+    med = float(np.median(d))
+    tflops = c.flops / (med * 1e-3) / 1e12
+    gbs = c.bytes / (med * 1e-3) / 1e9
+    if c.bound == "hbm":
+        achieved, peak, unit = gbs, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = tflops, MFMA_PEAK_TFLOPS[c.dt], "TFLOP/s"
+    return {
+        "algo": mm.ALGO_NAMES[c.plan.algo], "tile": c.info["tile"], "split_k": c.info["split_k"],
+        "dtype": synth.DTYPE_NAMES[c.dt], "a_shape": list(c.p.a_shape), "b_shape": list(c.p.b_shape),
+        "us_median": round(med * 1e3, 3), "us_p10": round(float(np.percentile(d, 10)) * 1e3, 3),
+        "us_p90": round(float(np.percentile(d, 90)) * 1e3, 3),
+        "tflops": round(tflops, 3), "hbm_gbs": round(gbs, 1), "bound": c.bound,
+        "roofline_frac": round(achieved / peak, 4), "roofline_unit": unit, "copies": c.copies,
+    }
+
+
+def cpu_baseline(products, seconds: float):
+    """The fp64 oracle on a random sample of the workload's outputs."""
+    import oracle
+
+    oracle.lib()
+    data = [(p, *p.make()) for p in products]
+    rng = np.random.default_rng(2024)
+
+    def run(n_per):
+        flops = 0.0
+        t0 = time.perf_counter()
+        for (p, a, b), n in zip(data, n_per):
+            shape = oracle.output_shape(p.a_shape, p.b_shape)
+            total = int(np.prod(shape, dtype=np.int64))
+            idx = rng.choice(total, size=min(n, total), replace=False)
+            oracle.matmul_at(a, b, p.dtype, idx)
+            flops += 2.0 * p.K * idx.size
+        return flops, time.perf_counter() - t0
+
+    w = np.array([p.K * 1.0 for p in products])
+    # calibrate on growing samples until one takes at least a second
+    n = 2000
+    while True:
+        f0, t0 = run([n] * len(products))
+        if t0 >= 1.0 or n >= 1 << 24:
+            break
+        n *= 4
+    rate = f0 / max(t0, 1e-9)
+    target = rate * seconds
+    # split the target FLOPs over products in proportion to their FLOPs
+    share = np.array([synth_flops(p) for p in products])
+    share = share / share.sum()
+    n_per = [max(1000, int(target * s / (2.0 * k))) for s, k in zip(share, w)]
+    f, t = run(n_per)
+    return {
+        "value": round(f / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+        "sample": (f"{sum(n_per)} random outputs ({', '.join(f'{p.name}: {n}' for p, n in zip(products, n_per))}); "
+                   f"{f:.3e} FLOP in {t:.1f} s, fp64 triple loop, OpenMP over outputs"),
+    }
+
+
+def synth_flops(p: synth.Product) -> float:
+    shape = np.broadcast_shapes(p.a_shape[:-2] if len(p.a_shape) > 2 else (), p.b_shape[:-2] if len(p.b_shape) > 2 else ())
+    M = p.a_shape[-2] if len(p.a_shape) > 1 else 1
+    N = p.b_shape[-1] if len(p.b_shape) > 1 else 1
+    return 2.0 * float(np.prod(shape)) * M * N * p.K
+
+
+def env_info():
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    return {
+        "gpu": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+        "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+        "host_cpus": os.cpu_count(), "omp_threads": os.environ.get("OMP_NUM_THREADS"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cases", action="store_true", help="skip the per-product table of the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", default=None, help="time only this product name (profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    mm.lib()
+
+    headline = synth.WORKLOADS[HEADLINE].products
+    if args.only:
+        prods = [p for p in synth.all_products() if p.name == args.only]
+        if not prods:
+            sys.exit(f"unknown product {args.only}")
+        cases = [Case(p, dev) for p in prods]
+        ms, per, _ = time_cases(cases, args.steps, args.warmup)
+        print(json.dumps({"only": args.only, "ms_per_step": ms, "cases": [case_report(c, d) for c, d in zip(cases, per)]}))
+        return
+
+    log(f"[bench] preparing {HEADLINE}")
+    hcases = [Case(p, dev) for p in headline]
+    ms, per, wall_ms = time_cases(hcases, args.steps, args.warmup)
+    flops = sum(c.flops for c in hcases)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {HEADLINE}: {ms:.4f} ms/step, {value:.2f} TFLOP/s")
+
+    # dominant kernel: the product with the largest average launch time
+    avgs = [float(np.mean(d)) for d in per]
+    dom = int(np.argmax(avgs))
+    dc = hcases[dom]
+    achieved = dc.flops / (avgs[dom] * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_PEAK_TFLOPS[dc.dt], "unit": "TFLOP/s",
+        "frac": round(achieved / MFMA_PEAK_TFLOPS[dc.dt], 4), "traffic": None,
+        "kernel": f"general {dc.info['tile']} on {dc.p.name}", "avg_launch_us": round(avgs[dom] * 1e3, 3),
+        "flops_per_launch": dc.flops,
+    }
+
+    out = {
+        "metric": "TFLOP/s (and HBM GB/s for skinny) per dtype/shape; % of MFMA/HBM roofline",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded normal(0,1)/sqrt(K) inputs)",
+        "config": {"workload": HEADLINE, "products": [[list(c.p.a_shape), list(c.p.b_shape)] for c in hcases],
+                   "flops_per_step": flops, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "headline_cases": {c.p.name: case_report(c, d) for c, d in zip(hcases, per)},
+    }
+    del hcases
+    torch.cuda.empty_cache()
+
+    if not args.no_cases:
+        table = {}
+        for p in synth.all_products():
+            if p in headline:
+                continue
+            log(f"[bench] case {p.name}")
+            c = Case(p, dev)
+            steps = max(10, args.steps // 2)
+            _, per_c, _ = time_cases([c], steps, max(3, args.warmup // 2))
+            table[p.name] = case_report(c, per_c[0])
+            log(f"[bench]   {table[p.name]}")
+            del c
+            torch.cuda.empty_cache()
+        out["cases"] = table
+
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(headline, args.cpu_seconds)
+        log(f"[bench]   {out['cpu_baseline']}")
+    out["env"] = env_info()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
