@@ -51,8 +51,11 @@ struct Align {
 
 // Tile table entry of the tiled (MFMA) kernels.
 struct TileCfg {
-    int bm, bn;  // block tile
-    int wm, wn;  // wave tile (4 waves per block)
+    int bm, bn;     // block tile
+    int wgm, wgn;   // waves along M and N
+    int bkb;        // bytes of K per row and LDS stage
+    int stages;     // LDS stages
+    int producers;  // waves that issue the global-to-LDS loads
 };
 
 // Number of tile table entries and the entries, per element type.

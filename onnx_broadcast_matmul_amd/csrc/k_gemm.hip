@@ -51,7 +51,7 @@ struct RawVec<4> {
 };
 
 template <int DT, int BM, int BN, bool VEC, bool SPLIT>
-__global__ __launch_bounds__(256) void k_gemm(KArgs a) {
+__global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
     using E = Elem<DT>;
     using S = typename E::S;
     constexpr int ES = (int)sizeof(S);
@@ -248,44 +248,368 @@ __global__ __launch_bounds__(256) void k_gemm(KArgs a) {
             }
 }
 
-template <int DT, int BM, int BN>
+
+// ---------------------------------------------------------------------------
+// Vectorized variant for 16-byte aligned rows: operands move from global
+// memory straight into LDS (gfx950 buffer loads with the LDS destination),
+// several stages deep, with no register staging.
+//
+// * A stage holds BKB bytes of K for the BM rows of A (row-major, K
+//   contiguous) and the same K slice of B for the BN columns in B's own
+//   row-major [k][n] layout.
+// * Each direct load moves 16 bytes per lane into LDS at base + 16 * lane.
+//   The LDS swizzle is realised by choosing which global chunk each lane
+//   fetches: A rows of 128 (64) bytes store logical chunk c at
+//   c ^ (row & 7) (c ^ ((row >> 1) & 3)); B rows store chunk c at
+//   c ^ (2 * (k & 3)).  Chunks outside the matrix (rows past M, columns past
+//   N, K past the partition end) take an offset outside the buffer range,
+//   for which the hardware returns zeros, so tails need no branches.
+// * MFMA A operands are 16-byte LDS reads of the swizzled rows.  B operands
+//   for the 16-bit types come from ds_read_b64_tr_b16: in each group of 16
+//   lanes, lanes 4r..4r+3 address row r of a 4 x 16 block of B and lane i
+//   receives column i, i.e. four consecutive k of one column -- two such
+//   reads give the eight k values of a 32x32x16 operand.  FP32 B operands
+//   are plain 4-byte reads of one column per lane.
+// * Only waves 0..PW-1 issue the direct loads.  Waves are dealt to the four
+//   SIMDs round-robin, so each SIMD pairs a producer with a wave that only
+//   computes: while a producer waits on a full memory queue, its partner
+//   keeps the matrix core busy.
+// * The loads are asm so the compiler does not serialise later LDS reads
+//   behind them; completion is awaited with explicit vmcnt before the
+//   per-stage barrier.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every buffer range used here
+
+// Raw buffer resource: 48-bit base, stride 0, 2^31 - 1 bytes of range.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xffff);
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from global into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void load_to_lds16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, bool SPLIT>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using E = Elem<DT>;
+    using S = typename E::S;
+    constexpr int NW = WGM * WGN;
+    constexpr int ES = (int)sizeof(S);
+    constexpr int VE = 16 / ES;            // elements per 16-byte chunk
+    constexpr int BK = BKB / ES;           // K elements per stage
+    constexpr int CA = BKB / 16;           // chunks per A row
+    constexpr int KS = BKB / 32;           // MFMA steps per stage (32 bytes of K each)
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int RBB = BN * ES;           // bytes of one B row (one k) in the tile
+    constexpr int CPR = RBB / 16;          // chunks per B row
+    constexpr int A_BYTES = BM * BKB;
+    constexpr int B_BYTES = BK * RBB;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int A_INSTR = A_BYTES / 1024 / PW;  // 1 KB direct loads per producer and stage
+    constexpr int B_INSTR = B_BYTES / 1024 / PW;
+    constexpr int LPW = A_INSTR + B_INSTR;
+    constexpr int A_RPB = 1024 / BKB;      // A rows per 1 KB load
+    constexpr int B_RPB = 1024 / RBB;      // B rows per 1 KB load
+    static_assert(CA == 4 || CA == 8, "A rows are 64 or 128 bytes");
+    static_assert(FM >= 1 && FN >= 1, "wave tile");
+    static_assert(PW >= 1 && PW <= NW, "producers");
+    static_assert(A_INSTR >= 1 && A_INSTR * PW * 1024 == A_BYTES, "A loads");
+    static_assert(B_INSTR >= 1 && B_INSTR * PW * 1024 == B_BYTES, "B loads");
+    static_assert(CPR >= 8 && RBB <= 1024, "B rows");
+    static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+    static_assert((STAGES - 2) * LPW < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave / WGN, wc = wave % WGN;
+
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t per_batch = tiles_m * tiles_n;
+    const int64_t nsplit = SPLIT ? a.split : 1;
+    const int64_t total = a.batch * per_batch * nsplit;
+    int64_t id = xcd_remap(blockIdx.x, total);
+    const int64_t sidx = SPLIT ? id % nsplit : 0;
+    id /= nsplit;
+    const int64_t b = id / per_batch;
+    const int64_t t = id % per_batch;
+    constexpr int64_t GM = 8;
+    const int64_t group = t / (GM * tiles_n);
+    const int64_t first_m = group * GM;
+    const int64_t gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+    const int64_t tm = first_m + (t % (GM * tiles_n)) % gsize;
+    const int64_t tn = (t % (GM * tiles_n)) / gsize;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    int64_t oa, ob;
+    batch_offsets(a.bd, b, oa, ob);
+    const char *Atile = (const char *)((const S *)a.A + oa + m0 * K);  // row m0, k = 0
+    const char *Btile = (const char *)((const S *)a.B + ob + n0);      // k = 0, column n0
+
+    const int64_t kbeg = SPLIT ? sidx * a.kchunk : 0;
+    const int64_t kend = SPLIT ? ((kbeg + a.kchunk) < K ? (kbeg + a.kchunk) : K) : K;
+    const int nk = (int)((kend - kbeg + BK - 1) / BK);
+
+    // Producer lane coordinates, fixed over K.
+    const bool producer = wave < PW;
+    uint32_t a_off[A_INSTR];
+    int a_k[A_INSTR];
+    bool a_ok[A_INSTR];
+#pragma unroll
+    for (int q = 0; q < A_INSTR; ++q) {
+        const int row = (wave * A_INSTR + q) * A_RPB + lane / CA;
+        const int p = lane % CA;
+        const int c = CA == 8 ? (p ^ (row & 7)) : (p ^ ((row >> 1) & 3));
+        a_off[q] = (uint32_t)(row * K * ES + c * 16);
+        a_k[q] = c * VE;
+        a_ok[q] = m0 + row < M;
+    }
+    uint32_t b_off[B_INSTR];
+    int b_k[B_INSTR];
+    bool b_ok[B_INSTR];
+#pragma unroll
+    for (int q = 0; q < B_INSTR; ++q) {
+        const int row = (wave * B_INSTR + q) * B_RPB + lane / CPR;  // k within the stage
+        const int p = lane % CPR;
+        const int c = p ^ (2 * (row & 3));
+        b_off[q] = (uint32_t)((int64_t)row * N * ES + c * 16);
+        b_k[q] = row;
+        b_ok[q] = n0 + c * VE < N;
+    }
+
+    auto issue_stage = [&](int st) {
+        if (!producer) return;
+        const uint32_t sbase = lds_base + (st % STAGES) * STAGE_BYTES;
+        const int64_t k0 = kbeg + (int64_t)st * BK;
+        const i32x4 ra = buffer_rsrc(Atile + k0 * ES);
+#pragma unroll
+        for (int q = 0; q < A_INSTR; ++q) {
+            const bool ok = a_ok[q] && k0 + a_k[q] < kend;
+            load_to_lds16(ra, sbase + (wave * A_INSTR + q) * 1024, ok ? a_off[q] : kOutOfRange);
+        }
+        const i32x4 rb = buffer_rsrc(Btile + k0 * N * ES);
+#pragma unroll
+        for (int q = 0; q < B_INSTR; ++q) {
+            const bool ok = b_ok[q] && k0 + b_k[q] < kend;
+            load_to_lds16(rb, sbase + A_BYTES + (wave * B_INSTR + q) * 1024, ok ? b_off[q] : kOutOfRange);
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    uint4 fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, int ks, int slot) {
+        const char *As = lds + buf * STAGE_BYTES;
+        const char *Bs = As + A_BYTES;
+        const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wr * WM + i * 32 + (lane & 31);
+            const int p = CA == 8 ? (c ^ (row & 7)) : (c ^ ((row >> 1) & 3));
+            fa[slot][i] = *(const uint4 *)(As + row * BKB + p * 16);
+        }
+        if constexpr (ES == 2) {
+            const int G = lane >> 4, jl = lane & 15;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = wc * WN + j * 32 + (G & 1) * 16 + (jl & 3) * 4;
+                uint2 h2[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = ks * 16 + (G >> 1) * 8 + h * 4 + (jl >> 2);
+                    const int p = (n >> 3) ^ (2 * (k & 3));
+                    const char *addr = Bs + k * RBB + p * 16 + ((n >> 2) & 1) * 8;
+                    if constexpr (DT == MM_BFLOAT16)
+                        h2[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                              (__attribute__((address_space(3))) bf16x4 *)(addr)));
+                    else
+                        h2[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                                              (__attribute__((address_space(3))) fp16x4 *)(addr)));
+                }
+                fb[slot][j] = make_uint4(h2[0].x, h2[0].y, h2[1].x, h2[1].y);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = wc * WN + j * 32 + (lane & 31);
+                uint32_t v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int k = c * 4 + e;
+                    const int p = (n >> 2) ^ (2 * (k & 3));
+                    v[e] = *(const uint32_t *)(Bs + k * RBB + p * 16 + (n & 3) * 4);
+                }
+                fb[slot][j] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    };
+    auto mfmas = [&](int slot) {
+        if constexpr (DT == MM_BFLOAT16) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[slot][i]),
+                                                                       __builtin_bit_cast(bf16x8, fb[slot][j]),
+                                                                       acc[i][j], 0, 0, 0);
+        } else if constexpr (DT == MM_FLOAT16) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[slot][i]),
+                                                                      __builtin_bit_cast(f16x8, fb[slot][j]),
+                                                                      acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const uint4 &x = fa[slot][i];
+                        const uint4 &y = fb[slot][j];
+                        const float av = __uint_as_float(e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w);
+                        const float bv = __uint_as_float(e == 0 ? y.x : e == 1 ? y.y : e == 2 ? y.z : y.w);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[i][j], 0, 0, 0);
+                    }
+        }
+    };
+
+    // Pipeline: STAGES - 1 stages in flight ahead of the one computed.
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue_stage(s);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // This wave's loads of stage kt are complete once at most the loads of
+        // the stages issued after it are still outstanding.
+        const int later = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
+        if (later >= STAGES - 2) wait_vmcnt<(STAGES - 2) * LPW>();
+        else if (STAGES > 3 && later == 1) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+        // After the barrier every wave's loads of stage kt have landed and every
+        // wave has finished reading stage kt - 1, whose buffer is refilled next.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
+        const int buf = kt % STAGES;
+        read_frags(buf, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) read_frags(buf, ks + 1, (ks + 1) & 1);
+            mfmas(ks & 1);
+        }
+    }
+
+    // Epilogue: 32x32 block (i, j), element r of a lane: row 8(r/4) + 4(lane/32) + r%4, column lane%32.
+    const int64_t ybase = b * M * N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wr * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int64_t col = n0 + wc * WN + j * 32 + (lane & 31);
+                if (row < M && col < N) {
+                    if constexpr (SPLIT) a.W[(sidx * a.batch + b) * M * N + row * N + col] = acc[i][j][r];
+                    else ((S *)a.Y)[ybase + row * N + col] = E::from_f32(acc[i][j][r]);
+                }
+            }
+#endif
+}
+
+template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW>
 static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t s) {
     const int64_t tiles = a.batch * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * (split ? a.split : 1);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 g((unsigned)tiles), blk(256);
-    if (vec) {
-        if (split) hipLaunchKernelGGL((k_gemm<DT, BM, BN, true, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((k_gemm<DT, BM, BN, true, false>), g, blk, 0, s, a);
+    const dim3 g((unsigned)tiles);
+    // Buffer offsets are 32-bit: one tile's rows of A and one stage's rows of
+    // B must each span less than 2 GiB.
+    constexpr int ES = DT == MM_FLOAT ? 4 : 2;
+    const bool fits = (int64_t)BM * a.K * ES < 0x7fff0000LL && (int64_t)(BKB / ES) * a.N * ES < 0x7fff0000LL;
+    if (vec && fits) {
+        const dim3 blk(64 * WGM * WGN);
+        if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, false>), g, blk, 0, s, a);
     } else {
-        if (split) hipLaunchKernelGGL((k_gemm<DT, BM, BN, false, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((k_gemm<DT, BM, BN, false, false>), g, blk, 0, s, a);
+        const dim3 blk(256);
+        if (vec) {
+            if (split) hipLaunchKernelGGL((k_gemm_generic<DT, BM, BN, true, true>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_generic<DT, BM, BN, true, false>), g, blk, 0, s, a);
+        } else {
+            if (split) hipLaunchKernelGGL((k_gemm_generic<DT, BM, BN, false, true>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_generic<DT, BM, BN, false, false>), g, blk, 0, s, a);
+        }
     }
     return hipGetLastError();
 }
 
+#define MM_TILE_CASE(DT, T, IDX)                                                                          \
+    case IDX:                                                                                             \
+        return launch_tile<DT, T[IDX].bm, T[IDX].bn, T[IDX].wgm, T[IDX].wgn, T[IDX].bkb, T[IDX].stages, \
+                           T[IDX].producers>(vec, split, a, s)
+
 template <int DT>
 static hipError_t launch_16(int tile, bool vec, bool split, const KArgs &a, hipStream_t s) {
     switch (tile) {
-    case 0: return launch_tile<DT, 256, 256>(vec, split, a, s);
-    case 1: return launch_tile<DT, 256, 128>(vec, split, a, s);
-    case 2: return launch_tile<DT, 128, 128>(vec, split, a, s);
-    case 3: return launch_tile<DT, 128, 64>(vec, split, a, s);
-    case 4: return launch_tile<DT, 64, 64>(vec, split, a, s);
+        MM_TILE_CASE(DT, kTiles16, 0);
+        MM_TILE_CASE(DT, kTiles16, 1);
+        MM_TILE_CASE(DT, kTiles16, 2);
+        MM_TILE_CASE(DT, kTiles16, 3);
+        MM_TILE_CASE(DT, kTiles16, 4);
     }
     return hipErrorInvalidValue;
 }
 
 static hipError_t launch_32(int tile, bool vec, bool split, const KArgs &a, hipStream_t s) {
     switch (tile) {
-    case 0: return launch_tile<MM_FLOAT, 128, 128>(vec, split, a, s);
-    case 1: return launch_tile<MM_FLOAT, 128, 64>(vec, split, a, s);
-    case 2: return launch_tile<MM_FLOAT, 64, 64>(vec, split, a, s);
+        MM_TILE_CASE(MM_FLOAT, kTiles32, 0);
+        MM_TILE_CASE(MM_FLOAT, kTiles32, 1);
+        MM_TILE_CASE(MM_FLOAT, kTiles32, 2);
+        MM_TILE_CASE(MM_FLOAT, kTiles32, 3);
     }
     return hipErrorInvalidValue;
 }
+#undef MM_TILE_CASE
 
-static_assert(kNumTiles16 == 5 && kNumTiles32 == 3, "launch switch must cover the tile table");
+static_assert(kNumTiles16 == 5 && kNumTiles32 == 4, "launch switch must cover the tile table");
 
 hipError_t launch_general(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s) {
     const bool vec = al.a && al.b;

@@ -56,8 +56,8 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Relative per-CU throughput of a tile entry (bigger tiles reuse each LDS
 // byte more often); used only to rank entries against each other.
 static double tile_quality(int dtype, int index) {
-    static const double q16[kNumTiles16] = {1.0, 0.92, 0.8, 0.6, 0.45};
-    static const double q32[kNumTiles32] = {1.0, 0.9, 0.8};
+    static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4};
+    static const double q32[kNumTiles32] = {1.0, 0.9, 0.8, 1.1};
     return dtype == MM_FLOAT ? q32[index] : q16[index];
 }
 
@@ -222,10 +222,10 @@ static void plan_split(mm_plan_s *p, int requested) {
     if (requested > 0) {
         s = requested;
     } else {
-        // Aim for about four workgroups per CU, with at least 512 K elements
-        // (eight LDS stages of FP32, or more of 16-bit) per partition.
-        int64_t want = cdiv(4 * (int64_t)kNumCUs, std::max<int64_t>(tiles, 1));
-        int64_t max_s = std::max<int64_t>(1, p->K / 512);
+        // Aim for about two workgroups per CU, with at least 1024 K elements
+        // per partition (the partials then cost little next to the inputs).
+        int64_t want = cdiv(2 * (int64_t)kNumCUs, std::max<int64_t>(tiles, 1));
+        int64_t max_s = std::max<int64_t>(1, p->K / 1024);
         s = std::min(want, max_s);
     }
     s = std::max<int64_t>(1, std::min(s, kblocks));

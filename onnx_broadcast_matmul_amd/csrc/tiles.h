@@ -1,9 +1,12 @@
 // tiles.h -- tile table of the tiled MFMA kernels (host and device).
 //
-// Every entry runs 4 waves (256 threads) in a 2 x 2 arrangement, each wave
-// owning a (bm/2) x (bn/2) sub-tile.  One LDS stage holds 128 bytes of K per
-// row (64 elements of a 16-bit type, 32 of FP32).  The selector picks an
-// entry per shape; tests force each one.
+// An entry is a block tile bm x bn run by wgm x wgn waves, each wave owning a
+// (bm/wgm) x (bn/wgn) sub-tile.  Eight waves put two waves on every SIMD, so
+// one wave's MFMAs cover the other's LDS and barrier waits.  The vectorized
+// kernel stages bkb bytes of K per row (64 elements of a 16-bit type, 32 of
+// FP32 for bkb = 128) in `stages` LDS buffers, filled by the first
+// `producers` waves.  The element-wise fallback kernel uses the block tile
+// only.  The selector picks an entry per shape; tests force each one.
 #pragma once
 
 #include "internal.h"
@@ -12,18 +15,19 @@ namespace mm {
 
 // FLOAT16 / BFLOAT16 entries.
 constexpr TileCfg kTiles16[] = {
-    {256, 256, 128, 128},
-    {256, 128, 128, 64},
-    {128, 128, 64, 64},
-    {128, 64, 64, 32},
-    {64, 64, 32, 32},
+    {256, 256, 2, 4, 128, 2, 4},
+    {256, 128, 2, 2, 128, 3, 4},
+    {128, 128, 2, 2, 128, 3, 4},
+    {128, 64, 2, 2, 128, 3, 4},
+    {64, 64, 2, 2, 128, 3, 4},
 };
 
 // FLOAT entries.
 constexpr TileCfg kTiles32[] = {
-    {128, 128, 64, 64},
-    {128, 64, 64, 32},
-    {64, 64, 32, 32},
+    {128, 128, 2, 2, 128, 3, 4},
+    {128, 64, 2, 2, 128, 3, 4},
+    {64, 64, 2, 2, 128, 3, 4},
+    {256, 128, 2, 4, 128, 3, 4},
 };
 
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
@@ -31,5 +35,6 @@ constexpr int kNumTiles32 = sizeof(kTiles32) / sizeof(kTiles32[0]);
 
 // K elements held per LDS stage (one 128-byte row segment).
 inline int stage_k(int dtype) { return dtype == MM_FLOAT ? 32 : 64; }
+static_assert(kTiles16[0].bkb == 128 && kTiles32[0].bkb == 128, "stage_k assumes 128-byte stages");
 
 }  // namespace mm
