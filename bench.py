@@ -76,10 +76,26 @@ class Case:
         self.plan.execute_ptr(a, b, y, stream)
 
 
-def time_cases(cases, steps: int, warmup: int):
-    """Run `steps` steps (each step: every case once), bracketed by device
-    synchronisation, with an event pair around every launch.  Returns the
-    step time in ms and per-case lists of launch durations in ms."""
+def _capture(cases, count: int, offset: int):
+    """A HIP graph holding `count` steps (each step: every case once)."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sp = torch.cuda.current_stream().cuda_stream
+        for k in range(count):
+            for c in cases:
+                c.run(offset + k, sp)
+    return g
+
+
+def time_cases(cases, steps: int, warmup: int, per_case_reps: int = 5):
+    """Time `steps` steps (each step: every case once) as one replay of a
+    captured HIP graph, bracketed by device synchronisation; launches then
+    follow each other on the GPU without host round trips.  Per-case launch
+    durations come from replays of a per-case graph of `steps` launches,
+    timed with events on the launch stream.  Returns (ms per step, per-case
+    lists of average launch durations in ms)."""
     import torch
 
     stream = torch.cuda.current_stream()
@@ -88,23 +104,41 @@ def time_cases(cases, steps: int, warmup: int):
         for c in cases:
             c.run(w, sp)
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-          for _ in cases]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_graph = _capture(cases, steps, warmup)
+    case_graphs = [_capture([c], steps, warmup) for c in cases]
+    step_graph.replay()  # untimed
+    for g in case_graphs:
+        g.replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for k in range(steps):
-        for ci, c in enumerate(cases):
-            ev[ci][k][0].record(stream)
-            c.run(warmup + k, sp)
-            ev[ci][k][1].record(stream)
-    end.record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    step_graph.replay()
+    e1.record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3
-    ms = start.elapsed_time(end) / steps
-    per = [[e0.elapsed_time(e1) for e0, e1 in ev[ci]] for ci in range(len(cases))]
-    return ms, per, wall / steps
+    ms = e0.elapsed_time(e1) / steps
+    per = []
+    for g in case_graphs:
+        d = []
+        for _ in range(per_case_reps):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            d.append(e0.elapsed_time(e1) / steps)
+        per.append(d)
+    return ms, per
+
+
+def check_graph_against_eager(c) -> bool:
+    """The graph-replayed output of the last buffer copy equals an eager
+    execution into a fresh buffer, bit for bit."""
+    import torch
+
+    i = c.copies - 1
+    ref = torch.empty_like(c.Y[i])
+    c.plan.execute_ptr(c.A[i].data_ptr(), c.B[i].data_ptr(), ref.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return bool(torch.equal(ref.view(torch.uint8), c.Y[i].view(torch.uint8)))
 
 
 def case_report(c: Case, durs_ms):
@@ -214,13 +248,14 @@ def main():
         if not prods:
             sys.exit(f"unknown product {args.only}")
         cases = [Case(p, dev) for p in prods]
-        ms, per, _ = time_cases(cases, args.steps, args.warmup)
+        ms, per = time_cases(cases, args.steps, args.warmup)
         print(json.dumps({"only": args.only, "ms_per_step": ms, "cases": [case_report(c, d) for c, d in zip(cases, per)]}))
         return
 
     log(f"[bench] preparing {HEADLINE}")
     hcases = [Case(p, dev) for p in headline]
-    ms, per, wall_ms = time_cases(hcases, args.steps, args.warmup)
+    ms, per = time_cases(hcases, args.steps, args.warmup)
+    graph_ok = all(check_graph_against_eager(c) for c in hcases)
     flops = sum(c.flops for c in hcases)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {HEADLINE}: {ms:.4f} ms/step, {value:.2f} TFLOP/s")
@@ -245,6 +280,8 @@ def main():
         "config": {"workload": HEADLINE, "products": [[list(c.p.a_shape), list(c.p.b_shape)] for c in hcases],
                    "flops_per_step": flops, "parallelism": "single GPU"},
         "roofline": roofline,
+        "timing": "HIP graph replay of the timed steps; events on the launch stream",
+        "graph_matches_eager": graph_ok,
         "headline_cases": {c.p.name: case_report(c, d) for c, d in zip(hcases, per)},
     }
     del hcases
@@ -258,7 +295,7 @@ def main():
             log(f"[bench] case {p.name}")
             c = Case(p, dev)
             steps = max(10, args.steps // 2)
-            _, per_c, _ = time_cases([c], steps, max(3, args.warmup // 2))
+            _, per_c = time_cases([c], steps, max(3, args.warmup // 2))
             table[p.name] = case_report(c, per_c[0])
             log(f"[bench]   {table[p.name]}")
             del c

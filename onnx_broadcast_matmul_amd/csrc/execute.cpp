@@ -68,6 +68,8 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
     al.a = aligned16(A) && (p->K * es) % 16 == 0;
     al.b = aligned16(B) && (p->N * es) % 16 == 0;
     al.y = aligned16(Y) && (p->N * es) % 16 == 0;
+    // Split-K partials are FP32 rows in a workspace of our own (aligned).
+    a.y_vec = p->algo == MM_ALGO_SPLIT_K ? (p->N * 4) % 16 == 0 : al.y;
 
     switch (p->algo) {
     case MM_ALGO_DIRECT:

@@ -38,7 +38,7 @@ struct KArgs {
     int64_t batch;
     int64_t kchunk;
     int32_t split;
-    int32_t pad_;
+    int32_t y_vec;  // output rows (Y, or the workspace) are whole 16-byte chunks
     BatchDesc bd;
 };
 

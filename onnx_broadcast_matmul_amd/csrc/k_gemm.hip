@@ -28,6 +28,8 @@
 // 16-bit types: v_mfma_f32_32x32x16_{bf16,f16}, lanes 0-31 carry K chunk 2s,
 // lanes 32-63 chunk 2s+1.  FP32: four v_mfma_f32_32x32x2_f32, element e of
 // the lane's chunk pairing k = 4(2s) + e with k = 4(2s+1) + e.
+#include <type_traits>
+
 #include "device.h"
 #include "tiles.h"
 
@@ -536,21 +538,62 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
         }
     }
 
-    // Epilogue: 32x32 block (i, j), element r of a lane: row 8(r/4) + 4(lane/32) + r%4, column lane%32.
-    const int64_t ybase = b * M * N;
+    // Epilogue through LDS: each wave narrows its accumulators into a
+    // row-major tile of output rows (16-byte chunks of row r at
+    // chunk ^ (r & 7)), then the workgroup writes whole 16-byte chunks of
+    // output rows.  Tiles larger than the stage buffers go in row passes.
+    // MFMA 32x32 block (i, j), element r of a lane: row 8(r/4) + 4(lane/32)
+    // + r%4, column lane % 32.
+    using O = typename std::conditional<SPLIT, float, S>::type;
+    constexpr int OS = (int)sizeof(O);
+    constexpr int OV = 16 / OS;            // output elements per chunk
+    constexpr int OCPR = BN * OS / 16;     // output chunks per tile row
+    constexpr int NP = (BM * BN * OS + STAGES * STAGE_BYTES - 1) / (STAGES * STAGE_BYTES);
+    constexpr int PR = BM / NP;            // tile rows per pass
+    static_assert(BM % NP == 0 && PR % 8 == 0, "epilogue passes");
+    O *tile = (O *)lds;
+    O *out = SPLIT ? (O *)(a.W + (sidx * a.batch + b) * M * N) : (O *)((S *)a.Y + b * M * N);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int pass = 0; pass < NP; ++pass) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wr * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int64_t col = n0 + wc * WN + j * 32 + (lane & 31);
-                if (row < M && col < N) {
-                    if constexpr (SPLIT) a.W[(sidx * a.batch + b) * M * N + row * N + col] = acc[i][j][r];
-                    else ((S *)a.Y)[ybase + row * N + col] = E::from_f32(acc[i][j][r]);
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rl = wr * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - pass * PR;
+                    if (NP == 1 || (rl >= 0 && rl < PR)) {
+                        const int cl = wc * WN + j * 32 + (lane & 31);
+                        const int ch = (cl / OV) ^ (rl & 7);
+                        O v;
+                        if constexpr (SPLIT) v = acc[i][j][r];
+                        else v = E::from_f32(acc[i][j][r]);
+                        tile[rl * BN + ch * OV + (cl % OV)] = v;
+                    }
+                }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int idx = tid; idx < PR * OCPR; idx += 64 * NW) {
+            const int rl = idx / OCPR, c = idx % OCPR;
+            const int64_t row = m0 + pass * PR + rl, col = n0 + (int64_t)c * OV;
+            if (row < M && col < N) {
+                const uint4 v = *(const uint4 *)&tile[rl * BN + (c ^ (rl & 7)) * OV];
+                O *dst = out + row * N + col;
+                if (a.y_vec) {
+                    // Rows are whole 16-byte chunks: the chunk lies inside the row.
+                    const u32x4 w = {v.x, v.y, v.z, v.w};
+                    __builtin_nontemporal_store(w, (u32x4 *)dst);
+                } else {
+                    O e[OV];
+                    __builtin_memcpy(e, &v, 16);
+#pragma unroll
+                    for (int q = 0; q < OV; ++q)
+                        if (col + q < N) dst[q] = e[q];
                 }
             }
+        }
+    }
 #endif
 }
 

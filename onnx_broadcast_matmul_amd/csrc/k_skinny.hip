@@ -6,30 +6,48 @@
 // (each B row streamed once per k and reused across the few output rows).
 // Each lane owns VE adjacent output columns and keeps MT x VE FP32
 // accumulators; the waves of a workgroup split K into contiguous slabs, so
-// every B element is read exactly once from HBM with 16-byte coalesced loads.
-// The per-wave partial sums meet in LDS and are added in wave order.
+// every B element is read exactly once from HBM with 16-byte coalesced
+// loads, and the next eight B rows are in flight while the current eight are
+// multiplied.  The per-wave partial sums meet in LDS and are added in wave
+// order.
 //
 // Skinny-N: same page, same table (N == 1 or very small N: vectorize the K
 // reduction, no B packing) and roadmap PR06.2 (several partial accumulators
-// over a unit-stride K body).  Lanes run along K with 16-byte loads of A, so
-// each A row is read exactly once; the few columns of B are kept in LDS
-// (transposed, K contiguous) and each lane accumulates R x NT partial sums,
-// reduced across the wavefront with a fixed butterfly at the end of the row.
+// over a unit-stride K body).  Eight consecutive lanes share one row of A and
+// read a full 128-byte line of it per step (16 bytes each), so each A row is
+// streamed once, coalesced.  The waves of a workgroup split K; the few
+// columns of B sit in LDS transposed (K contiguous) and are shared by the two
+// rows each lane carries.  16-bit inputs use the packed dot instructions
+// (two products into an FP32 sum).  Each lane's NT partial sums are reduced
+// over its 8-lane group with a fixed butterfly, then over the K-split waves in
+// wave order through LDS.
+#include <type_traits>
+
 #include "device.h"
 
 namespace mm {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bfloat2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ skinny-M
 
 constexpr int kSkMWaves = 8;
 
-template <int DT, int MT, bool VEC>
+// B rows per pipeline step: deep for one or two output rows, shallower as the
+// MT x VE accumulators take the registers.
+constexpr int skm_unroll(int mt) { return mt <= 2 ? 16 : (mt <= 4 ? 8 : (mt <= 8 ? 4 : 2)); }
+
+template <int DT, int MT, bool VEC, bool AVEC>
 __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
     using E = Elem<DT>;
     using S = typename E::S;
     constexpr int VE = VEC ? E::kVE : 1;  // columns per lane
     constexpr int COLS = 64 * VE;         // columns per workgroup
-    constexpr int KU = VEC ? E::kVE : 1;  // K rows per unrolled step
+    constexpr int U = skm_unroll(MT);
+    constexpr int AV = 16 / (int)sizeof(S);  // A elements per 16-byte load
+    // 16-byte A loads when rows allow them and each step covers whole chunks.
+    constexpr bool AV_OK = AVEC && U % AV == 0;
 
     __shared__ float red[kSkMWaves][COLS];
 
@@ -51,9 +69,10 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
     const S *__restrict__ Bb = (const S *)a.B + ob;
     const int64_t m0 = mg * MT;
     const int64_t n = cb * COLS + (int64_t)lane * VE;
+    const bool col_ok = n < N;
 
-    // Wave slab of K, a multiple of KU.
-    const int64_t kper = ((K + kSkMWaves - 1) / kSkMWaves + KU - 1) / KU * KU;
+    // Wave slab of K: a multiple of U rows (and of the A vector width).
+    const int64_t kper = ((K + kSkMWaves - 1) / kSkMWaves + U - 1) / U * U;
     const int64_t klo = wave * kper;
     const int64_t khi = (klo + kper) < K ? (klo + kper) : K;
 
@@ -63,30 +82,48 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
 #pragma unroll
         for (int v = 0; v < VE; ++v) acc[m][v] = 0.0f;
 
-    const bool col_ok = n < N;
-    for (int64_t k = klo; k < khi; k += KU) {
-        float bv[KU][VE];
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    for (int64_t k = klo; k < khi; k += U) {
+        // B rows k .. k+U-1: streamed once, so loaded non-temporally.
+        float bv[U][VE];
 #pragma unroll
-        for (int u = 0; u < KU; ++u) {
+        for (int u = 0; u < U; ++u) {
+            const bool ok = col_ok && k + u < khi;
             if constexpr (VEC) {
-                uint4 raw = (col_ok && k + u < khi) ? *(const uint4 *)(Bb + (k + u) * N + n) : make_uint4(0, 0, 0, 0);
+                u32x4 raw = {0, 0, 0, 0};
+                if (ok) raw = __builtin_nontemporal_load((const u32x4 *)(Bb + (k + u) * N + n));
                 S tmp[VE];
                 __builtin_memcpy(tmp, &raw, 16);
 #pragma unroll
                 for (int v = 0; v < VE; ++v) bv[u][v] = E::to_f32(tmp[v]);
             } else {
-                bv[u][0] = (col_ok && k + u < khi) ? E::to_f32(Bb[(k + u) * N + n]) : 0.0f;
+                bv[u][0] = ok ? E::to_f32(Bb[(k + u) * N + n]) : 0.0f;
             }
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const bool row_ok = m0 + m < M;
+            float av[U];
+            if constexpr (AV_OK) {
+                // K is a multiple of AV and k of U: whole aligned 16-byte chunks (wave-uniform).
 #pragma unroll
-            for (int u = 0; u < KU; ++u) {
-                const float av = (row_ok && k + u < khi) ? E::to_f32(Ab[(m0 + m) * K + k + u]) : 0.0f;
+                for (int q = 0; q < U / AV; ++q) {
+                    uint4 raw = make_uint4(0, 0, 0, 0);
+                    if (row_ok && k + q * AV < khi) raw = *(const uint4 *)(Ab + (m0 + m) * K + k + q * AV);
+                    S tmp[AV];
+                    __builtin_memcpy(tmp, &raw, 16);
 #pragma unroll
-                for (int v = 0; v < VE; ++v) acc[m][v] = fmaf(av, bv[u][v], acc[m][v]);
+                    for (int e = 0; e < AV; ++e) av[q * AV + e] = E::to_f32(tmp[e]);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    av[u] = (row_ok && k + u < khi) ? E::to_f32(Ab[(m0 + m) * K + k + u]) : 0.0f;
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int v = 0; v < VE; ++v) acc[m][v] = fmaf(av[u], bv[u][v], acc[m][v]);
         }
     }
 
@@ -109,178 +146,263 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
 }
 
 template <int DT, int MT>
-static hipError_t launch_skm(bool vec, const KArgs &a, hipStream_t s) {
+static hipError_t launch_skm(bool vec, bool avec, const KArgs &a, hipStream_t s) {
     const int cols = 64 * (vec ? Elem<DT>::kVE : 1);
     const int64_t blocks = a.batch * ((a.M + MT - 1) / MT) * ((a.N + cols - 1) / cols);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (vec) hipLaunchKernelGGL((k_skinny_m<DT, MT, true>), dim3((unsigned)blocks), dim3(64 * kSkMWaves), 0, s, a);
-    else hipLaunchKernelGGL((k_skinny_m<DT, MT, false>), dim3((unsigned)blocks), dim3(64 * kSkMWaves), 0, s, a);
+    const dim3 g((unsigned)blocks), blk(64 * kSkMWaves);
+    if (vec) {
+        if (avec) hipLaunchKernelGGL((k_skinny_m<DT, MT, true, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_skinny_m<DT, MT, true, false>), g, blk, 0, s, a);
+    } else {
+        if (avec) hipLaunchKernelGGL((k_skinny_m<DT, MT, false, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_skinny_m<DT, MT, false, false>), g, blk, 0, s, a);
+    }
     return hipGetLastError();
 }
 
 template <int DT>
-static hipError_t launch_skm_dt(bool vec, const KArgs &a, hipStream_t s) {
+static hipError_t launch_skm_dt(bool vec, bool avec, const KArgs &a, hipStream_t s) {
     // Smallest row group that covers M (B is then read once); M >= 16 uses
     // groups of 16 rows.
-    if (a.M <= 1) return launch_skm<DT, 1>(vec, a, s);
-    if (a.M <= 2) return launch_skm<DT, 2>(vec, a, s);
-    if (a.M <= 4) return launch_skm<DT, 4>(vec, a, s);
-    if (a.M <= 8) return launch_skm<DT, 8>(vec, a, s);
-    return launch_skm<DT, 16>(vec, a, s);
+    if (a.M <= 1) return launch_skm<DT, 1>(vec, avec, a, s);
+    if (a.M <= 2) return launch_skm<DT, 2>(vec, avec, a, s);
+    if (a.M <= 4) return launch_skm<DT, 4>(vec, avec, a, s);
+    if (a.M <= 8) return launch_skm<DT, 8>(vec, avec, a, s);
+    return launch_skm<DT, 16>(vec, avec, a, s);
 }
 
 hipError_t launch_skinny_m(int dtype, const Align &al, const KArgs &a, hipStream_t s) {
-    const bool vec = al.b && al.y;
+    const bool vec = al.b && al.y;  // B and Y rows in 16-byte chunks
+    const bool avec = al.a;         // A rows in 16-byte chunks
     switch (dtype) {
-    case MM_FLOAT: return launch_skm_dt<MM_FLOAT>(vec, a, s);
-    case MM_FLOAT16: return launch_skm_dt<MM_FLOAT16>(vec, a, s);
-    case MM_BFLOAT16: return launch_skm_dt<MM_BFLOAT16>(vec, a, s);
+    case MM_FLOAT: return launch_skm_dt<MM_FLOAT>(vec, avec, a, s);
+    case MM_FLOAT16: return launch_skm_dt<MM_FLOAT16>(vec, avec, a, s);
+    case MM_BFLOAT16: return launch_skm_dt<MM_BFLOAT16>(vec, avec, a, s);
     }
     return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------ skinny-N
 
-constexpr int kSkNRows = 4;           // rows per wave
-constexpr int kSkNBlockRows = 16;     // rows per workgroup (4 waves)
-constexpr int kSkNLdsBytes = 65536;   // B slab budget
+constexpr int kSkNWaves = 8;                            // 512 threads
+constexpr int kSkNKParts = 8;                           // waves splitting K
+constexpr int kSkNRowGroups = kSkNWaves / kSkNKParts;   // waves splitting rows
+constexpr int kSkNRowsPerLane = 2;
+constexpr int kSkNBlockRows = kSkNRowGroups * 8 * kSkNRowsPerLane;  // 16 rows per workgroup
+constexpr int kSkNLdsBytes = 65536;                     // B slab budget
 
-__device__ __forceinline__ float wave_sum(float v) {
-    // Fixed butterfly over the 64 lanes: every lane ends with the same sum.
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// Sum over the 8 lanes of each 8-lane group (fixed butterfly).
+__device__ __forceinline__ float group8_sum(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
     return v;
 }
 
-template <int DT, int NT, bool VEC>
-__global__ __launch_bounds__(256) void k_skinny_n(KArgs a) {
+template <int DT, int NT, bool VEC, bool BVEC>
+__global__ __launch_bounds__(64 * kSkNWaves) void k_skinny_n(KArgs a) {
     using E = Elem<DT>;
     using S = typename E::S;
     constexpr int ES = (int)sizeof(S);
-    constexpr int VE = VEC ? E::kVE : 1;           // K elements per lane and step
-    constexpr int KSTEP = 64 * VE;                  // K elements per wave step
-    constexpr int KS = (kSkNLdsBytes / (NT * ES)) / KSTEP * KSTEP;  // slab length
-    static_assert(KS >= KSTEP, "slab");
+    constexpr int VE = VEC ? 16 / ES : 1;  // K elements per lane and step
+    constexpr int KSTEP = 8 * VE;          // K elements per 8-lane group and step
+    constexpr int KALIGN = kSkNKParts * KSTEP;
+    constexpr int KS = (kSkNLdsBytes / (NT * ES)) / KALIGN * KALIGN;  // slab length
+    constexpr int R = kSkNRowsPerLane;
+    static_assert(KS >= KALIGN, "slab");
 
-    __shared__ __attribute__((aligned(16))) S bt[NT][KS];  // B slab, transposed: bt[n][k]
+    __shared__ __attribute__((aligned(16))) S bt[NT][KS];              // B slab, transposed: bt[n][k]
+    __shared__ float red[kSkNKParts][kSkNBlockRows][NT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kp = wave % kSkNKParts, rg = wave / kSkNKParts;
+    const int sub = lane & 7;    // position inside the 8-lane group
+    const int grp = lane >> 3;   // 8-lane group = row slot
+
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t nrb = (M + kSkNBlockRows - 1) / kSkNBlockRows;
     const int64_t nng = (N + NT - 1) / NT;
-    const int64_t nitems = a.batch * nng * nrb;
-    const int64_t nslabs = (K + KS - 1) / KS;
+    int64_t id = blockIdx.x;
+    const int64_t rb = id % nrb;
+    id /= nrb;
+    const int64_t ng = id % nng;
+    const int64_t b = id / nng;
 
-    int64_t loaded_key = -1;  // (batch, n-group) of the resident slab, single-slab case
-    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
-        const int64_t rb = item % nrb;
-        const int64_t ng = (item / nrb) % nng;
-        const int64_t b = item / (nrb * nng);
-        int64_t oa, ob;
-        batch_offsets(a.bd, b, oa, ob);
-        const S *__restrict__ Ab = (const S *)a.A + oa;
-        const S *__restrict__ Bb = (const S *)a.B + ob;
-        const int64_t n0 = ng * NT;
-        const int64_t r0 = rb * kSkNBlockRows + wave * kSkNRows;
+    int64_t oa, ob;
+    batch_offsets(a.bd, b, oa, ob);
+    const S *__restrict__ Ab = (const S *)a.A + oa;
+    const S *__restrict__ Bb = (const S *)a.B + ob;
+    const int64_t n0 = ng * NT;
 
-        float acc[kSkNRows][NT];
+    // Rows of this lane: slot r covers row rb*kSkNBlockRows + (r*kSkNRowGroups + rg)*8 + grp.
+    int64_t row[R];
+    bool row_ok[R];
 #pragma unroll
-        for (int r = 0; r < kSkNRows; ++r)
-#pragma unroll
-            for (int q = 0; q < NT; ++q) acc[r][q] = 0.0f;
+    for (int r = 0; r < R; ++r) {
+        row[r] = rb * kSkNBlockRows + (int64_t)(r * kSkNRowGroups + rg) * 8 + grp;
+        row_ok[r] = row[r] < M;
+    }
 
-        for (int64_t sl = 0; sl < nslabs; ++sl) {
-            const int64_t k0 = sl * KS;
-            const int64_t klen = (K - k0) < KS ? (K - k0) : KS;
-            const int64_t key = b * nng + ng;
-            if (nslabs > 1 || key != loaded_key) {
-                __syncthreads();
-                for (int64_t e = tid; e < (int64_t)NT * KS; e += 256) {
-                    const int64_t kk = e / NT, q = e % NT;
-                    S v = (S)0;
-                    if (kk < klen && n0 + q < N) v = Bb[(k0 + kk) * N + n0 + q];
-                    bt[q][kk] = v;
+    float acc[R][NT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int q = 0; q < NT; ++q) acc[r][q] = 0.0f;
+
+    for (int64_t k0 = 0; k0 < K; k0 += KS) {
+        const int64_t klen = (K - k0) < KS ? (K - k0) : KS;
+        __syncthreads();
+        if constexpr (BVEC) {
+            // B rows are exactly NT elements in whole 16-byte chunks: a thread
+            // loads BR consecutive rows and writes NT transposed 16-byte chunks.
+            constexpr int BR = 16 / ES;
+            constexpr int CPRW = NT * ES / 16;  // 16-byte chunks per B row
+            for (int64_t kb = tid; kb * BR < klen; kb += 64 * kSkNWaves) {
+                S vals[BR][NT];
+#pragma unroll
+                for (int r = 0; r < BR; ++r) {
+                    const int64_t kk = kb * BR + r;
+#pragma unroll
+                    for (int c = 0; c < CPRW; ++c) {
+                        uint4 v = make_uint4(0, 0, 0, 0);
+                        if (kk < klen) v = *(const uint4 *)(Bb + (k0 + kk) * NT + c * (16 / ES));
+                        __builtin_memcpy(&vals[r][c * (16 / ES)], &v, 16);
+                    }
                 }
-                __syncthreads();
-                loaded_key = key;
-            }
-            for (int64_t kk = (int64_t)lane * VE; kk < klen; kk += KSTEP) {
-                float bf[NT][VE];
 #pragma unroll
                 for (int q = 0; q < NT; ++q) {
-                    if constexpr (VEC) {
-                        S tmp[VE];
-                        __builtin_memcpy(tmp, &bt[q][kk], 16);
+                    S col[BR];
 #pragma unroll
-                        for (int v = 0; v < VE; ++v) bf[q][v] = E::to_f32(tmp[v]);
+                    for (int r = 0; r < BR; ++r) col[r] = vals[r][q];
+                    __builtin_memcpy(&bt[q][kb * BR], col, 16);
+                }
+            }
+        } else {
+            for (int64_t e = tid; e < (int64_t)NT * klen; e += 64 * kSkNWaves) {
+                const int64_t kk = e / NT, q = e % NT;
+                bt[q][kk] = (n0 + q < N) ? Bb[(k0 + kk) * N + n0 + q] : (S)0;
+            }
+        }
+        __syncthreads();
+        // This wave's part of the slab, a multiple of KSTEP long.
+        const int64_t part = ((klen + kSkNKParts - 1) / kSkNKParts + KSTEP - 1) / KSTEP * KSTEP;
+        const int64_t plo = kp * part;
+        const int64_t phi = (plo + part) < klen ? (plo + part) : klen;
+#pragma unroll 2
+        for (int64_t kk = plo + sub * VE; kk < phi; kk += KSTEP) {
+            if constexpr (VEC) {
+                // K is a multiple of VE, so the lane's chunk is wholly inside [0, klen).
+                uint4 bv[NT];
+#pragma unroll
+                for (int q = 0; q < NT; ++q) bv[q] = *(const uint4 *)&bt[q][kk];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                    u32x4 raw = {0, 0, 0, 0};  // A is streamed once: non-temporal
+                    if (row_ok[r]) raw = __builtin_nontemporal_load((const u32x4 *)(Ab + row[r] * K + k0 + kk));
+                    const uint4 av = make_uint4(raw[0], raw[1], raw[2], raw[3]);
+                    if constexpr (DT == MM_FLOAT) {
+#pragma unroll
+                        for (int q = 0; q < NT; ++q) {
+                            float s = acc[r][q];
+                            s = fmaf(__uint_as_float(av.x), __uint_as_float(bv[q].x), s);
+                            s = fmaf(__uint_as_float(av.y), __uint_as_float(bv[q].y), s);
+                            s = fmaf(__uint_as_float(av.z), __uint_as_float(bv[q].z), s);
+                            s = fmaf(__uint_as_float(av.w), __uint_as_float(bv[q].w), s);
+                            acc[r][q] = s;
+                        }
                     } else {
-                        bf[q][0] = E::to_f32(bt[q][kk]);
+                        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+                        for (int q = 0; q < NT; ++q) {
+                            const uint32_t bw[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
+                            float s = acc[r][q];
+#pragma unroll
+                            for (int w = 0; w < 4; ++w) {
+                                if constexpr (DT == MM_FLOAT16)
+                                    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, aw[w]),
+                                                               __builtin_bit_cast(half2_t, bw[w]), s, false);
+                                else
+                                    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfloat2_t, aw[w]),
+                                                                        __builtin_bit_cast(bfloat2_t, bw[w]), s, false);
+                            }
+                            acc[r][q] = s;
+                        }
                     }
                 }
+            } else {
+                float bv[NT];
 #pragma unroll
-                for (int r = 0; r < kSkNRows; ++r) {
-                    const int64_t row = r0 + r;
-                    float av[VE];
-                    if constexpr (VEC) {
-                        // K is a multiple of VE and kk < klen, so the chunk is in range.
-                        uint4 raw = row < M ? *(const uint4 *)(Ab + row * K + k0 + kk) : make_uint4(0, 0, 0, 0);
-                        S tmp[VE];
-                        __builtin_memcpy(tmp, &raw, 16);
+                for (int q = 0; q < NT; ++q) bv[q] = E::to_f32(bt[q][kk]);
 #pragma unroll
-                        for (int v = 0; v < VE; ++v) av[v] = E::to_f32(tmp[v]);
-                    } else {
-                        av[0] = row < M ? E::to_f32(Ab[row * K + k0 + kk]) : 0.0f;
-                    }
+                for (int r = 0; r < R; ++r) {
+                    const float av = row_ok[r] ? E::to_f32(Ab[row[r] * K + k0 + kk]) : 0.0f;
 #pragma unroll
-                    for (int q = 0; q < NT; ++q)
-#pragma unroll
-                        for (int v = 0; v < VE; ++v) acc[r][q] = fmaf(av[v], bf[q][v], acc[r][q]);
+                    for (int q = 0; q < NT; ++q) acc[r][q] = fmaf(av, bv[q], acc[r][q]);
                 }
             }
         }
+    }
 
-        S *__restrict__ Y = (S *)a.Y + b * M * N;
+    // Reduce over the 8-lane group, then over the K parts in wave order.
 #pragma unroll
-        for (int r = 0; r < kSkNRows; ++r) {
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int q = 0; q < NT; ++q) {
-                const float s = wave_sum(acc[r][q]);
-                const int64_t row = r0 + r;
-                if (lane == q && row < M && n0 + q < N) Y[row * N + n0 + q] = E::from_f32(s);
-            }
+        for (int q = 0; q < NT; ++q) {
+            const float s = group8_sum(acc[r][q]);
+            if (sub == 0) red[kp][(r * kSkNRowGroups + rg) * 8 + grp][q] = s;
         }
+    __syncthreads();
+    S *__restrict__ Y = (S *)a.Y + b * M * N;
+    for (int e = tid; e < kSkNBlockRows * NT; e += 64 * kSkNWaves) {
+        const int rl = e / NT, q = e % NT;
+        float s = red[0][rl][q];
+#pragma unroll
+        for (int p = 1; p < kSkNKParts; ++p) s += red[p][rl][q];
+        const int64_t rr = rb * kSkNBlockRows + rl;
+        if (rr < M && n0 + q < N) Y[rr * N + n0 + q] = E::from_f32(s);
     }
 }
 
 template <int DT, int NT>
-static hipError_t launch_skn(bool vec, const KArgs &a, hipStream_t s) {
+static hipError_t launch_skn(bool vec, bool bvec, const KArgs &a, hipStream_t s) {
     const int64_t items = a.batch * ((a.N + NT - 1) / NT) * ((a.M + kSkNBlockRows - 1) / kSkNBlockRows);
     if (items <= 0) return hipSuccess;
-    // Persistent workgroups: two per CU keep their B slab resident across rows.
-    const int64_t g = items < 2 * kNumCUs ? items : 2 * kNumCUs;
-    if (vec) hipLaunchKernelGGL((k_skinny_n<DT, NT, true>), dim3((unsigned)g), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_skinny_n<DT, NT, false>), dim3((unsigned)g), dim3(256), 0, s, a);
+    if (items > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 g((unsigned)items), blk(64 * kSkNWaves);
+    constexpr bool kWhole = NT * sizeof(typename Elem<DT>::S) % 16 == 0;
+    if constexpr (kWhole) {
+        if (bvec && a.N == NT) {
+            if (vec) hipLaunchKernelGGL((k_skinny_n<DT, NT, true, true>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((k_skinny_n<DT, NT, false, true>), g, blk, 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    if (vec) hipLaunchKernelGGL((k_skinny_n<DT, NT, true, false>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_skinny_n<DT, NT, false, false>), g, blk, 0, s, a);
     return hipGetLastError();
 }
 
 template <int DT>
-static hipError_t launch_skn_dt(bool vec, const KArgs &a, hipStream_t s) {
-    if (a.N <= 1) return launch_skn<DT, 1>(vec, a, s);
-    if (a.N <= 2) return launch_skn<DT, 2>(vec, a, s);
-    if (a.N <= 4) return launch_skn<DT, 4>(vec, a, s);
-    if (a.N <= 8) return launch_skn<DT, 8>(vec, a, s);
-    return launch_skn<DT, 16>(vec, a, s);
+static hipError_t launch_skn_dt(bool vec, bool bvec, const KArgs &a, hipStream_t s) {
+    if (a.N <= 1) return launch_skn<DT, 1>(vec, bvec, a, s);
+    if (a.N <= 2) return launch_skn<DT, 2>(vec, bvec, a, s);
+    if (a.N <= 4) return launch_skn<DT, 4>(vec, bvec, a, s);
+    if (a.N <= 8) return launch_skn<DT, 8>(vec, bvec, a, s);
+    return launch_skn<DT, 16>(vec, bvec, a, s);
 }
 
 hipError_t launch_skinny_n(int dtype, const Align &al, const KArgs &a, hipStream_t s) {
-    const bool vec = al.a;
+    const bool vec = al.a;   // A rows in 16-byte chunks
+    const bool bvec = al.b;  // B rows in 16-byte chunks
     switch (dtype) {
-    case MM_FLOAT: return launch_skn_dt<MM_FLOAT>(vec, a, s);
-    case MM_FLOAT16: return launch_skn_dt<MM_FLOAT16>(vec, a, s);
-    case MM_BFLOAT16: return launch_skn_dt<MM_BFLOAT16>(vec, a, s);
+    case MM_FLOAT: return launch_skn_dt<MM_FLOAT>(vec, bvec, a, s);
+    case MM_FLOAT16: return launch_skn_dt<MM_FLOAT16>(vec, bvec, a, s);
+    case MM_BFLOAT16: return launch_skn_dt<MM_BFLOAT16>(vec, bvec, a, s);
     }
     return hipErrorInvalidValue;
 }
