@@ -10,8 +10,8 @@ them in the 256 MB Infinity Cache.  The JSON line also carries:
   the timed region, against the FP32 MFMA peak;
 * ``cases``: every other workload product timed the same way (TFLOP/s,
   HBM GB/s and the fraction of its own roofline);
-* ``cpu_baseline``: the fp64 CPU oracle timed on a bounded random sample of
-  the headline workload's outputs on the host cores.
+* ``cpu_baseline``: the fp64 CPU oracle timed over whole steps of the
+  headline workload on the host cores (about ``--cpu-seconds`` of work).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cases]
        [--no-cpu] [--cpu-seconds S] [--only NAME]
@@ -161,43 +161,31 @@ def case_report(c: Case, durs_ms):
 
 
 def cpu_baseline(products, seconds: float):
-    """The fp64 oracle on a random sample of the workload's outputs."""
+    """The fp64 oracle run over whole steps of the workload.
+
+    Every product of the step is computed in full by ``oracle.matmul``; steps
+    repeat until ``seconds`` have passed, so the sample is a whole number of
+    complete steps and the rate is directly comparable with ``value``.
+    """
     import oracle
 
     oracle.lib()
     data = [(p, *p.make()) for p in products]
-    rng = np.random.default_rng(2024)
-
-    def run(n_per):
-        flops = 0.0
-        t0 = time.perf_counter()
-        for (p, a, b), n in zip(data, n_per):
-            shape = oracle.output_shape(p.a_shape, p.b_shape)
-            total = int(np.prod(shape, dtype=np.int64))
-            idx = rng.choice(total, size=min(n, total), replace=False)
-            oracle.matmul_at(a, b, p.dtype, idx)
-            flops += 2.0 * p.K * idx.size
-        return flops, time.perf_counter() - t0
-
-    w = np.array([p.K * 1.0 for p in products])
-    # calibrate on growing samples until one takes at least a second
-    n = 2000
+    step_flops = sum(synth_flops(p) for p in products)
+    steps = 0
+    t0 = time.perf_counter()
     while True:
-        f0, t0 = run([n] * len(products))
-        if t0 >= 1.0 or n >= 1 << 24:
+        for p, a, b in data:
+            oracle.matmul(a, b, p.dtype)
+        steps += 1
+        t = time.perf_counter() - t0
+        if t >= seconds:
             break
-        n *= 4
-    rate = f0 / max(t0, 1e-9)
-    target = rate * seconds
-    # split the target FLOPs over products in proportion to their FLOPs
-    share = np.array([synth_flops(p) for p in products])
-    share = share / share.sum()
-    n_per = [max(1000, int(target * s / (2.0 * k))) for s, k in zip(share, w)]
-    f, t = run(n_per)
+    f = steps * step_flops
     return {
         "value": round(f / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-        "sample": (f"{sum(n_per)} random outputs ({', '.join(f'{p.name}: {n}' for p, n in zip(products, n_per))}); "
-                   f"{f:.3e} FLOP in {t:.1f} s, fp64 triple loop, OpenMP over outputs"),
+        "sample": (f"{steps} whole steps of the workload ({' + '.join(p.name for p in products)}); "
+                   f"{f:.3e} FLOP in {t:.1f} s, fp64 accumulation, OpenMP over output rows"),
     }
 
 
@@ -227,7 +215,7 @@ def main():
     ap.add_argument("--no-cases", action="store_true", help="skip the per-product table of the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", default=None, help="time only this product name (profiling runs)")
+    ap.add_argument("--only", default=None, help="time only these products (comma-separated names; profiling runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -244,12 +232,16 @@ def main():
 
     headline = synth.WORKLOADS[HEADLINE].products
     if args.only:
-        prods = [p for p in synth.all_products() if p.name == args.only]
-        if not prods:
-            sys.exit(f"unknown product {args.only}")
-        cases = [Case(p, dev) for p in prods]
-        ms, per = time_cases(cases, args.steps, args.warmup)
-        print(json.dumps({"only": args.only, "ms_per_step": ms, "cases": [case_report(c, d) for c, d in zip(cases, per)]}))
+        names = args.only.split(",")
+        prods = [p for p in synth.all_products() if p.name in names]
+        if len(prods) != len(names):
+            sys.exit(f"unknown product in {args.only}")
+        for p in prods:
+            c = Case(p, dev)
+            _, per = time_cases([c], args.steps, args.warmup)
+            print(json.dumps({"only": p.name, "case": case_report(c, per[0])}), flush=True)
+            del c
+            torch.cuda.empty_cache()
         return
 
     log(f"[bench] preparing {HEADLINE}")

@@ -637,6 +637,9 @@ static hipError_t launch_16(int tile, bool vec, bool split, const KArgs &a, hipS
         MM_TILE_CASE(DT, kTiles16, 2);
         MM_TILE_CASE(DT, kTiles16, 3);
         MM_TILE_CASE(DT, kTiles16, 4);
+        MM_TILE_CASE(DT, kTiles16, 5);
+        MM_TILE_CASE(DT, kTiles16, 6);
+        MM_TILE_CASE(DT, kTiles16, 7);
     }
     return hipErrorInvalidValue;
 }
@@ -652,7 +655,7 @@ static hipError_t launch_32(int tile, bool vec, bool split, const KArgs &a, hipS
 }
 #undef MM_TILE_CASE
 
-static_assert(kNumTiles16 == 5 && kNumTiles32 == 4, "launch switch must cover the tile table");
+static_assert(kNumTiles16 == 8 && kNumTiles32 == 4, "launch switch must cover the tile table");
 
 hipError_t launch_general(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s) {
     const bool vec = al.a && al.b;

@@ -253,6 +253,57 @@ __global__ __launch_bounds__(64 * kSkNWaves) void k_skinny_n(KArgs a) {
 #pragma unroll
         for (int q = 0; q < NT; ++q) acc[r][q] = 0.0f;
 
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    // The wave's part of a slab of length klen: a multiple of KSTEP long.
+    auto part_bounds = [&](int64_t klen, int64_t &plo, int64_t &phi) {
+        const int64_t part = ((klen + kSkNKParts - 1) / kSkNKParts + KSTEP - 1) / KSTEP * KSTEP;
+        plo = kp * part;
+        phi = (plo + part) < klen ? (plo + part) : klen;
+    };
+    // A chunk (16 bytes) of row slot r at slab-relative k; A is streamed once: non-temporal.
+    auto load_a = [&](int r, int64_t k0, int64_t kk) -> uint4 {
+        u32x4 raw = {0, 0, 0, 0};
+        if (row_ok[r]) raw = __builtin_nontemporal_load((const u32x4 *)(Ab + row[r] * K + k0 + kk));
+        return make_uint4(raw[0], raw[1], raw[2], raw[3]);
+    };
+    // Multiply-accumulate one K chunk of both row slots against the B slab.
+    auto mac = [&](int64_t kk, const uint4 *av) {
+        uint4 bv[NT];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) bv[q] = *(const uint4 *)&bt[q][kk];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if constexpr (DT == MM_FLOAT) {
+#pragma unroll
+                for (int q = 0; q < NT; ++q) {
+                    float s = acc[r][q];
+                    s = fmaf(__uint_as_float(av[r].x), __uint_as_float(bv[q].x), s);
+                    s = fmaf(__uint_as_float(av[r].y), __uint_as_float(bv[q].y), s);
+                    s = fmaf(__uint_as_float(av[r].z), __uint_as_float(bv[q].z), s);
+                    s = fmaf(__uint_as_float(av[r].w), __uint_as_float(bv[q].w), s);
+                    acc[r][q] = s;
+                }
+            } else {
+                const uint32_t aw[4] = {av[r].x, av[r].y, av[r].z, av[r].w};
+#pragma unroll
+                for (int q = 0; q < NT; ++q) {
+                    const uint32_t bw[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
+                    float s = acc[r][q];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        if constexpr (DT == MM_FLOAT16)
+                            s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, aw[w]),
+                                                       __builtin_bit_cast(half2_t, bw[w]), s, false);
+                        else
+                            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfloat2_t, aw[w]),
+                                                                __builtin_bit_cast(bfloat2_t, bw[w]), s, false);
+                    }
+                    acc[r][q] = s;
+                }
+            }
+        }
+    };
+
     for (int64_t k0 = 0; k0 < K; k0 += KS) {
         const int64_t klen = (K - k0) < KS ? (K - k0) : KS;
         __syncthreads();
@@ -288,53 +339,19 @@ __global__ __launch_bounds__(64 * kSkNWaves) void k_skinny_n(KArgs a) {
             }
         }
         __syncthreads();
-        // This wave's part of the slab, a multiple of KSTEP long.
-        const int64_t part = ((klen + kSkNKParts - 1) / kSkNKParts + KSTEP - 1) / KSTEP * KSTEP;
-        const int64_t plo = kp * part;
-        const int64_t phi = (plo + part) < klen ? (plo + part) : klen;
+        int64_t plo, phi;
+        part_bounds(klen, plo, phi);
+        if constexpr (VEC) {
+            // K is a multiple of VE, so each lane's chunk lies wholly inside [0, klen).
 #pragma unroll 2
-        for (int64_t kk = plo + sub * VE; kk < phi; kk += KSTEP) {
-            if constexpr (VEC) {
-                // K is a multiple of VE, so the lane's chunk is wholly inside [0, klen).
-                uint4 bv[NT];
+            for (int64_t kk = plo + sub * VE; kk < phi; kk += KSTEP) {
+                uint4 av[R];
 #pragma unroll
-                for (int q = 0; q < NT; ++q) bv[q] = *(const uint4 *)&bt[q][kk];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                    u32x4 raw = {0, 0, 0, 0};  // A is streamed once: non-temporal
-                    if (row_ok[r]) raw = __builtin_nontemporal_load((const u32x4 *)(Ab + row[r] * K + k0 + kk));
-                    const uint4 av = make_uint4(raw[0], raw[1], raw[2], raw[3]);
-                    if constexpr (DT == MM_FLOAT) {
-#pragma unroll
-                        for (int q = 0; q < NT; ++q) {
-                            float s = acc[r][q];
-                            s = fmaf(__uint_as_float(av.x), __uint_as_float(bv[q].x), s);
-                            s = fmaf(__uint_as_float(av.y), __uint_as_float(bv[q].y), s);
-                            s = fmaf(__uint_as_float(av.z), __uint_as_float(bv[q].z), s);
-                            s = fmaf(__uint_as_float(av.w), __uint_as_float(bv[q].w), s);
-                            acc[r][q] = s;
-                        }
-                    } else {
-                        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-                        for (int q = 0; q < NT; ++q) {
-                            const uint32_t bw[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
-                            float s = acc[r][q];
-#pragma unroll
-                            for (int w = 0; w < 4; ++w) {
-                                if constexpr (DT == MM_FLOAT16)
-                                    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, aw[w]),
-                                                               __builtin_bit_cast(half2_t, bw[w]), s, false);
-                                else
-                                    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfloat2_t, aw[w]),
-                                                                        __builtin_bit_cast(bfloat2_t, bw[w]), s, false);
-                            }
-                            acc[r][q] = s;
-                        }
-                    }
-                }
-            } else {
+                for (int r = 0; r < R; ++r) av[r] = load_a(r, k0, kk);
+                mac(kk, av);
+            }
+        } else {
+            for (int64_t kk = plo + sub; kk < phi; kk += KSTEP) {
                 float bv[NT];
 #pragma unroll
                 for (int q = 0; q < NT; ++q) bv[q] = E::to_f32(bt[q][kk]);

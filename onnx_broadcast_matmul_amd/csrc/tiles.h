@@ -20,6 +20,9 @@ constexpr TileCfg kTiles16[] = {
     {128, 128, 2, 2, 128, 3, 4},
     {128, 64, 2, 2, 128, 3, 4},
     {64, 64, 2, 2, 128, 3, 4},
+    {128, 128, 2, 2, 128, 2, 4},
+    {128, 256, 2, 4, 128, 2, 4},
+    {256, 128, 4, 2, 128, 2, 4},
 };
 
 // FLOAT entries.
