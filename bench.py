@@ -43,6 +43,43 @@ ROTATE_BYTES = 1 << 30  # rotate input/output copies until a step touches >= 1 G
 MAX_COPIES = 16
 
 
+# Sources whose text fixes the tiled GEMM kernel's memory traffic; a traffic
+# record taken from hardware counters holds only while their hash matches.
+GEMM_SOURCES = ["k_gemm.hip", "tiles.h", "device.h", "internal.h"]
+
+
+def gemm_sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "onnx_broadcast_matmul_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(product: str, tile: int):
+    """HBM bytes per launch that rocprofv3 FETCH_SIZE + WRITE_SIZE passes
+    measured for this product and tile, scaled by the plain-copy calibration,
+    from a ``TRAFFIC`` line of a summary under profiles/; None when there is
+    no record or the kernel sources changed after the counters were taken."""
+    d = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(d):
+        return None
+    sha = gemm_sources_sha256()
+    for f in sorted(os.listdir(d)):
+        if not f.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(d, f)) as fh:
+            for line in fh:
+                if not line.startswith("TRAFFIC "):
+                    continue
+                kv = dict(t.split("=", 1) for t in line.split()[1:])
+                if kv.get("product") == product and int(kv.get("tile", -1)) == tile and kv.get("sources_sha256") == sha:
+                    return int(kv["bytes_per_launch"])
+    return None
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -216,6 +253,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", default=None, help="time only these products (comma-separated names; profiling runs)")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="run --warmup eager steps of the headline workload and exit (hardware-counter passes)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run three plain device copies of this many MiB and exit (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -231,6 +272,24 @@ def main():
     mm.lib()
 
     headline = synth.WORKLOADS[HEADLINE].products
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.eager_only:
+        cases = [Case(p, dev) for p in headline]
+        sp = torch.cuda.current_stream().cuda_stream
+        for w in range(args.warmup):
+            for c in cases:
+                c.run(w, sp)
+        torch.cuda.synchronize()
+        print(json.dumps({"eager_steps": args.warmup, "launches": {c.p.name: c.info for c in cases}}), flush=True)
+        return
     if args.only:
         names = args.only.split(",")
         prods = [p for p in synth.all_products() if p.name in names]
@@ -259,9 +318,9 @@ def main():
     achieved = dc.flops / (avgs[dom] * 1e-3) / 1e12
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_PEAK_TFLOPS[dc.dt], "unit": "TFLOP/s",
-        "frac": round(achieved / MFMA_PEAK_TFLOPS[dc.dt], 4), "traffic": None,
+        "frac": round(achieved / MFMA_PEAK_TFLOPS[dc.dt], 4), "traffic": recorded_traffic(dc.p.name, dc.info["tile"]),
         "kernel": f"general {dc.info['tile']} on {dc.p.name}", "avg_launch_us": round(avgs[dom] * 1e3, 3),
-        "flops_per_launch": dc.flops,
+        "flops_per_launch": dc.flops, "algorithmic_bytes_per_launch": dc.bytes,
     }
 
     out = {
