@@ -8,7 +8,8 @@
 //
 // Split-K reduction: same page, section "Parallel execution" (K partitioned
 // into partial products that are summed afterwards).  Partials are summed in
-// ascending partition order, so the result is bitwise reproducible.
+// an order fixed by the split count alone, so the result is bitwise
+// reproducible.
 #include "device.h"
 
 namespace mm {
@@ -44,18 +45,55 @@ __global__ __launch_bounds__(256) void k_fill_zero(S *__restrict__ Y, int64_t n)
 }
 
 // Y[i] = narrow(sum_{s=0}^{split-1} W[s][i]) for every output element i.
-template <int DT>
+//
+// A workgroup owns OG groups of four consecutive outputs and SG partition
+// lanes (OG * SG = 256).  Partition lane g sums the partitions g, g + SG,
+// g + 2 SG, ... in ascending order; the SG lane sums are then combined by a
+// fixed pairwise tree in LDS.  The order depends only on the split count, so
+// results are bitwise reproducible.  Lanes that share a partition read
+// consecutive outputs, so each load instruction covers contiguous memory.
+template <int DT, int SG, bool VEC>
 __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a) {
     using E = Elem<DT>;
     using S = typename E::S;
+    constexpr int OG = 256 / SG;
+    const int t = threadIdx.x, og = t % OG, sg = t / OG;
     const int64_t total = a.batch * a.M * a.N;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t o0 = ((int64_t)blockIdx.x * OG + og) * 4;
     const float *__restrict__ W = a.W;
-    S *__restrict__ Y = (S *)a.Y;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-        float acc = W[i];
-        for (int s = 1; s < a.split; ++s) acc += W[(int64_t)s * total + i];
-        Y[i] = E::from_f32(acc);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (o0 < total) {
+        if constexpr (VEC) {
+            // total is a multiple of 4: every group is whole and 16-byte aligned.
+#pragma unroll 4
+            for (int s = sg; s < a.split; s += SG) {
+                const float4 v = *(const float4 *)(W + (int64_t)s * total + o0);
+                acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+            }
+        } else {
+            for (int s = sg; s < a.split; s += SG)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (o0 + e < total) acc[e] += W[(int64_t)s * total + o0 + e];
+        }
+    }
+    __shared__ float red[SG][OG][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[sg][og][e] = acc[e];
+    __syncthreads();
+#pragma unroll
+    for (int w = SG / 2; w >= 1; w >>= 1) {
+        if (sg < w) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[sg][og][e] += red[sg + w][og][e];
+        }
+        __syncthreads();
+    }
+    if (sg == 0 && o0 < total) {
+        S *__restrict__ Y = (S *)a.Y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (o0 + e < total) Y[o0 + e] = E::from_f32(red[0][og][e]);
     }
 }
 
@@ -84,15 +122,36 @@ hipError_t launch_fill_zero(int dtype, void *Y, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DT, int SG>
+static hipError_t launch_reduce_sg(const KArgs &a, hipStream_t s) {
+    const int64_t total = a.batch * a.M * a.N;
+    const int64_t groups = (total + 3) / 4;
+    const int64_t g = (groups + 256 / SG - 1) / (256 / SG);
+    if (g > 0x7fffffff) return hipErrorInvalidValue;
+    if (total % 4 == 0) hipLaunchKernelGGL((k_splitk_reduce<DT, SG, true>), dim3((unsigned)g), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_splitk_reduce<DT, SG, false>), dim3((unsigned)g), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_reduce_dt(const KArgs &a, hipStream_t s) {
+    // Partition lanes: the split count rounded up to a power of two, at most 64.
+    if (a.split <= 1) return launch_reduce_sg<DT, 1>(a, s);
+    if (a.split <= 2) return launch_reduce_sg<DT, 2>(a, s);
+    if (a.split <= 4) return launch_reduce_sg<DT, 4>(a, s);
+    if (a.split <= 8) return launch_reduce_sg<DT, 8>(a, s);
+    if (a.split <= 16) return launch_reduce_sg<DT, 16>(a, s);
+    if (a.split <= 32) return launch_reduce_sg<DT, 32>(a, s);
+    return launch_reduce_sg<DT, 64>(a, s);
+}
+
 hipError_t launch_splitk_reduce(int dtype, const KArgs &a, hipStream_t s) {
-    const unsigned g = grid_for(a.batch * a.M * a.N, 65536);
     switch (dtype) {
-    case MM_FLOAT: hipLaunchKernelGGL(k_splitk_reduce<MM_FLOAT>, dim3(g), dim3(256), 0, s, a); break;
-    case MM_FLOAT16: hipLaunchKernelGGL(k_splitk_reduce<MM_FLOAT16>, dim3(g), dim3(256), 0, s, a); break;
-    case MM_BFLOAT16: hipLaunchKernelGGL(k_splitk_reduce<MM_BFLOAT16>, dim3(g), dim3(256), 0, s, a); break;
+    case MM_FLOAT: return launch_reduce_dt<MM_FLOAT>(a, s);
+    case MM_FLOAT16: return launch_reduce_dt<MM_FLOAT16>(a, s);
+    case MM_BFLOAT16: return launch_reduce_dt<MM_BFLOAT16>(a, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace mm

@@ -233,10 +233,10 @@ static void plan_split(mm_plan_s *p, int requested) {
     if (requested > 0) {
         s = requested;
     } else {
-        // Aim for about two workgroups per CU, with at least 1024 K elements
-        // per partition (the partials then cost little next to the inputs).
-        int64_t want = cdiv(2 * (int64_t)kNumCUs, std::max<int64_t>(tiles, 1));
-        int64_t max_s = std::max<int64_t>(1, p->K / 1024);
+        // Aim for about one workgroup per CU, with at least 256 K elements
+        // per partition (the partials then stay small next to the inputs).
+        int64_t want = cdiv((int64_t)kNumCUs, std::max<int64_t>(tiles, 1));
+        int64_t max_s = std::max<int64_t>(1, p->K / 256);
         s = std::min(want, max_s);
     }
     s = std::max<int64_t>(1, std::min(s, kblocks));
