@@ -14,13 +14,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-// FP32 -> BF16, round to nearest, ties to even; NaN stays a (quiet) NaN with
-// its sign, values beyond the largest finite BF16 round to infinity.
+// FP32 -> BF16, round to nearest, ties to even; NaN stays a (quiet) NaN,
+// values beyond the largest finite BF16 round to infinity.  gfx950 converts
+// in hardware (v_cvt_pk_bf16_f32), one instruction and no branches.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
 }
 
 // FP32 -> FP16 with the hardware conversion (IEEE round to nearest even,
@@ -51,6 +50,12 @@ struct Elem<MM_FLOAT16> {
     static constexpr int kVE = 8;
     __device__ static __forceinline__ float to_f32(S x) { return f16_to_f32(x); }
     __device__ static __forceinline__ S from_f32(float x) { return f32_to_f16(x); }
+    // Two narrowed values in one word, `lo` in the low half.
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
 };
 
 template <>
@@ -59,6 +64,12 @@ struct Elem<MM_BFLOAT16> {
     static constexpr int kVE = 8;
     __device__ static __forceinline__ float to_f32(S x) { return bf16_to_f32(x); }
     __device__ static __forceinline__ S from_f32(float x) { return f32_to_bf16(x); }
+    // Two narrowed values in one word, `lo` in the low half (one v_cvt_pk_bf16_f32).
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        const b2 v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
 };
 
 // Element offsets of the A and B matrices used by output batch `b`.

@@ -480,22 +480,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
             }
         }
     };
+    // The B fragment is the first MFMA operand, so each 32x32 accumulator holds
+    // the transposed output block: column n of the block in the MFMA's row
+    // position, row m in its column position.
     auto mfmas = [&](int slot) {
         if constexpr (DT == MM_BFLOAT16) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[slot][i]),
-                                                                       __builtin_bit_cast(bf16x8, fb[slot][j]),
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fb[slot][j]),
+                                                                       __builtin_bit_cast(bf16x8, fa[slot][i]),
                                                                        acc[i][j], 0, 0, 0);
         } else if constexpr (DT == MM_FLOAT16) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[slot][i]),
-                                                                      __builtin_bit_cast(f16x8, fb[slot][j]),
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fb[slot][j]),
+                                                                      __builtin_bit_cast(f16x8, fa[slot][i]),
                                                                       acc[i][j], 0, 0, 0);
         } else {
 #pragma unroll
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
                         const uint4 &y = fb[slot][j];
                         const float av = __uint_as_float(e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w);
                         const float bv = __uint_as_float(e == 0 ? y.x : e == 1 ? y.y : e == 2 ? y.z : y.w);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv, av, acc[i][j], 0, 0, 0);
                     }
         }
     };
@@ -538,47 +541,55 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
         }
     }
 
-    // Epilogue through LDS: each wave narrows its accumulators into a
-    // row-major tile of output rows (16-byte chunks of row r at
-    // chunk ^ (r & 7)), then the workgroup writes whole 16-byte chunks of
-    // output rows.  Tiles larger than the stage buffers go in row passes.
-    // MFMA 32x32 block (i, j), element r of a lane: row 8(r/4) + 4(lane/32)
-    // + r%4, column lane % 32.
+    // Epilogue through LDS.  Element r of a lane's accumulator block (i, j) is
+    // output row (lane % 32) and column 8(r/4) + 4(lane/32) + r%4 of the
+    // block, so the four elements r = 4q..4q+3 are four consecutive columns of
+    // one row: one 8-byte (16-bit output) or 16-byte (FP32) LDS write.  The
+    // tile is row-major with 16-byte chunk c of tile row r at c ^ (r % OCPR),
+    // which spreads the 32 rows of one write over distinct chunks; the
+    // workgroup then writes whole 16-byte chunks of output rows.  Tiles larger
+    // than the stage buffers go in row passes.
     using O = typename std::conditional<SPLIT, float, S>::type;
     constexpr int OS = (int)sizeof(O);
     constexpr int OV = 16 / OS;            // output elements per chunk
     constexpr int OCPR = BN * OS / 16;     // output chunks per tile row
     constexpr int NP = (BM * BN * OS + STAGES * STAGE_BYTES - 1) / (STAGES * STAGE_BYTES);
     constexpr int PR = BM / NP;            // tile rows per pass
-    static_assert(BM % NP == 0 && PR % 8 == 0, "epilogue passes");
-    O *tile = (O *)lds;
+    static_assert(BM % NP == 0, "epilogue passes");
+    static_assert((OCPR & (OCPR - 1)) == 0 && OCPR >= 8, "tile row swizzle");
+    char *tile = lds;
     O *out = SPLIT ? (O *)(a.W + (sidx * a.batch + b) * M * N) : (O *)((S *)a.Y + b * M * N);
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i) {
+            const int rl = wr * WM + i * 32 + (lane & 31) - pass * PR;
+            if (NP == 1 || (rl >= 0 && rl < PR)) {
+                char *trow = tile + rl * (BN * OS);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rl = wr * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - pass * PR;
-                    if (NP == 1 || (rl >= 0 && rl < PR)) {
-                        const int cl = wc * WN + j * 32 + (lane & 31);
-                        const int ch = (cl / OV) ^ (rl & 7);
-                        O v;
-                        if constexpr (SPLIT) v = acc[i][j][r];
-                        else v = E::from_f32(acc[i][j][r]);
-                        tile[rl * BN + ch * OV + (cl % OV)] = v;
+                    for (int q = 0; q < 4; ++q) {
+                        const int cl = wc * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+                        const int ch = (cl / OV) ^ (rl & (OCPR - 1));
+                        char *dst = trow + ch * 16 + (cl % OV) * OS;
+                        const f32x16 &v = acc[i][j];
+                        if constexpr (OS == 4) {
+                            *(float4 *)dst = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+                        } else {
+                            *(uint2 *)dst = make_uint2(E::pack2(v[4 * q], v[4 * q + 1]), E::pack2(v[4 * q + 2], v[4 * q + 3]));
+                        }
                     }
-                }
+            }
+        }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         for (int idx = tid; idx < PR * OCPR; idx += 64 * NW) {
             const int rl = idx / OCPR, c = idx % OCPR;
             const int64_t row = m0 + pass * PR + rl, col = n0 + (int64_t)c * OV;
             if (row < M && col < N) {
-                const uint4 v = *(const uint4 *)&tile[rl * BN + (c ^ (rl & 7)) * OV];
+                const uint4 v = *(const uint4 *)(tile + rl * (BN * OS) + (c ^ (rl & (OCPR - 1))) * 16);
                 O *dst = out + row * N + col;
                 if (a.y_vec) {
                     // Rows are whole 16-byte chunks: the chunk lies inside the row.
