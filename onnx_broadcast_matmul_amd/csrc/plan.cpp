@@ -57,38 +57,27 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // byte more often); used only to rank entries against each other.
 static double tile_quality(int dtype, int index) {
     static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8};
-    static const double q32[kNumTiles32] = {1.0, 0.9, 0.8, 1.1};
+    static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1};
     return dtype == MM_FLOAT ? q32[index] : q16[index];
-}
-
-// LDS bytes of a tile entry's stage buffers.
-static int64_t tile_lds_bytes(int dtype, const TileCfg *t) {
-    const int64_t es = elem_size(dtype);
-    return (int64_t)t->stages * ((int64_t)t->bm * t->bkb + (t->bkb / es) * t->bn * es);
 }
 
 // Estimated useful fraction of the machine for a tile entry: wave
 // quantization over the CUs, tile padding at the edges, and tile quality.
-// A tile that leaves room for a single workgroup per CU cannot hide the
-// load latency of a K loop of only one or two stages behind a neighbour.
-static double tile_score(int dtype, int index, int64_t batch, int64_t M, int64_t N, int64_t K) {
+static double tile_score(int dtype, int index, int64_t batch, int64_t M, int64_t N) {
     const TileCfg *t = tile_entry(dtype, index);
     int64_t tm = cdiv(M, t->bm), tn = cdiv(N, t->bn);
     double tiles = (double)batch * (double)tm * (double)tn;
     double waves = ceil(tiles / kNumCUs);
     double occ = tiles / (waves * kNumCUs);
     double pad = ((double)M * (double)N) / ((double)(tm * t->bm) * (double)(tn * t->bn));
-    const int64_t stage_k = t->bkb / elem_size(dtype);
-    const bool one_per_cu = 2 * tile_lds_bytes(dtype, t) > 160 * 1024;
-    const double short_k = (one_per_cu && K <= 2 * stage_k) ? 0.85 : 1.0;
-    return occ * pad * tile_quality(dtype, index) * short_k;
+    return occ * pad * tile_quality(dtype, index);
 }
 
-static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K) {
+static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N) {
     int best = 0;
     double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
-        double s = tile_score(dtype, i, batch, M, N, K);
+        double s = tile_score(dtype, i, batch, M, N);
         if (s > best_s + 1e-9) {
             best_s = s;
             best = i;
@@ -299,7 +288,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         if (req < 0 || req > tile_count(p->dtype))
             return fail(MM_ERR_BAD_OPTION, "tile %d out of range 0..%d", req, tile_count(p->dtype));
         if (req > 0) p->tile = req - 1;
-        else if (algo == MM_ALGO_GENERAL) p->tile = choose_tile(p->dtype, p->batch, M, N, K);
+        else if (algo == MM_ALGO_GENERAL) p->tile = choose_tile(p->dtype, p->batch, M, N);
         else p->tile = choose_split_tile(p->dtype, M, N);
         const TileCfg *t = tile_entry(p->dtype, p->tile);
         const int64_t tiles = p->batch * cdiv(M, t->bm) * cdiv(N, t->bn);

@@ -31,6 +31,7 @@ constexpr TileCfg kTiles32[] = {
     {128, 64, 2, 2, 128, 3, 4},
     {64, 64, 2, 2, 128, 3, 4},
     {256, 128, 2, 4, 128, 3, 4},
+    {128, 128, 2, 2, 128, 2, 4},
 };
 
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
