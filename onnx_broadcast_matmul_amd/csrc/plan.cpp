@@ -387,7 +387,7 @@ mm_status mm_tile_config(int dtype, int index, int *bm, int *bn, int *bk) {
     if (!t) return fail(MM_ERR_BAD_OPTION, "no tile %d for dtype %d", index, dtype);
     if (bm) *bm = t->bm;
     if (bn) *bn = t->bn;
-    if (bk) *bk = stage_k(dtype);
+    if (bk) *bk = t->bkb / elem_size(dtype);
     return MM_OK;
 }
 

@@ -37,8 +37,16 @@ constexpr TileCfg kTiles32[] = {
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
 constexpr int kNumTiles32 = sizeof(kTiles32) / sizeof(kTiles32[0]);
 
-// K elements held per LDS stage (one 128-byte row segment).
+// K granularity of split-K partitions: 128 bytes of K, a whole number of
+// LDS stages of every tile entry.
 inline int stage_k(int dtype) { return dtype == MM_FLOAT ? 32 : 64; }
-static_assert(kTiles16[0].bkb == 128 && kTiles32[0].bkb == 128, "stage_k assumes 128-byte stages");
+constexpr bool stages_divide_128() {
+    for (const TileCfg &t : kTiles16)
+        if (128 % t.bkb != 0) return false;
+    for (const TileCfg &t : kTiles32)
+        if (128 % t.bkb != 0) return false;
+    return true;
+}
+static_assert(stages_divide_128(), "split-K granularity must be a whole number of stages");
 
 }  // namespace mm
