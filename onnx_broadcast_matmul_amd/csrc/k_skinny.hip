@@ -21,6 +21,16 @@
 // (two products into an FP32 sum).  Each lane's NT partial sums are reduced
 // over its 8-lane group with a fixed butterfly, then over the K-split waves in
 // wave order through LDS.
+//
+// Skinny-N with eight columns and K <= 4096 (16-bit types) has a kernel of
+// its own, built around the access pattern that streams A fastest: every
+// load instruction of a wave reads 1 KB of one row (16 bytes per lane).  The
+// eight waves of a workgroup take the eight 512-element parts of K; a lane
+// keeps its 8 x 8 slice of B in registers, forms 8 rows x 8 columns of
+// partial dot products, and a transpose-reduce over the 64 lanes (register
+// swaps across the wave halves and rows, then DPP exchanges, all in a fixed
+// order) leaves lane L with the sum for row L / 8, column L % 8.  B is staged
+// once per workgroup through LDS; A is read once, non-temporally.
 #include <type_traits>
 
 #include "device.h"
@@ -385,6 +395,167 @@ __global__ __launch_bounds__(64 * kSkNWaves) void k_skinny_n(KArgs a) {
     }
 }
 
+// ------------------------------------------------- skinny-N, eight columns
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// v[0..63] of every lane -> v[0] of lane L = sum over all 64 lanes of v[L].
+// Each step pairs lanes that hold the same index set across one lane bit and
+// keeps the half of the indices named by that bit: bits 5 and 4 with the
+// gfx950 half-wave and row swaps, bits 3..0 with DPP row mirror, half-row
+// mirror and quad permutations.  The order of additions is fixed.
+__device__ __forceinline__ void transpose_reduce64(float *v, int lane) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 32]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 16]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // row mirror: lane j <-> 15 - j
+        const float x = v[i] + dpp_move<0x140>(v[i]), y = v[i + 8] + dpp_move<0x140>(v[i + 8]);
+        v[i] = b3 ? y : x;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // half-row mirror: lane j <-> 7 - j
+        const float x = v[i] + dpp_move<0x141>(v[i]), y = v[i + 4] + dpp_move<0x141>(v[i + 4]);
+        v[i] = b2 ? y : x;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // quad permutation [2, 3, 0, 1]
+        const float x = v[i] + dpp_move<0x4E>(v[i]), y = v[i + 2] + dpp_move<0x4E>(v[i + 2]);
+        v[i] = b1 ? y : x;
+    }
+    {  // quad permutation [1, 0, 3, 2]
+        const float x = v[0] + dpp_move<0xB1>(v[0]), y = v[1] + dpp_move<0xB1>(v[1]);
+        v[0] = b0 ? y : x;
+    }
+}
+
+constexpr int kSkN8MaxK = 4096;  // eight waves x 512 elements of K
+constexpr int kSkN8Rows = 16;    // rows per workgroup: two rounds of eight
+
+// LDS position of B row k (16 bytes: its eight columns): lanes of one read
+// instruction take rows 8 apart, so the low bits are permuted by bits 3..5.
+__device__ __forceinline__ int skn8_pos(int k) { return k ^ ((k >> 3) & 7); }
+
+template <int DT>
+__global__ __launch_bounds__(512) void k_skinny_n8(KArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using E = Elem<DT>;
+    using S = typename E::S;
+    static_assert(sizeof(S) == 2, "16-bit element types");
+    constexpr int NT = 8, RR = 8, ROUNDS = kSkN8Rows / RR;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) uint4 bs[kSkN8MaxK];
+    __shared__ float red[8][ROUNDS][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t M = a.M, K = a.K;
+    const int64_t nrb = (M + kSkN8Rows - 1) / kSkN8Rows;
+    const int64_t b = blockIdx.x / nrb;
+    const int64_t row0 = (blockIdx.x % nrb) * kSkN8Rows;
+    int64_t oa, ob;
+    batch_offsets(a.bd, b, oa, ob);
+    const S *__restrict__ A = (const S *)a.A + oa;
+    const uint4 *__restrict__ B = (const uint4 *)((const S *)a.B + ob);  // row k of B = chunk k
+    const int k0 = wave * 512 + lane * 8;  // this lane's eight elements of K
+    const bool kin = k0 < K;
+
+    // Every load below is unconditional, from an address clamped into the
+    // operand, and out-of-range values are replaced by zeros afterwards: no
+    // branch separates the loads, so they are all in flight together.
+    // B rows in flight first, then the first round of A rows.
+    uint4 bg[kSkN8MaxK / 512];
+#pragma unroll
+    for (int i = 0; i < kSkN8MaxK / 512; ++i) {
+        const int k = tid + i * 512;
+        bg[i] = B[k < K ? k : K - 1];
+    }
+    const int kc = kin ? k0 : 0;
+    uint32_t av[RR][4];
+    auto load_a = [&](int r) {
+#pragma unroll
+        for (int i = 0; i < RR; ++i) {
+            const int64_t row = row0 + r * RR + i;
+            const bool ok = kin && row < M;
+            const u32x4 t = __builtin_nontemporal_load((const u32x4 *)(A + (row < M ? row : M - 1) * K + kc));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[i][e] = ok ? t[e] : 0u;
+        }
+    };
+    load_a(0);
+    // Rows k >= K hold copies of row K - 1 and are never read.
+#pragma unroll
+    for (int i = 0; i < kSkN8MaxK / 512; ++i) bs[skn8_pos(tid + i * 512)] = bg[i];
+    __syncthreads();
+
+    // This lane's slice of B as (k, k + 1) pairs per column.
+    uint32_t bp[NT][4];
+    {
+        uint32_t w[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 r = bs[skn8_pos(kc + i)];
+            w[i][0] = kin ? r.x : 0u; w[i][1] = kin ? r.y : 0u;
+            w[i][2] = kin ? r.z : 0u; w[i][3] = kin ? r.w : 0u;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const uint32_t lo = (w[2 * p][n / 2] >> (16 * (n & 1))) & 0xffffu;
+                const uint32_t hi = (w[2 * p + 1][n / 2] >> (16 * (n & 1))) & 0xffffu;
+                bp[n][p] = lo | (hi << 16);
+            }
+    }
+
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        if (r > 0) load_a(r);
+        float v[RR * NT];
+#pragma unroll
+        for (int i = 0; i < RR; ++i)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                float s = 0.0f;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    if constexpr (DT == MM_FLOAT16)
+                        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, av[i][p]),
+                                                   __builtin_bit_cast(half2_t, bp[n][p]), s, false);
+                    else
+                        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfloat2_t, av[i][p]),
+                                                            __builtin_bit_cast(bfloat2_t, bp[n][p]), s, false);
+                }
+                v[i * NT + n] = s;
+            }
+        transpose_reduce64(v, lane);
+        red[wave][r][lane] = v[0];
+    }
+    __syncthreads();
+    S *__restrict__ Y = (S *)a.Y + b * M * NT;
+    if (tid < ROUNDS * 64) {
+        const int r = tid / 64, j = tid % 64;
+        float s = red[0][r][j];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) s += red[w][r][j];
+        const int64_t row = row0 + r * RR + j / NT;
+        if (row < M) Y[row * NT + j % NT] = E::from_f32(s);
+    }
+#endif
+}
+
 template <int DT, int NT>
 static hipError_t launch_skn(bool vec, bool bvec, const KArgs &a, hipStream_t s) {
     const int64_t items = a.batch * ((a.N + NT - 1) / NT) * ((a.M + kSkNBlockRows - 1) / kSkNBlockRows);
@@ -406,6 +577,15 @@ static hipError_t launch_skn(bool vec, bool bvec, const KArgs &a, hipStream_t s)
 
 template <int DT>
 static hipError_t launch_skn_dt(bool vec, bool bvec, const KArgs &a, hipStream_t s) {
+    if constexpr (DT != MM_FLOAT) {
+        if (vec && bvec && a.N == 8 && a.K <= kSkN8MaxK) {
+            const int64_t blocks = a.batch * ((a.M + kSkN8Rows - 1) / kSkN8Rows);
+            if (blocks <= 0) return hipSuccess;
+            if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(k_skinny_n8<DT>, dim3((unsigned)blocks), dim3(512), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if (a.N <= 1) return launch_skn<DT, 1>(vec, bvec, a, s);
     if (a.N <= 2) return launch_skn<DT, 2>(vec, bvec, a, s);
     if (a.N <= 4) return launch_skn<DT, 4>(vec, bvec, a, s);

@@ -100,6 +100,18 @@ def test_split_counts(dt, split, dev):
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+def test_skinny_n_eight_columns(dt, dev):
+    """Eight output columns: ragged row counts, K from one chunk to the
+    4096 limit of the register-slice kernel and past it, batched and
+    broadcast B, and small-integer exactness."""
+    cases = [((37, 8), (8, 8)), ((1000, 520), (520, 8)), ((300, 4096), (4096, 8)),
+             ((3, 50, 1024), (3, 1024, 8)), ((2, 40, 2048), (2048, 8)), ((70, 4104), (4104, 8))]
+    for i, (sa, sb) in enumerate(cases):
+        plan, _, _ = parity(sa, sb, dt, dev, algo=mm.ALGO_SKINNY_N, seed=40 + i)
+        parity(sa, sb, dt, dev, algo=mm.ALGO_SKINNY_N, seed=40 + i, dist=("int",), exact=True)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
 @pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
 def test_small_integer_bit_exact(dt, algo, dev):
     parity((2, 130, 1000), (1000, 70), dt, dev, algo=algo, dist=("int",), exact=True)
