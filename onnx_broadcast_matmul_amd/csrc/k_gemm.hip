@@ -651,7 +651,6 @@ static hipError_t launch_16(int tile, bool vec, bool split, const KArgs &a, hipS
         MM_TILE_CASE(DT, kTiles16, 5);
         MM_TILE_CASE(DT, kTiles16, 6);
         MM_TILE_CASE(DT, kTiles16, 7);
-        MM_TILE_CASE(DT, kTiles16, 8);
     }
     return hipErrorInvalidValue;
 }
@@ -663,13 +662,12 @@ static hipError_t launch_32(int tile, bool vec, bool split, const KArgs &a, hipS
         MM_TILE_CASE(MM_FLOAT, kTiles32, 2);
         MM_TILE_CASE(MM_FLOAT, kTiles32, 3);
         MM_TILE_CASE(MM_FLOAT, kTiles32, 4);
-        MM_TILE_CASE(MM_FLOAT, kTiles32, 5);
     }
     return hipErrorInvalidValue;
 }
 #undef MM_TILE_CASE
 
-static_assert(kNumTiles16 == 9 && kNumTiles32 == 6, "launch switch must cover the tile table");
+static_assert(kNumTiles16 == 8 && kNumTiles32 == 5, "launch switch must cover the tile table");
 
 hipError_t launch_general(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s) {
     const bool vec = al.a && al.b;

@@ -56,8 +56,8 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Relative per-CU throughput of a tile entry (bigger tiles reuse each LDS
 // byte more often); used only to rank entries against each other.
 static double tile_quality(int dtype, int index) {
-    static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.3};
-    static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.3};
+    static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8};
+    static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1};
     return dtype == MM_FLOAT ? q32[index] : q16[index];
 }
 
@@ -86,16 +86,14 @@ static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N) {
     return best;
 }
 
-// Smallest-padding tile for split-K (its output is tiny by construction);
-// among equals, the deepest pipeline, since each partition streams its slices
-// of A and B once.
+// Smallest-padding tile for split-K (its output is tiny by construction).
 static int choose_split_tile(int dtype, int64_t M, int64_t N) {
     int best = 0;
     double best_pad = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
         const TileCfg *t = tile_entry(dtype, i);
         double pad = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
-        if (pad > best_pad + 1e-9 || (pad > best_pad - 1e-9 && t->stages > tile_entry(dtype, best)->stages)) {
+        if (pad > best_pad + 1e-9) {
             best_pad = pad;
             best = i;
         }

@@ -6,10 +6,7 @@
 // kernel stages bkb bytes of K per row (64 elements of a 16-bit type, 32 of
 // FP32 for bkb = 128) in `stages` LDS buffers, filled by the first
 // `producers` waves.  The element-wise fallback kernel uses the block tile
-// only.  The selector picks an entry per shape; tests force each one.  The
-// last entry of each table keeps seven 16 KB stages in flight: split-K
-// partitions stream their A and B slices once, so a deep pipeline, not
-// operand reuse, decides their speed.
+// only.  The selector picks an entry per shape; tests force each one.
 #pragma once
 
 #include "internal.h"
@@ -26,7 +23,6 @@ constexpr TileCfg kTiles16[] = {
     {128, 128, 2, 2, 128, 2, 4},
     {128, 256, 2, 4, 128, 2, 4},
     {256, 128, 4, 2, 128, 2, 4},
-    {64, 64, 2, 2, 128, 8, 4},
 };
 
 // FLOAT entries.
@@ -36,7 +32,6 @@ constexpr TileCfg kTiles32[] = {
     {64, 64, 2, 2, 128, 3, 4},
     {256, 128, 2, 4, 128, 3, 4},
     {128, 128, 2, 2, 128, 2, 4},
-    {64, 64, 2, 2, 128, 8, 4},
 };
 
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
