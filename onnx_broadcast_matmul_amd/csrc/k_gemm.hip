@@ -262,10 +262,14 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
 // * Each direct load moves 16 bytes per lane into LDS at base + 16 * lane.
 //   The LDS swizzle is realised by choosing which global chunk each lane
 //   fetches: A rows of 128 (64) bytes store logical chunk c at
-//   c ^ (row & 7) (c ^ ((row >> 1) & 3)); B rows store chunk c at
-//   c ^ (2 * (k & 3)).  Chunks outside the matrix (rows past M, columns past
-//   N, K past the partition end) take an offset outside the buffer range,
-//   for which the hardware returns zeros, so tails need no branches.
+//   c ^ ((row >> 1) & 7) (c ^ ((row >> 2) & 3)), so the 16 rows that one
+//   quarter-wave of fragment reads touches fall on 16 distinct 16-byte bank
+//   groups; B rows store chunk c at c ^ bswz(k), chosen so that one
+//   transposing read (16-bit) or one column read (FP32) touches distinct
+//   bank groups across its lanes.  Chunks outside the matrix (rows past M,
+//   columns past N, K past the partition end) take an offset outside the
+//   buffer range, for which the hardware returns zeros, so tails need no
+//   branches.
 // * MFMA A operands are 16-byte LDS reads of the swizzled rows.  B operands
 //   for the 16-bit types come from ds_read_b64_tr_b16: in each group of 16
 //   lanes, lanes 4r..4r+3 address row r of a 4 x 16 block of B and lane i
@@ -345,6 +349,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
     static_assert(CPR >= 8 && RBB <= 1024, "B rows");
     static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
     static_assert((STAGES - 2) * LPW < 64, "vmcnt range");
+    static_assert((CPR & (CPR - 1)) == 0, "B row chunks");
+    // 16-byte chunk position swizzles of A rows and B rows (see above).
+    // 16-bit B: a transposing read covers k = 4 consecutive rows and n = 4
+    // chunks per half-wave; FP32 B: the two half-waves read rows k and k + 4.
+    auto aswz = [](int row) { return CA == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
+    auto bswz = [](int k) {
+        if constexpr (ES == 4) return 8 * ((k >> 2) & 1);
+        else if constexpr (CPR >= 16) return 4 * (k & 3);
+        else return 4 * ((k >> 1) & 1);
+    };
 
     __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds);
@@ -390,7 +404,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
     for (int q = 0; q < A_INSTR; ++q) {
         const int row = (wave * A_INSTR + q) * A_RPB + lane / CA;
         const int p = lane % CA;
-        const int c = CA == 8 ? (p ^ (row & 7)) : (p ^ ((row >> 1) & 3));
+        const int c = p ^ aswz(row);
         a_off[q] = (uint32_t)(row * K * ES + c * 16);
         a_k[q] = c * VE;
         a_ok[q] = m0 + row < M;
@@ -402,7 +416,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
     for (int q = 0; q < B_INSTR; ++q) {
         const int row = (wave * B_INSTR + q) * B_RPB + lane / CPR;  // k within the stage
         const int p = lane % CPR;
-        const int c = p ^ (2 * (row & 3));
+        const int c = p ^ bswz(row);
         b_off[q] = (uint32_t)((int64_t)row * N * ES + c * 16);
         b_k[q] = row;
         b_ok[q] = n0 + c * VE < N;
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int row = wr * WM + i * 32 + (lane & 31);
-            const int p = CA == 8 ? (c ^ (row & 7)) : (c ^ ((row >> 1) & 3));
+            const int p = c ^ aswz(row);
             fa[slot][i] = *(const uint4 *)(As + row * BKB + p * 16);
         }
         if constexpr (ES == 2) {
@@ -454,7 +468,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int k = ks * 16 + (G >> 1) * 8 + h * 4 + (jl >> 2);
-                    const int p = (n >> 3) ^ (2 * (k & 3));
+                    const int p = (n >> 3) ^ bswz(k);
                     const char *addr = Bs + k * RBB + p * 16 + ((n >> 2) & 1) * 8;
                     if constexpr (DT == MM_BFLOAT16)
                         h2[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -473,7 +487,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int k = c * 4 + e;
-                    const int p = (n >> 2) ^ (2 * (k & 3));
+                    const int p = (n >> 2) ^ bswz(k);
                     v[e] = *(const uint32_t *)(Bs + k * RBB + p * 16 + (n & 3) * 4);
                 }
                 fb[slot][j] = make_uint4(v[0], v[1], v[2], v[3]);
