@@ -56,6 +56,7 @@ struct TileCfg {
     int bkb;        // bytes of K per row and LDS stage
     int stages;     // LDS stages
     int producers;  // waves that issue the global-to-LDS loads
+    int kgroups;    // wave groups that split each stage's K steps (1: none)
 };
 
 // Number of tile table entries and the entries, per element type.

@@ -318,12 +318,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, bool SPLIT>
-__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
+template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool SPLIT>
+__global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using E = Elem<DT>;
     using S = typename E::S;
-    constexpr int NW = WGM * WGN;
+    constexpr int NWC = WGM * WGN;         // waves of one K group
+    constexpr int NW = NWC * KG;
     constexpr int ES = (int)sizeof(S);
     constexpr int VE = 16 / ES;            // elements per 16-byte chunk
     constexpr int BK = BKB / ES;           // K elements per stage
@@ -350,6 +351,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
     static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
     static_assert((STAGES - 2) * LPW < 64, "vmcnt range");
     static_assert((CPR & (CPR - 1)) == 0, "B row chunks");
+    static_assert(KG >= 1 && KS % KG == 0, "K groups split the MFMA steps of a stage");
     // 16-byte chunk position swizzles of A rows and B rows (see above).
     // 16-bit B: a transposing read covers k = 4 consecutive rows and n = 4
     // chunks per half-wave; FP32 B: the two half-waves read rows k and k + 4.
@@ -366,7 +368,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wr = wave / WGN, wc = wave % WGN;
+    const int kg = wave / NWC;             // K group: MFMA steps kg, kg + KG, ...
+    const int wr = (wave % NWC) / WGN, wc = wave % WGN;
 
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -547,11 +550,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
         const int buf = kt % STAGES;
-        read_frags(buf, 0, 0);
+        if constexpr (KG == 1) {
+            read_frags(buf, 0, 0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) read_frags(buf, ks + 1, (ks + 1) & 1);
-            mfmas(ks & 1);
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS) read_frags(buf, ks + 1, (ks + 1) & 1);
+                mfmas(ks & 1);
+            }
+        } else {
+            read_frags(buf, kg, 0);
+#pragma unroll
+            for (int j = 0; j < KS / KG; ++j) {
+                if (j + 1 < KS / KG) read_frags(buf, kg + (j + 1) * KG, (j + 1) & 1);
+                mfmas(j & 1);
+            }
         }
     }
 
@@ -573,6 +585,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
     static_assert((OCPR & (OCPR - 1)) == 0 && OCPR >= 8, "tile row swizzle");
     char *tile = lds;
     O *out = SPLIT ? (O *)(a.W + (sidx * a.batch + b) * M * N) : (O *)((S *)a.Y + b * M * N);
+    if constexpr (KG > 1) {
+        // Groups 1..KG-1 hand their accumulators to group 0 through LDS
+        // (element-major, lane-contiguous), which adds them in group order.
+        static_assert((KG - 1) * BM * BN * 4 <= STAGES * STAGE_BYTES, "K-group exchange fits in LDS");
+        float *xch = (float *)lds;
+        const int wq = wave % NWC;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kg > 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        xch[((((kg - 1) * NWC + wq) * FM + i) * FN * 16 + j * 16 + r) * 64 + lane] = acc[i][j][r];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kg == 0) {
+#pragma unroll
+            for (int g = 1; g < KG; ++g)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc[i][j][r] += xch[((((g - 1) * NWC + wq) * FM + i) * FN * 16 + j * 16 + r) * 64 + lane];
+        }
+    }
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
@@ -580,7 +621,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int rl = wr * WM + i * 32 + (lane & 31) - pass * PR;
-            if (NP == 1 || (rl >= 0 && rl < PR)) {
+            if (kg == 0 && (NP == 1 || (rl >= 0 && rl < PR))) {
                 char *trow = tile + rl * (BN * OS);
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
@@ -622,7 +663,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_lds_dma(KArgs a) {
 #endif
 }
 
-template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW>
+template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG>
 static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t s) {
     const int64_t tiles = a.batch * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * (split ? a.split : 1);
     if (tiles <= 0) return hipSuccess;
@@ -633,9 +674,9 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
     constexpr int ES = DT == MM_FLOAT ? 4 : 2;
     const bool fits = (int64_t)BM * a.K * ES < 0x7fff0000LL && (int64_t)(BKB / ES) * a.N * ES < 0x7fff0000LL;
     if (vec && fits) {
-        const dim3 blk(64 * WGM * WGN);
-        if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, false>), g, blk, 0, s, a);
+        const dim3 blk(64 * WGM * WGN * KG);
+        if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false>), g, blk, 0, s, a);
     } else {
         const dim3 blk(256);
         if (vec) {
@@ -652,7 +693,7 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
 #define MM_TILE_CASE(DT, T, IDX)                                                                          \
     case IDX:                                                                                             \
         return launch_tile<DT, T[IDX].bm, T[IDX].bn, T[IDX].wgm, T[IDX].wgn, T[IDX].bkb, T[IDX].stages, \
-                           T[IDX].producers>(vec, split, a, s)
+                           T[IDX].producers, T[IDX].kgroups>(vec, split, a, s)
 
 template <int DT>
 static hipError_t launch_16(int tile, bool vec, bool split, const KArgs &a, hipStream_t s) {
@@ -665,6 +706,8 @@ static hipError_t launch_16(int tile, bool vec, bool split, const KArgs &a, hipS
         MM_TILE_CASE(DT, kTiles16, 5);
         MM_TILE_CASE(DT, kTiles16, 6);
         MM_TILE_CASE(DT, kTiles16, 7);
+        MM_TILE_CASE(DT, kTiles16, 8);
+        MM_TILE_CASE(DT, kTiles16, 9);
     }
     return hipErrorInvalidValue;
 }
@@ -676,12 +719,14 @@ static hipError_t launch_32(int tile, bool vec, bool split, const KArgs &a, hipS
         MM_TILE_CASE(MM_FLOAT, kTiles32, 2);
         MM_TILE_CASE(MM_FLOAT, kTiles32, 3);
         MM_TILE_CASE(MM_FLOAT, kTiles32, 4);
+        MM_TILE_CASE(MM_FLOAT, kTiles32, 5);
+        MM_TILE_CASE(MM_FLOAT, kTiles32, 6);
     }
     return hipErrorInvalidValue;
 }
 #undef MM_TILE_CASE
 
-static_assert(kNumTiles16 == 8 && kNumTiles32 == 5, "launch switch must cover the tile table");
+static_assert(kNumTiles16 == 10 && kNumTiles32 == 7, "launch switch must cover the tile table");
 
 hipError_t launch_general(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s) {
     const bool vec = al.a && al.b;

@@ -56,8 +56,8 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Relative per-CU throughput of a tile entry (bigger tiles reuse each LDS
 // byte more often); used only to rank entries against each other.
 static double tile_quality(int dtype, int index) {
-    static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8};
-    static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1};
+    static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5};
+    static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15};
     return dtype == MM_FLOAT ? q32[index] : q16[index];
 }
 

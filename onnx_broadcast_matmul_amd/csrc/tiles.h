@@ -1,7 +1,9 @@
 // tiles.h -- tile table of the tiled MFMA kernels (host and device).
 //
 // An entry is a block tile bm x bn run by wgm x wgn waves, each wave owning a
-// (bm/wgm) x (bn/wgn) sub-tile.  Eight waves put two waves on every SIMD, so
+// (bm/wgm) x (bn/wgn) sub-tile; with kgroups > 1 there are kgroups such sets
+// of waves, each taking every kgroups-th MFMA step of a stage, and their
+// accumulators are added in group order before the epilogue.  Eight waves put two waves on every SIMD, so
 // one wave's MFMAs cover the other's LDS and barrier waits.  The vectorized
 // kernel stages bkb bytes of K per row (64 elements of a 16-bit type, 32 of
 // FP32 for bkb = 128) in `stages` LDS buffers, filled by the first
@@ -15,23 +17,27 @@ namespace mm {
 
 // FLOAT16 / BFLOAT16 entries.
 constexpr TileCfg kTiles16[] = {
-    {256, 256, 2, 4, 128, 2, 4},
-    {256, 128, 2, 2, 128, 3, 4},
-    {128, 128, 2, 2, 128, 3, 4},
-    {128, 64, 2, 2, 128, 3, 4},
-    {64, 64, 2, 2, 128, 3, 4},
-    {128, 128, 2, 2, 128, 2, 4},
-    {128, 256, 2, 4, 128, 2, 4},
-    {256, 128, 4, 2, 128, 2, 4},
+    {256, 256, 2, 4, 128, 2, 4, 1},
+    {256, 128, 2, 2, 128, 3, 4, 1},
+    {128, 128, 2, 2, 128, 3, 4, 1},
+    {128, 64, 2, 2, 128, 3, 4, 1},
+    {64, 64, 2, 2, 128, 3, 4, 1},
+    {128, 128, 2, 2, 128, 2, 4, 1},
+    {128, 256, 2, 4, 128, 2, 4, 1},
+    {256, 128, 4, 2, 128, 2, 4, 1},
+    {64, 64, 2, 2, 128, 3, 4, 2},
+    {128, 128, 2, 2, 128, 2, 4, 2},
 };
 
 // FLOAT entries.
 constexpr TileCfg kTiles32[] = {
-    {128, 128, 2, 2, 128, 3, 4},
-    {128, 64, 2, 2, 128, 3, 4},
-    {64, 64, 2, 2, 128, 3, 4},
-    {256, 128, 2, 4, 128, 3, 4},
-    {128, 128, 2, 2, 128, 2, 4},
+    {128, 128, 2, 2, 128, 3, 4, 1},
+    {128, 64, 2, 2, 128, 3, 4, 1},
+    {64, 64, 2, 2, 128, 3, 4, 1},
+    {256, 128, 2, 4, 128, 3, 4, 1},
+    {128, 128, 2, 2, 128, 2, 4, 1},
+    {64, 64, 2, 2, 128, 3, 4, 2},
+    {128, 128, 2, 2, 128, 2, 4, 2},
 };
 
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
