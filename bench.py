@@ -36,9 +36,10 @@ from onnx_broadcast_matmul_amd import synth  # noqa: E402
 
 HEADLINE = "fp32_square_and_batched_broadcast"
 # MI355X published peaks: HBM3E 8 TB/s; dense MFMA FP32 157.3 TFLOP/s,
-# FP16/BF16 2.5 PFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP/clk = 2516.6).
+# FP16/BF16 2.5 PFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP/clk = 2516.6), FP64
+# 78.6 TFLOP/s.
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {mm.FLOAT: 157.3, mm.FLOAT16: 2516.6, mm.BFLOAT16: 2516.6}
+MFMA_PEAK_TFLOPS = {mm.FLOAT: 157.3, mm.FLOAT16: 2516.6, mm.BFLOAT16: 2516.6, mm.DOUBLE: 78.6}
 ROTATE_BYTES = 1 << 30  # rotate input/output copies until a step touches >= 1 GiB
 MAX_COPIES = 16
 

@@ -14,7 +14,9 @@
  * dimensions broadcast NumPy style (right-aligned, 1 stretches, otherwise
  * equal).  Inputs and output share one element type; FLOAT16 and BFLOAT16
  * products accumulate in FP32 and are narrowed once, at the end, with
- * round-to-nearest-even.
+ * round-to-nearest-even.  DOUBLE products accumulate in double on the FP64
+ * matrix cores (page "MatMul Kernel Design", section "Types and algorithm
+ * selection": the adapter takes DOUBLE with the same shape rules).
  *
  * Usage: create a plan once per (A shape, B shape, type); execute it any
  * number of times on device buffers; destroy it.  Plan creation touches no
@@ -27,7 +29,7 @@
  *
  * Ownership: the caller owns A, B and Y and keeps them alive until the work
  * enqueued on the stream has completed.  The plan owns its metadata and, for
- * the split-K algorithm, an FP32 workspace on the device of the first
+ * the split-K algorithm, an FP32 (DOUBLE: double) workspace on the device of the first
  * execution (allocated by that first mm_execute, freed by mm_plan_destroy).
  * Because of that workspace, executions of one split-K plan must not overlap
  * on different streams; use one plan per stream.
@@ -50,8 +52,9 @@ extern "C" {
 #define MM_MAX_BATCH_DIMS 8
 #define MM_MAX_RANK (MM_MAX_BATCH_DIMS + 2)
 
-/* Element types: the ONNX TensorProto codes.  DOUBLE is recognised and
- * rejected with MM_ERR_DTYPE (not supported by this library yet). */
+/* Element types: the ONNX TensorProto codes.  DOUBLE has no skinny-M /
+ * skinny-N kernels: the plan runs its skinny shapes on the tiled FP64 kernel,
+ * and forcing SKINNY_M or SKINNY_N for DOUBLE gives MM_ERR_BAD_OPTION. */
 typedef enum mm_dtype {
     MM_FLOAT = 1,
     MM_FLOAT16 = 10,
@@ -83,7 +86,7 @@ typedef enum mm_algo {
     MM_ALGO_DIRECT = 3,    /* tiny products: one thread per output */
     MM_ALGO_SKINNY_M = 4,  /* small M (GEMV): B streamed once along N */
     MM_ALGO_SKINNY_N = 5,  /* small N: A streamed once along K */
-    MM_ALGO_SPLIT_K = 6,   /* tiny output, long K: FP32 partials + ordered reduce */
+    MM_ALGO_SPLIT_K = 6,   /* tiny output, long K: FP32 (DOUBLE: double) partials + ordered reduce */
     MM_ALGO_GENERAL = 7    /* tiled MFMA GEMM with LDS double buffering */
 } mm_algo;
 
@@ -117,7 +120,7 @@ typedef struct mm_plan_info {
     int32_t tile;             /* tile table entry + 1 (0 if not a tiled algorithm) */
     int32_t split_k;          /* K partitions (1 unless SPLIT_K) */
     int64_t k_chunk;          /* K elements per partition */
-    int64_t workspace_bytes;  /* FP32 workspace the plan needs on the device */
+    int64_t workspace_bytes;  /* workspace the plan needs on the device (FP32 or double partials) */
     double flops;             /* 2 * batch * M * N * K of the un-folded problem */
     double min_bytes;         /* element size * (numel A + numel B + numel Y) */
 } mm_plan_info;

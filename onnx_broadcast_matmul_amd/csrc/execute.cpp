@@ -68,12 +68,14 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
     al.a = aligned16(A) && (p->K * es) % 16 == 0;
     al.b = aligned16(B) && (p->N * es) % 16 == 0;
     al.y = aligned16(Y) && (p->N * es) % 16 == 0;
-    // Split-K partials are FP32 rows in a workspace of our own (aligned).
+    // Split-K partials are FP32 rows (double for DOUBLE) in a workspace of
+    // our own (aligned); only the 16- and 32-bit kernels read y_vec.
     a.y_vec = p->algo == MM_ALGO_SPLIT_K ? (p->N * 4) % 16 == 0 : al.y;
 
+    const bool f64 = p->dtype == MM_DOUBLE;
     switch (p->algo) {
     case MM_ALGO_DIRECT:
-        e = launch_direct(p->dtype, a, s);
+        e = f64 ? launch_direct_f64(a, s) : launch_direct(p->dtype, a, s);
         break;
     case MM_ALGO_SKINNY_M:
         e = launch_skinny_m(p->dtype, al, a, s);
@@ -82,14 +84,19 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
         e = launch_skinny_n(p->dtype, al, a, s);
         break;
     case MM_ALGO_GENERAL:
-        e = launch_general(p->dtype, p->tile, al, false, a, s);
+        e = f64 ? launch_general_f64(p->tile, al, false, a, s) : launch_general(p->dtype, p->tile, al, false, a, s);
         break;
     case MM_ALGO_SPLIT_K: {
         mm_status st = ensure_workspace(p);
         if (st != MM_OK) return st;
         a.W = (float *)p->ws;
-        e = launch_general(p->dtype, p->tile, al, true, a, s);
-        if (e == hipSuccess) e = launch_splitk_reduce(p->dtype, a, s);
+        if (f64) {
+            e = launch_general_f64(p->tile, al, true, a, s);
+            if (e == hipSuccess) e = launch_splitk_reduce_f64(a, s);
+        } else {
+            e = launch_general(p->dtype, p->tile, al, true, a, s);
+            if (e == hipSuccess) e = launch_splitk_reduce(p->dtype, a, s);
+        }
         break;
     }
     default:

@@ -28,7 +28,7 @@ struct BatchDesc {
 // Arguments of every kernel (passed by value).  M is the number of rows of
 // one product as the kernels see it (batch*M when A's batch is folded into
 // the rows).  Y is dense [batch][M][N]; W is the split-K workspace
-// [split][batch][M][N] in FP32.
+// [split][batch][M][N] in FP32 (in double for DOUBLE products).
 struct KArgs {
     const void *A;
     const void *B;
@@ -72,5 +72,9 @@ hipError_t launch_general(int dtype, int tile, const Align &al, bool split, cons
 hipError_t launch_splitk_reduce(int dtype, const KArgs &a, hipStream_t s);
 hipError_t launch_skinny_m(int dtype, const Align &al, const KArgs &a, hipStream_t s);
 hipError_t launch_skinny_n(int dtype, const Align &al, const KArgs &a, hipStream_t s);
+// DOUBLE kernels (k_f64.hip); W holds double partials for split-K.
+hipError_t launch_direct_f64(const KArgs &a, hipStream_t s);
+hipError_t launch_general_f64(int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);
+hipError_t launch_splitk_reduce_f64(const KArgs &a, hipStream_t s);
 
 }  // namespace mm

@@ -41,15 +41,17 @@ void clear_error() { g_last_error.clear(); }
 int tile_count(int dtype) {
     if (dtype == MM_FLOAT) return kNumTiles32;
     if (dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) return kNumTiles16;
+    if (dtype == MM_DOUBLE) return kNumTiles64;
     return 0;
 }
 
 const TileCfg *tile_entry(int dtype, int index) {
     if (index < 0 || index >= tile_count(dtype)) return nullptr;
+    if (dtype == MM_DOUBLE) return &kTiles64[index];
     return dtype == MM_FLOAT ? &kTiles32[index] : &kTiles16[index];
 }
 
-int elem_size(int dtype) { return dtype == MM_FLOAT ? 4 : 2; }
+int elem_size(int dtype) { return dtype == MM_DOUBLE ? 8 : dtype == MM_FLOAT ? 4 : 2; }
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -58,6 +60,8 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static double tile_quality(int dtype, int index) {
     static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5};
     static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15};
+    static const double q64[kNumTiles64] = {1.0, 0.8};
+    if (dtype == MM_DOUBLE) return q64[index];
     return dtype == MM_FLOAT ? q32[index] : q16[index];
 }
 
@@ -232,7 +236,8 @@ static void plan_split(mm_plan_s *p, int requested) {
     int64_t chunk_blocks = cdiv(kblocks, s);
     p->kchunk = chunk_blocks * bk;
     p->split = (int32_t)cdiv(p->K, p->kchunk);
-    p->workspace_bytes = (int64_t)p->split * p->batch * p->kernel_m * p->N * (int64_t)sizeof(float);
+    const int64_t part_bytes = p->dtype == MM_DOUBLE ? 8 : 4;  // partials: FP32, or double for DOUBLE
+    p->workspace_bytes = (int64_t)p->split * p->batch * p->kernel_m * p->N * part_bytes;
 }
 
 static mm_status check_limits(const mm_plan_s *p) {
@@ -278,9 +283,14 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         } else {
             algo = MM_ALGO_GENERAL;
         }
+        // DOUBLE has no skinny kernels: its skinny shapes take the tiled
+        // FP64 kernel, which still reads the large operand once.
+        if (p->dtype == MM_DOUBLE && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N)) algo = MM_ALGO_GENERAL;
     }
     if (algo < MM_ALGO_DIRECT || algo > MM_ALGO_GENERAL)
         return fail(MM_ERR_BAD_OPTION, "force_algo %d is not a forcible algorithm", algo);
+    if (p->dtype == MM_DOUBLE && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N))
+        return fail(MM_ERR_BAD_OPTION, "DOUBLE has no skinny-M / skinny-N kernel (force GENERAL or DIRECT)");
     p->algo = algo;
 
     if (algo == MM_ALGO_GENERAL || algo == MM_ALGO_SPLIT_K) {
@@ -316,8 +326,7 @@ mm_status mm_plan_create_ex(const int64_t *a_shape, int a_rank, const int64_t *b
     if (!out) return fail(MM_ERR_NULL_ARG, "out is NULL");
     *out = nullptr;
     if ((!a_shape && a_rank > 0) || (!b_shape && b_rank > 0)) return fail(MM_ERR_NULL_ARG, "shape pointer is NULL");
-    if (dtype == MM_DOUBLE) return fail(MM_ERR_DTYPE, "DOUBLE is not supported yet");
-    if (dtype != MM_FLOAT && dtype != MM_FLOAT16 && dtype != MM_BFLOAT16)
+    if (dtype != MM_FLOAT && dtype != MM_FLOAT16 && dtype != MM_BFLOAT16 && dtype != MM_DOUBLE)
         return fail(MM_ERR_DTYPE, "unknown element type %d", dtype);
     if (opt && opt->reserved != 0) return fail(MM_ERR_BAD_OPTION, "reserved option field must be 0");
     mm_plan_s *p = new (std::nothrow) mm_plan_s();

@@ -40,12 +40,21 @@ constexpr TileCfg kTiles32[] = {
     {128, 128, 2, 2, 128, 2, 4, 2},
 };
 
+// DOUBLE entries (k_f64.hip: 4 waves, 16 doubles of K per stage, two
+// register-staged LDS buffers; the wave, stage and producer fields are those
+// of that kernel).
+constexpr TileCfg kTiles64[] = {
+    {128, 128, 2, 2, 128, 2, 4, 1},
+    {64, 64, 2, 2, 128, 2, 4, 1},
+};
+
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
 constexpr int kNumTiles32 = sizeof(kTiles32) / sizeof(kTiles32[0]);
+constexpr int kNumTiles64 = sizeof(kTiles64) / sizeof(kTiles64[0]);
 
 // K granularity of split-K partitions: 128 bytes of K, a whole number of
 // LDS stages of every tile entry.
-inline int stage_k(int dtype) { return dtype == MM_FLOAT ? 32 : 64; }
+inline int stage_k(int dtype) { return dtype == MM_DOUBLE ? 16 : dtype == MM_FLOAT ? 32 : 64; }
 constexpr bool stages_divide_128() {
     for (const TileCfg &t : kTiles16)
         if (128 % t.bkb != 0) return false;

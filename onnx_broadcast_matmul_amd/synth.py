@@ -5,11 +5,13 @@ it holds none of the matrix-product arithmetic.  Both the GPU path (tests,
 benchmark) and the CPU oracle consume exactly the bit patterns it returns.
 
 Recipe: numpy ``default_rng`` (PCG64) seeded with ``[seed, product, operand]``
-draws float32 values in fixed chunks of ``CHUNK`` elements; uniform(lo, hi)
-is ``lo + (hi - lo) * U[0,1)``, normal(0, s) is ``s * N(0,1)``; "int" draws
-integers uniformly from {-2, ..., 2}.  The float32 values are then rounded to
-the element type: FLOAT16 by numpy's float32->float16 conversion, BFLOAT16 by
-torch's float32->bfloat16 conversion (both round to nearest, ties to even).
+draws float32 values (float64 values for DOUBLE, so that their products do
+not fit a double exactly) in fixed chunks of ``CHUNK`` elements; uniform(lo,
+hi) is ``lo + (hi - lo) * U[0,1)``, normal(0, s) is ``s * N(0,1)``; "int"
+draws integers uniformly from {-2, ..., 2}.  The float32 values are then
+rounded to the element type: FLOAT16 by numpy's float32->float16 conversion,
+BFLOAT16 by torch's float32->bfloat16 conversion (both round to nearest, ties
+to even).
 """
 from __future__ import annotations
 
@@ -19,35 +21,36 @@ from typing import List, Sequence, Tuple
 
 import numpy as np
 
-FLOAT, FLOAT16, BFLOAT16 = 1, 10, 16
-DTYPE_NAMES = {FLOAT: "fp32", FLOAT16: "fp16", BFLOAT16: "bf16"}
-ELEM_SIZE = {FLOAT: 4, FLOAT16: 2, BFLOAT16: 2}
+FLOAT, FLOAT16, DOUBLE, BFLOAT16 = 1, 10, 11, 16
+DTYPE_NAMES = {FLOAT: "fp32", FLOAT16: "fp16", DOUBLE: "fp64", BFLOAT16: "bf16"}
+ELEM_SIZE = {FLOAT: 4, FLOAT16: 2, DOUBLE: 8, BFLOAT16: 2}
 CHUNK = 1 << 24
 
 
-def _draw(rng: np.random.Generator, n: int, dist: Tuple) -> np.ndarray:
-    out = np.empty(n, dtype=np.float32)
+def _draw(rng: np.random.Generator, n: int, dist: Tuple, ft=np.float32) -> np.ndarray:
+    out = np.empty(n, dtype=ft)
     kind = dist[0]
     for s in range(0, n, CHUNK):
         e = min(n, s + CHUNK)
         if kind == "uniform":
             lo, hi = dist[1], dist[2]
-            out[s:e] = rng.random(e - s, dtype=np.float32)
-            out[s:e] *= np.float32(hi - lo)
-            out[s:e] += np.float32(lo)
+            out[s:e] = rng.random(e - s, dtype=ft)
+            out[s:e] *= ft(hi - lo)
+            out[s:e] += ft(lo)
         elif kind == "normal":
-            out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
-            out[s:e] *= np.float32(dist[1])
+            out[s:e] = rng.standard_normal(e - s, dtype=ft)
+            out[s:e] *= ft(dist[1])
         elif kind == "int":
-            out[s:e] = rng.integers(-2, 3, e - s).astype(np.float32)
+            out[s:e] = rng.integers(-2, 3, e - s).astype(ft)
         else:
             raise ValueError(f"unknown distribution {dist}")
     return out
 
 
 def to_storage(x32: np.ndarray, dtype: int) -> np.ndarray:
-    """float32 values -> element storage (float32, or uint16 bit patterns)."""
-    if dtype == FLOAT:
+    """float32 values (float64 for DOUBLE) -> element storage (float32,
+    float64, or uint16 bit patterns)."""
+    if dtype == FLOAT or dtype == DOUBLE:
         return x32
     if dtype == FLOAT16:
         return x32.astype(np.float16).view(np.uint16)
@@ -66,17 +69,18 @@ def to_storage(x32: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def generate(shape: Sequence[int], dtype: int, dist: Tuple, seed: Sequence[int]) -> np.ndarray:
-    """Storage array (float32, or uint16 bits for 16-bit types) of ``shape``."""
+    """Storage array (float32, float64, or uint16 bits for 16-bit types) of ``shape``."""
     n = int(np.prod(shape, dtype=np.int64)) if len(shape) else 1
     rng = np.random.default_rng(list(seed))
-    return to_storage(_draw(rng, n, dist), dtype).reshape(tuple(shape))
+    ft = np.float64 if dtype == DOUBLE else np.float32
+    return to_storage(_draw(rng, n, dist, ft), dtype).reshape(tuple(shape))
 
 
 def as_torch(storage: np.ndarray, dtype: int):
     """CPU torch tensor viewing the same bits with the element type."""
     import torch
 
-    if dtype == FLOAT:
+    if dtype == FLOAT or dtype == DOUBLE:
         return torch.from_numpy(np.ascontiguousarray(storage))
     t = torch.from_numpy(np.ascontiguousarray(storage).view(np.int16))
     return t.view(torch.float16 if dtype == FLOAT16 else torch.bfloat16)
@@ -87,7 +91,7 @@ def from_torch(t) -> np.ndarray:
     import torch
 
     t = t.detach().cpu().contiguous()
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.float64):
         return t.numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -154,6 +158,12 @@ def _workloads() -> dict:
                 _normal_over_sqrt_k(128), 5, 1),
         Product("bf16_pv_4x32x2048x2048_by_4x32x2048x128", (4, 32, 2048, 2048), (4, 32, 2048, 128), BFLOAT16,
                 _normal_over_sqrt_k(2048), 5, 2),
+    ])
+    # DOUBLE: the square and batch-broadcast shapes again, in FP64.
+    w["fp64_square_and_batched_broadcast"] = Workload("fp64_square_and_batched_broadcast", [
+        Product("fp64_1024_square", (1024, 1024), (1024, 1024), DOUBLE, _normal_over_sqrt_k(1024), 6, 0),
+        Product("fp64_8x1x512x512_by_1x6x512x512", (8, 1, 512, 512), (1, 6, 512, 512), DOUBLE,
+                _normal_over_sqrt_k(512), 6, 1),
     ])
     return w
 

@@ -12,6 +12,13 @@ accumulation with final narrowing, page "MatMul Kernel Design", section
   16-bit patterns), or -- for results so close to zero that the output ulp is
   finer than FP32 accumulation noise -- meets the FLOAT rule above.  The
   number of elements that pass only through the second clause is reported.
+* DOUBLE output: ``max |y - o| <= 2 * gamma_K * K * max|A| * max|B|`` with
+  ``gamma_K = K u / (1 - K u)``, ``u = 2^-53``.  Products of doubles round,
+  so the oracle is no longer exact: the standard bound for a dot product
+  formed in floating point with any summation order (Higham, "Accuracy and
+  Stability of Numerical Algorithms", 2nd ed., section 3.1) puts both the
+  result and the oracle within ``gamma_K * sum_k |a_k b_k|`` of the exact
+  value, and ``sum_k |a_k b_k| <= K max|A| max|B|``.
 * Exact mode (small-integer-valued inputs): ``y == narrow(o)`` bit for bit.
 * NaN matches only NaN; an infinity matches only the same infinity.
 """
@@ -27,6 +34,13 @@ from . import BFLOAT16, DOUBLE, FLOAT, FLOAT16, decode, narrow
 
 def fp32_tolerance(K: int, amax: float, bmax: float) -> float:
     return 1e-4 * math.sqrt(max(int(K), 0)) * float(amax) * float(bmax)
+
+
+def fp64_tolerance(K: int, amax: float, bmax: float) -> float:
+    u = 2.0 ** -53
+    k = max(int(K), 0)
+    gamma = k * u / (1.0 - k * u)
+    return 2.0 * gamma * k * float(amax) * float(bmax)
 
 
 def abs_max(x: np.ndarray, dtype: int) -> float:
@@ -80,7 +94,7 @@ def check(y: np.ndarray, o: np.ndarray, dtype: int, K: int, amax: float, bmax: f
     y = np.asarray(y).reshape(-1)
     if y.size != o.size:
         return Report(False, int(y.size), math.inf, 0.0, detail=f"size {y.size} != {o.size}")
-    tol = fp32_tolerance(K, amax, bmax)
+    tol = fp64_tolerance(K, amax, bmax) if dtype == DOUBLE else fp32_tolerance(K, amax, bmax)
     if y.size == 0:
         return Report(True, 0, 0.0, tol)
     if dtype in (FLOAT16, BFLOAT16):

@@ -2,7 +2,9 @@
 
 Tolerances (oracle/compare.py): FP32 max|y-o| <= 1e-4*sqrt(K)*max|A|*max|B|;
 FP16/BF16 within 2 ulp of the narrowed oracle value (or the FP32 rule for
-results near zero); bit-exact on small-integer-valued inputs.  Every
+results near zero); DOUBLE max|y-o| <= 2*gamma_K*K*max|A|*max|B| (both sides
+round their products); bit-exact on small-integer-valued inputs.  DOUBLE has
+no skinny kernels, so its cases skip the forced skinny algorithms.  Every
 algorithm is forced on every element type over shapes that span several
 tiles and ragged tails, plus broadcast, rank-one, empty, K == 0, unaligned
 and special-value cases, and the full-size workload products on sampled
@@ -20,10 +22,21 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-DTYPES = [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16]
-DT_IDS = {mm.FLOAT: "fp32", mm.FLOAT16: "fp16", mm.BFLOAT16: "bf16"}
+DTYPES = [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16, mm.DOUBLE]
+DT_IDS = {mm.FLOAT: "fp32", mm.FLOAT16: "fp16", mm.BFLOAT16: "bf16", mm.DOUBLE: "fp64"}
 ALGOS = [mm.ALGO_DIRECT, mm.ALGO_SKINNY_M, mm.ALGO_SKINNY_N, mm.ALGO_SPLIT_K, mm.ALGO_GENERAL]
 U1 = ("uniform", -1.0, 1.0)
+
+
+def algos_for(dt, algos=ALGOS):
+    """The forcible algorithms of an element type (DOUBLE has no skinny kernels)."""
+    if dt == mm.DOUBLE:
+        return [a for a in algos if a not in (mm.ALGO_SKINNY_M, mm.ALGO_SKINNY_N)]
+    return list(algos)
+
+
+def dt_algo_params(algos=ALGOS):
+    return [pytest.param(dt, a, id=f"{mm.ALGO_NAMES[a]}-{DT_IDS[dt]}") for dt in DTYPES for a in algos_for(dt, algos)]
 
 
 @pytest.fixture(scope="module")
@@ -71,8 +84,7 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
-@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+@pytest.mark.parametrize("dt,algo", dt_algo_params())
 @pytest.mark.parametrize("sa,sb", RAGGED, ids=lambda s: "x".join(map(str, s)))
 def test_forced_algorithms(sa, sb, dt, algo, dev):
     parity(sa, sb, dt, dev, algo=algo)
@@ -99,7 +111,7 @@ def test_split_counts(dt, split, dev):
         parity(sa, sb, dt, dev, algo=mm.ALGO_SPLIT_K, split=split, seed=split, dist=("int",), exact=True)
 
 
-@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("dt", [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
 def test_skinny_n_eight_columns(dt, dev):
     """Eight output columns: ragged row counts, K from one chunk to the
     4096 limit of the register-slice kernel and past it, batched and
@@ -111,15 +123,13 @@ def test_skinny_n_eight_columns(dt, dev):
         parity(sa, sb, dt, dev, algo=mm.ALGO_SKINNY_N, seed=40 + i, dist=("int",), exact=True)
 
 
-@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
-@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+@pytest.mark.parametrize("dt,algo", dt_algo_params())
 def test_small_integer_bit_exact(dt, algo, dev):
     parity((2, 130, 1000), (1000, 70), dt, dev, algo=algo, dist=("int",), exact=True)
     parity((70, 333), (333, 9), dt, dev, algo=algo, dist=("int",), exact=True)
 
 
-@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
-@pytest.mark.parametrize("algo", [0] + ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+@pytest.mark.parametrize("dt,algo", dt_algo_params([0] + ALGOS))
 def test_broadcast_equals_materialized(dt, algo, dev):
     """Zero-stride broadcast reads give bitwise the same result as an
     explicitly repeated batch under the same kernel."""
@@ -146,7 +156,7 @@ def test_rank_one(dt, dev):
     assert tuple(ys.shape) == ()
     _, yb, _ = parity((K,), (3, K, 40), dt, dev)
     assert tuple(yb.shape) == (3, 40)
-    for algo in ALGOS:
+    for algo in algos_for(dt):
         a = synth.generate((K,), dt, U1, [3, 0])
         b = synth.generate((K, 80), dt, U1, [3, 1])
         y1 = synth.from_torch(run_plan(mm.Plan((K,), (K, 80), dt, force_algo=algo), a, b, dt, dev))
@@ -169,8 +179,7 @@ def test_empty_and_zero_k(dt, dev):
         assert torch.all(Y == 0).item()
 
 
-@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
-@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+@pytest.mark.parametrize("dt,algo", dt_algo_params())
 def test_deterministic(dt, algo, dev):
     sa, sb = (2, 200, 700), (700, 150)
     a = synth.generate(sa, dt, U1, [11, 0])
@@ -181,8 +190,7 @@ def test_deterministic(dt, algo, dev):
     assert np.array_equal(y1.view(np.uint8), y2.view(np.uint8))
 
 
-@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
-@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+@pytest.mark.parametrize("dt,algo", dt_algo_params())
 def test_unaligned_pointers(dt, algo, dev):
     """Operands that start one element past a 16-byte boundary take the
     element-wise load paths."""
@@ -202,24 +210,25 @@ def test_unaligned_pointers(dt, algo, dev):
     assert rep.ok, str(rep)
 
 
-@pytest.mark.parametrize("dt", DTYPES, ids=DT_IDS.get)
-@pytest.mark.parametrize("algo", ALGOS, ids=lambda a: mm.ALGO_NAMES[a])
+@pytest.mark.parametrize("dt,algo", dt_algo_params())
 def test_special_values(dt, algo, dev):
     """An infinity or NaN in A reaches exactly the outputs of its row, as in
     the oracle (NaN stays NaN through the narrowing)."""
     sa, sb = (40, 128), (128, 24)
     a = synth.generate(sa, dt, U1, [17, 0])
     b = synth.generate(sb, dt, U1, [17, 1])
-    inf_bits = {mm.FLOAT: np.float32(np.inf), mm.FLOAT16: np.uint16(0x7C00), mm.BFLOAT16: np.uint16(0x7F80)}[dt]
-    nan_bits = {mm.FLOAT: np.float32(np.nan), mm.FLOAT16: np.uint16(0x7E00), mm.BFLOAT16: np.uint16(0x7FC0)}[dt]
+    inf_bits = {mm.FLOAT: np.float32(np.inf), mm.FLOAT16: np.uint16(0x7C00), mm.BFLOAT16: np.uint16(0x7F80),
+                mm.DOUBLE: np.float64(np.inf)}[dt]
+    nan_bits = {mm.FLOAT: np.float32(np.nan), mm.FLOAT16: np.uint16(0x7E00), mm.BFLOAT16: np.uint16(0x7FC0),
+                mm.DOUBLE: np.float64(np.nan)}[dt]
     a[3, 5] = inf_bits
     a[7, 9] = nan_bits
     plan = mm.Plan(sa, sb, dt, force_algo=algo)
     Y = run_plan(plan, a, b, dt, dev)
     o = oracle.matmul(a, b, dt)
-    finite = np.isfinite(oracle.decode(a, dt) if dt != mm.FLOAT else a)
-    rep = check(synth.from_torch(Y), o, dt, 128, float(np.abs(oracle.decode(a, dt) if dt != mm.FLOAT else a)[finite].max()),
-                abs_max(b, dt))
+    av = np.asarray(a, dtype=np.float64) if dt in (mm.FLOAT, mm.DOUBLE) else oracle.decode(a, dt)
+    finite = np.isfinite(av)
+    rep = check(synth.from_torch(Y), o, dt, 128, float(np.abs(av[finite]).max()), abs_max(b, dt))
     assert rep.ok, str(rep)
 
 

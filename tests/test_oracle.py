@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from oracle import BFLOAT16, DOUBLE, FLOAT, FLOAT16
-from oracle.compare import check, fp32_tolerance, ulp_distance16
+from oracle.compare import check, fp32_tolerance, fp64_tolerance, ulp_distance16
 from onnx_broadcast_matmul_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -341,3 +341,34 @@ def test_comparator_fp32_rule():
     y = (o + 1.5 * tol).astype(np.float32)
     assert not check(y, o, FLOAT, K, amax, bmax).ok
     assert check(o.astype(np.float32), o, FLOAT, K, amax, bmax, exact=True).ok
+
+
+def test_comparator_fp64_rule():
+    """DOUBLE: the bound 2 gamma_K K max|A| max|B| holds for the oracle against
+    an independent float64 product (numpy), and a product formed in FP32
+    arithmetic from the same double inputs is far outside it."""
+    K = 256
+    u = 2.0 ** -53
+    tol = fp64_tolerance(K, 2.0, 3.0)
+    assert tol == pytest.approx(2 * (K * u / (1 - K * u)) * K * 6.0)
+    o = np.array([1.0, -2.0])
+    assert check(o + 0.9 * tol, o, DOUBLE, K, 2.0, 3.0).ok
+    assert not check(o + 1.5 * tol, o, DOUBLE, K, 2.0, 3.0).ok
+    rng = np.random.default_rng(21)
+    A = rng.uniform(-1.0, 1.0, (40, K))
+    B = rng.uniform(-1.0, 1.0, (K, 30))
+    Y = oracle.matmul(A, B, DOUBLE)
+    amax, bmax = np.abs(A).max(), np.abs(B).max()
+    assert check(np.matmul(A, B), Y, DOUBLE, K, amax, bmax).ok
+    y32 = np.matmul(A.astype(np.float32), B.astype(np.float32)).astype(np.float64)
+    assert not check(y32, Y, DOUBLE, K, amax, bmax).ok
+
+
+def test_double_small_integers_exact():
+    """DOUBLE inputs with small integer values: every partial sum is an
+    integer far below 2^53, so the oracle equals the int64 product."""
+    rng = np.random.default_rng(5)
+    Ai = rng.integers(-2, 3, (3, 17, 300))
+    Bi = rng.integers(-2, 3, (300, 11))
+    Y = oracle.matmul(Ai.astype(np.float64), Bi.astype(np.float64), DOUBLE)
+    assert np.array_equal(Y, np.matmul(Ai, Bi).astype(np.float64))

@@ -74,8 +74,8 @@ def test_output_shapes_match_numpy_exhaustive():
     ((2, 3), (4, 5), mm.FLOAT, mm.ERR_K_MISMATCH),
     ((2, 2, 3), (3, 3, 4), mm.FLOAT, mm.ERR_BROADCAST),
     ((0, 2, 3), (2, 3, 4), mm.FLOAT, mm.ERR_BROADCAST),
-    ((2, 3), (3, 4), mm.DOUBLE, mm.ERR_DTYPE),
     ((2, 3), (3, 4), 7, mm.ERR_DTYPE),
+    ((2, 3), (3, 4), 12, mm.ERR_DTYPE),
 ])
 def test_plan_errors(sa, sb, dtype, status):
     plan, st = _try_plan(sa, sb, dtype)
@@ -257,3 +257,37 @@ def test_info_flops_bytes():
     info = mm.Plan((8, 1, 512, 512), (1, 6, 512, 512), mm.FLOAT).info()
     assert info["flops"] == 2.0 * 48 * 512 ** 3
     assert info["min_bytes"] == 4.0 * (8 * 512 * 512 + 6 * 512 * 512 + 48 * 512 * 512)
+
+
+# ---------------------------------------------------------------- DOUBLE
+
+@pytest.mark.parametrize("sa,sb,algo", [
+    ((4, 64, 96), (96, 80), mm.ALGO_DIRECT),
+    ((1024, 1024), (1024, 1024), mm.ALGO_GENERAL),
+    ((32, 1, 4096), (32, 4096, 4096), mm.ALGO_GENERAL),   # skinny-M shape: no FP64 skinny kernel
+    ((8192, 4096), (4096, 8), mm.ALGO_GENERAL),           # skinny-N shape
+    ((64, 131072), (131072, 64), mm.ALGO_SPLIT_K),
+])
+def test_double_plans(sa, sb, algo):
+    """DOUBLE goes through the same plan as the other types; its skinny
+    shapes take the tiled FP64 kernel and split-K keeps double partials."""
+    plan = mm.Plan(sa, sb, mm.DOUBLE)
+    assert plan.algo == algo
+    inf = plan.info()
+    assert inf["dtype"] == mm.DOUBLE
+    if algo == mm.ALGO_SPLIT_K:
+        assert inf["workspace_bytes"] == inf["split_k"] * inf["batch"] * inf["kernel_m"] * inf["N"] * 8
+        assert inf["k_chunk"] % 16 == 0
+    na = int(np.prod(sa)); nb = int(np.prod(sb))
+    assert inf["min_bytes"] == 8.0 * (na + nb + plan.output_numel)
+
+
+@pytest.mark.parametrize("algo", [mm.ALGO_SKINNY_M, mm.ALGO_SKINNY_N])
+def test_double_rejects_forced_skinny(algo):
+    plan, st = _try_plan((64, 64), (64, 8), mm.DOUBLE, force_algo=algo)
+    assert plan is None and st == mm.ERR_BAD_OPTION
+
+
+def test_double_tile_table():
+    assert mm.lib().mm_tile_count(mm.DOUBLE) == 2
+    assert mm.tile_configs(mm.DOUBLE) == [(128, 128, 16), (64, 64, 16)]
