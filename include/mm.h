@@ -123,6 +123,10 @@ typedef struct mm_plan_info {
     int64_t workspace_bytes;  /* workspace the plan needs on the device (FP32 or double partials) */
     double flops;             /* 2 * batch * M * N * K of the un-folded problem */
     double min_bytes;         /* element size * (numel A + numel B + numel Y) */
+    int64_t tail_col;         /* GENERAL: > 0 when output columns [tail_col, N) run as a
+                                 second launch (last-round balancing), else 0 */
+    int32_t tail_tile;        /* tile table entry + 1 of that second launch (0 if none) */
+    int32_t reserved_;
 } mm_plan_info;
 
 /* Create a plan for Y = MatMul(A, B) with A of shape a_shape[0..a_rank) and

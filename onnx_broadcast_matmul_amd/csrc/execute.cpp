@@ -58,6 +58,8 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
     a.M = p->kernel_m;
     a.N = p->N;
     a.K = p->K;
+    a.ldb = p->N;
+    a.ldy = p->N;
     a.batch = p->batch;
     a.kchunk = p->kchunk;
     a.split = p->split;
@@ -84,7 +86,27 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
         e = launch_skinny_n(p->dtype, al, a, s);
         break;
     case MM_ALGO_GENERAL:
-        e = f64 ? launch_general_f64(p->tile, al, false, a, s) : launch_general(p->dtype, p->tile, al, false, a, s);
+        if (f64) {
+            e = launch_general_f64(p->tile, al, false, a, s);
+        } else if (p->tail_col > 0) {
+            // Columns [0, tail_col) in whole rounds of `tile`, then the rest
+            // with `tail_tile`; both read B and write Y with the full pitch N.
+            KArgs m = a;
+            m.N = p->tail_col;
+            e = launch_general(p->dtype, p->tile, al, false, m, s);
+            if (e == hipSuccess) {
+                KArgs r = a;
+                r.N = p->N - p->tail_col;
+                r.B = (const char *)B + p->tail_col * es;
+                r.Y = (char *)Y + p->tail_col * es;
+                Align ar = al;
+                ar.b = al.b && aligned16(r.B);
+                r.y_vec = al.y && aligned16(r.Y) && (r.N * es) % 16 == 0;
+                e = launch_general(p->dtype, p->tail_tile, ar, false, r, s);
+            }
+        } else {
+            e = launch_general(p->dtype, p->tile, al, false, a, s);
+        }
         break;
     case MM_ALGO_SPLIT_K: {
         mm_status st = ensure_workspace(p);

@@ -27,14 +27,18 @@ struct BatchDesc {
 
 // Arguments of every kernel (passed by value).  M is the number of rows of
 // one product as the kernels see it (batch*M when A's batch is folded into
-// the rows).  Y is dense [batch][M][N]; W is the split-K workspace
-// [split][batch][M][N] in FP32 (in double for DOUBLE products).
+// the rows).  Y is [batch][M][N] with rows ldy elements apart (batches M*ldy
+// apart) and B's rows are ldb elements apart; both equal N except in the
+// tiled kernels' column sub-launches, where N is the width of a column range
+// of wider matrices.  W is the split-K workspace [split][batch][M][N] in
+// FP32 (in double for DOUBLE products), always dense.
 struct KArgs {
     const void *A;
     const void *B;
     void *Y;
     float *W;
     int64_t M, N, K;
+    int64_t ldb, ldy;  // row pitches of B and Y in elements
     int64_t batch;
     int64_t kchunk;
     int32_t split;

@@ -133,12 +133,12 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
             if constexpr (VEC) {
                 using V = typename RawVec<CW * ES>::T;
                 V v;
-                if (gk < kend && gn < N) v = *(const V *)(Bb + gk * N + gn);
+                if (gk < kend && gn < N) v = *(const V *)(Bb + gk * a.ldb + gn);
                 else __builtin_memset(&v, 0, sizeof(v));
                 __builtin_memcpy(&rb[r][0], &v, sizeof(v));
             } else {
 #pragma unroll
-                for (int j = 0; j < CW; ++j) rb[r][j] = (gk < kend && gn + j < N) ? Bb[gk * N + gn + j] : (S)0;
+                for (int j = 0; j < CW; ++j) rb[r][j] = (gk < kend && gn + j < N) ? Bb[gk * a.ldb + gn + j] : (S)0;
             }
         }
     };
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
     }
 
     // ---- epilogue: 32x32 block (i, j), element r of lane: row 8(r/4) + 4(lane/32) + r%4, column lane%32.
-    const int64_t ybase = b * M * N;
+    const int64_t ybase = b * M * a.ldy;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
                     if constexpr (SPLIT) {
                         a.W[(sidx * a.batch + b) * M * N + row * N + col] = acc[i][j][r];
                     } else {
-                        ((S *)a.Y)[ybase + row * N + col] = E::from_f32(acc[i][j][r]);
+                        ((S *)a.Y)[ybase + row * a.ldy + col] = E::from_f32(acc[i][j][r]);
                     }
                 }
             }
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         const int row = (wave * B_INSTR + q) * B_RPB + lane / CPR;  // k within the stage
         const int p = lane % CPR;
         const int c = p ^ bswz(row);
-        b_off[q] = (uint32_t)((int64_t)row * N * ES + c * 16);
+        b_off[q] = (uint32_t)((int64_t)row * a.ldb * ES + c * 16);
         b_k[q] = row;
         b_ok[q] = n0 + c * VE < N;
     }
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             const bool ok = a_ok[q] && k0 + a_k[q] < kend;
             load_to_lds16(ra, sbase + (wave * A_INSTR + q) * 1024, ok ? a_off[q] : kOutOfRange);
         }
-        const i32x4 rb = buffer_rsrc(Btile + k0 * N * ES);
+        const i32x4 rb = buffer_rsrc(Btile + k0 * a.ldb * ES);
 #pragma unroll
         for (int q = 0; q < B_INSTR; ++q) {
             const bool ok = b_ok[q] && k0 + b_k[q] < kend;
@@ -584,7 +584,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     static_assert(BM % NP == 0, "epilogue passes");
     static_assert((OCPR & (OCPR - 1)) == 0 && OCPR >= 8, "tile row swizzle");
     char *tile = lds;
-    O *out = SPLIT ? (O *)(a.W + (sidx * a.batch + b) * M * N) : (O *)((S *)a.Y + b * M * N);
+    // Output rows: the dense workspace (pitch N) or Y (pitch ldy).
+    const int64_t ldo = SPLIT ? N : a.ldy;
+    O *out = SPLIT ? (O *)(a.W + (sidx * a.batch + b) * M * N) : (O *)((S *)a.Y + b * M * a.ldy);
     if constexpr (KG > 1) {
         // Groups 1..KG-1 hand their accumulators to group 0 through LDS
         // (element-major, lane-contiguous), which adds them in group order.
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             const int64_t row = m0 + pass * PR + rl, col = n0 + (int64_t)c * OV;
             if (row < M && col < N) {
                 const uint4 v = *(const uint4 *)(tile + rl * (BN * OS) + (c ^ (rl & (OCPR - 1))) * 16);
-                O *dst = out + row * N + col;
+                O *dst = out + row * ldo + col;
                 if (a.y_vec) {
                     // Rows are whole 16-byte chunks: the chunk lies inside the row.
                     const u32x4 w = {v.x, v.y, v.z, v.w};
@@ -672,7 +674,7 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
     // Buffer offsets are 32-bit: one tile's rows of A and one stage's rows of
     // B must each span less than 2 GiB.
     constexpr int ES = DT == MM_FLOAT ? 4 : 2;
-    const bool fits = (int64_t)BM * a.K * ES < 0x7fff0000LL && (int64_t)(BKB / ES) * a.N * ES < 0x7fff0000LL;
+    const bool fits = (int64_t)BM * a.K * ES < 0x7fff0000LL && (int64_t)(BKB / ES) * a.ldb * ES < 0x7fff0000LL;
     if (vec && fits) {
         const dim3 blk(64 * WGM * WGN * KG);
         if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true>), g, blk, 0, s, a);

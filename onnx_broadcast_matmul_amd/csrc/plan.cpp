@@ -90,6 +90,57 @@ static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N) {
     return best;
 }
 
+// LDS bytes of a tile entry's stage buffers, and the workgroups of that
+// entry one CU holds (160 KB of LDS per CU).
+static int64_t tile_lds_bytes(const TileCfg *t) { return (int64_t)t->stages * t->bkb * (t->bm + t->bn); }
+static int64_t tile_wgs_per_cu(const TileCfg *t) { return std::max<int64_t>(1, (160 * 1024) / tile_lds_bytes(t)); }
+
+static int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        const int64_t r = a % b;
+        a = b;
+        b = r;
+    }
+    return a;
+}
+
+// Last-round balancing for a large tile (one workgroup per CU).  When the
+// tiles leave the last round of workgroups less than half full, the leading
+// output columns are covered by whole rounds of the chosen tile and the
+// remaining columns by a second launch with the tile that suits that
+// narrower rectangle best -- if the estimate (in units of one chosen-tile
+// duration, scaled by tile area and relative tile throughput) gains at
+// least 3 %.  The roadmap page's participation sizing ("Parallel
+// execution") makes the same trade between partition count and workers.
+static void plan_tail(mm_plan_s *p) {
+    p->tail_col = 0;
+    p->tail_tile = -1;
+    if (p->dtype == MM_DOUBLE) return;
+    const TileCfg *t = tile_entry(p->dtype, p->tile);
+    if (tile_wgs_per_cu(t) != 1) return;
+    const int64_t rows = p->batch * cdiv(p->kernel_m, t->bm);
+    const int64_t tn = cdiv(p->N, t->bn);
+    const int64_t T = rows * tn;
+    const int64_t rem = T % kNumCUs;
+    if (T <= kNumCUs || rem == 0 || rem > kNumCUs / 2) return;
+    const int64_t step = kNumCUs / gcd64(rows % kNumCUs == 0 ? kNumCUs : rows % kNumCUs, kNumCUs);
+    const int64_t c_main = ((tn - 1) / step) * step;  // whole rounds, at least one column left over
+    if (c_main <= 0) return;
+    const int64_t n_rem = p->N - c_main * t->bn;
+    const int rt = choose_tile(p->dtype, p->batch, p->kernel_m, n_rem);
+    const TileCfg *r = tile_entry(p->dtype, rt);
+    const int64_t T_rem = p->batch * cdiv(p->kernel_m, r->bm) * cdiv(n_rem, r->bn);
+    const double without = (double)cdiv(T, kNumCUs);
+    const double with_split = (double)(rows * c_main) / kNumCUs +
+                              (double)cdiv(T_rem, kNumCUs * tile_wgs_per_cu(r)) * ((double)r->bm * r->bn) /
+                                  ((double)t->bm * t->bn) * tile_quality(p->dtype, p->tile) /
+                                  tile_quality(p->dtype, rt);
+    if (with_split < 0.97 * without) {
+        p->tail_col = c_main * t->bn;
+        p->tail_tile = rt;
+    }
+}
+
 // Smallest-padding tile for split-K (its output is tiny by construction).
 static int choose_split_tile(int dtype, int64_t M, int64_t N) {
     int best = 0;
@@ -250,6 +301,8 @@ static mm_status check_limits(const mm_plan_s *p) {
 static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
     const int64_t M = p->kernel_m, N = p->N, K = p->K;
     p->tile = -1;
+    p->tail_col = 0;
+    p->tail_tile = -1;
     p->split = 1;
     p->kchunk = K;
     p->workspace_bytes = 0;
@@ -300,6 +353,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         if (req > 0) p->tile = req - 1;
         else if (algo == MM_ALGO_GENERAL) p->tile = choose_tile(p->dtype, p->batch, M, N);
         else p->tile = choose_split_tile(p->dtype, M, N);
+        if (algo == MM_ALGO_GENERAL && req == 0) plan_tail(p);
         const TileCfg *t = tile_entry(p->dtype, p->tile);
         const int64_t tiles = p->batch * cdiv(M, t->bm) * cdiv(N, t->bn);
         if (algo == MM_ALGO_SPLIT_K) {
@@ -381,6 +435,8 @@ mm_status mm_plan_get_info(mm_plan_t p, mm_plan_info *info) {
     info->split_k = p->split;
     info->k_chunk = p->kchunk;
     info->workspace_bytes = p->workspace_bytes;
+    info->tail_col = p->tail_col;
+    info->tail_tile = p->tail_tile >= 0 ? p->tail_tile + 1 : 0;
     info->flops = 2.0 * (double)p->total_batch * (double)p->M * (double)p->N * (double)p->K;
     int64_t na = 1, nb = 1;
     for (int i = 0; i < p->a_rank; ++i) na *= p->a_shape[i];

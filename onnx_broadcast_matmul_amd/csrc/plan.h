@@ -24,6 +24,11 @@ struct mm_plan_s {
     mm::BatchDesc bd = {};
     int algo = MM_ALGO_EMPTY;
     int tile = -1;  // tile table index (tiled algorithms)
+    // GENERAL only: when tail_col > 0, the tile `tile` covers output columns
+    // [0, tail_col) in whole rounds of workgroups and a second launch with
+    // tile `tail_tile` covers [tail_col, N).
+    int64_t tail_col = 0;
+    int tail_tile = -1;
     int32_t split = 1;
     int64_t kchunk = 0;
     int64_t workspace_bytes = 0;

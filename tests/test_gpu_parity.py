@@ -232,6 +232,36 @@ def test_special_values(dt, algo, dev):
     assert rep.ok, str(rep)
 
 
+@pytest.mark.parametrize("dt", [mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
+@pytest.mark.parametrize("n", [11000, 11002])
+def test_tail_split(dt, n, dev):
+    """Last-round balancing: columns [0, tail_col) run with the plan's tile
+    and the rest with the tail tile.  The result equals, bit for bit, each
+    column range of a single launch forced to the corresponding tile (a
+    tile's per-element summation order does not depend on N), and matches
+    the oracle on sampled outputs around the boundary.  N = 11002 has rows
+    that are not whole 16-byte chunks (element-wise loads and stores)."""
+    sa, sb = (8192, 128), (128, n)
+    a = synth.generate(sa, dt, ("int",), [31, 0])
+    b = synth.generate(sb, dt, ("int",), [31, 1])
+    plan = mm.Plan(sa, sb, dt)
+    inf = plan.info()
+    assert plan.algo == mm.ALGO_GENERAL and inf["tail_col"] > 0, inf
+    c = inf["tail_col"]
+    y = synth.from_torch(run_plan(plan, a, b, dt, dev))
+    ym = synth.from_torch(run_plan(mm.Plan(sa, sb, dt, force_algo=mm.ALGO_GENERAL, tile=inf["tile"]), a, b, dt, dev))
+    yr = synth.from_torch(run_plan(mm.Plan(sa, sb, dt, force_algo=mm.ALGO_GENERAL, tile=inf["tail_tile"]), a, b, dt, dev))
+    assert np.array_equal(y[:, :c], ym[:, :c])
+    assert np.array_equal(y[:, c:], yr[:, c:])
+    rng = np.random.default_rng(3)
+    rows = rng.integers(0, sa[0], 400)
+    cols = np.concatenate([rng.integers(0, n, 200), rng.integers(c - 8, min(n, c + 8), 200)])
+    idx = np.unique(rows * n + cols)
+    o = oracle.matmul_at(a, b, dt, idx)
+    rep = check(y.reshape(-1)[idx], o, dt, sa[-1], abs_max(a, dt), abs_max(b, dt), exact=True)
+    assert rep.ok, str(rep)
+
+
 # ------------------------------------------------------------ full-size workloads
 
 def _sample_indices(shape, n, rng):

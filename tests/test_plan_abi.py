@@ -291,3 +291,25 @@ def test_double_rejects_forced_skinny(algo):
 def test_double_tile_table():
     assert mm.lib().mm_tile_count(mm.DOUBLE) == 2
     assert mm.tile_configs(mm.DOUBLE) == [(128, 128, 16), (64, 64, 16)]
+
+
+# ---------------------------------------------------------------- last-round balancing
+
+def test_tail_split_plans():
+    """A large tile that leaves the last round of workgroups less than half
+    full covers the leading columns in whole rounds and hands the rest to a
+    second launch; shapes whose tiles fill whole rounds, forced tiles and
+    DOUBLE keep one launch."""
+    p = mm.Plan((16, 512, 4096), (4096, 11008), mm.BFLOAT16)
+    inf = p.info()
+    assert inf["tile"] == 1 and inf["tail_col"] == 10240 and inf["tail_tile"] >= 1
+    bm, bn, _ = mm.tile_configs(mm.BFLOAT16)[inf["tile"] - 1]
+    tiles_main = (inf["kernel_m"] // bm) * (inf["tail_col"] // bn)
+    assert tiles_main % 256 == 0  # whole rounds on 256 CUs
+    for sa, sb, dt in [((4, 32, 2048, 128), (4, 32, 128, 2048), mm.BFLOAT16),
+                       ((8192, 8192), (8192, 8192), mm.BFLOAT16),
+                       ((1024, 1024), (1024, 1024), mm.FLOAT),
+                       ((16, 512, 4096), (4096, 11008), mm.DOUBLE)]:
+        assert mm.Plan(sa, sb, dt).info()["tail_col"] == 0
+    forced = mm.Plan((16, 512, 4096), (4096, 11008), mm.BFLOAT16, force_algo=mm.ALGO_GENERAL, tile=1)
+    assert forced.info()["tail_col"] == 0
