@@ -13,6 +13,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
 // FP32 -> BF16, round to nearest, ties to even; NaN stays a (quiet) NaN,
 // values beyond the largest finite BF16 round to infinity.  gfx950 converts
@@ -71,6 +73,39 @@ struct Elem<MM_BFLOAT16> {
         return __builtin_bit_cast(uint32_t, v);
     }
 };
+
+// ---- direct global-to-LDS loads (gfx950 buffer loads with the LDS destination)
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every buffer range used here: the load returns zeros
+
+// Raw buffer resource: 48-bit base, stride 0, 2^31 - 1 bytes of range.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xffff);
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from global into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void load_to_lds16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Element offsets of the A and B matrices used by output batch `b`.
 __device__ __forceinline__ void batch_offsets(const BatchDesc &bd, int64_t b, int64_t &oa, int64_t &ob) {

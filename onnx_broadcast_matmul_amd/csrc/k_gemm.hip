@@ -285,39 +285,6 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
 //   per-stage barrier.
 // ---------------------------------------------------------------------------
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every buffer range used here
-
-// Raw buffer resource: 48-bit base, stride 0, 2^31 - 1 bytes of range.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void *base) {
-    const uint64_t p = (uint64_t)(uintptr_t)base;
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xffff);
-    r[2] = 0x7fffffff;
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 16 bytes per lane from global into LDS at lds_base + 16 * lane.
-__device__ __forceinline__ void load_to_lds16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_base), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N), other counters unconstrained.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool SPLIT>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)

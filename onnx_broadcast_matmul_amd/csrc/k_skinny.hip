@@ -23,14 +23,12 @@
 // wave order through LDS.
 //
 // Skinny-N with eight columns and K <= 4096 (16-bit types) has a kernel of
-// its own, built around the access pattern that streams A fastest: every
-// load instruction of a wave reads 1 KB of one row (16 bytes per lane).  The
-// eight waves of a workgroup take the eight 512-element parts of K; a lane
-// keeps its 8 x 8 slice of B in registers, forms 8 rows x 8 columns of
-// partial dot products, and a transpose-reduce over the 64 lanes (register
-// swaps across the wave halves and rows, then DPP exchanges, all in a fixed
-// order) leaves lane L with the sum for row L / 8, column L % 8.  B is staged
-// once per workgroup through LDS; A is read once, non-temporally.
+// its own on the matrix cores: v_mfma_f32_16x16x32 multiplies 16 rows of A
+// by 32 elements of K against the 8 columns padded to 16, so the reduction
+// costs a few MFMAs instead of the packed dot products and cross-lane sums,
+// whose VALU time was about half the memory time.  A is loaded straight into
+// the MFMA operand layout with every load of a wave in flight at once; each
+// wave's slice of B is read through LDS with transposing reads.
 #include <type_traits>
 
 #include "device.h"
@@ -397,66 +395,32 @@ __global__ __launch_bounds__(64 * kSkNWaves) void k_skinny_n(KArgs a) {
 
 // ------------------------------------------------- skinny-N, eight columns
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-
-// v[0..63] of every lane -> v[0] of lane L = sum over all 64 lanes of v[L].
-// Each step pairs lanes that hold the same index set across one lane bit and
-// keeps the half of the indices named by that bit: bits 5 and 4 with the
-// gfx950 half-wave and row swaps, bits 3..0 with DPP row mirror, half-row
-// mirror and quad permutations.  The order of additions is fixed.
-__device__ __forceinline__ void transpose_reduce64(float *v, int lane) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 32]), false, false);
-        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 16]), false, false);
-        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {  // row mirror: lane j <-> 15 - j
-        const float x = v[i] + dpp_move<0x140>(v[i]), y = v[i + 8] + dpp_move<0x140>(v[i + 8]);
-        v[i] = b3 ? y : x;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {  // half-row mirror: lane j <-> 7 - j
-        const float x = v[i] + dpp_move<0x141>(v[i]), y = v[i + 4] + dpp_move<0x141>(v[i + 4]);
-        v[i] = b2 ? y : x;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {  // quad permutation [2, 3, 0, 1]
-        const float x = v[i] + dpp_move<0x4E>(v[i]), y = v[i + 2] + dpp_move<0x4E>(v[i + 2]);
-        v[i] = b1 ? y : x;
-    }
-    {  // quad permutation [1, 0, 3, 2]
-        const float x = v[0] + dpp_move<0xB1>(v[0]), y = v[1] + dpp_move<0xB1>(v[1]);
-        v[0] = b0 ? y : x;
-    }
-}
-
 constexpr int kSkN8MaxK = 4096;  // eight waves x 512 elements of K
-constexpr int kSkN8Rows = 16;    // rows per workgroup: two rounds of eight
 
-// LDS position of B row k (16 bytes: its eight columns): lanes of one read
-// instruction take rows 8 apart, so the low bits are permuted by bits 3..5.
-__device__ __forceinline__ int skn8_pos(int k) { return k ^ ((k >> 3) & 7); }
+// Eight columns on the matrix cores.  A workgroup of 8 waves owns 16 rows
+// of A; wave w owns elements 512 w .. 512 w + 511 of K (K <= 4096).  Each
+// v_mfma_f32_16x16x32 multiplies the 16 rows by 32 elements of K against
+// the 8 columns of B padded to 16 with zeros.  A is loaded straight into
+// the operand layout (lane l: row l % 16, elements 8 (l / 16) .. + 7 of the
+// K step), all 16 K steps of the wave in flight at once.  The wave's 8 KB
+// slice of B sits in LDS in its own row-major layout, and the B operand
+// comes from two gfx950 transposing reads per K step (lanes of columns 8 ..
+// 15 point at a zero pad).  The eight waves' partial sums meet in LDS and
+// are added in wave order.
+constexpr int kSkN8Rows = 16;  // rows per workgroup
 
 template <int DT>
 __global__ __launch_bounds__(512) void k_skinny_n8(KArgs a) {
+    constexpr int RB = 1;  // 16-row blocks per wave (two, with 32 rows per workgroup, measured 13 % slower)
 #if defined(__HIP_DEVICE_COMPILE__)
     using E = Elem<DT>;
     using S = typename E::S;
     static_assert(sizeof(S) == 2, "16-bit element types");
-    constexpr int NT = 8, RR = 8, ROUNDS = kSkN8Rows / RR;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) uint4 bs[kSkN8MaxK];
-    __shared__ float red[8][ROUNDS][64];
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    constexpr int BW = 512 * 16;  // B bytes per wave: 512 rows of 8 columns
+    __shared__ __attribute__((aligned(16))) char lds[8 * BW + 16];
+    char *zero = lds + 8 * BW;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -468,90 +432,98 @@ __global__ __launch_bounds__(512) void k_skinny_n8(KArgs a) {
     int64_t oa, ob;
     batch_offsets(a.bd, b, oa, ob);
     const S *__restrict__ A = (const S *)a.A + oa;
-    const uint4 *__restrict__ B = (const uint4 *)((const S *)a.B + ob);  // row k of B = chunk k
-    const int k0 = wave * 512 + lane * 8;  // this lane's eight elements of K
-    const bool kin = k0 < K;
+    const uint4 *__restrict__ Bg = (const uint4 *)((const S *)a.B + ob);  // row k of B = chunk k
+    const int kw = wave * 512;
 
-    // Every load below is unconditional, from an address clamped into the
-    // operand, and out-of-range values are replaced by zeros afterwards: no
-    // branch separates the loads, so they are all in flight together.
-    // B rows in flight first, then the first round of A rows.
-    uint4 bg[kSkN8MaxK / 512];
+    // Loads are unconditional from clamped addresses; values outside the
+    // operands become zeros.  B first (it is needed first), then every K
+    // step of A.  K is a multiple of 8, so a lane's 8 elements of K lie
+    // wholly inside or outside.
+    uint4 bg[8];
 #pragma unroll
-    for (int i = 0; i < kSkN8MaxK / 512; ++i) {
-        const int k = tid + i * 512;
-        bg[i] = B[k < K ? k : K - 1];
+    for (int i = 0; i < 8; ++i) {
+        const int64_t k = kw + 64 * i + lane;
+        const uint4 v = Bg[k < K ? k : 0];
+        bg[i] = k < K ? v : make_uint4(0, 0, 0, 0);
     }
-    const int kc = kin ? k0 : 0;
-    uint32_t av[RR][4];
-    auto load_a = [&](int r) {
+    // K elements of step s for lane group g: 32 s + 8 g .. + 7.  (Giving each
+    // lane 64 contiguous bytes over four steps instead was measured 40 %
+    // slower: each load instruction then touches 16 B pieces spread over the
+    // rows rather than 64 contiguous bytes of each.)
+    auto kstep = [](int s, int g) { return 32 * s + 8 * g; };
+    uint32_t av[RB][16][4];
 #pragma unroll
-        for (int i = 0; i < RR; ++i) {
-            const int64_t row = row0 + r * RR + i;
-            const bool ok = kin && row < M;
-            const u32x4 t = __builtin_nontemporal_load((const u32x4 *)(A + (row < M ? row : M - 1) * K + kc));
+    for (int rb = 0; rb < RB; ++rb) {
+        const int64_t arow = row0 + rb * 16 + (lane & 15);
+        const bool rok = arow < M;
+        const S *ap = A + (rok ? arow : M - 1) * K;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) av[i][e] = ok ? t[e] : 0u;
+        for (int s = 0; s < 16; ++s) {
+            const int64_t k = kw + kstep(s, lane >> 4);
+            const u32x4 t = __builtin_nontemporal_load((const u32x4 *)(ap + (k < K ? k : 0)));
+            const bool ok = rok && k < K;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[rb][s][e] = ok ? t[e] : 0u;
         }
-    };
-    load_a(0);
-    // Rows k >= K hold copies of row K - 1 and are never read.
+    }
+    char *bw = lds + wave * BW;
 #pragma unroll
-    for (int i = 0; i < kSkN8MaxK / 512; ++i) bs[skn8_pos(tid + i * 512)] = bg[i];
+    for (int i = 0; i < 8; ++i) *(uint4 *)(bw + (64 * i + lane) * 16) = bg[i];
+    if (tid == 0) *(uint4 *)zero = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
-    // This lane's slice of B as (k, k + 1) pairs per column.
-    uint32_t bp[NT][4];
-    {
-        uint32_t w[8][4];
+    // B operand of K step s: in each 16-lane group g, lanes 4r + j address
+    // 4 columns of block row r = B row 32 s + 8 g + 4 h + r (j = 0, 1) or the
+    // zero pad (j = 2, 3); lane i of the group receives column i of the
+    // four rows.
+    const int g = lane >> 4, gr = (lane >> 2) & 3, gj = lane & 3;
+    f32x4v acc[RB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 r = bs[skn8_pos(kc + i)];
-            w[i][0] = kin ? r.x : 0u; w[i][1] = kin ? r.y : 0u;
-            w[i][2] = kin ? r.z : 0u; w[i][3] = kin ? r.w : 0u;
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        uint2 h2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kr = kstep(s, g) + 4 * h + gr;
+            const char *addr = gj < 2 ? bw + kr * 16 + gj * 8 : zero;
+            if constexpr (DT == MM_BFLOAT16)
+                h2[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                      (__attribute__((address_space(3))) bf16x4 *)(addr)));
+            else
+                h2[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                                      (__attribute__((address_space(3))) fp16x4 *)(addr)));
         }
+        const uint4 bv = make_uint4(h2[0].x, h2[0].y, h2[1].x, h2[1].y);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const uint32_t lo = (w[2 * p][n / 2] >> (16 * (n & 1))) & 0xffffu;
-                const uint32_t hi = (w[2 * p + 1][n / 2] >> (16 * (n & 1))) & 0xffffu;
-                bp[n][p] = lo | (hi << 16);
-            }
+        for (int rb = 0; rb < RB; ++rb) {
+            const uint4 avv = make_uint4(av[rb][s][0], av[rb][s][1], av[rb][s][2], av[rb][s][3]);
+            if constexpr (DT == MM_FLOAT16)
+                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, avv),
+                                                                 __builtin_bit_cast(f16x8, bv), acc[rb], 0, 0, 0);
+            else
+                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, avv),
+                                                                  __builtin_bit_cast(bf16x8, bv), acc[rb], 0, 0, 0);
+        }
     }
 
-#pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-        if (r > 0) load_a(r);
-        float v[RR * NT];
-#pragma unroll
-        for (int i = 0; i < RR; ++i)
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                float s = 0.0f;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    if constexpr (DT == MM_FLOAT16)
-                        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, av[i][p]),
-                                                   __builtin_bit_cast(half2_t, bp[n][p]), s, false);
-                    else
-                        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfloat2_t, av[i][p]),
-                                                            __builtin_bit_cast(bfloat2_t, bp[n][p]), s, false);
-                }
-                v[i * NT + n] = s;
-            }
-        transpose_reduce64(v, lane);
-        red[wave][r][lane] = v[0];
-    }
+    // Element r of acc is row 4 (lane / 16) + r, column lane % 16.
     __syncthreads();
-    S *__restrict__ Y = (S *)a.Y + b * M * NT;
-    if (tid < ROUNDS * 64) {
-        const int r = tid / 64, j = tid % 64;
-        float s = red[0][r][j];
+    float *red = (float *)lds;  // [wave][rb][r][lane]
 #pragma unroll
-        for (int w = 1; w < 8; ++w) s += red[w][r][j];
-        const int64_t row = row0 + r * RR + j / NT;
-        if (row < M) Y[row * NT + j % NT] = E::from_f32(s);
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[((wave * RB + rb) * 4 + r) * 64 + lane] = acc[rb][r];
+    __syncthreads();
+    if (tid < kSkN8Rows * 8) {
+        const int orow = tid >> 3, ocol = tid & 7;
+        const int rb = orow >> 4, rr = orow & 15;
+        const int ln = (rr >> 2) * 16 + ocol, r = rr & 3;
+        float sum = red[(rb * 4 + r) * 64 + ln];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) sum += red[((w * RB + rb) * 4 + r) * 64 + ln];
+        const int64_t row = row0 + orow;
+        if (row < M) ((S *)a.Y)[(b * M + row) * 8 + ocol] = E::from_f32(sum);
     }
 #endif
 }
