@@ -324,7 +324,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     // chunks per half-wave; FP32 B: the two half-waves read rows k and k + 4.
     auto aswz = [](int row) { return CA == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
     auto bswz = [](int k) {
-        if constexpr (ES == 4) return 8 * ((k >> 2) & 1);
+        if constexpr (ES == 4) return CPR >= 16 ? 8 * ((k >> 2) & 1) : 0;  // 8 chunks: no room to move
         else if constexpr (CPR >= 16) return 4 * (k & 3);
         else return 4 * ((k >> 1) & 1);
     };
@@ -647,13 +647,18 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
         if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false>), g, blk, 0, s, a);
     } else {
-        const dim3 blk(256);
+        // The register-staged kernel needs at least 64 x 64 (2 x 2 waves of
+        // 32 x 32): narrower entries fall back to 64-wide tiles on their own grid.
+        constexpr int GM = BM < 64 ? 64 : BM, GN = BN < 64 ? 64 : BN;
+        const int64_t gt = a.batch * ((a.M + GM - 1) / GM) * ((a.N + GN - 1) / GN) * (split ? a.split : 1);
+        if (gt > 0x7fffffff) return hipErrorInvalidValue;
+        const dim3 gg((unsigned)gt), blk(256);
         if (vec) {
-            if (split) hipLaunchKernelGGL((k_gemm_generic<DT, BM, BN, true, true>), g, blk, 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_generic<DT, BM, BN, true, false>), g, blk, 0, s, a);
+            if (split) hipLaunchKernelGGL((k_gemm_generic<DT, GM, GN, true, true>), gg, blk, 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_generic<DT, GM, GN, true, false>), gg, blk, 0, s, a);
         } else {
-            if (split) hipLaunchKernelGGL((k_gemm_generic<DT, BM, BN, false, true>), g, blk, 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_generic<DT, BM, BN, false, false>), g, blk, 0, s, a);
+            if (split) hipLaunchKernelGGL((k_gemm_generic<DT, GM, GN, false, true>), gg, blk, 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_generic<DT, GM, GN, false, false>), gg, blk, 0, s, a);
         }
     }
     return hipGetLastError();
