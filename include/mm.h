@@ -73,7 +73,9 @@ typedef enum mm_status {
     MM_ERR_BAD_OPTION = 7,   /* invalid mm_plan_options field */
     MM_ERR_TOO_LARGE = 8,    /* a size exceeds what the kernels index */
     MM_ERR_ALLOC = 9,        /* host or device allocation failed */
-    MM_ERR_HIP = 10          /* a HIP runtime call failed (see mm_last_error) */
+    MM_ERR_HIP = 10,         /* a HIP runtime call failed (see mm_last_error) */
+    MM_ERR_SIZE = 11,        /* a constant B whose element count is not the planned B's */
+    MM_ERR_NO_CONSTANT_B = 12 /* mm_execute_constant_b on a plan that owns no B */
 } mm_status;
 
 /* Algorithms (page "Gemm and MatMul Performance Roadmap", section "Target
@@ -155,6 +157,32 @@ void mm_plan_destroy(mm_plan_t plan);
  * Pointers need no particular alignment (16-byte aligned buffers take the
  * vectorized kernels).  MM_ERR_HIP reports a failed launch or allocation. */
 mm_status mm_execute(mm_plan_t plan, const void *A, const void *B, void *Y, void *stream);
+
+/* Constant B (page "MatMul Kernel Design": the reusable plan can own a
+ * constant B, giving callers a lifetime independent of the source buffer;
+ * that storage must hold exactly the planned matrix, and the B-less execute
+ * is rejected when the plan owns no B).
+ *
+ * mm_plan_set_constant_b copies `numel` elements of the planned type from
+ * the device buffer B (the dense B tensor of the planned shape) into device
+ * memory the plan owns, on the current device, ordered on `stream` (a
+ * hipStream_t; NULL = null stream), and returns once the copy has completed:
+ * the caller may then reuse or free B.  Calling it again replaces the
+ * contents.  Errors: MM_ERR_NULL_ARG (NULL plan, or NULL B with numel > 0),
+ * MM_ERR_SIZE (numel differs from the planned B's element count),
+ * MM_ERR_ALLOC, MM_ERR_HIP (copy failed, or the plan already holds B on
+ * another device).  The storage is freed by mm_plan_destroy.
+ *
+ * mm_execute_constant_b is mm_execute with B taken from that storage.  It
+ * gives MM_ERR_NO_CONSTANT_B when the plan owns no B, and MM_ERR_HIP when
+ * called on a device other than the one holding it.  A plan with a constant
+ * B may still be executed with an explicit B through mm_execute. */
+mm_status mm_plan_set_constant_b(mm_plan_t plan, const void *B, int64_t numel, void *stream);
+
+/* 1 if the plan owns a constant B, 0 if not (or for a NULL plan). */
+int mm_plan_has_constant_b(mm_plan_t plan);
+
+mm_status mm_execute_constant_b(mm_plan_t plan, const void *A, void *Y, void *stream);
 
 /* Output shape: writes up to MM_MAX_RANK entries to `shape` and the rank to
  * *rank (0 when both inputs are rank one). */

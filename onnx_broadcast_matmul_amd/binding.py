@@ -26,6 +26,7 @@ ALGO_NAMES = {0: "auto", 1: "empty", 2: "zero_fill", 3: "direct", 4: "skinny_m",
 
 ERR_NULL_ARG, ERR_RANK, ERR_NEG_DIM, ERR_K_MISMATCH, ERR_BROADCAST = 1, 2, 3, 4, 5
 ERR_DTYPE, ERR_BAD_OPTION, ERR_TOO_LARGE, ERR_ALLOC, ERR_HIP = 6, 7, 8, 9, 10
+ERR_SIZE, ERR_NO_CONSTANT_B = 11, 12
 
 
 class MMError(RuntimeError):
@@ -96,6 +97,12 @@ def lib() -> ctypes.CDLL:
         L.mm_tile_config.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                      ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
         L.mm_tile_config.restype = ctypes.c_int
+        L.mm_plan_set_constant_b.argtypes = [vp, vp, ctypes.c_int64, vp]
+        L.mm_plan_set_constant_b.restype = ctypes.c_int
+        L.mm_plan_has_constant_b.argtypes = [vp]
+        L.mm_plan_has_constant_b.restype = ctypes.c_int
+        L.mm_execute_constant_b.argtypes = [vp, vp, vp, vp]
+        L.mm_execute_constant_b.restype = ctypes.c_int
         L.mm_status_string.argtypes = [ctypes.c_int]
         L.mm_status_string.restype = ctypes.c_char_p
         L.mm_last_error.argtypes = []
@@ -231,6 +238,45 @@ class Plan:
             stream = torch.cuda.current_stream(Y.device)
         with self._lock:
             self.execute_ptr(A.data_ptr(), B.data_ptr(), Y.data_ptr(), stream.cuda_stream)
+
+    # ---- plan-owned constant B
+    def set_constant_b_ptr(self, B: int, numel: int, stream: int = 0) -> None:
+        """mm_plan_set_constant_b on a raw device pointer (copy completes before return)."""
+        _check(lib().mm_plan_set_constant_b(self._handle, ctypes.c_void_p(B), ctypes.c_int64(numel),
+                                            ctypes.c_void_p(stream)))
+
+    def set_constant_b(self, B, stream=None) -> None:
+        """Copy the device tensor B (the planned B shape and type) into plan-owned storage."""
+        import torch
+
+        if B.dtype != torch_dtype(self.dtype) or tuple(B.shape) != self.b_shape or not B.is_contiguous():
+            raise ValueError(f"B must be a contiguous {torch_dtype(self.dtype)} tensor of shape {self.b_shape}")
+        if stream is None:
+            stream = torch.cuda.current_stream(B.device)
+        with self._lock:
+            self.set_constant_b_ptr(B.data_ptr(), B.numel(), stream.cuda_stream)
+
+    @property
+    def has_constant_b(self) -> bool:
+        return bool(lib().mm_plan_has_constant_b(self._handle))
+
+    def execute_constant_b_ptr(self, A: int, Y: int, stream: int = 0) -> None:
+        """mm_execute_constant_b on raw device pointers."""
+        _check(lib().mm_execute_constant_b(self._handle, ctypes.c_void_p(A), ctypes.c_void_p(Y),
+                                           ctypes.c_void_p(stream)))
+
+    def execute_constant_b(self, A, Y, stream=None) -> None:
+        """mm_execute_constant_b on torch device tensors (B is the plan's own)."""
+        import torch
+
+        want = torch_dtype(self.dtype)
+        for name, t, shape in (("A", A, self.a_shape), ("Y", Y, self.output_shape)):
+            if t.dtype != want or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {want} tensor of shape {tuple(shape)}")
+        if stream is None:
+            stream = torch.cuda.current_stream(Y.device)
+        with self._lock:
+            self.execute_constant_b_ptr(A.data_ptr(), Y.data_ptr(), stream.cuda_stream)
 
 
 _plan_cache = {}

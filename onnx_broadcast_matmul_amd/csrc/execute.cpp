@@ -128,8 +128,74 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
     return MM_OK;
 }
 
+mm_status mm_plan_set_constant_b(mm_plan_t p, const void *B, int64_t numel, void *stream) {
+    clear_error();
+    if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
+    if (numel != p->b_numel)
+        return fail(MM_ERR_SIZE, "constant B has %lld elements; the planned B has %lld", (long long)numel,
+                    (long long)p->b_numel);
+    if (!B && numel > 0) return fail(MM_ERR_NULL_ARG, "B is NULL");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(p->cb_mutex);
+    if (p->cb && p->cb_device != dev)
+        return fail(MM_ERR_HIP, "plan holds its constant B on device %d; setting it on device %d needs its own plan",
+                    p->cb_device, dev);
+    const size_t bytes = (size_t)numel * (size_t)elem_size(p->dtype);
+    if (bytes > 0) {
+        if (!p->cb) {
+            void *ptr = nullptr;
+            e = hipMalloc(&ptr, bytes);
+            if (e != hipSuccess)
+                return fail(MM_ERR_ALLOC, "hipMalloc of %zu constant-B bytes: %s", bytes, hipGetErrorString(e));
+            p->cb = ptr;
+            p->cb_device = dev;
+        }
+        hipStream_t s = (hipStream_t)stream;
+        e = hipMemcpyAsync(p->cb, B, bytes, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "constant-B copy");
+    }
+    p->cb_set = true;
+    return MM_OK;
+}
+
+int mm_plan_has_constant_b(mm_plan_t p) {
+    if (!p) return 0;
+    std::lock_guard<std::mutex> lock(p->cb_mutex);
+    return p->cb_set ? 1 : 0;
+}
+
+mm_status mm_execute_constant_b(mm_plan_t p, const void *A, void *Y, void *stream) {
+    clear_error();
+    if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
+    const void *B = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(p->cb_mutex);
+        if (!p->cb_set) return fail(MM_ERR_NO_CONSTANT_B, "the plan owns no constant B (mm_plan_set_constant_b)");
+        if (p->cb) {
+            int dev = -1;
+            hipError_t e = hipGetDevice(&dev);
+            if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+            if (dev != p->cb_device)
+                return fail(MM_ERR_HIP, "plan holds its constant B on device %d; executing on device %d",
+                            p->cb_device, dev);
+        }
+        B = p->cb;
+    }
+    return mm_execute(p, A, B, Y, stream);
+}
+
 void mm_plan_destroy(mm_plan_t p) {
     if (!p) return;
+    if (p->cb) {
+        int cur = -1;
+        bool have_cur = hipGetDevice(&cur) == hipSuccess;
+        if (hipSetDevice(p->cb_device) == hipSuccess) (void)hipFree(p->cb);
+        if (have_cur) (void)hipSetDevice(cur);
+        p->cb = nullptr;
+    }
     if (p->ws) {
         int cur = -1;
         bool have_cur = hipGetDevice(&cur) == hipSuccess;

@@ -171,6 +171,8 @@ static mm_status resolve(const int64_t *a_shape, int a_rank, const int64_t *b_sh
 
     p->a_rank = a_rank;
     p->b_rank = b_rank;
+    p->b_numel = 1;
+    for (int i = 0; i < b_rank; ++i) p->b_numel *= b_shape[i];
     memcpy(p->a_shape, a_shape, sizeof(int64_t) * a_rank);
     memcpy(p->b_shape, b_shape, sizeof(int64_t) * b_rank);
 
@@ -469,6 +471,8 @@ const char *mm_status_string(mm_status s) {
     case MM_ERR_TOO_LARGE: return "size too large";
     case MM_ERR_ALLOC: return "allocation failed";
     case MM_ERR_HIP: return "HIP runtime error";
+    case MM_ERR_SIZE: return "constant B size differs from the planned B";
+    case MM_ERR_NO_CONSTANT_B: return "plan owns no constant B";
     }
     return "unknown status";
 }

@@ -37,6 +37,13 @@ struct mm_plan_s {
     std::mutex ws_mutex;
     void *ws = nullptr;
     int ws_device = -1;
+
+    // Plan-owned constant B (mm_plan_set_constant_b).
+    std::mutex cb_mutex;
+    bool cb_set = false;
+    void *cb = nullptr;
+    int cb_device = -1;
+    int64_t b_numel = 0;  // elements of the planned B tensor
 };
 
 namespace mm {

@@ -262,6 +262,52 @@ def test_tail_split(dt, n, dev):
     assert rep.ok, str(rep)
 
 
+@pytest.mark.parametrize("dt,algo", dt_algo_params([0] + ALGOS))
+def test_constant_b(dt, algo, dev):
+    """A plan-owned constant B: after the copy the source buffer is
+    overwritten and freed, and mm_execute_constant_b still equals
+    mm_execute with the original B bit for bit; setting B again replaces it.
+    B is broadcast over A's batch (kept dense by a second batch axis)."""
+    sa, sb = (3, 2, 70, 300), (2, 300, 90)
+    a = synth.generate(sa, dt, U1, [41, 0])
+    b1 = synth.generate(sb, dt, U1, [41, 1])
+    b2 = synth.generate(sb, dt, U1, [41, 2])
+    plan = mm.Plan(sa, sb, dt, force_algo=algo)
+    A = synth.as_torch(a, dt).to(dev)
+    src = synth.as_torch(b1, dt).to(dev)
+    plan.set_constant_b(src)
+    assert plan.has_constant_b
+    src.fill_(float("nan"))
+    del src
+    torch.cuda.synchronize()
+    for b in (b1, b2):
+        if b is b2:
+            plan.set_constant_b(synth.as_torch(b2, dt).to(dev))
+        Yc = _sentinel(plan.output_shape, dt, dev)
+        plan.execute_constant_b(A, Yc)
+        Ye = run_plan(plan, a, b, dt, dev)
+        torch.cuda.synchronize()
+        assert np.array_equal(synth.from_torch(Yc).view(np.uint8), synth.from_torch(Ye).view(np.uint8))
+        rep = check(synth.from_torch(Yc), oracle.matmul(a, b, dt), dt, sa[-1], abs_max(a, dt), abs_max(b, dt))
+        assert rep.ok, str(rep)
+
+
+def test_constant_b_tail_split(dev):
+    """Constant B under the two-launch column split of a large BF16 product."""
+    dt = mm.BFLOAT16
+    sa, sb = (16, 512, 64), (64, 11008)
+    a = synth.generate(sa, dt, ("int",), [43, 0])
+    b = synth.generate(sb, dt, ("int",), [43, 1])
+    plan = mm.Plan(sa, sb, dt)
+    assert plan.info()["tail_col"] > 0
+    plan.set_constant_b(synth.as_torch(b, dt).to(dev))
+    Yc = _sentinel(plan.output_shape, dt, dev)
+    plan.execute_constant_b(synth.as_torch(a, dt).to(dev), Yc)
+    Ye = run_plan(plan, a, b, dt, dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.from_torch(Yc), synth.from_torch(Ye))
+
+
 # ------------------------------------------------------------ full-size workloads
 
 def _sample_indices(shape, n, rng):

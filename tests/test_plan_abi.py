@@ -313,3 +313,25 @@ def test_tail_split_plans():
         assert mm.Plan(sa, sb, dt).info()["tail_col"] == 0
     forced = mm.Plan((16, 512, 4096), (4096, 11008), mm.BFLOAT16, force_algo=mm.ALGO_GENERAL, tile=1)
     assert forced.info()["tail_col"] == 0
+
+
+# ---------------------------------------------------------------- constant B
+
+def test_constant_b_errors_before_any_gpu_call():
+    """The constant-B storage must hold exactly the planned matrix, and the
+    B-less execute is refused while the plan owns no B (both checked before
+    any device call)."""
+    L = mm.lib()
+    p = mm.Plan((4, 64, 96), (96, 80), mm.FLOAT)
+    assert not p.has_constant_b
+    with pytest.raises(mm.MMError) as e:
+        p.execute_constant_b_ptr(0, 0)
+    assert e.value.status == mm.ERR_NO_CONSTANT_B
+    for numel in (96 * 80 - 1, 96 * 80 + 1, 0):
+        with pytest.raises(mm.MMError) as e:
+            p.set_constant_b_ptr(0, numel)
+        assert e.value.status == mm.ERR_SIZE
+    assert L.mm_plan_set_constant_b(None, None, 0, None) == mm.ERR_NULL_ARG
+    assert L.mm_plan_has_constant_b(None) == 0
+    assert L.mm_execute_constant_b(None, None, None, None) == mm.ERR_NULL_ARG
+    assert not p.has_constant_b
