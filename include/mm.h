@@ -184,6 +184,48 @@ int mm_plan_has_constant_b(mm_plan_t plan);
 
 mm_status mm_execute_constant_b(mm_plan_t plan, const void *A, void *Y, void *stream);
 
+/* ONNX Gemm on the same engine (page "Gemm and MatMul Performance Roadmap",
+ * section "Scope and type matrix": Gemm takes rank-2 inputs, alpha, beta,
+ * an optional broadcast bias and transA / transB; section "Remaining
+ * pull-request sequence", PR02: no, scalar, row, column and full C layouts
+ * are consumed directly, with no expanded M x N bias):
+ *
+ *   Y[m][n] = alpha * sum_k A'[m][k] * B'[k][n] + beta * C(m, n)
+ *
+ * A' = A ([M, K]) or, with trans_a, A stored [K, M] read transposed; B' = B
+ * ([K, N]) or, with trans_b, B stored [N, K] read transposed.  C is absent
+ * (c_rank = -1: Y = alpha * A'B') or has rank 0..2 and broadcasts
+ * unidirectionally to [M, N]: [] / [1] / [1, 1] scalar, [N] / [1, N] one
+ * value per column, [M, 1] one value per row, [M, N] full.  A, B, C and Y
+ * share the element type (FLOAT, FLOAT16 or BFLOAT16; DOUBLE gives
+ * MM_ERR_DTYPE); 16-bit types accumulate in FP32 and alpha * sum + beta * c
+ * is formed in FP32 before the single narrowing.  Y is dense [M, N]. */
+typedef struct mm_gemm_desc {
+    int64_t a_rows, a_cols; /* stored A shape */
+    int64_t b_rows, b_cols; /* stored B shape */
+    int32_t trans_a, trans_b;
+    int32_t c_rank;         /* -1 (no C), 0, 1 or 2 */
+    int32_t reserved;       /* must be 0 */
+    int64_t c_shape[2];     /* the first c_rank entries are used */
+    float alpha, beta;
+} mm_gemm_desc;
+
+/* Create a Gemm plan (shapes, transposes, C's layout and the algorithm are
+ * resolved once; errors as for mm_plan_create, plus MM_ERR_BROADCAST for a
+ * C that does not broadcast to [M, N] and MM_ERR_BAD_OPTION for an invalid
+ * descriptor or an option the Gemm path does not run: forced SKINNY_M /
+ * SKINNY_N, or a tile outside the transposed-operand subset when an operand
+ * is transposed).  `opt` may be NULL.  The plan answers the introspection
+ * calls above (output shape [M, N]). */
+mm_status mm_gemm_plan_create(const mm_gemm_desc *desc, int dtype, const mm_plan_options *opt, mm_plan_t *out);
+
+/* Enqueue Y = Gemm(A, B, C) on `stream`.  C must be non-NULL exactly when
+ * the plan has one (else MM_ERR_NULL_ARG); K == 0 gives Y = beta * C (or
+ * zeros) without reading A or B.  Other rules as for mm_execute.  A Gemm
+ * plan is refused by mm_execute and a MatMul plan by mm_gemm_execute
+ * (MM_ERR_BAD_OPTION). */
+mm_status mm_gemm_execute(mm_plan_t plan, const void *A, const void *B, const void *C, void *Y, void *stream);
+
 /* Output shape: writes up to MM_MAX_RANK entries to `shape` and the rank to
  * *rank (0 when both inputs are rank one). */
 mm_status mm_plan_output_shape(mm_plan_t plan, int64_t *shape, int *rank);

@@ -57,6 +57,17 @@ class PlanInfo(ctypes.Structure):
     ]
 
 
+class GemmDesc(ctypes.Structure):
+    _fields_ = [
+        ("a_rows", ctypes.c_int64), ("a_cols", ctypes.c_int64),
+        ("b_rows", ctypes.c_int64), ("b_cols", ctypes.c_int64),
+        ("trans_a", ctypes.c_int32), ("trans_b", ctypes.c_int32),
+        ("c_rank", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("c_shape", ctypes.c_int64 * 2),
+        ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+    ]
+
+
 _lib = None
 _lib_lock = threading.Lock()
 
@@ -103,6 +114,11 @@ def lib() -> ctypes.CDLL:
         L.mm_plan_has_constant_b.restype = ctypes.c_int
         L.mm_execute_constant_b.argtypes = [vp, vp, vp, vp]
         L.mm_execute_constant_b.restype = ctypes.c_int
+        L.mm_gemm_plan_create.argtypes = [ctypes.POINTER(GemmDesc), ctypes.c_int, ctypes.POINTER(PlanOptions),
+                                           ctypes.POINTER(vp)]
+        L.mm_gemm_plan_create.restype = ctypes.c_int
+        L.mm_gemm_execute.argtypes = [vp, vp, vp, vp, vp, vp]
+        L.mm_gemm_execute.restype = ctypes.c_int
         L.mm_status_string.argtypes = [ctypes.c_int]
         L.mm_status_string.restype = ctypes.c_char_p
         L.mm_last_error.argtypes = []
@@ -277,6 +293,56 @@ class Plan:
             stream = torch.cuda.current_stream(Y.device)
         with self._lock:
             self.execute_constant_b_ptr(A.data_ptr(), Y.data_ptr(), stream.cuda_stream)
+
+
+class GemmPlan(Plan):
+    """mm_gemm_plan_create / mm_gemm_execute: ONNX Gemm of rank-2 A, B with
+    transA / transB, alpha, beta and an optional C broadcast to [M, N]."""
+
+    def __init__(self, a_shape, b_shape, dtype: int, trans_a: bool = False, trans_b: bool = False,
+                 c_shape=None, alpha: float = 1.0, beta: float = 1.0, force_algo: int = 0, tile: int = 0,
+                 split_k: int = 0):
+        L = lib()
+        self._handle = ctypes.c_void_p()
+        self.a_shape = tuple(int(d) for d in a_shape)
+        self.b_shape = tuple(int(d) for d in b_shape)
+        self.c_shape = None if c_shape is None else tuple(int(d) for d in c_shape)
+        self.dtype = int(dtype)
+        if len(self.a_shape) != 2 or len(self.b_shape) != 2:
+            raise ValueError("Gemm takes rank-2 A and B")
+        d = GemmDesc()
+        d.a_rows, d.a_cols = self.a_shape
+        d.b_rows, d.b_cols = self.b_shape
+        d.trans_a, d.trans_b = int(trans_a), int(trans_b)
+        d.c_rank = -1 if self.c_shape is None else len(self.c_shape)
+        for i, v in enumerate(self.c_shape or ()):
+            d.c_shape[i] = v
+        d.alpha, d.beta = float(alpha), float(beta)
+        opt = PlanOptions(force_algo, tile, split_k, 0)
+        _check(L.mm_gemm_plan_create(ctypes.byref(d), self.dtype, ctypes.byref(opt), ctypes.byref(self._handle)))
+        self._lock = threading.Lock()
+
+    def execute_ptr(self, A: int, B: int, Y: int, stream: int = 0, C: int = 0) -> None:
+        _check(lib().mm_gemm_execute(self._handle, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(C),
+                                     ctypes.c_void_p(Y), ctypes.c_void_p(stream)))
+
+    def execute(self, A, B, Y, C=None, stream=None) -> None:
+        import torch
+
+        want = torch_dtype(self.dtype)
+        checks = [("A", A, self.a_shape), ("B", B, self.b_shape), ("Y", Y, self.output_shape)]
+        if self.c_shape is not None:
+            if C is None:
+                raise ValueError("this Gemm plan has a C")
+            checks.append(("C", C, self.c_shape))
+        for name, t, shape in checks:
+            if t.dtype != want or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {want} tensor of shape {tuple(shape)}")
+        if stream is None:
+            stream = torch.cuda.current_stream(Y.device)
+        with self._lock:
+            self.execute_ptr(A.data_ptr(), B.data_ptr(), Y.data_ptr(), stream.cuda_stream,
+                             C.data_ptr() if C is not None else 0)
 
 
 _plan_cache = {}

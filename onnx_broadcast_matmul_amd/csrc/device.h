@@ -107,6 +107,21 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Gemm epilogue for output (m, n): alpha * acc + beta * C(m, n), C read in
+// its broadcast layout (scalar, per column n, per row m, or full); without C
+// the result is alpha * acc.  Positions outside the output read nothing.
+template <typename E>
+__device__ __forceinline__ float gemm_epilogue(const KArgs &a, float acc, int64_t m, int64_t n) {
+    if (a.c_mode == kBiasNone) return a.alpha * acc;
+    float c = 0.0f;
+    if (m < a.M && n < a.N) {
+        const typename E::S *C = (const typename E::S *)a.C;
+        const int64_t idx = a.c_mode == kBiasScalar ? 0 : a.c_mode == kBiasRow ? n : a.c_mode == kBiasCol ? m : m * a.ldc + n;
+        c = E::to_f32(C[idx]);
+    }
+    return a.alpha * acc + a.beta * c;
+}
+
 // Element offsets of the A and B matrices used by output batch `b`.
 __device__ __forceinline__ void batch_offsets(const BatchDesc &bd, int64_t b, int64_t &oa, int64_t &ob) {
     oa = 0;

@@ -34,11 +34,8 @@ static mm_status ensure_workspace(mm_plan_s *p) {
     return MM_OK;
 }
 
-extern "C" {
-
-mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *stream) {
-    clear_error();
-    if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
+// Launches of a MatMul or Gemm plan (C: the Gemm bias, NULL if none).
+static mm_status execute_impl(mm_plan_s *p, const void *A, const void *B, const void *C, void *Y, void *stream) {
     if (p->algo == MM_ALGO_EMPTY) return MM_OK;
     if (!Y) return fail(MM_ERR_NULL_ARG, "Y is NULL for a non-empty output");
     hipStream_t s = (hipStream_t)stream;
@@ -47,7 +44,8 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
         e = launch_fill_zero(p->dtype, Y, p->out_numel, s);
         return e == hipSuccess ? MM_OK : hip_fail(e, "zero-fill launch");
     }
-    if (!A || !B) return fail(MM_ERR_NULL_ARG, "A or B is NULL");
+    if (p->K > 0 && (!A || !B)) return fail(MM_ERR_NULL_ARG, "A or B is NULL");
+    if (p->is_gemm && p->c_mode != kBiasNone && !C) return fail(MM_ERR_NULL_ARG, "the plan has a C but C is NULL");
 
     KArgs a;
     memset(&a, 0, sizeof(a));
@@ -58,8 +56,19 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
     a.M = p->kernel_m;
     a.N = p->N;
     a.K = p->K;
-    a.ldb = p->N;
+    a.lda = p->ta ? p->M : p->K;
+    a.ldb = p->tb ? p->K : p->N;
     a.ldy = p->N;
+    if (p->is_gemm) {
+        a.ta = p->ta;
+        a.tb = p->tb;
+        a.gemm_epi = 1;
+        a.c_mode = p->c_mode;
+        a.alpha = p->alpha;
+        a.beta = p->beta;
+        a.C = C;
+        a.ldc = p->ldc;
+    }
     a.batch = p->batch;
     a.kchunk = p->kchunk;
     a.split = p->split;
@@ -67,8 +76,8 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
 
     const int64_t es = elem_size(p->dtype);
     Align al;
-    al.a = aligned16(A) && (p->K * es) % 16 == 0;
-    al.b = aligned16(B) && (p->N * es) % 16 == 0;
+    al.a = aligned16(A) && (a.lda * es) % 16 == 0;
+    al.b = aligned16(B) && (a.ldb * es) % 16 == 0;
     al.y = aligned16(Y) && (p->N * es) % 16 == 0;
     // Split-K partials are FP32 rows (double for DOUBLE) in a workspace of
     // our own (aligned); only the 16- and 32-bit kernels read y_vec.
@@ -126,6 +135,22 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
     }
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     return MM_OK;
+}
+
+extern "C" {
+
+mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *stream) {
+    clear_error();
+    if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
+    if (p->is_gemm) return fail(MM_ERR_BAD_OPTION, "a Gemm plan runs through mm_gemm_execute");
+    return execute_impl(p, A, B, nullptr, Y, stream);
+}
+
+mm_status mm_gemm_execute(mm_plan_t p, const void *A, const void *B, const void *C, void *Y, void *stream) {
+    clear_error();
+    if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
+    if (!p->is_gemm) return fail(MM_ERR_BAD_OPTION, "a MatMul plan runs through mm_execute");
+    return execute_impl(p, A, B, C, Y, stream);
 }
 
 mm_status mm_plan_set_constant_b(mm_plan_t p, const void *B, int64_t numel, void *stream) {

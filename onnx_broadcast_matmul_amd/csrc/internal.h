@@ -38,13 +38,27 @@ struct KArgs {
     void *Y;
     float *W;
     int64_t M, N, K;
-    int64_t ldb, ldy;  // row pitches of B and Y in elements
+    int64_t lda, ldb, ldy;  // row pitches of the stored A, stored B and Y, in elements
     int64_t batch;
     int64_t kchunk;
     int32_t split;
     int32_t y_vec;  // output rows (Y, or the workspace) are whole 16-byte chunks
     BatchDesc bd;
+    // Gemm: A stored transposed ([K][M], lda = M) and/or B stored transposed
+    // ([N][K], ldb = K); the kernels then read A'[m][k] = A[k][m] and
+    // B'[k][n] = B[n][k].  The epilogue Y = alpha * acc + beta * C(m, n) is
+    // applied when gemm_epi is set (C broadcast per c_mode, C's rows ldc
+    // elements apart); MatMul leaves all of this zero.
+    int32_t ta, tb;
+    int32_t gemm_epi;
+    int32_t c_mode;  // a GemmBias value
+    float alpha, beta;
+    const void *C;
+    int64_t ldc;
 };
+
+// Layouts of the Gemm bias C, unidirectionally broadcast to (M, N).
+enum GemmBias { kBiasNone = 0, kBiasScalar = 1, kBiasRow = 2, kBiasCol = 3, kBiasFull = 4 };
 
 // Which operands allow 16-byte vector access: the base pointer is 16-byte
 // aligned and every row starts on a 16-byte boundary (A: K elements per row;
@@ -73,6 +87,8 @@ const TileCfg *tile_entry(int dtype, int index);
 hipError_t launch_direct(int dtype, const KArgs &a, hipStream_t s);
 hipError_t launch_fill_zero(int dtype, void *Y, int64_t n, hipStream_t s);
 hipError_t launch_general(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);
+// The same for transposed operands (a.ta / a.tb); only the kTransTiles entries.
+hipError_t launch_general_t(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);
 hipError_t launch_splitk_reduce(int dtype, const KArgs &a, hipStream_t s);
 hipError_t launch_skinny_m(int dtype, const Align &al, const KArgs &a, hipStream_t s);
 hipError_t launch_skinny_n(int dtype, const Align &al, const KArgs &a, hipStream_t s);

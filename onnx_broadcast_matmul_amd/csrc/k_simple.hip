@@ -4,7 +4,8 @@
 // Direct: page "Gemm and MatMul Performance Roadmap", section "Target
 // computation algorithm" (tiny matrices: an un-packed kernel, since staging
 // costs more than the arithmetic).  One thread computes one output element
-// with an FP32 accumulator over ascending k.
+// with an FP32 accumulator over ascending k (for Gemm: of the transposed
+// operands when asked, then the alpha / beta / C epilogue).
 //
 // Split-K reduction: same page, section "Parallel execution" (K partitioned
 // into partial products that are summed afterwards).  Partials are summed in
@@ -30,10 +31,13 @@ __global__ __launch_bounds__(256) void k_direct(KArgs a) {
         const int64_t b = idx / (M * N);
         int64_t oa, ob;
         batch_offsets(a.bd, b, oa, ob);
-        const S *ap = A + oa + m * K;
-        const S *bp = B + ob + n;
+        // A'[m][k] and B'[k][n], each stored as given or transposed (Gemm).
+        const S *ap = A + oa + (a.ta ? m : m * a.lda);
+        const S *bp = B + ob + (a.tb ? n * a.ldb : n);
+        const int64_t sak = a.ta ? a.lda : 1, sbk = a.tb ? 1 : a.ldb;
         float acc = 0.0f;
-        for (int64_t k = 0; k < K; ++k) acc = fmaf(E::to_f32(ap[k]), E::to_f32(bp[k * N]), acc);
+        for (int64_t k = 0; k < K; ++k) acc = fmaf(E::to_f32(ap[k * sak]), E::to_f32(bp[k * sbk]), acc);
+        if (a.gemm_epi) acc = gemm_epilogue<E>(a, acc, m, n);
         Y[idx] = E::from_f32(acc);
     }
 }
@@ -94,7 +98,11 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a) {
         S *__restrict__ Y = (S *)a.Y;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (o0 + e < total) Y[o0 + e] = E::from_f32(red[0][og][e]);
+            if (o0 + e < total) {
+                float v = red[0][og][e];
+                if (a.gemm_epi) v = gemm_epilogue<E>(a, v, (o0 + e) / a.N, (o0 + e) % a.N);
+                Y[o0 + e] = E::from_f32(v);
+            }
     }
 }
 
@@ -153,7 +161,11 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_wave(KArgs a) {
         S *__restrict__ Y = (S *)a.Y;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (o0 + e < total) Y[o0 + e] = E::from_f32(acc[e]);
+            if (o0 + e < total) {
+                float v = acc[e];
+                if (a.gemm_epi) v = gemm_epilogue<E>(a, v, (o0 + e) / a.N, (o0 + e) % a.N);
+                Y[o0 + e] = E::from_f32(v);
+            }
     }
 }
 

@@ -77,10 +77,25 @@ static double tile_score(int dtype, int index, int64_t batch, int64_t M, int64_t
     return occ * pad * tile_quality(dtype, index);
 }
 
-static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N) {
-    int best = 0;
+// Tile entries a plan may use: every entry, except that transposed operands
+// (Gemm) have kernels only for the kTransTiles subset.
+static bool tile_allowed(int dtype, int index, bool transposed) {
+    if (!transposed) return true;
+    if (dtype == MM_FLOAT) {
+        for (int t : kTransTiles32)
+            if (t == index) return true;
+    } else {
+        for (int t : kTransTiles16)
+            if (t == index) return true;
+    }
+    return false;
+}
+
+static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, bool transposed = false) {
+    int best = -1;
     double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
+        if (!tile_allowed(dtype, i, transposed)) continue;
         double s = tile_score(dtype, i, batch, M, N);
         if (s > best_s + 1e-9) {
             best_s = s;
@@ -115,7 +130,7 @@ static int64_t gcd64(int64_t a, int64_t b) {
 static void plan_tail(mm_plan_s *p) {
     p->tail_col = 0;
     p->tail_tile = -1;
-    if (p->dtype == MM_DOUBLE) return;
+    if (p->dtype == MM_DOUBLE || p->is_gemm) return;
     const TileCfg *t = tile_entry(p->dtype, p->tile);
     if (tile_wgs_per_cu(t) != 1) return;
     const int64_t rows = p->batch * cdiv(p->kernel_m, t->bm);
@@ -142,10 +157,11 @@ static void plan_tail(mm_plan_s *p) {
 }
 
 // Smallest-padding tile for split-K (its output is tiny by construction).
-static int choose_split_tile(int dtype, int64_t M, int64_t N) {
-    int best = 0;
+static int choose_split_tile(int dtype, int64_t M, int64_t N, bool transposed = false) {
+    int best = -1;
     double best_pad = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
+        if (!tile_allowed(dtype, i, transposed)) continue;
         const TileCfg *t = tile_entry(dtype, i);
         double pad = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
         if (pad > best_pad + 1e-9) {
@@ -313,7 +329,9 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         return MM_OK;
     }
     if (K == 0) {
-        p->algo = MM_ALGO_ZERO_FILL;
+        // MatMul: the empty sum.  Gemm: Y = beta * C (or alpha * 0), formed by
+        // the direct kernel without reading A or B.
+        p->algo = p->is_gemm ? MM_ALGO_DIRECT : MM_ALGO_ZERO_FILL;
         return MM_OK;
     }
     mm_status st = check_limits(p);
@@ -341,20 +359,31 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         // DOUBLE has no skinny kernels: its skinny shapes take the tiled
         // FP64 kernel, which still reads the large operand once.
         if (p->dtype == MM_DOUBLE && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N)) algo = MM_ALGO_GENERAL;
+        // Gemm (transposes, epilogue) runs on the direct, tiled and split-K kernels.
+        if (p->is_gemm && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N)) algo = MM_ALGO_GENERAL;
     }
     if (algo < MM_ALGO_DIRECT || algo > MM_ALGO_GENERAL)
         return fail(MM_ERR_BAD_OPTION, "force_algo %d is not a forcible algorithm", algo);
     if (p->dtype == MM_DOUBLE && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N))
         return fail(MM_ERR_BAD_OPTION, "DOUBLE has no skinny-M / skinny-N kernel (force GENERAL or DIRECT)");
+    if (p->is_gemm && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N))
+        return fail(MM_ERR_BAD_OPTION, "Gemm runs on the direct, general and split-K kernels only");
     p->algo = algo;
 
     if (algo == MM_ALGO_GENERAL || algo == MM_ALGO_SPLIT_K) {
         int req = opt ? opt->tile : 0;
         if (req < 0 || req > tile_count(p->dtype))
             return fail(MM_ERR_BAD_OPTION, "tile %d out of range 0..%d", req, tile_count(p->dtype));
-        if (req > 0) p->tile = req - 1;
-        else if (algo == MM_ALGO_GENERAL) p->tile = choose_tile(p->dtype, p->batch, M, N);
-        else p->tile = choose_split_tile(p->dtype, M, N);
+        const bool transposed = p->ta || p->tb;
+        if (req > 0) {
+            p->tile = req - 1;
+            if (!tile_allowed(p->dtype, p->tile, transposed))
+                return fail(MM_ERR_BAD_OPTION, "tile %d has no kernel for transposed operands", req);
+        } else if (algo == MM_ALGO_GENERAL) {
+            p->tile = choose_tile(p->dtype, p->batch, M, N, transposed);
+        } else {
+            p->tile = choose_split_tile(p->dtype, M, N, transposed);
+        }
         if (algo == MM_ALGO_GENERAL && req == 0) plan_tail(p);
         const TileCfg *t = tile_entry(p->dtype, p->tile);
         const int64_t tiles = p->batch * cdiv(M, t->bm) * cdiv(N, t->bn);
@@ -401,6 +430,74 @@ mm_status mm_plan_create_ex(const int64_t *a_shape, int a_rank, const int64_t *b
 mm_status mm_plan_create(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank, int dtype,
                          mm_plan_t *out) {
     return mm_plan_create_ex(a_shape, a_rank, b_shape, b_rank, dtype, nullptr, out);
+}
+
+mm_status mm_gemm_plan_create(const mm_gemm_desc *d, int dtype, const mm_plan_options *opt, mm_plan_t *out) {
+    clear_error();
+    if (!out) return fail(MM_ERR_NULL_ARG, "out is NULL");
+    *out = nullptr;
+    if (!d) return fail(MM_ERR_NULL_ARG, "descriptor is NULL");
+    if (dtype != MM_FLOAT && dtype != MM_FLOAT16 && dtype != MM_BFLOAT16)
+        return fail(MM_ERR_DTYPE, "Gemm supports FLOAT, FLOAT16 and BFLOAT16 (got %d)", dtype);
+    if (d->reserved != 0 || (opt && opt->reserved != 0)) return fail(MM_ERR_BAD_OPTION, "reserved field must be 0");
+    if ((d->trans_a != 0 && d->trans_a != 1) || (d->trans_b != 0 && d->trans_b != 1))
+        return fail(MM_ERR_BAD_OPTION, "trans_a / trans_b must be 0 or 1");
+    if (d->c_rank < -1 || d->c_rank > 2) return fail(MM_ERR_BAD_OPTION, "c_rank %d is not -1, 0, 1 or 2", d->c_rank);
+    if (d->a_rows < 0 || d->a_cols < 0 || d->b_rows < 0 || d->b_cols < 0)
+        return fail(MM_ERR_NEG_DIM, "a Gemm operand dimension is negative");
+    const int64_t M = d->trans_a ? d->a_cols : d->a_rows;
+    const int64_t K = d->trans_a ? d->a_rows : d->a_cols;
+    const int64_t Kb = d->trans_b ? d->b_cols : d->b_rows;
+    const int64_t N = d->trans_b ? d->b_rows : d->b_cols;
+    if (K != Kb)
+        return fail(MM_ERR_K_MISMATCH, "inner dimensions differ: A' has K=%lld, B' has K=%lld", (long long)K,
+                    (long long)Kb);
+    // C right-aligned against (M, N); each dimension 1 or the output's.
+    int c_mode = kBiasNone;
+    int64_t cr = 1, cc = 1;
+    if (d->c_rank >= 1) cc = d->c_shape[d->c_rank - 1];
+    if (d->c_rank == 2) cr = d->c_shape[0];
+    if (cr < 0 || cc < 0) return fail(MM_ERR_NEG_DIM, "a C dimension is negative");
+    if (d->c_rank >= 0) {
+        if ((cr != 1 && cr != M) || (cc != 1 && cc != N))
+            return fail(MM_ERR_BROADCAST, "C [%lld, %lld] does not broadcast to [%lld, %lld]", (long long)cr,
+                        (long long)cc, (long long)M, (long long)N);
+        c_mode = (cr == 1 && cc == 1) ? kBiasScalar : cr == 1 ? kBiasRow : cc == 1 ? kBiasCol : kBiasFull;
+    }
+    mm_plan_s *p = new (std::nothrow) mm_plan_s();
+    if (!p) return fail(MM_ERR_ALLOC, "host allocation failed");
+    p->dtype = dtype;
+    p->is_gemm = true;
+    p->ta = d->trans_a;
+    p->tb = d->trans_b;
+    p->alpha = d->alpha;
+    p->beta = d->beta;
+    p->c_mode = c_mode;
+    p->ldc = c_mode == kBiasFull ? N : 0;
+    p->a_rank = p->b_rank = 2;
+    p->a_shape[0] = d->a_rows;
+    p->a_shape[1] = d->a_cols;
+    p->b_shape[0] = d->b_rows;
+    p->b_shape[1] = d->b_cols;
+    p->b_numel = d->b_rows * d->b_cols;
+    p->out_rank = 2;
+    p->out_shape[0] = M;
+    p->out_shape[1] = N;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->out_numel = M * N;
+    p->total_batch = 1;
+    p->batch = 1;
+    p->kernel_m = M;
+    p->folded = 0;
+    mm_status st = select_algo(p, opt);
+    if (st != MM_OK) {
+        delete p;
+        return st;
+    }
+    *out = p;
+    return MM_OK;
 }
 
 mm_status mm_plan_output_shape(mm_plan_t p, int64_t *shape, int *rank) {

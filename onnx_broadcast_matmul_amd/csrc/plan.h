@@ -38,6 +38,13 @@ struct mm_plan_s {
     void *ws = nullptr;
     int ws_device = -1;
 
+    // Gemm (mm_gemm_plan_create): transposed operands, epilogue, C layout.
+    bool is_gemm = false;
+    int ta = 0, tb = 0;
+    float alpha = 1.0f, beta = 0.0f;
+    int c_mode = 0;  // mm::GemmBias
+    int64_t ldc = 0;
+
     // Plan-owned constant B (mm_plan_set_constant_b).
     std::mutex cb_mutex;
     bool cb_set = false;

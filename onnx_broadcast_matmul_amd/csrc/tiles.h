@@ -48,6 +48,10 @@ constexpr TileCfg kTiles64[] = {
     {64, 64, 2, 2, 128, 2, 4, 1},
 };
 
+// Entries instantiated for transposed operands (Gemm's transA / transB).
+constexpr int kTransTiles16[] = {0, 5, 4};
+constexpr int kTransTiles32[] = {4, 2};
+
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
 constexpr int kNumTiles32 = sizeof(kTiles32) / sizeof(kTiles32[0]);
 constexpr int kNumTiles64 = sizeof(kTiles64) / sizeof(kTiles64[0]);

@@ -32,6 +32,7 @@ STATUS = {
     4: "batch dimensions not broadcastable",
     5: "unknown dtype",
     6: "allocation failed",
+    7: "Gemm operand shapes do not fit",
 }
 
 
@@ -82,6 +83,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
         L.oracle_decode_bf16.restype = ctypes.c_double
         L.oracle_threads.restype = ctypes.c_int
+        L.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                  i64p, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_void_p]
+        L.oracle_gemm_at.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p, i64p, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -158,6 +166,51 @@ def decode(bits: np.ndarray, dtype: int) -> np.ndarray:
     bits = _storage(np.asarray(bits), dtype)
     out = np.empty(bits.shape, dtype=np.float64)
     st = lib().oracle_decode_array(dtype, bits.ctypes.data, bits.size, out.ctypes.data)
+    if st:
+        raise OracleError(st)
+    return out
+
+
+def gemm(a: np.ndarray, b: np.ndarray, dtype: int, trans_a: bool = False, trans_b: bool = False,
+         c: np.ndarray = None, alpha: float = 1.0, beta: float = 1.0) -> np.ndarray:
+    """ONNX Gemm of stored rank-2 tensors (raw storage as for ``matmul``):
+    alpha * A' B' + beta * C, with C (optional) broadcast to [M, N].  alpha
+    and beta are taken as given (float64).  Returns float64 [M, N]."""
+    a = _storage(a, dtype)
+    b = _storage(b, dtype)
+    if a.ndim != 2 or b.ndim != 2:
+        raise OracleError(7)
+    M = a.shape[1] if trans_a else a.shape[0]
+    N = b.shape[0] if trans_b else b.shape[1]
+    y = np.empty(M * N, dtype=np.float64)
+    cptr, cshape, crank = None, _shape_arr(()), -1
+    if c is not None:
+        c = _storage(c, dtype)
+        cptr, cshape, crank = c.ctypes.data, _shape_arr(c.shape), c.ndim
+    st = lib().oracle_gemm(dtype, a.ctypes.data, a.shape[0], a.shape[1], int(trans_a), b.ctypes.data,
+                           b.shape[0], b.shape[1], int(trans_b), cptr, cshape, crank, float(alpha), float(beta),
+                           y.ctypes.data)
+    if st:
+        raise OracleError(st)
+    return y.reshape(M, N)
+
+
+def gemm_at(a: np.ndarray, b: np.ndarray, dtype: int, flat_idx, trans_a: bool = False, trans_b: bool = False,
+            c: np.ndarray = None, alpha: float = 1.0, beta: float = 1.0) -> np.ndarray:
+    """Selected Gemm outputs (flat row-major indices into [M, N]) as float64."""
+    a = _storage(a, dtype)
+    b = _storage(b, dtype)
+    if a.ndim != 2 or b.ndim != 2:
+        raise OracleError(7)
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    out = np.empty(idx.size, dtype=np.float64)
+    cptr, cshape, crank = None, _shape_arr(()), -1
+    if c is not None:
+        c = _storage(c, dtype)
+        cptr, cshape, crank = c.ctypes.data, _shape_arr(c.shape), c.ndim
+    st = lib().oracle_gemm_at(dtype, a.ctypes.data, a.shape[0], a.shape[1], int(trans_a), b.ctypes.data,
+                              b.shape[0], b.shape[1], int(trans_b), cptr, cshape, crank, float(alpha), float(beta),
+                              idx.ctypes.data, idx.size, out.ctypes.data)
     if st:
         raise OracleError(st)
     return out

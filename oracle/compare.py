@@ -19,6 +19,10 @@ accumulation with final narrowing, page "MatMul Kernel Design", section
   Stability of Numerical Algorithms", 2nd ed., section 3.1) puts both the
   result and the oracle within ``gamma_K * sum_k |a_k b_k|`` of the exact
   value, and ``sum_k |a_k b_k| <= K max|A| max|B|``.
+* Gemm (FLOAT, and the second clause for 16-bit outputs): ``|alpha|`` times
+  the FLOAT rule, plus ``4 * 2^-24 * (|alpha| K max|A| max|B| + |beta|
+  max|C|)`` for the FP32 roundings of ``alpha * sum + beta * c`` (each term
+  is at most that large).
 * Exact mode (small-integer-valued inputs): ``y == narrow(o)`` bit for bit.
 * NaN matches only NaN; an infinity matches only the same infinity.
 """
@@ -41,6 +45,12 @@ def fp64_tolerance(K: int, amax: float, bmax: float) -> float:
     k = max(int(K), 0)
     gamma = k * u / (1.0 - k * u)
     return 2.0 * gamma * k * float(amax) * float(bmax)
+
+
+def gemm_tolerance(K: int, amax: float, bmax: float, cmax: float, alpha: float, beta: float) -> float:
+    k = max(int(K), 0)
+    return (abs(alpha) * fp32_tolerance(k, amax, bmax)
+            + 4.0 * 2.0 ** -24 * (abs(alpha) * k * amax * bmax + abs(beta) * cmax))
 
 
 def abs_max(x: np.ndarray, dtype: int) -> float:
@@ -87,14 +97,16 @@ def _special_mismatch(yv: np.ndarray, o: np.ndarray) -> np.ndarray:
 
 
 def check(y: np.ndarray, o: np.ndarray, dtype: int, K: int, amax: float, bmax: float,
-          exact: bool = False) -> Report:
+          exact: bool = False, tol: float = None) -> Report:
     """Compare stored results ``y`` (float32 array, or uint16 bit patterns) with
-    fp64 oracle values ``o`` of the same shape."""
+    fp64 oracle values ``o`` of the same shape.  ``tol`` overrides the
+    absolute rule (Gemm passes ``gemm_tolerance``)."""
     o = np.asarray(o, dtype=np.float64).reshape(-1)
     y = np.asarray(y).reshape(-1)
     if y.size != o.size:
         return Report(False, int(y.size), math.inf, 0.0, detail=f"size {y.size} != {o.size}")
-    tol = fp64_tolerance(K, amax, bmax) if dtype == DOUBLE else fp32_tolerance(K, amax, bmax)
+    if tol is None:
+        tol = fp64_tolerance(K, amax, bmax) if dtype == DOUBLE else fp32_tolerance(K, amax, bmax)
     if y.size == 0:
         return Report(True, 0, 0.0, tol)
     if dtype in (FLOAT16, BFLOAT16):

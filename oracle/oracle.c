@@ -392,6 +392,83 @@ int oracle_matmul_at(int dtype, const void *A, const int64_t *a_shape, int a_ran
     return OR_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Gemm (page "Gemm and MatMul Performance Roadmap", section "Scope and type */
+/* matrix": rank-2 inputs, alpha, beta, optional broadcast bias, transA and  */
+/* transB):                                                                  */
+/*   Y[m][n] = alpha * sum_k A'[m][k] * B'[k][n] + beta * C(m, n)            */
+/* with A' = A, or A transposed (A stored [K][M]); B' = B, or B transposed    */
+/* (B stored [N][K]); C broadcast unidirectionally to [M][N] NumPy style:     */
+/* right-aligned, a dimension of 1 stretches, otherwise it must equal the    */
+/* output's.  Without C the bias term is absent (beta unused).  The sum runs */
+/* over ascending k in double, then alpha * sum + beta * c is formed in      */
+/* double.                                                                   */
+/* ------------------------------------------------------------------------ */
+
+#define OR_ERR_SHAPE 7 /* Gemm operand ranks / sizes do not fit */
+
+static int gemm_impl(int dtype, const void *A, int64_t a_rows, int64_t a_cols, int trans_a, const void *B,
+                     int64_t b_rows, int64_t b_cols, int trans_b, const void *C, const int64_t *c_shape, int c_rank,
+                     double alpha, double beta, const int64_t *flat_idx, int64_t n_idx, double *Y)
+{
+    if (!dtype_ok(dtype)) return OR_ERR_DTYPE;
+    if (build_tables() != OR_OK) return OR_ERR_ALLOC;
+    if (a_rows < 0 || a_cols < 0 || b_rows < 0 || b_cols < 0) return OR_ERR_NEGATIVE;
+    int64_t M = trans_a ? a_cols : a_rows;
+    int64_t K = trans_a ? a_rows : a_cols;
+    int64_t Kb = trans_b ? b_cols : b_rows;
+    int64_t N = trans_b ? b_rows : b_cols;
+    if (K != Kb) return OR_ERR_K;
+    /* C's dimensions, right-aligned against (M, N) and padded with 1. */
+    int64_t cr = 1, cc = 1;
+    if (C) {
+        if (c_rank < 0 || c_rank > 2) return OR_ERR_SHAPE;
+        if (c_rank == 1) cc = c_shape[0];
+        if (c_rank == 2) {
+            cr = c_shape[0];
+            cc = c_shape[1];
+        }
+        if (cr < 0 || cc < 0) return OR_ERR_NEGATIVE;
+        if ((cr != 1 && cr != M) || (cc != 1 && cc != N)) return OR_ERR_BROADCAST;
+    }
+    const int64_t count = flat_idx ? n_idx : M * N;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t f = flat_idx ? flat_idx[i] : i;
+        const int64_t m = f / N, n = f % N;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = load_elem(A, dtype, trans_a ? k * M + m : m * K + k);
+            double b = load_elem(B, dtype, trans_b ? n * K + k : k * N + n);
+            acc += a * b;
+        }
+        double y = alpha * acc;
+        if (C) {
+            int64_t ci = (cr == 1 ? 0 : m) * cc + (cc == 1 ? 0 : n);
+            y += beta * load_elem(C, dtype, ci);
+        }
+        Y[i] = y;
+    }
+    return OR_OK;
+}
+
+int oracle_gemm(int dtype, const void *A, int64_t a_rows, int64_t a_cols, int trans_a, const void *B,
+                int64_t b_rows, int64_t b_cols, int trans_b, const void *C, const int64_t *c_shape, int c_rank,
+                double alpha, double beta, double *Y)
+{
+    return gemm_impl(dtype, A, a_rows, a_cols, trans_a, B, b_rows, b_cols, trans_b, C, c_shape, c_rank, alpha,
+                     beta, 0, 0, Y);
+}
+
+/* Selected outputs, by flat row-major index into [M, N]. */
+int oracle_gemm_at(int dtype, const void *A, int64_t a_rows, int64_t a_cols, int trans_a, const void *B,
+                   int64_t b_rows, int64_t b_cols, int trans_b, const void *C, const int64_t *c_shape, int c_rank,
+                   double alpha, double beta, const int64_t *flat_idx, int64_t count, double *out)
+{
+    return gemm_impl(dtype, A, a_rows, a_cols, trans_a, B, b_rows, b_cols, trans_b, C, c_shape, c_rank, alpha,
+                     beta, flat_idx, count, out);
+}
+
 /* Number of OpenMP threads the loops above use (for reporting). */
 int oracle_threads(void)
 {

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.compare import abs_max, check
+from oracle.compare import abs_max, check, gemm_tolerance
 from onnx_broadcast_matmul_amd import binding as mm
 from onnx_broadcast_matmul_amd import synth
 
@@ -306,6 +306,107 @@ def test_constant_b_tail_split(dev):
     Ye = run_plan(plan, a, b, dt, dev)
     torch.cuda.synchronize()
     assert np.array_equal(synth.from_torch(Yc), synth.from_torch(Ye))
+
+
+# ------------------------------------------------------------ Gemm
+
+GEMM_DTYPES = [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16]
+GEMM_TRANS = [(0, 0), (1, 0), (0, 1), (1, 1)]
+GEMM_LAYOUTS = [None, (), ("N",), ("M", 1), ("M", "N")]
+
+
+def _cs(layout, M, N):
+    return None if layout is None else tuple(M if d == "M" else N if d == "N" else d for d in layout)
+
+
+def gemm_parity(M, N, K, dt, ta, tb, layout, dev, algo=0, alpha=0.75, beta=-1.5, dist=U1, seed=0, exact=False,
+                offset=0):
+    sa = (K, M) if ta else (M, K)
+    sb = (N, K) if tb else (K, N)
+    cs = _cs(layout, M, N)
+    a = synth.generate(sa, dt, dist, [seed, 0])
+    b = synth.generate(sb, dt, dist, [seed, 1])
+    c = None if cs is None else synth.generate(cs, dt, dist, [seed, 2])
+    plan = mm.GemmPlan(sa, sb, dt, ta, tb, cs, alpha, beta, force_algo=algo)
+    if algo:
+        assert plan.algo == algo
+
+    def dev_tensor(x, shape):
+        # `offset` elements past the allocation start: unaligned operands
+        t = torch.empty(int(np.prod(shape)) + offset, dtype=mm.torch_dtype(dt), device=dev)[offset:].view(shape)
+        t.copy_(synth.as_torch(x, dt).reshape(shape).to(dev))
+        return t
+
+    A, B = dev_tensor(a, sa), dev_tensor(b, sb)
+    C = None if c is None else dev_tensor(c, cs)
+    Y = torch.full((M * N + offset,), float("nan"), dtype=mm.torch_dtype(dt), device=dev)[offset:].view(M, N)
+    plan.execute(A, B, Y, C)
+    torch.cuda.synchronize()
+    o = oracle.gemm(a, b, dt, bool(ta), bool(tb), c, alpha, beta)
+    cmax = 0.0 if c is None else abs_max(c, dt)
+    tol = gemm_tolerance(K, abs_max(a, dt), abs_max(b, dt), cmax, alpha, beta)
+    rep = check(synth.from_torch(Y), o, dt, K, abs_max(a, dt), abs_max(b, dt), exact=exact, tol=tol)
+    assert rep.ok, f"Gemm {sa} {sb} ta={ta} tb={tb} C={cs} {DT_IDS[dt]} {mm.ALGO_NAMES[plan.algo]}: {rep}"
+    return plan
+
+
+@pytest.mark.parametrize("dt", GEMM_DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("ta,tb", GEMM_TRANS, ids=lambda t: f"t{t}")
+@pytest.mark.parametrize("algo", [mm.ALGO_DIRECT, mm.ALGO_SPLIT_K, mm.ALGO_GENERAL], ids=lambda a: mm.ALGO_NAMES[a])
+def test_gemm(dt, ta, tb, algo, dev):
+    """Gemm with every transpose combination, every C layout (none, scalar,
+    per column, per row, full) and each algorithm, on ragged sizes."""
+    for i, layout in enumerate(GEMM_LAYOUTS):
+        gemm_parity(300, 200, 520, dt, ta, tb, layout, dev, algo=algo, seed=60 + i)
+
+
+@pytest.mark.parametrize("dt", GEMM_DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("ta,tb", GEMM_TRANS, ids=lambda t: f"t{t}")
+def test_gemm_exact_unaligned_and_zero_k(dt, ta, tb, dev):
+    """Small-integer inputs with integer alpha / beta are bit-exact; operands
+    one element off 16-byte alignment take the element-wise kernel; K == 0
+    gives beta * C without reading A or B."""
+    gemm_parity(130, 70, 1000, dt, ta, tb, ("M", "N"), dev, algo=mm.ALGO_GENERAL, alpha=2.0, beta=-3.0,
+                dist=("int",), exact=True, seed=70)
+    gemm_parity(130, 70, 1000, dt, ta, tb, ("N",), dev, algo=mm.ALGO_SPLIT_K, alpha=2.0, beta=-3.0,
+                dist=("int",), exact=True, seed=71)
+    gemm_parity(96, 64, 256, dt, ta, tb, ("M", 1), dev, algo=mm.ALGO_GENERAL, seed=72, offset=1)
+    M, N = 33, 17
+    sa, sb, cs = ((0, M) if ta else (M, 0)), ((N, 0) if tb else (0, N)), (M, 1)
+    a0 = synth.generate(sa, dt, U1, [73, 0])
+    b0 = synth.generate(sb, dt, U1, [73, 1])
+    c = synth.generate(cs, dt, U1, [73, 2])
+    plan = mm.GemmPlan(sa, sb, dt, ta, tb, cs, 0.5, -2.0)
+    assert plan.algo == mm.ALGO_DIRECT
+    Y = _sentinel((M, N), dt, dev)
+    Cd = synth.as_torch(c, dt).to(dev)
+    plan.execute_ptr(0, 0, Y.data_ptr(), torch.cuda.current_stream().cuda_stream, Cd.data_ptr())
+    torch.cuda.synchronize()
+    o = oracle.gemm(a0, b0, dt, bool(ta), bool(tb), c, 0.5, -2.0)
+    rep = check(synth.from_torch(Y), o, dt, 0, 0.0, 0.0, tol=gemm_tolerance(0, 0.0, 0.0, abs_max(c, dt), 0.5, -2.0))
+    assert rep.ok, str(rep)
+
+
+def test_gemm_linear_layer_full_size(dev):
+    """The transformer projection as a linear layer: Y = X W^T + b with
+    X [8192, 4096], W [11008, 4096] (stored [N, K]) and a per-column bias, in
+    BF16, checked on sampled outputs."""
+    dt = mm.BFLOAT16
+    M, N, K = 8192, 11008, 4096
+    x = synth.generate((M, K), dt, ("normal", 0.02), [80, 0])
+    w = synth.generate((N, K), dt, ("normal", 0.02), [80, 1])
+    bias = synth.generate((N,), dt, ("normal", 0.02), [80, 2])
+    plan = mm.GemmPlan((M, K), (N, K), dt, False, True, (N,), 1.0, 1.0)
+    print(f"\n[full-size] Gemm linear layer {mm.ALGO_NAMES[plan.algo]} tile {plan.info()['tile']}", flush=True)
+    Y = _sentinel((M, N), dt, dev)
+    plan.execute(synth.as_torch(x, dt).to(dev), synth.as_torch(w, dt).to(dev), Y, synth.as_torch(bias, dt).to(dev))
+    torch.cuda.synchronize()
+    assert torch.isfinite(Y.float()).all().item()
+    idx = _sample_indices((M, N), 3000, np.random.default_rng(81))
+    o = oracle.gemm_at(x, w, dt, idx, False, True, bias, 1.0, 1.0)
+    tol = gemm_tolerance(K, abs_max(x, dt), abs_max(w, dt), abs_max(bias, dt), 1.0, 1.0)
+    rep = check(synth.from_torch(Y).reshape(-1)[idx], o, dt, K, abs_max(x, dt), abs_max(w, dt), tol=tol)
+    assert rep.ok, str(rep)
 
 
 # ------------------------------------------------------------ full-size workloads

@@ -335,3 +335,55 @@ def test_constant_b_errors_before_any_gpu_call():
     assert L.mm_plan_has_constant_b(None) == 0
     assert L.mm_execute_constant_b(None, None, None, None) == mm.ERR_NULL_ARG
     assert not p.has_constant_b
+
+
+# ---------------------------------------------------------------- Gemm
+
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_gemm_plan_shapes(ta, tb):
+    M, N, K = 300, 200, 520
+    sa = (K, M) if ta else (M, K)
+    sb = (N, K) if tb else (K, N)
+    p = mm.GemmPlan(sa, sb, mm.BFLOAT16, trans_a=ta, trans_b=tb, c_shape=(N,), alpha=0.5, beta=2.0)
+    assert p.output_shape == (M, N) and p.output_numel == M * N
+    inf = p.info()
+    assert (inf["M"], inf["N"], inf["K"]) == (M, N, K) and inf["algo"] == mm.ALGO_GENERAL
+    if ta or tb:  # transposed operands: only the tiles instantiated for them
+        assert inf["tile"] - 1 in (0, 5, 4)
+    assert inf["tail_col"] == 0
+    # skinny shapes of a Gemm take the tiled kernel
+    assert mm.GemmPlan((1, 4096), (4096, 4096), mm.FLOAT16).algo == mm.ALGO_GENERAL
+    assert mm.GemmPlan((4096, 64), (64, 0), mm.FLOAT16).algo == mm.ALGO_EMPTY
+    assert mm.GemmPlan((64, 0), (0, 32), mm.FLOAT16, c_shape=(1,)).algo == mm.ALGO_DIRECT  # Y = beta * C
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sa=(4, 3), sb=(4, 5)), mm.ERR_K_MISMATCH),
+    (dict(sa=(4, 3), sb=(3, 5), c_shape=(4, 2)), mm.ERR_BROADCAST),
+    (dict(sa=(4, 3), sb=(3, 5), c_shape=(4,)), mm.ERR_BROADCAST),
+    (dict(sa=(4, 3), sb=(3, 5), c_shape=(5, 4)), mm.ERR_BROADCAST),
+    (dict(sa=(4, -3), sb=(3, 5)), mm.ERR_NEG_DIM),
+    (dict(sa=(4, 3), sb=(3, 5), c_shape=(-1,)), mm.ERR_NEG_DIM),
+    (dict(sa=(4, 3), sb=(3, 5), dtype=mm.DOUBLE), mm.ERR_DTYPE),
+    (dict(sa=(64, 64), sb=(64, 8), force_algo=mm.ALGO_SKINNY_N), mm.ERR_BAD_OPTION),
+    (dict(sa=(64, 64), sb=(64, 64), trans_a=1, force_algo=mm.ALGO_GENERAL, tile=2), mm.ERR_BAD_OPTION),
+])
+def test_gemm_plan_errors(kw, status):
+    kw = dict(kw)
+    sa, sb = kw.pop("sa"), kw.pop("sb")
+    dt = kw.pop("dtype", mm.FLOAT16)
+    with pytest.raises(mm.MMError) as e:
+        mm.GemmPlan(sa, sb, dt, **kw)
+    assert e.value.status == status
+
+
+def test_gemm_execute_checks_before_any_gpu_call():
+    """A Gemm plan is refused by mm_execute and a MatMul plan by
+    mm_gemm_execute; a plan with C refuses a NULL C."""
+    L = mm.lib()
+    g = mm.GemmPlan((64, 32), (32, 16), mm.FLOAT, c_shape=(1, 16))
+    m = mm.Plan((64, 32), (32, 16), mm.FLOAT)
+    fake = ctypes.c_void_p(1 << 40)
+    assert L.mm_execute(g.handle, fake, fake, fake, None) == mm.ERR_BAD_OPTION
+    assert L.mm_gemm_execute(m.handle, fake, fake, None, fake, None) == mm.ERR_BAD_OPTION
+    assert L.mm_gemm_execute(g.handle, fake, fake, None, fake, None) == mm.ERR_NULL_ARG
