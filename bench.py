@@ -114,6 +114,39 @@ class Case:
         self.plan.execute_ptr(a, b, y, stream)
 
 
+class GemmCase:
+    """One Gemm product on the device, with rotated buffer copies."""
+
+    def __init__(self, product: synth.GemmProduct, dev):
+        import torch
+
+        self.p = product
+        self.dt = product.dtype
+        self.plan = mm.GemmPlan(product.a_shape, product.b_shape, self.dt, product.trans_a, product.trans_b,
+                                product.c_shape, product.alpha, product.beta)
+        self.info = self.plan.info()
+        a, b, c = product.make()
+        A = synth.as_torch(a, self.dt).to(dev)
+        B = synth.as_torch(b, self.dt).to(dev)
+        C = synth.as_torch(c, self.dt).to(dev)
+        es = synth.ELEM_SIZE[self.dt]
+        self.bytes = float(es * (a.size + b.size + c.size + product.M * product.N))
+        self.flops = 2.0 * product.M * product.N * product.K
+        del a, b, c
+        self.copies = int(min(MAX_COPIES, max(1, math.ceil(ROTATE_BYTES / self.bytes))))
+        self.A = [A] + [A.clone() for _ in range(self.copies - 1)]
+        self.B = [B] + [B.clone() for _ in range(self.copies - 1)]
+        self.C = [C] + [C.clone() for _ in range(self.copies - 1)]
+        self.Y = [torch.empty((product.M, product.N), dtype=mm.torch_dtype(self.dt), device=dev)
+                  for _ in range(self.copies)]
+        self.bound = "hbm" if self.flops / self.bytes < MFMA_PEAK_TFLOPS[self.dt] * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+
+    def run(self, i: int, stream: int) -> None:
+        k = i % self.copies
+        self.plan.execute_ptr(self.A[k].data_ptr(), self.B[k].data_ptr(), self.Y[k].data_ptr(), stream,
+                              self.C[k].data_ptr())
+
+
 def _capture(cases, count: int, offset: int):
     """A HIP graph holding `count` steps (each step: every case once)."""
     import torch
@@ -293,11 +326,11 @@ def main():
         return
     if args.only:
         names = args.only.split(",")
-        prods = [p for p in synth.all_products() if p.name in names]
+        prods = [p for p in synth.all_products() + synth.GEMM_PRODUCTS if p.name in names]
         if len(prods) != len(names):
             sys.exit(f"unknown product in {args.only}")
         for p in prods:
-            c = Case(p, dev)
+            c = GemmCase(p, dev) if isinstance(p, synth.GemmProduct) else Case(p, dev)
             _, per = time_cases([c], args.steps, args.warmup)
             print(json.dumps({"only": p.name, "case": case_report(c, per[0])}), flush=True)
             del c
@@ -350,6 +383,16 @@ def main():
             _, per_c = time_cases([c], steps, max(3, args.warmup // 2))
             table[p.name] = case_report(c, per_c[0])
             log(f"[bench]   {table[p.name]}")
+            del c
+            torch.cuda.empty_cache()
+        for gp in synth.GEMM_PRODUCTS:
+            log(f"[bench] gemm case {gp.name}")
+            c = GemmCase(gp, dev)
+            steps = max(10, args.steps // 2)
+            _, per_c = time_cases([c], steps, max(3, args.warmup // 2))
+            table[gp.name] = case_report(c, per_c[0])
+            table[gp.name]["op"] = f"Gemm transA={int(gp.trans_a)} transB={int(gp.trans_b)} C={list(gp.c_shape)}"
+            log(f"[bench]   {table[gp.name]}")
             del c
             torch.cuda.empty_cache()
         out["cases"] = table

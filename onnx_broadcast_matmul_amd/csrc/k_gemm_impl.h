@@ -624,6 +624,39 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         }
     }
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    // Gemm bias values this lane needs, loaded once: per column (the lane's
+    // four columns of each (j, q) group), per row (one per row block i), or
+    // a single scalar.  A full C is read in the loop below.
+    constexpr bool EPI = !SPLIT;
+    float bias_col[EPI ? FN : 1][4][4];
+    float bias_row[EPI ? FM : 1];
+    float bias_one = 0.0f;
+    int cmode = kBiasNone;
+    if constexpr (EPI) {
+        if (a.gemm_epi) {
+            cmode = a.c_mode;
+            const S *Cp = (const S *)a.C;
+            if (cmode == kBiasScalar) bias_one = E::to_f32(Cp[0]);
+            if (cmode == kBiasRow) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int64_t gn = n0 + wc * WN + j * 32 + 8 * q + 4 * (lane >> 5) + e;
+                            bias_col[j][q][e] = gn < N ? E::to_f32(Cp[gn]) : 0.0f;
+                        }
+            }
+            if (cmode == kBiasCol) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int64_t gm = m0 + wr * WM + i * 32 + (lane & 31);
+                    bias_row[i] = gm < M ? E::to_f32(Cp[gm]) : 0.0f;
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -641,11 +674,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
                         char *dst = trow + ch * 16 + (cl % OV) * OS;
                         const f32x16 &v = acc[i][j];
                         float w[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-                        if constexpr (!SPLIT) {
+                        if constexpr (EPI) {
                             if (a.gemm_epi) {
-                                const int64_t gm = m0 + wr * WM + i * 32 + (lane & 31);
+                                if (cmode == kBiasFull) {
+                                    const int64_t gm = m0 + wr * WM + i * 32 + (lane & 31);
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) w[e] = gemm_epilogue<E>(a, w[e], gm, n0 + cl + e);
+                                    for (int e = 0; e < 4; ++e) w[e] = gemm_epilogue<E>(a, w[e], gm, n0 + cl + e);
+                                } else {
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) {
+                                        const float c = cmode == kBiasRow ? bias_col[j][q][e]
+                                                        : cmode == kBiasCol ? bias_row[i]
+                                                                            : bias_one;
+                                        w[e] = cmode == kBiasNone ? a.alpha * w[e] : a.alpha * w[e] + a.beta * c;
+                                    }
+                                }
                             }
                         }
                         if constexpr (OS == 4) {

@@ -171,5 +171,46 @@ def _workloads() -> dict:
 WORKLOADS = _workloads()
 
 
+@dataclass
+class GemmProduct:
+    """One ONNX Gemm: Y = alpha * A'B' + beta * C with A' = A or A^T
+    (stored [K, M]), B' = B or B^T (stored [N, K]) and C of ``c_shape``."""
+
+    name: str
+    M: int
+    N: int
+    K: int
+    trans_a: bool
+    trans_b: bool
+    c_shape: Tuple[int, ...]
+    alpha: float
+    beta: float
+    dtype: int
+    dist: Tuple
+    seed: int
+
+    @property
+    def a_shape(self) -> Tuple[int, ...]:
+        return (self.K, self.M) if self.trans_a else (self.M, self.K)
+
+    @property
+    def b_shape(self) -> Tuple[int, ...]:
+        return (self.N, self.K) if self.trans_b else (self.K, self.N)
+
+    def make(self):
+        a = generate(self.a_shape, self.dtype, self.dist, [self.seed, 0, 0])
+        b = generate(self.b_shape, self.dtype, self.dist, [self.seed, 0, 1])
+        c = None if self.c_shape is None else generate(self.c_shape, self.dtype, self.dist, [self.seed, 0, 2])
+        return a, b, c
+
+
+# Gemm: the transformer projection as a linear layer, X W^T + bias, with the
+# weight stored [N, K] as such layers keep it.
+GEMM_PRODUCTS = [
+    GemmProduct("bf16_linear_8192x4096_by_11008x4096T_bias", 8192, 11008, 4096, False, True, (11008,), 1.0, 1.0,
+                BFLOAT16, ("normal", 0.02), 7),
+]
+
+
 def all_products() -> List[Product]:
     return [p for w in WORKLOADS.values() for p in w.products]
