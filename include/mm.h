@@ -214,8 +214,7 @@ typedef struct mm_gemm_desc {
  * resolved once; errors as for mm_plan_create, plus MM_ERR_BROADCAST for a
  * C that does not broadcast to [M, N] and MM_ERR_BAD_OPTION for an invalid
  * descriptor or an option the Gemm path does not run: forced SKINNY_M /
- * SKINNY_N, or a tile outside the transposed-operand subset when an operand
- * is transposed).  `opt` may be NULL.  The plan answers the introspection
+ * SKINNY_N, or a tile outside the Gemm subset of the tile table).  `opt` may be NULL.  The plan answers the introspection
  * calls above (output shape [M, N]). */
 mm_status mm_gemm_plan_create(const mm_gemm_desc *desc, int dtype, const mm_plan_options *opt, mm_plan_t *out);
 

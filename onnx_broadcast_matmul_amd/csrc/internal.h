@@ -87,7 +87,8 @@ const TileCfg *tile_entry(int dtype, int index);
 hipError_t launch_direct(int dtype, const KArgs &a, hipStream_t s);
 hipError_t launch_fill_zero(int dtype, void *Y, int64_t n, hipStream_t s);
 hipError_t launch_general(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);
-// The same for transposed operands (a.ta / a.tb); only the kTransTiles entries.
+// The same for Gemm plans (epilogue, transposed operands); only the
+// kTransTiles entries.
 hipError_t launch_general_t(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);
 hipError_t launch_splitk_reduce(int dtype, const KArgs &a, hipStream_t s);
 hipError_t launch_skinny_m(int dtype, const Align &al, const KArgs &a, hipStream_t s);

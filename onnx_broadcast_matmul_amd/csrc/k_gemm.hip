@@ -43,7 +43,7 @@ static hipError_t launch_32(int tile, bool vec, bool split, const KArgs &a, hipS
 static_assert(kNumTiles16 == 10 && kNumTiles32 == 7, "launch switch must cover the tile table");
 
 hipError_t launch_general(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s) {
-    if (a.ta || a.tb) return launch_general_t(dtype, tile, al, split, a, s);
+    if (a.gemm_epi || a.ta || a.tb) return launch_general_t(dtype, tile, al, split, a, s);
     const bool vec = al.a && al.b;
     switch (dtype) {
     case MM_FLOAT: return launch_32(tile, vec, split, a, s);

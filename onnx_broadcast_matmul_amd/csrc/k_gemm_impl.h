@@ -293,7 +293,8 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
 //   per-stage barrier.
 // ---------------------------------------------------------------------------
 
-template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool SPLIT, bool TA, bool TB>
+template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool SPLIT, bool TA, bool TB,
+          bool GEMM>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using E = Elem<DT>;
@@ -627,7 +628,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     // Gemm bias values this lane needs, loaded once: per column (the lane's
     // four columns of each (j, q) group), per row (one per row block i), or
     // a single scalar.  A full C is read in the loop below.
-    constexpr bool EPI = !SPLIT;
+    // Only the Gemm instantiations carry the epilogue's registers and code.
+    constexpr bool EPI = GEMM && !SPLIT;
     float bias_col[EPI ? FN : 1][4][4];
     float bias_row[EPI ? FM : 1];
     float bias_one = 0.0f;
@@ -723,7 +725,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 #endif
 }
 
-template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool TA = false, bool TB = false>
+template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool TA = false, bool TB = false,
+          bool GEMM = false>
 static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t s) {
     const int64_t tiles = a.batch * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * (split ? a.split : 1);
     if (tiles <= 0) return hipSuccess;
@@ -737,8 +740,9 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
     const bool fits = a_span * ES < 0x7fff0000LL && b_span * ES < 0x7fff0000LL;
     if (vec && fits) {
         const dim3 blk(64 * WGM * WGN * KG);
-        if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB>), g, blk, 0, s, a);
+        // Split-K partials take no epilogue (the reduction applies it).
+        if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB, false>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, GEMM>), g, blk, 0, s, a);
     } else {
         // The register-staged kernel needs at least 64 x 64 (2 x 2 waves of
         // 32 x 32): narrower entries fall back to 64-wide tiles on their own grid.

@@ -1,8 +1,8 @@
-// k_gemm_t.hip -- launch switch of the tiled GEMM for transposed operands
-// (Gemm's transA / transB): the same kernels as k_gemm.hip, instantiated
-// with A staged from its [K][M] layout and/or B from its [N][K] layout, for
-// the tile subset kTransTiles16 / kTransTiles32.  A separate translation
-// unit so the two sets of instantiations compile in parallel.
+// k_gemm_t.hip -- launch switch of the tiled GEMM for Gemm plans: the same
+// kernels as k_gemm.hip, instantiated with the alpha / beta / C epilogue and
+// with A staged from its [K][M] layout and/or B from its [N][K] layout when
+// transposed, for the tile subset kTransTiles16 / kTransTiles32.  A separate
+// translation unit so the two sets of instantiations compile in parallel.
 #include "k_gemm_impl.h"
 
 namespace mm {
@@ -11,10 +11,12 @@ template <int DT, const TileCfg *T, int IDX>
 static hipError_t launch_t_tile(bool vec, bool split, const KArgs &a, hipStream_t s) {
     constexpr TileCfg c = T[IDX];
     if (a.ta && a.tb)
-        return launch_tile<DT, c.bm, c.bn, c.wgm, c.wgn, c.bkb, c.stages, c.producers, c.kgroups, true, true>(vec, split, a, s);
+        return launch_tile<DT, c.bm, c.bn, c.wgm, c.wgn, c.bkb, c.stages, c.producers, c.kgroups, true, true, true>(vec, split, a, s);
     if (a.ta)
-        return launch_tile<DT, c.bm, c.bn, c.wgm, c.wgn, c.bkb, c.stages, c.producers, c.kgroups, true, false>(vec, split, a, s);
-    return launch_tile<DT, c.bm, c.bn, c.wgm, c.wgn, c.bkb, c.stages, c.producers, c.kgroups, false, true>(vec, split, a, s);
+        return launch_tile<DT, c.bm, c.bn, c.wgm, c.wgn, c.bkb, c.stages, c.producers, c.kgroups, true, false, true>(vec, split, a, s);
+    if (a.tb)
+        return launch_tile<DT, c.bm, c.bn, c.wgm, c.wgn, c.bkb, c.stages, c.producers, c.kgroups, false, true, true>(vec, split, a, s);
+    return launch_tile<DT, c.bm, c.bn, c.wgm, c.wgn, c.bkb, c.stages, c.producers, c.kgroups, false, false, true>(vec, split, a, s);
 }
 
 static_assert(sizeof(kTransTiles16) / sizeof(int) == 3 && kTransTiles16[0] == 0 && kTransTiles16[1] == 5 &&

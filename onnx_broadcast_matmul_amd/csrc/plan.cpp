@@ -77,10 +77,10 @@ static double tile_score(int dtype, int index, int64_t batch, int64_t M, int64_t
     return occ * pad * tile_quality(dtype, index);
 }
 
-// Tile entries a plan may use: every entry, except that transposed operands
-// (Gemm) have kernels only for the kTransTiles subset.
-static bool tile_allowed(int dtype, int index, bool transposed) {
-    if (!transposed) return true;
+// Tile entries a plan may use: every entry, except that Gemm plans have
+// kernels only for the kTransTiles subset.
+static bool tile_allowed(int dtype, int index, bool gemm) {
+    if (!gemm) return true;
     if (dtype == MM_FLOAT) {
         for (int t : kTransTiles32)
             if (t == index) return true;
@@ -91,11 +91,11 @@ static bool tile_allowed(int dtype, int index, bool transposed) {
     return false;
 }
 
-static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, bool transposed = false) {
+static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, bool gemm = false) {
     int best = -1;
     double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
-        if (!tile_allowed(dtype, i, transposed)) continue;
+        if (!tile_allowed(dtype, i, gemm)) continue;
         double s = tile_score(dtype, i, batch, M, N);
         if (s > best_s + 1e-9) {
             best_s = s;
@@ -157,11 +157,11 @@ static void plan_tail(mm_plan_s *p) {
 }
 
 // Smallest-padding tile for split-K (its output is tiny by construction).
-static int choose_split_tile(int dtype, int64_t M, int64_t N, bool transposed = false) {
+static int choose_split_tile(int dtype, int64_t M, int64_t N, bool gemm = false) {
     int best = -1;
     double best_pad = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
-        if (!tile_allowed(dtype, i, transposed)) continue;
+        if (!tile_allowed(dtype, i, gemm)) continue;
         const TileCfg *t = tile_entry(dtype, i);
         double pad = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
         if (pad > best_pad + 1e-9) {
@@ -374,15 +374,14 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         int req = opt ? opt->tile : 0;
         if (req < 0 || req > tile_count(p->dtype))
             return fail(MM_ERR_BAD_OPTION, "tile %d out of range 0..%d", req, tile_count(p->dtype));
-        const bool transposed = p->ta || p->tb;
         if (req > 0) {
             p->tile = req - 1;
-            if (!tile_allowed(p->dtype, p->tile, transposed))
-                return fail(MM_ERR_BAD_OPTION, "tile %d has no kernel for transposed operands", req);
+            if (!tile_allowed(p->dtype, p->tile, p->is_gemm))
+                return fail(MM_ERR_BAD_OPTION, "tile %d has no Gemm kernel", req);
         } else if (algo == MM_ALGO_GENERAL) {
-            p->tile = choose_tile(p->dtype, p->batch, M, N, transposed);
+            p->tile = choose_tile(p->dtype, p->batch, M, N, p->is_gemm);
         } else {
-            p->tile = choose_split_tile(p->dtype, M, N, transposed);
+            p->tile = choose_split_tile(p->dtype, M, N, p->is_gemm);
         }
         if (algo == MM_ALGO_GENERAL && req == 0) plan_tail(p);
         const TileCfg *t = tile_entry(p->dtype, p->tile);

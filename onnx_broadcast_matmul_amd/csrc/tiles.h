@@ -48,7 +48,7 @@ constexpr TileCfg kTiles64[] = {
     {64, 64, 2, 2, 128, 2, 4, 1},
 };
 
-// Entries instantiated for transposed operands (Gemm's transA / transB).
+// Entries instantiated for Gemm (its epilogue and transA / transB).
 constexpr int kTransTiles16[] = {0, 5, 4};
 constexpr int kTransTiles32[] = {4, 2};
 
