@@ -1,11 +1,11 @@
-"""CPU oracle for ONNX MatMul -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for ONNX MatMul, Gemm and MatMulInteger -- TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never calls it and
 shares no code with it.
 
 The arithmetic lives in ``oracle.c`` (plain C, fp64 accumulation over an
-explicit broadcast index walk); this module only builds it with gcc and
+explicit broadcast index walk; exact int64 sums for MatMulInteger); this module only builds it with gcc and
 marshals numpy arrays through ctypes.  ``compare.py`` holds the comparator
 that applies the parity tolerances.
 """
@@ -32,7 +32,7 @@ STATUS = {
     4: "batch dimensions not broadcastable",
     5: "unknown dtype",
     6: "allocation failed",
-    7: "Gemm operand shapes do not fit",
+    7: "Gemm operand shapes or zero-point kinds do not fit",
 }
 
 
@@ -90,6 +90,10 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                      ctypes.c_void_p, i64p, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        int_args = [ctypes.c_void_p, i64p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, i64p, ctypes.c_int,
+                    ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+        L.oracle_matmul_integer.argtypes = int_args + [ctypes.c_void_p]
+        L.oracle_matmul_integer_at.argtypes = int_args + [i64p, ctypes.c_int64, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -214,6 +218,63 @@ def gemm_at(a: np.ndarray, b: np.ndarray, dtype: int, flat_idx, trans_a: bool = 
     if st:
         raise OracleError(st)
     return out
+
+
+def _int_operand(x: np.ndarray):
+    x = np.ascontiguousarray(x)
+    if x.dtype not in (np.uint8, np.int8):
+        raise TypeError(f"MatMulInteger operands are uint8 / int8, got {x.dtype}")
+    return x, int(x.dtype == np.int8)
+
+
+def _int_zero_point(zp, operand_dtype):
+    """(pointer, kind, keep-alive array): kind 0 none, 1 scalar (0-d), 2
+    vector (1-d)."""
+    if zp is None:
+        return None, 0, None
+    zp = np.array(zp, dtype=operand_dtype, copy=True)  # keeps a 0-d value 0-d
+    kind = 1 if zp.ndim == 0 else 2
+    return zp.ctypes.data, kind, zp
+
+
+def _int_call(a, b, za, zb, flat_idx):
+    a, a_signed = _int_operand(a)
+    b, b_signed = _int_operand(b)
+    pza, kza, za = _int_zero_point(za, a.dtype)
+    pzb, kzb, zb = _int_zero_point(zb, b.dtype)
+    if kza == 2 and za.size != (1 if a.ndim == 1 else a.shape[-2]):
+        raise ValueError("A zero-point vector must have one entry per row")
+    if kzb == 2 and zb.size != (1 if b.ndim == 1 else b.shape[-1]):
+        raise ValueError("B zero-point vector must have one entry per column")
+    args = [a.ctypes.data, _shape_arr(a.shape), a.ndim, a_signed, b.ctypes.data, _shape_arr(b.shape), b.ndim,
+            b_signed, pza, kza, pzb, kzb]
+    if flat_idx is None:
+        shape = output_shape(a.shape, b.shape)
+        y = np.empty(int(np.prod(shape, dtype=np.int64)), dtype=np.int32)
+        st = lib().oracle_matmul_integer(*args, y.ctypes.data)
+        if st:
+            raise OracleError(st)
+        return y.reshape(shape)
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    out = np.empty(idx.size, dtype=np.int32)
+    st = lib().oracle_matmul_integer_at(*args, idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), idx.size,
+                                        out.ctypes.data)
+    if st:
+        raise OracleError(st)
+    return out
+
+
+def matmul_integer(a: np.ndarray, b: np.ndarray, a_zero_point=None, b_zero_point=None) -> np.ndarray:
+    """ONNX MatMulInteger of uint8 / int8 arrays: the exact sum of
+    (a - za)(b - zb) reduced modulo 2^32, as int32 of the output shape.  A
+    zero point is None, a 0-d value, or a 1-d vector (A: one per row, B: one
+    per column)."""
+    return _int_call(a, b, a_zero_point, b_zero_point, None)
+
+
+def matmul_integer_at(a, b, flat_idx, a_zero_point=None, b_zero_point=None) -> np.ndarray:
+    """Selected MatMulInteger outputs (flat row-major indices) as int32."""
+    return _int_call(a, b, a_zero_point, b_zero_point, flat_idx)
 
 
 def threads() -> int:

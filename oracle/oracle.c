@@ -31,6 +31,9 @@
  * 16-bit types.  The rounding mode itself is a reading (nearest-even), since
  * the pages do not name it.
  *
+ * MatMulInteger (exact integer sums reduced modulo 2^32) sits at the end of
+ * the file.
+ *
  * Parity pins: see tests/test_oracle.py (shape rules against numpy.matmul,
  * closed forms, identity and permutation products, small-integer exactness,
  * broadcast equals explicit repetition, narrowing against numpy float16 and a
@@ -467,6 +470,94 @@ int oracle_gemm_at(int dtype, const void *A, int64_t a_rows, int64_t a_cols, int
 {
     return gemm_impl(dtype, A, a_rows, a_cols, trans_a, B, b_rows, b_cols, trans_b, C, c_shape, c_rank, alpha,
                      beta, flat_idx, count, out);
+}
+
+/* ------------------------------------------------------------------------ */
+/* MatMulInteger (page "Gemm and MatMul Performance Roadmap", section        */
+/* "Remaining pull-request sequence", Roadmap PR09.1: INT8 or UINT8 A and B, */
+/* optional zero points -- one value, or one per row of A / per column of   */
+/* B --, the MatMul broadcasting and rank-one rules, INT32 accumulation     */
+/* modulo 2^32):                                                             */
+/*   Y[i][m][n] = sum_k (A[iA(i)][m][k] - za(m)) * (B[iB(i)][k][n] - zb(n))  */
+/* Each product is formed exactly in int64 and summed exactly in int64      */
+/* (|term| <= 255^2, so no overflow below K = 2^47); the sum is then reduced */
+/* modulo 2^32 to the INT32 two's-complement value.  Reading: a vector zero  */
+/* point has M (A) or N (B) entries and is shared by every batch.           */
+/* ------------------------------------------------------------------------ */
+
+#define OR_ZP_NONE 0
+#define OR_ZP_SCALAR 1
+#define OR_ZP_VECTOR 2
+
+static int64_t load_byte(const void *base, int is_signed, int64_t idx)
+{
+    return is_signed ? (int64_t)((const int8_t *)base)[idx] : (int64_t)((const uint8_t *)base)[idx];
+}
+
+static int64_t zero_point(const void *zp, int kind, int is_signed, int64_t i)
+{
+    if (kind == OR_ZP_NONE) return 0;
+    return load_byte(zp, is_signed, kind == OR_ZP_SCALAR ? 0 : i);
+}
+
+/* Exact sum reduced modulo 2^32, as the INT32 two's-complement value. */
+static int32_t wrap32(int64_t v)
+{
+    uint32_t u = (uint32_t)((uint64_t)v & 0xffffffffu);
+    return u >= 0x80000000u ? (int32_t)((int64_t)u - 4294967296LL) : (int32_t)u;
+}
+
+static int integer_impl(const void *A, const int64_t *a_shape, int a_rank, int a_signed, const void *B,
+                        const int64_t *b_shape, int b_rank, int b_signed, const void *za, int za_kind,
+                        const void *zb, int zb_kind, const int64_t *flat_idx, int64_t n_idx, int32_t *Y)
+{
+    if (za_kind < OR_ZP_NONE || za_kind > OR_ZP_VECTOR || zb_kind < OR_ZP_NONE || zb_kind > OR_ZP_VECTOR)
+        return OR_ERR_SHAPE;
+    if ((za_kind != OR_ZP_NONE && !za) || (zb_kind != OR_ZP_NONE && !zb)) return OR_ERR_SHAPE;
+    shapes_t s;
+    int st = resolve(a_shape, a_rank, b_shape, b_rank, &s);
+    if (st != OR_OK) return st;
+    const int64_t total = s.nbatch * s.M * s.N;
+    const int64_t count = flat_idx ? n_idx : total;
+    if (flat_idx && count > 0 && total == 0) {
+        shapes_free(&s);
+        return OR_ERR_BROADCAST;
+    }
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t f = flat_idx ? flat_idx[i] : i;
+        const int64_t n = f % s.N;
+        const int64_t m = (f / s.N) % s.M;
+        const int64_t bi = f / (s.N * s.M);
+        int64_t offa, offb;
+        batch_offsets(&s, bi, &offa, &offb);
+        const int64_t a0 = zero_point(za, za_kind, a_signed, m);
+        const int64_t b0 = zero_point(zb, zb_kind, b_signed, n);
+        int64_t acc = 0;
+        for (int64_t k = 0; k < s.K; ++k)
+            acc += (load_byte(A, a_signed, offa + m * s.K + k) - a0) * (load_byte(B, b_signed, offb + k * s.N + n) - b0);
+        Y[i] = wrap32(acc);
+    }
+    shapes_free(&s);
+    return OR_OK;
+}
+
+/* Full MatMulInteger: Y receives nbatch*M*N INT32 values in row-major order. */
+int oracle_matmul_integer(const void *A, const int64_t *a_shape, int a_rank, int a_signed, const void *B,
+                          const int64_t *b_shape, int b_rank, int b_signed, const void *za, int za_kind,
+                          const void *zb, int zb_kind, int32_t *Y)
+{
+    return integer_impl(A, a_shape, a_rank, a_signed, B, b_shape, b_rank, b_signed, za, za_kind, zb, zb_kind, 0, 0,
+                        Y);
+}
+
+/* Selected MatMulInteger outputs, by flat row-major index into the output. */
+int oracle_matmul_integer_at(const void *A, const int64_t *a_shape, int a_rank, int a_signed, const void *B,
+                             const int64_t *b_shape, int b_rank, int b_signed, const void *za, int za_kind,
+                             const void *zb, int zb_kind, const int64_t *flat_idx, int64_t count, int32_t *out)
+{
+    return integer_impl(A, a_shape, a_rank, a_signed, B, b_shape, b_rank, b_signed, za, za_kind, zb, zb_kind,
+                        flat_idx, count, out);
 }
 
 /* Number of OpenMP threads the loops above use (for reporting). */

@@ -457,3 +457,106 @@ def test_gemm_at_equals_full():
     Y = oracle.gemm(A, B, FLOAT, True, True, C, 0.5, -2.0)
     idx = rng.choice(Y.size, 50, replace=False)
     assert np.array_equal(oracle.gemm_at(A, B, FLOAT, idx, True, True, C, 0.5, -2.0), Y.reshape(-1)[idx])
+
+
+# ---- MatMulInteger (page "Gemm and MatMul Performance Roadmap", section
+# "Remaining pull-request sequence", Roadmap PR09.1)
+
+_INT_TYPES = {"u8": np.uint8, "s8": np.int8}
+
+
+def _int_draw(rng, shape, t):
+    lo, hi = (0, 256) if t == np.uint8 else (-128, 128)
+    return rng.integers(lo, hi, size=shape).astype(t)
+
+
+def _numpy_integer(a, b, za, zb):
+    """numpy int64 matmul of the zero-point-shifted operands, reduced modulo 2^32."""
+    a64 = a.astype(np.int64)
+    b64 = b.astype(np.int64)
+    if za is not None:
+        za64 = np.asarray(za).astype(np.int64)
+        a64 = a64 - (za64[:, None] if za64.ndim == 1 else za64)
+    if zb is not None:
+        zb64 = np.asarray(zb).astype(np.int64)
+        b64 = b64 - zb64  # a vector broadcasts along the last (column) axis
+    y = np.matmul(a64, b64)
+    return (y & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+
+
+@pytest.mark.parametrize("ta,tb", list(itertools.product(_INT_TYPES, _INT_TYPES)))
+@pytest.mark.parametrize("zka,zkb", [("none", "none"), ("scalar", "none"), ("none", "vector"),
+                                     ("vector", "scalar"), ("scalar", "scalar"), ("vector", "vector")])
+def test_integer_matches_numpy(ta, tb, zka, zkb):
+    rng = np.random.default_rng(hash((ta, tb, zka, zkb)) % 2**32)
+    A = _int_draw(rng, (2, 1, 5, 37), _INT_TYPES[ta])
+    B = _int_draw(rng, (3, 37, 6), _INT_TYPES[tb])
+    za = {"none": None, "scalar": _int_draw(rng, (), _INT_TYPES[ta]), "vector": _int_draw(rng, (5,), _INT_TYPES[ta])}[zka]
+    zb = {"none": None, "scalar": _int_draw(rng, (), _INT_TYPES[tb]), "vector": _int_draw(rng, (6,), _INT_TYPES[tb])}[zkb]
+    y = oracle.matmul_integer(A, B, za, zb)
+    assert y.dtype == np.int32 and y.shape == (2, 3, 5, 6)
+    np.testing.assert_array_equal(y, _numpy_integer(A, B, za, zb))
+
+
+def test_integer_wraps_modulo_2_32():
+    # 255 * 255 * 40000 = 2601000000 exceeds 2^31 - 1: the INT32 result is
+    # that value minus 2^32.
+    K = 40000
+    A = np.full((1, K), 255, np.uint8)
+    B = np.full((K, 1), 255, np.uint8)
+    assert oracle.matmul_integer(A, B)[0, 0] == 255 * 255 * K - 2**32
+    # (-128)(-128) * 2^18 = 2^32: wraps to exactly zero.
+    K = 1 << 18
+    A = np.full((K,), -128, np.int8)
+    B = np.full((K,), -128, np.int8)
+    y = oracle.matmul_integer(A, B)
+    assert y.shape == () and int(y) == 0
+    # With zero points: (0 - 255)(255 - 0)... unsigned A at 0 minus za 255 is -255.
+    K = 70000
+    A = np.zeros((1, K), np.uint8)
+    B = np.full((K, 1), 255, np.uint8)
+    exact = -255 * 255 * K
+    assert oracle.matmul_integer(A, B, np.uint8(255), None)[0, 0] == exact + 2**32
+
+
+def test_integer_zero_point_closed_forms():
+    rng = np.random.default_rng(7)
+    M, K, N = 6, 9, 9
+    za = _int_draw(rng, (M,), np.uint8)
+    A = np.repeat(za[:, None], K, axis=1)  # every row equals its zero point
+    B = _int_draw(rng, (K, N), np.int8)
+    assert not oracle.matmul_integer(A, B, za, None).any()
+    # B - zb = identity: Y = A - za, per row and per column zero points.
+    A = _int_draw(rng, (M, K), np.int8)
+    zaa = _int_draw(rng, (M,), np.int8)
+    zb = rng.integers(0, 255, size=(N,)).astype(np.uint8)
+    B = (zb[None, :].astype(np.int64) + np.eye(K, N, dtype=np.int64)).astype(np.uint8)
+    want = A.astype(np.int32) - zaa.astype(np.int32)[:, None]
+    np.testing.assert_array_equal(oracle.matmul_integer(A, B, zaa, zb), want)
+
+
+def test_integer_broadcast_rank1_and_at():
+    rng = np.random.default_rng(11)
+    A = _int_draw(rng, (4, 1, 3, 20), np.uint8)
+    B = _int_draw(rng, (5, 20, 7), np.int8)
+    za, zb = np.uint8(3), _int_draw(rng, (7,), np.int8)
+    y = oracle.matmul_integer(A, B, za, zb)
+    assert y.shape == oracle.output_shape(A.shape, B.shape) == (4, 5, 3, 7)
+    for i in range(4):
+        for j in range(5):
+            np.testing.assert_array_equal(y[i, j], oracle.matmul_integer(A[i, 0], B[j], za, zb))
+    # rank-one A: the row of the promoted [1, K] product, M axis removed.
+    a1 = A[0, 0, 1]
+    np.testing.assert_array_equal(oracle.matmul_integer(a1, B, za, zb),
+                                  oracle.matmul_integer(a1[None, :], B, za, zb)[:, 0, :])
+    idx = rng.integers(0, y.size, size=50)
+    np.testing.assert_array_equal(oracle.matmul_integer_at(A, B, idx, za, zb), y.reshape(-1)[idx])
+
+
+def test_integer_rejects_bad_operands():
+    with pytest.raises(TypeError):
+        oracle.matmul_integer(np.zeros((2, 2), np.float32), np.zeros((2, 2), np.uint8))
+    with pytest.raises(ValueError):
+        oracle.matmul_integer(np.zeros((3, 2), np.uint8), np.zeros((2, 2), np.uint8), np.zeros(2, np.uint8))
+    with pytest.raises(oracle.OracleError):
+        oracle.matmul_integer(np.zeros((3, 2), np.uint8), np.zeros((3, 2), np.uint8))
