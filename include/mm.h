@@ -57,6 +57,9 @@ extern "C" {
  * and forcing SKINNY_M or SKINNY_N for DOUBLE gives MM_ERR_BAD_OPTION. */
 typedef enum mm_dtype {
     MM_FLOAT = 1,
+    MM_UINT8 = 2,  /* MatMulInteger inputs */
+    MM_INT8 = 3,   /* MatMulInteger inputs */
+    MM_INT32 = 6,  /* MatMulInteger output */
     MM_FLOAT16 = 10,
     MM_DOUBLE = 11,
     MM_BFLOAT16 = 16
@@ -225,6 +228,36 @@ mm_status mm_gemm_plan_create(const mm_gemm_desc *desc, int dtype, const mm_plan
  * (MM_ERR_BAD_OPTION). */
 mm_status mm_gemm_execute(mm_plan_t plan, const void *A, const void *B, const void *C, void *Y, void *stream);
 
+/* MatMulInteger (page "Gemm and MatMul Performance Roadmap", section
+ * "Remaining pull-request sequence", Roadmap PR09.1: mixed INT8 / UINT8 operands,
+ * optional scalar or per-row / per-column zero points, the MatMul batch
+ * broadcasting and rank-one rules, and INT32 accumulation defined as
+ * arithmetic modulo 2^32):
+ *
+ *   Y[i, m, n] = sum_k (A[iA(i), m, k] - za) * (B[iB(i), k, n] - zb)
+ *
+ * a_type / b_type: MM_UINT8 or MM_INT8.  Zero points (same type as their
+ * operand): MM_ZP_NONE (0), MM_ZP_SCALAR (one value) or MM_ZP_VECTOR (A: one
+ * value per row, [M]; B: one value per column, [N]; shared by every batch).
+ * Y is INT32 of the MatMul output shape.  The plan may own a device
+ * workspace for row / column sums (allocated by the first execution, freed
+ * by mm_plan_destroy); as for split-K, one plan must not run on two streams
+ * at once.  Errors as for mm_plan_create, plus MM_ERR_DTYPE for other types
+ * and MM_ERR_BAD_OPTION for an unknown zero-point kind or an option other
+ * than DIRECT / GENERAL with an INT8 tile. */
+enum { MM_ZP_NONE = 0, MM_ZP_SCALAR = 1, MM_ZP_VECTOR = 2 };
+
+mm_status mm_int_plan_create(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank, int a_type,
+                             int b_type, int a_zp_kind, int b_zp_kind, const mm_plan_options *opt, mm_plan_t *out);
+
+/* Enqueue the MatMulInteger product on `stream`.  a_zero_point /
+ * b_zero_point must be non-NULL exactly for the kinds other than
+ * MM_ZP_NONE (MM_ERR_NULL_ARG otherwise).  Other rules as for mm_execute;
+ * MM_ERR_BAD_OPTION for a plan that is not a MatMulInteger plan (and
+ * mm_execute refuses MatMulInteger plans). */
+mm_status mm_int_execute(mm_plan_t plan, const void *A, const void *B, const void *a_zero_point,
+                         const void *b_zero_point, void *Y, void *stream);
+
 /* Output shape: writes up to MM_MAX_RANK entries to `shape` and the rank to
  * *rank (0 when both inputs are rank one). */
 mm_status mm_plan_output_shape(mm_plan_t plan, int64_t *shape, int *rank);
@@ -242,7 +275,8 @@ size_t mm_plan_workspace_bytes(mm_plan_t plan);
 /* Fill *info with everything the plan resolved. */
 mm_status mm_plan_get_info(mm_plan_t plan, mm_plan_info *info);
 
-/* Tile table of the tiled kernels for `dtype`: number of entries. */
+/* Tile table of the tiled kernels for `dtype`: number of entries
+ * (MM_UINT8, MM_INT8 and MM_INT32 all name the MatMulInteger table). */
 int mm_tile_count(int dtype);
 
 /* Entry `index` (0-based) of the tile table: block rows, block columns and

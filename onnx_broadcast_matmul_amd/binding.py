@@ -16,6 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmm.so")
 
 FLOAT, FLOAT16, DOUBLE, BFLOAT16 = 1, 10, 11, 16
+UINT8, INT8, INT32 = 2, 3, 6
+ZP_NONE, ZP_SCALAR, ZP_VECTOR = 0, 1, 2
 MAX_BATCH_DIMS = 8
 MAX_RANK = MAX_BATCH_DIMS + 2
 
@@ -119,6 +121,11 @@ def lib() -> ctypes.CDLL:
         L.mm_gemm_plan_create.restype = ctypes.c_int
         L.mm_gemm_execute.argtypes = [vp, vp, vp, vp, vp, vp]
         L.mm_gemm_execute.restype = ctypes.c_int
+        L.mm_int_plan_create.argtypes = [i64p, ctypes.c_int, i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.POINTER(PlanOptions), ctypes.POINTER(vp)]
+        L.mm_int_plan_create.restype = ctypes.c_int
+        L.mm_int_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        L.mm_int_execute.restype = ctypes.c_int
         L.mm_status_string.argtypes = [ctypes.c_int]
         L.mm_status_string.restype = ctypes.c_char_p
         L.mm_last_error.argtypes = []
@@ -343,6 +350,73 @@ class GemmPlan(Plan):
         with self._lock:
             self.execute_ptr(A.data_ptr(), B.data_ptr(), Y.data_ptr(), stream.cuda_stream,
                              C.data_ptr() if C is not None else 0)
+
+
+def torch_int_code(dt) -> int:
+    import torch
+
+    codes = {torch.uint8: UINT8, torch.int8: INT8}
+    if dt not in codes:
+        raise TypeError(f"MatMulInteger takes uint8 / int8 tensors, not {dt}")
+    return codes[dt]
+
+
+class IntPlan(Plan):
+    """mm_int_plan_create / mm_int_execute: ONNX MatMulInteger (UINT8 / INT8
+    operands, optional scalar or per-row / per-column zero points, INT32
+    output modulo 2^32)."""
+
+    def __init__(self, a_shape, b_shape, a_type: int, b_type: int, a_zp: int = ZP_NONE, b_zp: int = ZP_NONE,
+                 force_algo: int = 0, tile: int = 0):
+        L = lib()
+        self._handle = ctypes.c_void_p()
+        self.a_shape = tuple(int(d) for d in a_shape)
+        self.b_shape = tuple(int(d) for d in b_shape)
+        self.a_type, self.b_type = int(a_type), int(b_type)
+        self.a_zp, self.b_zp = int(a_zp), int(b_zp)
+        self.dtype = INT32
+        opt = PlanOptions(force_algo, tile, 0, 0)
+        _check(L.mm_int_plan_create(_shape(self.a_shape), len(self.a_shape), _shape(self.b_shape), len(self.b_shape),
+                                    self.a_type, self.b_type, self.a_zp, self.b_zp, ctypes.byref(opt),
+                                    ctypes.byref(self._handle)))
+        self._lock = threading.Lock()
+
+    def zero_point_numel(self, which: str) -> int:
+        """Elements the plan reads from the A or B zero point (0 for none)."""
+        kind = self.a_zp if which == "a" else self.b_zp
+        if kind == ZP_NONE:
+            return 0
+        if kind == ZP_SCALAR:
+            return 1
+        inf = self.info()
+        return inf["M"] if which == "a" else inf["N"]
+
+    def execute_ptr(self, A: int, B: int, Y: int, stream: int = 0, a_zp: int = 0, b_zp: int = 0) -> None:
+        _check(lib().mm_int_execute(self._handle, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(a_zp),
+                                    ctypes.c_void_p(b_zp), ctypes.c_void_p(Y), ctypes.c_void_p(stream)))
+
+    def execute(self, A, B, Y, a_zp=None, b_zp=None, stream=None) -> None:
+        import torch
+
+        tdt = {UINT8: torch.uint8, INT8: torch.int8}
+        checks = [("A", A, self.a_shape, tdt[self.a_type]), ("B", B, self.b_shape, tdt[self.b_type]),
+                  ("Y", Y, self.output_shape, torch.int32)]
+        for which, zp, typ in (("a", a_zp, self.a_type), ("b", b_zp, self.b_type)):
+            n = self.zero_point_numel(which)
+            if (zp is None) != (n == 0):
+                raise ValueError(f"{which}_zp: the plan expects {'none' if n == 0 else f'{n} value(s)'}")
+            if zp is not None:
+                if zp.numel() != n:
+                    raise ValueError(f"{which}_zp has {zp.numel()} elements, the plan reads {n}")
+                checks.append((f"{which}_zp", zp, tuple(zp.shape), tdt[typ]))
+        for name, t, shape, want in checks:
+            if t.dtype != want or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {want} tensor of shape {tuple(shape)}")
+        if stream is None:
+            stream = torch.cuda.current_stream(Y.device)
+        with self._lock:
+            self.execute_ptr(A.data_ptr(), B.data_ptr(), Y.data_ptr(), stream.cuda_stream,
+                             a_zp.data_ptr() if a_zp is not None else 0, b_zp.data_ptr() if b_zp is not None else 0)
 
 
 _plan_cache = {}

@@ -11,6 +11,7 @@ namespace mm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -74,6 +75,16 @@ struct Elem<MM_BFLOAT16> {
     }
 };
 
+// MatMulInteger operands (fed to the signed INT8 matrix cores; see KArgs).
+template <>
+struct Elem<MM_INT8> {
+    using S = int8_t;
+    static constexpr int kVE = 16;
+    __device__ static __forceinline__ float to_f32(S x) { return (float)x; }
+    __device__ static __forceinline__ S from_f32(float x) { return (S)x; }
+    __device__ static __forceinline__ uint32_t pack2(float, float) { return 0u; }
+};
+
 // ---- direct global-to-LDS loads (gfx950 buffer loads with the LDS destination)
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -120,6 +131,17 @@ __device__ __forceinline__ float gemm_epilogue(const KArgs &a, float acc, int64_
         c = E::to_f32(C[idx]);
     }
     return a.alpha * acc + a.beta * c;
+}
+
+// MatMulInteger: zero point minus the INT8 offset of a UINT8 operand, as a
+// 32-bit value (modulo 2^32): mode 0 none, 1 scalar, 2 one per index i.
+__device__ __forceinline__ uint32_t int_zp(const void *zp, int mode, int is_signed, int64_t i) {
+    int32_t z = 0;
+    if (mode != 0) {
+        const int64_t at = mode == 1 ? 0 : i;
+        z = is_signed ? (int32_t)((const int8_t *)zp)[at] : (int32_t)((const uint8_t *)zp)[at];
+    }
+    return (uint32_t)(z - (is_signed ? 0 : 128));
 }
 
 // Element offsets of the A and B matrices used by output batch `b`.

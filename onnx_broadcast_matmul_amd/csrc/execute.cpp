@@ -143,13 +143,82 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
     clear_error();
     if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
     if (p->is_gemm) return fail(MM_ERR_BAD_OPTION, "a Gemm plan runs through mm_gemm_execute");
+    if (p->is_int) return fail(MM_ERR_BAD_OPTION, "a MatMulInteger plan runs through mm_int_execute");
     return execute_impl(p, A, B, nullptr, Y, stream);
+}
+
+mm_status mm_int_execute(mm_plan_t p, const void *A, const void *B, const void *za, const void *zb, void *Y,
+                         void *stream) {
+    clear_error();
+    if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
+    if (!p->is_int) return fail(MM_ERR_BAD_OPTION, "not a MatMulInteger plan");
+    if (p->algo == MM_ALGO_EMPTY) return MM_OK;
+    if (!Y) return fail(MM_ERR_NULL_ARG, "Y is NULL for a non-empty output");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (p->algo == MM_ALGO_ZERO_FILL) {
+        e = launch_fill_zero(MM_INT32, Y, p->out_numel, s);
+        return e == hipSuccess ? MM_OK : hip_fail(e, "zero-fill launch");
+    }
+    if (!A || !B) return fail(MM_ERR_NULL_ARG, "A or B is NULL");
+    if ((p->zpa_kind != MM_ZP_NONE && !za) || (p->zpb_kind != MM_ZP_NONE && !zb))
+        return fail(MM_ERR_NULL_ARG, "a zero point the plan expects is NULL");
+    KArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = A;
+    a.B = B;
+    a.Y = Y;
+    a.M = p->kernel_m;
+    a.N = p->N;
+    a.K = p->K;
+    a.lda = p->K;
+    a.ldb = p->N;
+    a.ldy = p->N;
+    a.batch = p->batch;
+    a.kchunk = p->K;
+    a.split = 1;
+    a.bd = p->bd;
+    a.a_signed = p->a_type == MM_INT8;
+    a.b_signed = p->b_type == MM_INT8;
+    a.flip_a = a.a_signed ? 0u : 0x80808080u;
+    a.flip_b = a.b_signed ? 0u : 0x80808080u;
+    a.zpa_mode = p->zpa_kind;
+    a.zpb_mode = p->zpb_kind;
+    a.zpa = za;
+    a.zpb = zb;
+    a.zp_rows = p->M > 0 ? p->M : 1;
+    a.y_vec = aligned16(Y) && (p->N * 4) % 16 == 0;
+    bool tiled = p->algo == MM_ALGO_GENERAL;
+    if (tiled) {
+        // The tiled kernel streams 16-byte chunks of A rows and B rows, with
+        // 32-bit offsets within one tile of A rows and one stage of B rows.
+        const TileCfg *t = tile_entry(MM_INT8, p->tile);
+        tiled = aligned16(A) && aligned16(B) && p->K % 16 == 0 && p->N % 16 == 0 &&
+                (int64_t)t->bm * p->K < 0x7fff0000LL && (int64_t)t->bkb * p->N < 0x7fff0000LL;
+    }
+    if (!tiled) {
+        e = launch_int_direct(a, s);
+        return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
+    }
+    int32_t *ra = nullptr, *cb = nullptr;
+    if (p->need_ra || p->need_cb) {
+        mm_status st = ensure_workspace(p);
+        if (st != MM_OK) return st;
+        int32_t *w = (int32_t *)p->ws;
+        if (p->need_ra) ra = w;
+        if (p->need_cb) cb = w + (p->need_ra ? p->int_a_rows : 0);
+    }
+    a.ra = ra;
+    a.cb = cb;
+    e = launch_int_sums(a, p->int_a_rows, p->int_b_mats, ra, cb, s);
+    if (e == hipSuccess) e = launch_general_int(p->tile, a, s);
+    return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
 }
 
 mm_status mm_gemm_execute(mm_plan_t p, const void *A, const void *B, const void *C, void *Y, void *stream) {
     clear_error();
     if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
-    if (!p->is_gemm) return fail(MM_ERR_BAD_OPTION, "a MatMul plan runs through mm_execute");
+    if (!p->is_gemm) return fail(MM_ERR_BAD_OPTION, "not a Gemm plan");
     return execute_impl(p, A, B, C, Y, stream);
 }
 

@@ -55,6 +55,23 @@ struct KArgs {
     float alpha, beta;
     const void *C;
     int64_t ldc;
+    // MatMulInteger: UINT8 operands are fed to the signed INT8 matrix cores
+    // with their sign bit flipped (x - 128); flip_a / flip_b are then
+    // 0x80808080.  zpa / zpb are the zero points (a_signed / b_signed give
+    // their type; zp_mode: 0 none, 1 scalar, 2 per row of A / per column of
+    // B); ra / cb hold the row sums of A' per A row and the column sums of
+    // B' per B matrix (int32, modulo 2^32).  The tiled kernel pads the last
+    // K stage with zero bytes, which the flip turns into -128: with both
+    // operands flipped each padded k adds (-128)(-128) to every sum, and the
+    // epilogue takes that known amount off again.
+    uint32_t flip_a, flip_b;
+    int32_t a_signed, b_signed;
+    int32_t zpa_mode, zpb_mode;
+    const void *zpa;
+    const void *zpb;
+    const int32_t *ra;
+    const int32_t *cb;
+    int64_t zp_rows;  // rows of one A matrix: a per-row zero point is indexed by row % zp_rows
 };
 
 // Layouts of the Gemm bias C, unidirectionally broadcast to (M, N).
@@ -93,6 +110,12 @@ hipError_t launch_general_t(int dtype, int tile, const Align &al, bool split, co
 hipError_t launch_splitk_reduce(int dtype, const KArgs &a, hipStream_t s);
 hipError_t launch_skinny_m(int dtype, const Align &al, const KArgs &a, hipStream_t s);
 hipError_t launch_skinny_n(int dtype, const Align &al, const KArgs &a, hipStream_t s);
+// MatMulInteger kernels (k_int.hip): the direct kernel, the row / column
+// sum passes (ra over a_rows rows of A, cb over b_mats B matrices; either
+// may be NULL) and the INT8 tiled kernel for the kTiles8 entries.
+hipError_t launch_int_direct(const KArgs &a, hipStream_t s);
+hipError_t launch_int_sums(const KArgs &a, int64_t a_rows, int64_t b_mats, int32_t *ra, int32_t *cb, hipStream_t s);
+hipError_t launch_general_int(int tile, const KArgs &a, hipStream_t s);
 // DOUBLE kernels (k_f64.hip); W holds double partials for split-K.
 hipError_t launch_direct_f64(const KArgs &a, hipStream_t s);
 hipError_t launch_general_f64(int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);

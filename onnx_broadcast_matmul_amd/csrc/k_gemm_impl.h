@@ -340,8 +340,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     auto aswz = [](int row) { return CA == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
     auto mswz = [](int k, int cpr) {  // k-row of cpr chunks
         if constexpr (ES == 4) return cpr >= 16 ? 8 * ((k >> 2) & 1) : 0;  // 8 chunks: no room to move
+        else if constexpr (ES == 1) return k & 7;  // a transposing 8-bit read covers 8 consecutive k-rows
         else return cpr >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
     };
+    static_assert(DT != MM_INT8 || (KG == 1 && !SPLIT), "INT8: no K groups, no split-K");
     auto bswz = [&](int k) { return mswz(k, CPR); };
 
     __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
@@ -373,6 +375,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 
     int64_t oa, ob;
     batch_offsets(a.bd, b, oa, ob);
+    // MatMulInteger: this product's A rows and B matrix in the sum tables.
+    const int64_t ra_base = DT == MM_INT8 ? oa / (K > 0 ? K : 1) : 0;
+    const int64_t cb_base = DT == MM_INT8 ? ob / (K * N > 0 ? K * N : 1) * N : 0;
     // Tile origins (k = 0): row m0 of A (column m0 of a transposed A) and
     // column n0 of B (row n0 of a transposed B).
     const char *Atile = (const char *)((const S *)a.A + oa + (TA ? m0 : m0 * a.lda));
@@ -445,13 +450,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         }
     };
 
-    f32x16 acc[FM][FN];
+    using AccT = typename std::conditional<DT == MM_INT8, i32x16, f32x16>::type;
+    AccT acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
     uint4 fa[2][FM], fb[2][FN];
     // Fragment of K-contiguous rows: chunk c of row `row`.
@@ -461,7 +467,24 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     // Fragment of M/N-contiguous k-rows (rbytes per row, cpr chunks): the
     // lane's 8 (16-bit) or 4 (FP32) consecutive k of index base + lane % 32.
     auto read_mn = [&](const char *Xs, int rbytes, int cpr, int base, int ks, int c) -> uint4 {
-        if constexpr (ES == 2) {
+        if constexpr (ES == 1) {
+            // 8-bit transposing reads: in each 16-lane group, lanes 2r, 2r + 1
+            // address the two 8-byte halves of row r of an 8 x 16 block and
+            // lane i receives column i -- two reads give 16 consecutive k.
+            const int G = lane >> 4, jl = lane & 15;
+            const int n = base + (G & 1) * 16 + (jl & 1) * 8;
+            uint2 h2[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = ks * 32 + (G >> 1) * 16 + h * 8 + (jl >> 1);
+                const int p = (n >> 4) ^ mswz(k, cpr);
+                const char *addr = Xs + k * rbytes + p * 16 + ((n >> 3) & 1) * 8;
+                typedef int i32x2v __attribute__((ext_vector_type(2)));
+                h2[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                                      (__attribute__((address_space(3))) i32x2v *)(addr)));
+            }
+            return make_uint4(h2[0].x, h2[0].y, h2[1].x, h2[1].y);
+        } else if constexpr (ES == 2) {
             const int G = lane >> 4, jl = lane & 15;
             const int n = base + (G & 1) * 16 + (jl & 3) * 4;
             uint2 h2[2];
@@ -504,12 +527,32 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             if constexpr (TB) fb[slot][j] = read_k(Bs, wc * WN + j * 32 + (lane & 31), c);
             else fb[slot][j] = read_mn(Bs, RBB, CPR, wc * WN + j * 32, ks, c);
         }
+        if constexpr (DT == MM_INT8) {  // UINT8 operands: x - 128 in INT8
+            const uint32_t fa_x = a.flip_a, fb_x = a.flip_b;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                fa[slot][i].x ^= fa_x; fa[slot][i].y ^= fa_x; fa[slot][i].z ^= fa_x; fa[slot][i].w ^= fa_x;
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                fb[slot][j].x ^= fb_x; fb[slot][j].y ^= fb_x; fb[slot][j].z ^= fb_x; fb[slot][j].w ^= fb_x;
+            }
+        }
     };
     // The B fragment is the first MFMA operand, so each 32x32 accumulator holds
     // the transposed output block: column n of the block in the MFMA's row
     // position, row m in its column position.
     auto mfmas = [&](int slot) {
-        if constexpr (DT == MM_BFLOAT16) {
+        if constexpr (DT == MM_INT8) {
+            typedef int i32x4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4v, fb[slot][j]),
+                                                                     __builtin_bit_cast(i32x4v, fa[slot][i]),
+                                                                     acc[i][j], 0, 0, 0);
+        } else if constexpr (DT == MM_BFLOAT16) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -583,7 +626,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     // which spreads the 32 rows of one write over distinct chunks; the
     // workgroup then writes whole 16-byte chunks of output rows.  Tiles larger
     // than the stage buffers go in row passes.
-    using O = typename std::conditional<SPLIT, float, S>::type;
+    using O = typename std::conditional<SPLIT, float, typename std::conditional<DT == MM_INT8, int32_t, S>::type>::type;
     constexpr int OS = (int)sizeof(O);
     constexpr int OV = 16 / OS;            // output elements per chunk
     constexpr int OCPR = BN * OS / 16;     // output chunks per tile row
@@ -594,7 +637,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     char *tile = lds;
     // Output rows: the dense workspace (pitch N) or Y (pitch ldy).
     const int64_t ldo = SPLIT ? N : a.ldy;
-    O *out = SPLIT ? (O *)(a.W + (sidx * a.batch + b) * M * N) : (O *)((S *)a.Y + b * M * a.ldy);
+    O *out = SPLIT ? (O *)(a.W + (sidx * a.batch + b) * M * N) : (O *)a.Y + b * M * a.ldy;
     if constexpr (KG > 1) {
         // Groups 1..KG-1 hand their accumulators to group 0 through LDS
         // (element-major, lane-contiguous), which adds them in group order.
@@ -674,8 +717,16 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
                         const int cl = wc * WN + j * 32 + 8 * q + 4 * (lane >> 5);
                         const int ch = (cl / OV) ^ (rl & (OCPR - 1));
                         char *dst = trow + ch * 16 + (cl % OV) * OS;
-                        const f32x16 &v = acc[i][j];
-                        float w[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+                        if constexpr (DT == MM_INT8) {
+                            // Raw INT32 sums of the fed operands; the zero-point
+                            // terms are applied per output chunk below.
+                            const AccT &v = acc[i][j];
+                            *(uint4 *)dst = make_uint4((uint32_t)v[4 * q], (uint32_t)v[4 * q + 1],
+                                                       (uint32_t)v[4 * q + 2], (uint32_t)v[4 * q + 3]);
+                            continue;
+                        }
+                        const AccT &v = acc[i][j];
+                        float w[4] = {(float)v[4 * q], (float)v[4 * q + 1], (float)v[4 * q + 2], (float)v[4 * q + 3]};
                         if constexpr (EPI) {
                             if (a.gemm_epi) {
                                 if (cmode == kBiasFull) {
@@ -706,7 +757,27 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             const int rl = idx / OCPR, c = idx % OCPR;
             const int64_t row = m0 + pass * PR + rl, col = n0 + (int64_t)c * OV;
             if (row < M && col < N) {
-                const uint4 v = *(const uint4 *)(tile + rl * (BN * OS) + (c ^ (rl & (OCPR - 1))) * 16);
+                uint4 v = *(const uint4 *)(tile + rl * (BN * OS) + (c ^ (rl & (OCPR - 1))) * 16);
+                if constexpr (DT == MM_INT8) {
+                    // Y = P - zb'[n] RA[m] - za'[m] (CB[n] - K zb'[n]), modulo
+                    // 2^32 (see KArgs); rows and the zero-point period are
+                    // below 2^31.
+                    const uint32_t za = int_zp(a.zpa, a.zpa_mode, a.a_signed, (uint32_t)row % (uint32_t)a.zp_rows);
+                    const uint32_t rsum = a.ra ? (uint32_t)a.ra[ra_base + row] : 0u;
+                    // Zero-byte K padding, flipped on both sides: 16384 per padded k.
+                    const uint32_t pad = (a.flip_a && a.flip_b) ? (uint32_t)((int64_t)nk * BK - (kend - kbeg)) * 16384u : 0u;
+                    uint32_t y[4] = {v.x - pad, v.y - pad, v.z - pad, v.w - pad};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t gn = col + e;
+                        if (gn < N) {
+                            const uint32_t zb = int_zp(a.zpb, a.zpb_mode, a.b_signed, gn);
+                            if (a.ra) y[e] -= zb * rsum;
+                            if (a.cb) y[e] -= za * ((uint32_t)a.cb[cb_base + gn] - (uint32_t)K * zb);
+                        }
+                    }
+                    v = make_uint4(y[0], y[1], y[2], y[3]);
+                }
                 O *dst = out + row * ldo + col;
                 if (a.y_vec) {
                     // Rows are whole 16-byte chunks: the chunk lies inside the row.
@@ -734,11 +805,18 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
     const dim3 g((unsigned)tiles);
     // Buffer offsets are 32-bit: one tile's rows of A and one stage's rows of
     // B must each span less than 2 GiB.
-    constexpr int ES = DT == MM_FLOAT ? 4 : 2;
+    constexpr int ES = (int)sizeof(typename Elem<DT>::S);
     const int64_t a_span = TA ? (int64_t)(BKB / ES) * a.lda : (int64_t)BM * a.lda;  // stored rows one tile stage spans
     const int64_t b_span = TB ? (int64_t)BN * a.ldb : (int64_t)(BKB / ES) * a.ldb;
     const bool fits = a_span * ES < 0x7fff0000LL && b_span * ES < 0x7fff0000LL;
-    if (vec && fits) {
+    if constexpr (DT == MM_INT8) {
+        // INT8 runs only this kernel, unsplit; the plan and execute layer
+        // send other cases to the direct integer kernel.
+        if (!(vec && fits) || split) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false>), g,
+                           dim3(64 * WGM * WGN * KG), 0, s, a);
+        return hipGetLastError();
+    } else if (vec && fits) {
         const dim3 blk(64 * WGM * WGN * KG);
         // Split-K partials take no epilogue (the reduction applies it).
         if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB, false>), g, blk, 0, s, a);

@@ -190,6 +190,7 @@ hipError_t launch_direct(int dtype, const KArgs &a, hipStream_t s) {
 hipError_t launch_fill_zero(int dtype, void *Y, int64_t n, hipStream_t s) {
     const unsigned g = grid_for(n, 65536);
     if (dtype == MM_DOUBLE) hipLaunchKernelGGL(k_fill_zero<double>, dim3(g), dim3(256), 0, s, (double *)Y, n);
+    else if (dtype == MM_INT32) hipLaunchKernelGGL(k_fill_zero<int32_t>, dim3(g), dim3(256), 0, s, (int32_t *)Y, n);
     else if (dtype == MM_FLOAT) hipLaunchKernelGGL(k_fill_zero<float>, dim3(g), dim3(256), 0, s, (float *)Y, n);
     else hipLaunchKernelGGL(k_fill_zero<uint16_t>, dim3(g), dim3(256), 0, s, (uint16_t *)Y, n);
     return hipGetLastError();

@@ -42,16 +42,21 @@ int tile_count(int dtype) {
     if (dtype == MM_FLOAT) return kNumTiles32;
     if (dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) return kNumTiles16;
     if (dtype == MM_DOUBLE) return kNumTiles64;
+    if (dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) return kNumTiles8;
     return 0;
 }
 
 const TileCfg *tile_entry(int dtype, int index) {
     if (index < 0 || index >= tile_count(dtype)) return nullptr;
     if (dtype == MM_DOUBLE) return &kTiles64[index];
+    if (dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) return &kTiles8[index];
     return dtype == MM_FLOAT ? &kTiles32[index] : &kTiles16[index];
 }
 
-int elem_size(int dtype) { return dtype == MM_DOUBLE ? 8 : dtype == MM_FLOAT ? 4 : 2; }
+int elem_size(int dtype) {
+    if (dtype == MM_INT8 || dtype == MM_UINT8) return 1;
+    return dtype == MM_DOUBLE ? 8 : (dtype == MM_FLOAT || dtype == MM_INT32) ? 4 : 2;
+}
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -61,7 +66,9 @@ static double tile_quality(int dtype, int index) {
     static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5};
     static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15};
     static const double q64[kNumTiles64] = {1.0, 0.8};
+    static const double q8[kNumTiles8] = {1.0, 0.75};
     if (dtype == MM_DOUBLE) return q64[index];
+    if (dtype == MM_INT32) return q8[index];
     return dtype == MM_FLOAT ? q32[index] : q16[index];
 }
 
@@ -130,7 +137,7 @@ static int64_t gcd64(int64_t a, int64_t b) {
 static void plan_tail(mm_plan_s *p) {
     p->tail_col = 0;
     p->tail_tile = -1;
-    if (p->dtype == MM_DOUBLE || p->is_gemm) return;
+    if (p->dtype == MM_DOUBLE || p->is_gemm || p->is_int) return;
     const TileCfg *t = tile_entry(p->dtype, p->tile);
     if (tile_wgs_per_cu(t) != 1) return;
     const int64_t rows = p->batch * cdiv(p->kernel_m, t->bm);
@@ -361,6 +368,8 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         if (p->dtype == MM_DOUBLE && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N)) algo = MM_ALGO_GENERAL;
         // Gemm (transposes, epilogue) runs on the direct, tiled and split-K kernels.
         if (p->is_gemm && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N)) algo = MM_ALGO_GENERAL;
+        // MatMulInteger runs on the direct and tiled INT8 kernels.
+        if (p->is_int && algo != MM_ALGO_DIRECT) algo = MM_ALGO_GENERAL;
     }
     if (algo < MM_ALGO_DIRECT || algo > MM_ALGO_GENERAL)
         return fail(MM_ERR_BAD_OPTION, "force_algo %d is not a forcible algorithm", algo);
@@ -368,6 +377,8 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         return fail(MM_ERR_BAD_OPTION, "DOUBLE has no skinny-M / skinny-N kernel (force GENERAL or DIRECT)");
     if (p->is_gemm && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N))
         return fail(MM_ERR_BAD_OPTION, "Gemm runs on the direct, general and split-K kernels only");
+    if (p->is_int && algo != MM_ALGO_DIRECT && algo != MM_ALGO_GENERAL)
+        return fail(MM_ERR_BAD_OPTION, "MatMulInteger runs on the direct and general kernels only");
     p->algo = algo;
 
     if (algo == MM_ALGO_GENERAL || algo == MM_ALGO_SPLIT_K) {
@@ -429,6 +440,47 @@ mm_status mm_plan_create_ex(const int64_t *a_shape, int a_rank, const int64_t *b
 mm_status mm_plan_create(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank, int dtype,
                          mm_plan_t *out) {
     return mm_plan_create_ex(a_shape, a_rank, b_shape, b_rank, dtype, nullptr, out);
+}
+
+mm_status mm_int_plan_create(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank, int a_type,
+                             int b_type, int a_zp_kind, int b_zp_kind, const mm_plan_options *opt, mm_plan_t *out) {
+    clear_error();
+    if (!out) return fail(MM_ERR_NULL_ARG, "out is NULL");
+    *out = nullptr;
+    if ((!a_shape && a_rank > 0) || (!b_shape && b_rank > 0)) return fail(MM_ERR_NULL_ARG, "shape pointer is NULL");
+    auto int_type = [](int t) { return t == MM_UINT8 || t == MM_INT8; };
+    if (!int_type(a_type) || !int_type(b_type))
+        return fail(MM_ERR_DTYPE, "MatMulInteger takes UINT8 / INT8 operands (got %d, %d)", a_type, b_type);
+    auto zp_ok = [](int z) { return z == MM_ZP_NONE || z == MM_ZP_SCALAR || z == MM_ZP_VECTOR; };
+    if (!zp_ok(a_zp_kind) || !zp_ok(b_zp_kind)) return fail(MM_ERR_BAD_OPTION, "unknown zero-point kind");
+    if (opt && opt->reserved != 0) return fail(MM_ERR_BAD_OPTION, "reserved option field must be 0");
+    mm_plan_s *p = new (std::nothrow) mm_plan_s();
+    if (!p) return fail(MM_ERR_ALLOC, "host allocation failed");
+    p->dtype = MM_INT32;
+    p->is_int = true;
+    p->a_type = a_type;
+    p->b_type = b_type;
+    p->zpa_kind = a_zp_kind;
+    p->zpb_kind = b_zp_kind;
+    mm_status st = resolve(a_shape, a_rank, b_shape, b_rank, p);
+    if (st == MM_OK) st = select_algo(p, opt);
+    if (st != MM_OK) {
+        delete p;
+        return st;
+    }
+    // Row sums of A' are needed when zb' can be non-zero, column sums of B'
+    // when za' can be (a UINT8 operand has a non-zero offset).
+    if (p->algo == MM_ALGO_GENERAL && p->K > 0) {
+        int64_t na = 1;
+        for (int i = 0; i < a_rank; ++i) na *= a_shape[i];
+        p->int_a_rows = na / p->K;
+        p->int_b_mats = p->N > 0 ? p->b_numel / (p->K * p->N) : 0;
+        p->need_ra = b_type == MM_UINT8 || b_zp_kind != MM_ZP_NONE;
+        p->need_cb = a_type == MM_UINT8 || a_zp_kind != MM_ZP_NONE;
+        p->workspace_bytes = 4 * ((p->need_ra ? p->int_a_rows : 0) + (p->need_cb ? p->int_b_mats * p->N : 0));
+    }
+    *out = p;
+    return MM_OK;
 }
 
 mm_status mm_gemm_plan_create(const mm_gemm_desc *d, int dtype, const mm_plan_options *opt, mm_plan_t *out) {
@@ -539,7 +591,10 @@ mm_status mm_plan_get_info(mm_plan_t p, mm_plan_info *info) {
     int64_t na = 1, nb = 1;
     for (int i = 0; i < p->a_rank; ++i) na *= p->a_shape[i];
     for (int i = 0; i < p->b_rank; ++i) nb *= p->b_shape[i];
-    info->min_bytes = (double)elem_size(p->dtype) * ((double)na + (double)nb + (double)p->out_numel);
+    if (p->is_int)  // one-byte inputs, INT32 output
+        info->min_bytes = (double)na + (double)nb + 4.0 * (double)p->out_numel;
+    else
+        info->min_bytes = (double)elem_size(p->dtype) * ((double)na + (double)nb + (double)p->out_numel);
     return MM_OK;
 }
 
@@ -550,7 +605,10 @@ mm_status mm_tile_config(int dtype, int index, int *bm, int *bn, int *bk) {
     if (!t) return fail(MM_ERR_BAD_OPTION, "no tile %d for dtype %d", index, dtype);
     if (bm) *bm = t->bm;
     if (bn) *bn = t->bn;
-    if (bk) *bk = t->bkb / elem_size(dtype);
+    // K elements per stage: INT8 tiles stage one-byte elements (the table is
+    // shared by the MM_UINT8 / MM_INT8 / MM_INT32 codes).
+    const bool int_code = dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32;
+    if (bk) *bk = t->bkb / (int_code ? 1 : elem_size(dtype));
     return MM_OK;
 }
 

@@ -52,9 +52,16 @@ constexpr TileCfg kTiles64[] = {
 constexpr int kTransTiles16[] = {0, 5, 4};
 constexpr int kTransTiles32[] = {4, 2};
 
+// INT8 entries (MatMulInteger; B rows need at least 128 bytes per stage row).
+constexpr TileCfg kTiles8[] = {
+    {256, 256, 2, 4, 128, 2, 4, 1},
+    {128, 128, 2, 2, 128, 2, 4, 1},
+};
+
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
 constexpr int kNumTiles32 = sizeof(kTiles32) / sizeof(kTiles32[0]);
 constexpr int kNumTiles64 = sizeof(kTiles64) / sizeof(kTiles64[0]);
+constexpr int kNumTiles8 = sizeof(kTiles8) / sizeof(kTiles8[0]);
 
 // K granularity of split-K partitions: 128 bytes of K, a whole number of
 // LDS stages of every tile entry.

@@ -212,5 +212,49 @@ GEMM_PRODUCTS = [
 ]
 
 
+def generate_int(shape: Sequence[int], signed: bool, seed: Sequence[int], lo: int = None, hi: int = None) -> np.ndarray:
+    """int8 (signed) or uint8 array of ``shape``, uniform over [lo, hi]
+    (default: the whole type range)."""
+    lo = (-128 if signed else 0) if lo is None else lo
+    hi = (127 if signed else 255) if hi is None else hi
+    n = int(np.prod(shape, dtype=np.int64)) if len(shape) else 1
+    rng = np.random.default_rng(list(seed))
+    v = rng.integers(lo, hi + 1, size=n, dtype=np.int16)
+    return v.astype(np.int8 if signed else np.uint8).reshape(tuple(shape))
+
+
+@dataclass
+class IntProduct:
+    """One MatMulInteger: shapes, operand signedness, zero-point kinds
+    (0 none, 1 scalar, 2 per row of A / per column of B) and seed; operands
+    uniform over their whole type range."""
+
+    name: str
+    a_shape: Tuple[int, ...]
+    b_shape: Tuple[int, ...]
+    a_signed: bool
+    b_signed: bool
+    a_zp: int
+    b_zp: int
+    seed: int
+
+    def make(self):
+        a = generate_int(self.a_shape, self.a_signed, [self.seed, 0, 0])
+        b = generate_int(self.b_shape, self.b_signed, [self.seed, 0, 1])
+        m = 1 if len(self.a_shape) == 1 else self.a_shape[-2]
+        n = 1 if len(self.b_shape) == 1 else self.b_shape[-1]
+        za = None if self.a_zp == 0 else generate_int(() if self.a_zp == 1 else (m,), self.a_signed, [self.seed, 0, 2])
+        zb = None if self.b_zp == 0 else generate_int(() if self.b_zp == 1 else (n,), self.b_signed, [self.seed, 0, 3])
+        return a, b, za, zb
+
+
+# MatMulInteger: the transformer projection quantized as the pages' integer
+# benchmark quantizes it -- UINT8 activations with one zero point, INT8
+# weights without one.
+INT_PRODUCTS = [
+    IntProduct("u8s8_16x512x4096_by_4096x11008", (16, 512, 4096), (4096, 11008), False, True, 1, 0, 9),
+]
+
+
 def all_products() -> List[Product]:
     return [p for w in WORKLOADS.values() for p in w.products]

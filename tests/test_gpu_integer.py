@@ -1,0 +1,165 @@
+"""GPU parity of MatMulInteger (page "Gemm and MatMul Performance Roadmap",
+section "Remaining pull-request sequence", Roadmap PR09.1): the HIP kernels
+behind mm_int_plan_create / mm_int_execute against the CPU oracle's exact
+integer sums reduced modulo 2^32.  Integer results have exactly one correct
+value, so every comparison is bit-exact: all four operand signedness
+combinations, no / scalar / per-row (A) / per-column (B) zero points, both
+kernels (direct and tiled) and every tile entry, ragged sizes, broadcast and
+folded batches, rank-one operands, empty and K == 0 outputs, the cases the
+tiled kernel hands to the direct one (K or N not a multiple of 16, operands
+off 16-byte alignment), accumulator wrap-around, and the full-size quantized
+transformer projection on sampled outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from onnx_broadcast_matmul_amd import binding as mm
+from onnx_broadcast_matmul_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SENTINEL = 0x5EADBEEF  # an output the kernels never write keeps this value
+SIGN = {"u8": False, "s8": True}
+CODE = {False: mm.UINT8, True: mm.INT8}
+ZP = {"none": mm.ZP_NONE, "scalar": mm.ZP_SCALAR, "vector": mm.ZP_VECTOR}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mm.lib()  # the native library must load: no fallback exists
+    return torch.device("cuda:0")
+
+
+def _device(x, dev, offset=0):
+    """Device copy of a uint8 / int8 array, starting `offset` bytes into its
+    allocation (offset 1 takes the operand off 16-byte alignment)."""
+    t = torch.from_numpy(np.ascontiguousarray(x).reshape(-1))
+    buf = torch.empty(t.numel() + offset, dtype=t.dtype, device=dev)
+    buf[offset:] = t.to(dev)
+    return buf[offset:].view(x.shape)
+
+
+def _zero_point(kind, signed, n, seed):
+    if kind == "none":
+        return None
+    return synth.generate_int(() if kind == "scalar" else (n,), signed, seed)
+
+
+def int_run(plan, a, b, za, zb, dev, a_off=0, b_off=0):
+    Y = torch.full(plan.output_shape, SENTINEL, dtype=torch.int32, device=dev)
+    plan.execute(_device(a, dev, a_off), _device(b, dev, b_off), Y,
+                 None if za is None else _device(np.atleast_1d(za), dev).view(za.shape),
+                 None if zb is None else _device(np.atleast_1d(zb), dev).view(zb.shape))
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def int_parity(sa, sb, ta, tb, zka, zkb, dev, algo=0, tile=0, seed=0, a_off=0, b_off=0):
+    sa_, sb_ = SIGN[ta], SIGN[tb]
+    a = synth.generate_int(sa, sa_, [seed, 0])
+    b = synth.generate_int(sb, sb_, [seed, 1])
+    m = 1 if len(sa) == 1 else sa[-2]
+    n = 1 if len(sb) == 1 else sb[-1]
+    za = _zero_point(zka, sa_, m, [seed, 2])
+    zb = _zero_point(zkb, sb_, n, [seed, 3])
+    plan = mm.IntPlan(sa, sb, CODE[sa_], CODE[sb_], ZP[zka], ZP[zkb], force_algo=algo, tile=tile)
+    if algo:
+        assert plan.algo == algo
+    y = int_run(plan, a, b, za, zb, dev, a_off, b_off)
+    o = oracle.matmul_integer(a, b, za, zb)
+    assert y.shape == o.shape
+    bad = np.flatnonzero(y.reshape(-1) != o.reshape(-1))
+    assert bad.size == 0, (f"{sa} x {sb} {ta}{tb} zp {zka}/{zkb} algo={mm.ALGO_NAMES[plan.algo]} "
+                           f"tile={plan.info()['tile']}: {bad.size} of {o.size} differ, first at {bad[:5]}: "
+                           f"{y.reshape(-1)[bad[:5]]} vs {o.reshape(-1)[bad[:5]]}")
+    return plan
+
+
+TYPES = [("u8", "u8"), ("u8", "s8"), ("s8", "u8"), ("s8", "s8")]
+ZPS = [("none", "none"), ("scalar", "vector"), ("vector", "scalar")]
+
+
+@pytest.mark.parametrize("ta,tb", TYPES, ids=lambda t: t)
+@pytest.mark.parametrize("zka,zkb", ZPS, ids=lambda z: z)
+@pytest.mark.parametrize("algo", [mm.ALGO_DIRECT, mm.ALGO_GENERAL], ids=lambda a: mm.ALGO_NAMES[a])
+def test_int_signedness_and_zero_points(ta, tb, zka, zkb, algo, dev):
+    """Broadcast batches [2,1] x [3] over ragged M, several N tiles, and a K
+    that leaves the last 128-byte stage partly padded."""
+    int_parity((2, 1, 200, 400), (3, 400, 272), ta, tb, zka, zkb, dev, algo=algo, seed=1)
+
+
+@pytest.mark.parametrize("tile", [1, 2])
+@pytest.mark.parametrize("ta,tb", [("u8", "s8"), ("s8", "u8")], ids=lambda t: t)
+def test_int_every_tile(tile, ta, tb, dev):
+    int_parity((700, 1024), (1024, 600), ta, tb, "vector", "vector", dev, algo=mm.ALGO_GENERAL, tile=tile, seed=2)
+    int_parity((700, 1024), (1024, 600), ta, tb, "none", "none", dev, algo=mm.ALGO_GENERAL, tile=tile, seed=3)
+
+
+def test_int_folded_batch_per_row_zero_point(dev):
+    """B shared by every batch: A's batches fold into the rows of one
+    product, and A's per-row zero point repeats every M rows."""
+    p = int_parity((4, 96, 256), (256, 160), "u8", "u8", "vector", "vector", dev, seed=4)
+    assert p.info()["folded"] and p.info()["kernel_m"] == 384 and p.algo == mm.ALGO_GENERAL
+
+
+@pytest.mark.parametrize("case", ["k200", "n100", "a_off", "b_off"])
+def test_int_direct_handoff(case, dev):
+    """Plans for the tiled kernel whose operands it cannot stream (K or N not
+    a multiple of 16, A or B off 16-byte alignment) run the direct kernel."""
+    sa, sb, ao, bo = (300, 512), (512, 256), 0, 0
+    if case == "k200":
+        sa, sb = (300, 200), (200, 256)
+    elif case == "n100":
+        sb = (512, 100)
+    elif case == "a_off":
+        ao = 1
+    else:
+        bo = 1
+    int_parity(sa, sb, "s8", "u8", "scalar", "vector", dev, algo=mm.ALGO_GENERAL, seed=5, a_off=ao, b_off=bo)
+
+
+def test_int_rank_one_empty_zero_k(dev):
+    int_parity((1000,), (1000, 320), "u8", "s8", "scalar", "vector", dev, seed=6)
+    int_parity((3, 130, 512), (512,), "s8", "s8", "vector", "scalar", dev, seed=7)
+    int_parity((512,), (512,), "u8", "u8", "vector", "vector", dev, seed=8)
+    for sa, sb in (((0, 64), (64, 32)), ((5, 64), (64, 0)), ((64, 0), (0, 32)), ((2, 3, 0), (0, 7))):
+        int_parity(sa, sb, "u8", "s8", "scalar", "scalar", dev, seed=9)
+
+
+def test_int_wraps_modulo_2_32(dev):
+    """Sums beyond the INT32 range wrap: 16384 * 2^18 = 2^32 gives 0 in the
+    matrix-core accumulator itself; 255 * 255 * 40000 - 2^32 comes from the
+    UINT8 corrections."""
+    K = 1 << 18
+    a = np.full((64, K), -128, np.int8)
+    b = np.full((K, 64), -128, np.int8)
+    plan = mm.IntPlan(a.shape, b.shape, mm.INT8, mm.INT8)
+    assert plan.algo == mm.ALGO_GENERAL
+    y = int_run(plan, a, b, None, None, dev)
+    assert oracle.matmul_integer_at(a, b, [0, 4095])[0] == 0 and not y.any()
+    K = 40000
+    a = np.full((64, K), 255, np.uint8)
+    b = np.full((K, 64), 255, np.uint8)
+    plan = mm.IntPlan(a.shape, b.shape, mm.UINT8, mm.UINT8)
+    y = int_run(plan, a, b, None, None, dev)
+    want = 255 * 255 * K - 2**32
+    assert oracle.matmul_integer_at(a, b, [7])[0] == want and (y == want).all()
+
+
+def test_int_full_size_projection(dev):
+    """The quantized transformer projection at full size, in the
+    configuration the benchmark times, on sampled outputs."""
+    prod = synth.INT_PRODUCTS[0]
+    a, b, za, zb = prod.make()
+    plan = mm.IntPlan(prod.a_shape, prod.b_shape, CODE[prod.a_signed], CODE[prod.b_signed], prod.a_zp, prod.b_zp)
+    print(f"\n[full-size] {prod.name} {mm.ALGO_NAMES[plan.algo]} tile {plan.info()['tile']}", flush=True)
+    y = int_run(plan, a, b, za, zb, dev).reshape(-1)
+    rng = np.random.default_rng(90)
+    idx = np.unique(np.concatenate([rng.choice(y.size, 3000, replace=False), [0, y.size - 1]]))
+    o = oracle.matmul_integer_at(a, b, idx, za, zb)
+    np.testing.assert_array_equal(y[idx], o)
+    assert not (y == SENTINEL).any()

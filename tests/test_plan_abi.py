@@ -386,3 +386,79 @@ def test_gemm_execute_checks_before_any_gpu_call():
     assert L.mm_execute(g.handle, fake, fake, fake, None) == mm.ERR_BAD_OPTION
     assert L.mm_gemm_execute(m.handle, fake, fake, None, fake, None) == mm.ERR_BAD_OPTION
     assert L.mm_gemm_execute(g.handle, fake, fake, None, fake, None) == mm.ERR_NULL_ARG
+
+
+# ---------------------------------------------------------------- MatMulInteger
+
+@pytest.mark.parametrize("ta,tb,zka,zkb,ra,cb", [
+    (mm.INT8, mm.INT8, mm.ZP_NONE, mm.ZP_NONE, False, False),
+    (mm.UINT8, mm.INT8, mm.ZP_NONE, mm.ZP_NONE, False, True),
+    (mm.INT8, mm.UINT8, mm.ZP_NONE, mm.ZP_NONE, True, False),
+    (mm.INT8, mm.INT8, mm.ZP_SCALAR, mm.ZP_NONE, False, True),
+    (mm.INT8, mm.INT8, mm.ZP_NONE, mm.ZP_VECTOR, True, False),
+    (mm.UINT8, mm.UINT8, mm.ZP_VECTOR, mm.ZP_SCALAR, True, True),
+])
+def test_int_plan_workspace(ta, tb, zka, zkb, ra, cb):
+    """Row sums of A (one per stored row) are kept only when zb' can be
+    non-zero, column sums of B (one per column of each stored B matrix) only
+    when za' can be."""
+    p = mm.IntPlan((4, 1, 64, 128), (3, 128, 96), ta, tb, zka, zkb)
+    assert p.output_shape == (4, 3, 64, 96)
+    inf = p.info()
+    assert inf["dtype"] == mm.INT32 and inf["algo"] == mm.ALGO_GENERAL and not inf["folded"]
+    assert inf["min_bytes"] == 4 * 64 * 128 + 3 * 128 * 96 + 4 * 4 * 3 * 64 * 96
+    assert p.workspace_bytes == 4 * ((4 * 64 if ra else 0) + (3 * 96 if cb else 0))
+
+
+def test_int_plan_algorithms():
+    u8, s8 = mm.UINT8, mm.INT8
+    f = mm.IntPlan((8, 64, 256), (256, 128), u8, s8)
+    assert f.info()["folded"] and f.info()["kernel_m"] == 512 and f.algo == mm.ALGO_GENERAL
+    assert f.workspace_bytes == 4 * 128  # column sums of the one shared B
+    assert mm.IntPlan((1, 4096), (4096, 4096), s8, s8).algo == mm.ALGO_GENERAL  # no skinny kernels
+    assert mm.IntPlan((4096, 4096), (4096, 1), s8, s8).algo == mm.ALGO_GENERAL
+    assert mm.IntPlan((8, 16), (16, 8), s8, s8).algo == mm.ALGO_DIRECT
+    assert mm.IntPlan((64, 0), (0, 32), s8, u8).algo == mm.ALGO_ZERO_FILL
+    assert mm.IntPlan((0, 64), (64, 32), s8, u8).algo == mm.ALGO_EMPTY
+    d = mm.IntPlan((512, 512), (512, 512), u8, u8, force_algo=mm.ALGO_DIRECT)
+    assert d.algo == mm.ALGO_DIRECT and d.workspace_bytes == 0
+    t = mm.IntPlan((512, 512), (512, 512), u8, u8, force_algo=mm.ALGO_GENERAL, tile=2)
+    assert t.info()["tile"] == 2
+    assert mm.tile_configs(mm.INT8) == mm.tile_configs(mm.UINT8) == [(256, 256, 128), (128, 128, 128)]
+    assert mm.tile_configs(mm.INT32) == mm.tile_configs(mm.INT8)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ta=mm.FLOAT), mm.ERR_DTYPE),
+    (dict(tb=mm.INT32), mm.ERR_DTYPE),
+    (dict(zka=3), mm.ERR_BAD_OPTION),
+    (dict(zkb=-1), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_SKINNY_M), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_SPLIT_K), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_GENERAL, tile=3), mm.ERR_BAD_OPTION),
+    (dict(sb=(100, 64)), mm.ERR_K_MISMATCH),
+    (dict(sa=(3, 64, 128), sb=(2, 128, 64)), mm.ERR_BROADCAST),
+])
+def test_int_plan_errors(kw, status):
+    kw = dict(kw)
+    sa, sb = kw.pop("sa", (64, 128)), kw.pop("sb", (128, 64))
+    args = (kw.pop("ta", mm.INT8), kw.pop("tb", mm.UINT8), kw.pop("zka", 0), kw.pop("zkb", 0))
+    with pytest.raises(mm.MMError) as e:
+        mm.IntPlan(sa, sb, *args, **kw)
+    assert e.value.status == status
+
+
+def test_int_execute_checks_before_any_gpu_call():
+    """A MatMulInteger plan is refused by mm_execute and a MatMul plan by
+    mm_int_execute; a plan with zero points refuses NULL zero points."""
+    L = mm.lib()
+    q = mm.IntPlan((64, 256), (256, 128), mm.UINT8, mm.INT8, mm.ZP_SCALAR, mm.ZP_VECTOR)
+    m = mm.Plan((64, 32), (32, 16), mm.FLOAT)
+    fake = ctypes.c_void_p(1 << 40)
+    assert L.mm_execute(q.handle, fake, fake, fake, None) == mm.ERR_BAD_OPTION
+    assert L.mm_int_execute(m.handle, fake, fake, None, None, fake, None) == mm.ERR_BAD_OPTION
+    assert L.mm_int_execute(q.handle, fake, fake, None, fake, fake, None) == mm.ERR_NULL_ARG
+    assert L.mm_int_execute(q.handle, fake, fake, fake, None, fake, None) == mm.ERR_NULL_ARG
+    assert L.mm_int_execute(q.handle, None, fake, fake, fake, fake, None) == mm.ERR_NULL_ARG
+    assert L.mm_int_execute(None, fake, fake, fake, fake, fake, None) == mm.ERR_NULL_ARG
+    assert L.mm_int_plan_create(None, 2, None, 2, mm.INT8, mm.INT8, 0, 0, None, None) == mm.ERR_NULL_ARG
