@@ -37,9 +37,9 @@ from onnx_broadcast_matmul_amd import synth  # noqa: E402
 HEADLINE = "fp32_square_and_batched_broadcast"
 # MI355X published peaks: HBM3E 8 TB/s; dense MFMA FP32 157.3 TFLOP/s,
 # FP16/BF16 2.5 PFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP/clk = 2516.6), FP64
-# 78.6 TFLOP/s.
+# 78.6 TFLOP/s, INT8 5.0 POP/s (8192 OP/clk per CU = 5033.2 TOP/s).
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {mm.FLOAT: 157.3, mm.FLOAT16: 2516.6, mm.BFLOAT16: 2516.6, mm.DOUBLE: 78.6}
+MFMA_PEAK_TFLOPS = {mm.FLOAT: 157.3, mm.FLOAT16: 2516.6, mm.BFLOAT16: 2516.6, mm.DOUBLE: 78.6, mm.INT8: 5033.2}
 ROTATE_BYTES = 1 << 30  # rotate input/output copies until a step touches >= 1 GiB
 MAX_COPIES = 16
 
@@ -147,6 +147,50 @@ class GemmCase:
                               self.C[k].data_ptr())
 
 
+class IntCase:
+    """One MatMulInteger product on the device, with rotated buffer copies;
+    a launch is the whole mm_int_execute (sum passes and the tiled kernel)."""
+
+    def __init__(self, product: synth.IntProduct, dev):
+        import torch
+
+        self.p = product
+        self.dt = mm.INT8
+        code = {True: mm.INT8, False: mm.UINT8}
+        self.plan = mm.IntPlan(product.a_shape, product.b_shape, code[product.a_signed], code[product.b_signed],
+                               product.a_zp, product.b_zp)
+        self.info = self.plan.info()
+        a, b, za, zb = product.make()
+        A = torch.from_numpy(a).to(dev)
+        B = torch.from_numpy(b).to(dev)
+        self.za = None if za is None else torch.from_numpy(np.atleast_1d(za)).to(dev)
+        self.zb = None if zb is None else torch.from_numpy(np.atleast_1d(zb)).to(dev)
+        del a, b
+        self.bytes = self.info["min_bytes"]
+        self.flops = self.info["flops"]
+        self.copies = int(min(MAX_COPIES, max(1, math.ceil(ROTATE_BYTES / self.bytes))))
+        self.A = [A] + [A.clone() for _ in range(self.copies - 1)]
+        self.B = [B] + [B.clone() for _ in range(self.copies - 1)]
+        self.Y = [torch.empty(self.plan.output_shape, dtype=torch.int32, device=dev) for _ in range(self.copies)]
+        self.bound = "hbm" if self.flops / self.bytes < MFMA_PEAK_TFLOPS[self.dt] * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+
+    def run(self, i: int, stream: int) -> None:
+        k = i % self.copies
+        self.plan.execute_ptr(self.A[k].data_ptr(), self.B[k].data_ptr(), self.Y[k].data_ptr(), stream,
+                              self.za.data_ptr() if self.za is not None else 0,
+                              self.zb.data_ptr() if self.zb is not None else 0)
+
+
+def int_case_report(c: IntCase, durs_ms):
+    r = case_report(c, durs_ms)
+    r["tops"] = r.pop("tflops")
+    if r["roofline_unit"] == "TFLOP/s":
+        r["roofline_unit"] = "TOP/s"
+    r["dtype"] = ("s8" if c.p.a_signed else "u8") + ("s8" if c.p.b_signed else "u8") + "->i32"
+    r["op"] = f"MatMulInteger zero points A={['none', 'scalar', 'per row'][c.p.a_zp]} B={['none', 'scalar', 'per column'][c.p.b_zp]}"
+    return r
+
+
 def _capture(cases, count: int, offset: int):
     """A HIP graph holding `count` steps (each step: every case once)."""
     import torch
@@ -223,7 +267,7 @@ def case_report(c: Case, durs_ms):
         achieved, peak, unit = tflops, MFMA_PEAK_TFLOPS[c.dt], "TFLOP/s"
     return {
         "algo": mm.ALGO_NAMES[c.plan.algo], "tile": c.info["tile"], "split_k": c.info["split_k"],
-        "dtype": synth.DTYPE_NAMES[c.dt], "a_shape": list(c.p.a_shape), "b_shape": list(c.p.b_shape),
+        "dtype": synth.DTYPE_NAMES.get(c.dt, str(c.dt)), "a_shape": list(c.p.a_shape), "b_shape": list(c.p.b_shape),
         "us_median": round(med * 1e3, 3), "us_p10": round(float(np.percentile(d, 10)) * 1e3, 3),
         "us_p90": round(float(np.percentile(d, 90)) * 1e3, 3),
         "tflops": round(tflops, 3), "hbm_gbs": round(gbs, 1), "bound": c.bound,
@@ -326,13 +370,17 @@ def main():
         return
     if args.only:
         names = args.only.split(",")
-        prods = [p for p in synth.all_products() + synth.GEMM_PRODUCTS if p.name in names]
+        prods = [p for p in synth.all_products() + synth.GEMM_PRODUCTS + synth.INT_PRODUCTS if p.name in names]
         if len(prods) != len(names):
             sys.exit(f"unknown product in {args.only}")
         for p in prods:
-            c = GemmCase(p, dev) if isinstance(p, synth.GemmProduct) else Case(p, dev)
+            if isinstance(p, synth.IntProduct):
+                c = IntCase(p, dev)
+            else:
+                c = GemmCase(p, dev) if isinstance(p, synth.GemmProduct) else Case(p, dev)
             _, per = time_cases([c], args.steps, args.warmup)
-            print(json.dumps({"only": p.name, "case": case_report(c, per[0])}), flush=True)
+            rep = int_case_report(c, per[0]) if isinstance(c, IntCase) else case_report(c, per[0])
+            print(json.dumps({"only": p.name, "case": rep}), flush=True)
             del c
             torch.cuda.empty_cache()
         return
@@ -393,6 +441,15 @@ def main():
             table[gp.name] = case_report(c, per_c[0])
             table[gp.name]["op"] = f"Gemm transA={int(gp.trans_a)} transB={int(gp.trans_b)} C={list(gp.c_shape)}"
             log(f"[bench]   {table[gp.name]}")
+            del c
+            torch.cuda.empty_cache()
+        for ip in synth.INT_PRODUCTS:
+            log(f"[bench] integer case {ip.name}")
+            c = IntCase(ip, dev)
+            steps = max(10, args.steps // 2)
+            _, per_c = time_cases([c], steps, max(3, args.warmup // 2))
+            table[ip.name] = int_case_report(c, per_c[0])
+            log(f"[bench]   {table[ip.name]}")
             del c
             torch.cuda.empty_cache()
         out["cases"] = table

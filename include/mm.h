@@ -239,10 +239,9 @@ mm_status mm_gemm_execute(mm_plan_t plan, const void *A, const void *B, const vo
  * a_type / b_type: MM_UINT8 or MM_INT8.  Zero points (same type as their
  * operand): MM_ZP_NONE (0), MM_ZP_SCALAR (one value) or MM_ZP_VECTOR (A: one
  * value per row, [M]; B: one value per column, [N]; shared by every batch).
- * Y is INT32 of the MatMul output shape.  The plan may own a device
- * workspace for row / column sums (allocated by the first execution, freed
- * by mm_plan_destroy); as for split-K, one plan must not run on two streams
- * at once.  Errors as for mm_plan_create, plus MM_ERR_DTYPE for other types
+ * Y is INT32 of the MatMul output shape.  MatMulInteger plans own no
+ * workspace and may run on several streams at once.  Errors as for
+ * mm_plan_create, plus MM_ERR_DTYPE for other types
  * and MM_ERR_BAD_OPTION for an unknown zero-point kind or an option other
  * than DIRECT / GENERAL with an INT8 tile. */
 enum { MM_ZP_NONE = 0, MM_ZP_SCALAR = 1, MM_ZP_VECTOR = 2 };

@@ -200,18 +200,9 @@ mm_status mm_int_execute(mm_plan_t p, const void *A, const void *B, const void *
         e = launch_int_direct(a, s);
         return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
     }
-    int32_t *ra = nullptr, *cb = nullptr;
-    if (p->need_ra || p->need_cb) {
-        mm_status st = ensure_workspace(p);
-        if (st != MM_OK) return st;
-        int32_t *w = (int32_t *)p->ws;
-        if (p->need_ra) ra = w;
-        if (p->need_cb) cb = w + (p->need_ra ? p->int_a_rows : 0);
-    }
-    a.ra = ra;
-    a.cb = cb;
-    e = launch_int_sums(a, p->int_a_rows, p->int_b_mats, ra, cb, s);
-    if (e == hipSuccess) e = launch_general_int(p->tile, a, s);
+    a.sum_a = p->need_ra;
+    a.sum_b = p->need_cb;
+    e = launch_general_int(p->tile, a, s);
     return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
 }
 

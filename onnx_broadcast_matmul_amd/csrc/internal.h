@@ -59,18 +59,16 @@ struct KArgs {
     // with their sign bit flipped (x - 128); flip_a / flip_b are then
     // 0x80808080.  zpa / zpb are the zero points (a_signed / b_signed give
     // their type; zp_mode: 0 none, 1 scalar, 2 per row of A / per column of
-    // B); ra / cb hold the row sums of A' per A row and the column sums of
-    // B' per B matrix (int32, modulo 2^32).  The tiled kernel pads the last
-    // K stage with zero bytes, which the flip turns into -128: with both
-    // operands flipped each padded k adds (-128)(-128) to every sum, and the
-    // epilogue takes that known amount off again.
+    // B).  sum_a / sum_b ask the tiled kernel for the row sums of A' / the
+    // column sums of B' (needed when the other operand's shifted zero point
+    // can be non-zero); it forms them from the operand fragments it already
+    // holds.
     uint32_t flip_a, flip_b;
     int32_t a_signed, b_signed;
     int32_t zpa_mode, zpb_mode;
     const void *zpa;
     const void *zpb;
-    const int32_t *ra;
-    const int32_t *cb;
+    int32_t sum_a, sum_b;
     int64_t zp_rows;  // rows of one A matrix: a per-row zero point is indexed by row % zp_rows
 };
 
@@ -114,7 +112,6 @@ hipError_t launch_skinny_n(int dtype, const Align &al, const KArgs &a, hipStream
 // sum passes (ra over a_rows rows of A, cb over b_mats B matrices; either
 // may be NULL) and the INT8 tiled kernel for the kTiles8 entries.
 hipError_t launch_int_direct(const KArgs &a, hipStream_t s);
-hipError_t launch_int_sums(const KArgs &a, int64_t a_rows, int64_t b_mats, int32_t *ra, int32_t *cb, hipStream_t s);
 hipError_t launch_general_int(int tile, const KArgs &a, hipStream_t s);
 // DOUBLE kernels (k_f64.hip); W holds double partials for split-K.
 hipError_t launch_direct_f64(const KArgs &a, hipStream_t s);

@@ -375,9 +375,6 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 
     int64_t oa, ob;
     batch_offsets(a.bd, b, oa, ob);
-    // MatMulInteger: this product's A rows and B matrix in the sum tables.
-    const int64_t ra_base = DT == MM_INT8 ? oa / (K > 0 ? K : 1) : 0;
-    const int64_t cb_base = DT == MM_INT8 ? ob / (K * N > 0 ? K * N : 1) * N : 0;
     // Tile origins (k = 0): row m0 of A (column m0 of a transposed A) and
     // column n0 of B (row n0 of a transposed B).
     const char *Atile = (const char *)((const S *)a.A + oa + (TA ? m0 : m0 * a.lda));
@@ -460,6 +457,17 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
     uint4 fa[2][FM], fb[2][FN];
+    // MatMulInteger: running row sums of A' (waves of column 0 hold every
+    // row of the tile) and column sums of B' (waves of row 0 hold every
+    // column), over the stages' K including the zero padding of the last.
+    constexpr int SA = DT == MM_INT8 ? FM : 1, SB = DT == MM_INT8 ? FN : 1;
+    int32_t rs_acc[SA], cs_acc[SB];
+#pragma unroll
+    for (int i = 0; i < SA; ++i) rs_acc[i] = 0;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) cs_acc[j] = 0;
+    const bool do_rs = DT == MM_INT8 && a.sum_a && wc == 0;
+    const bool do_cs = DT == MM_INT8 && a.sum_b && wr == 0;
     // Fragment of K-contiguous rows: chunk c of row `row`.
     auto read_k = [&](const char *Xs, int row, int c) -> uint4 {
         return *(const uint4 *)(Xs + row * BKB + ((c ^ aswz(row)) * 16));
@@ -536,6 +544,29 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 fb[slot][j].x ^= fb_x; fb[slot][j].y ^= fb_x; fb[slot][j].z ^= fb_x; fb[slot][j].w ^= fb_x;
+            }
+            // Byte sums of the 16 k this lane holds: dot products with ones.
+            if (do_rs) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const uint4 &f = fa[slot][i];
+                    int s = rs_acc[i];
+                    s = __builtin_amdgcn_sdot4((int)f.x, 0x01010101, s, false);
+                    s = __builtin_amdgcn_sdot4((int)f.y, 0x01010101, s, false);
+                    s = __builtin_amdgcn_sdot4((int)f.z, 0x01010101, s, false);
+                    rs_acc[i] = __builtin_amdgcn_sdot4((int)f.w, 0x01010101, s, false);
+                }
+            }
+            if (do_cs) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const uint4 &f = fb[slot][j];
+                    int s = cs_acc[j];
+                    s = __builtin_amdgcn_sdot4((int)f.x, 0x01010101, s, false);
+                    s = __builtin_amdgcn_sdot4((int)f.y, 0x01010101, s, false);
+                    s = __builtin_amdgcn_sdot4((int)f.z, 0x01010101, s, false);
+                    cs_acc[j] = __builtin_amdgcn_sdot4((int)f.w, 0x01010101, s, false);
+                }
             }
         }
     };
@@ -614,6 +645,26 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             for (int j = 0; j < KS / KG; ++j) {
                 if (j + 1 < KS / KG) read_frags(buf, kg + (j + 1) * KG, (j + 1) & 1);
                 mfmas(j & 1);
+            }
+        }
+    }
+
+    // MatMulInteger sums: lanes l and l + 32 held the two 16-k halves of
+    // each step; the totals go to a small LDS table read by the store loop.
+    __shared__ int32_t sums_lds[DT == MM_INT8 ? BM + BN : 1];
+    if constexpr (DT == MM_INT8) {
+        if (do_rs) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int s = rs_acc[i] + __shfl_xor(rs_acc[i], 32);
+                if (lane < 32) sums_lds[wr * WM + i * 32 + lane] = s;
+            }
+        }
+        if (do_cs) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int s = cs_acc[j] + __shfl_xor(cs_acc[j], 32);
+                if (lane < 32) sums_lds[BM + wc * WN + j * 32 + lane] = s;
             }
         }
     }
@@ -759,21 +810,25 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             if (row < M && col < N) {
                 uint4 v = *(const uint4 *)(tile + rl * (BN * OS) + (c ^ (rl & (OCPR - 1))) * 16);
                 if constexpr (DT == MM_INT8) {
-                    // Y = P - zb'[n] RA[m] - za'[m] (CB[n] - K zb'[n]), modulo
-                    // 2^32 (see KArgs); rows and the zero-point period are
-                    // below 2^31.
+                    // Over the padded reduction length Kp (zero bytes after
+                    // K, i.e. raw values 0) the kernel holds P = sum A'B',
+                    // RA = sum A' and CB = sum B'; then
+                    //   Y = P - zb' RA - za' (CB - Kp zb') - (Kp - K) za zb
+                    // modulo 2^32, with za' = za - offset_A, zb' = zb -
+                    // offset_B and raw zero points za, zb.  Rows and the
+                    // zero-point period are below 2^31.
                     const uint32_t za = int_zp(a.zpa, a.zpa_mode, a.a_signed, (uint32_t)row % (uint32_t)a.zp_rows);
-                    const uint32_t rsum = a.ra ? (uint32_t)a.ra[ra_base + row] : 0u;
-                    // Zero-byte K padding, flipped on both sides: 16384 per padded k.
-                    const uint32_t pad = (a.flip_a && a.flip_b) ? (uint32_t)((int64_t)nk * BK - (kend - kbeg)) * 16384u : 0u;
-                    uint32_t y[4] = {v.x - pad, v.y - pad, v.z - pad, v.w - pad};
+                    const uint32_t za_raw = za + (a.a_signed ? 0u : 128u);
+                    const uint32_t kp = (uint32_t)((int64_t)nk * BK), pad = kp - (uint32_t)K;
+                    const uint32_t rsum = a.sum_a ? (uint32_t)sums_lds[pass * PR + rl] : 0u;
+                    uint32_t y[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int64_t gn = col + e;
                         if (gn < N) {
                             const uint32_t zb = int_zp(a.zpb, a.zpb_mode, a.b_signed, gn);
-                            if (a.ra) y[e] -= zb * rsum;
-                            if (a.cb) y[e] -= za * ((uint32_t)a.cb[cb_base + gn] - (uint32_t)K * zb);
+                            const uint32_t csum = a.sum_b ? (uint32_t)sums_lds[BM + c * OV + e] : 0u;
+                            y[e] -= zb * rsum + za * (csum - kp * zb) + pad * za_raw * (zb + (a.b_signed ? 0u : 128u));
                         }
                     }
                     v = make_uint4(y[0], y[1], y[2], y[3]);

@@ -14,50 +14,14 @@
 //
 //   Y = sum A'B' - zb' RA[m] - za' (CB[n] - K zb')   (all modulo 2^32).
 //
-// (The tiled kernel's zero-filled K tail becomes -128 under the flip; with
-// both operands flipped the epilogue removes the 16384 each padded k adds.)
-//
-// The sums come from two small passes before the tiled kernel (only those
-// the zero points need); k_int_direct computes the definition directly for
-// tiny, unaligned or 2 GiB-spanning products.  Integer arithmetic modulo
-// 2^32 is exact and associative, so every order gives the same bits.
+// The tiled kernel (k_gemm_impl.h) forms RA and CB itself from the operand
+// fragments it feeds the matrix cores, over its padded reduction length;
+// k_int_direct computes the definition directly for tiny, unaligned or
+// 2 GiB-spanning products.  Integer arithmetic modulo 2^32 is exact and
+// associative, so every order gives the same bits.
 #include "k_gemm_impl.h"
 
 namespace mm {
-
-// RA[r] = sum_k A'[r][k] for every stored row r of A (rows of K bytes); one
-// wave per row.
-__global__ __launch_bounds__(256) void k_int_rowsum(const uint8_t *__restrict__ A, int64_t rows, int64_t K,
-                                                    uint32_t flip, int32_t *__restrict__ ra) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= rows) return;  // whole waves leave together
-    const uint8_t *row = A + r * K;
-    uint32_t s = 0;
-    for (int64_t k = lane; k < K; k += 64) s += (uint32_t)(int32_t)(int8_t)(row[k] ^ (uint8_t)flip);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += (uint32_t)__shfl_xor((int)s, off);
-    if (lane == 0) ra[r] = (int32_t)s;
-}
-
-// CB[j][n] += sum over one 256-element K slice of B'[j][k][n]; CB starts at
-// zero.  Grid: (column blocks, K slices, B matrices).
-__global__ __launch_bounds__(256) void k_int_colsum(const uint8_t *__restrict__ B, int64_t K, int64_t N,
-                                                    uint32_t flip, int32_t *__restrict__ cb) {
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
-    const int64_t j = blockIdx.z;
-    const int64_t k0 = (int64_t)blockIdx.y * 256, k1 = k0 + 256 < K ? k0 + 256 : K;
-    const uint8_t *col = B + j * K * N + n;
-    uint32_t s = 0;
-    for (int64_t k = k0; k < k1; ++k) s += (uint32_t)(int32_t)(int8_t)(col[k * N] ^ (uint8_t)flip);
-    atomicAdd((unsigned int *)&cb[j * N + n], s);
-}
-
-__global__ __launch_bounds__(256) void k_int_fill_zero(int32_t *__restrict__ p, int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0;
-}
 
 // One thread per output: the definition, in 32-bit modular arithmetic.
 __global__ __launch_bounds__(256) void k_int_direct(KArgs a) {
@@ -91,31 +55,6 @@ hipError_t launch_int_direct(const KArgs &a, hipStream_t s) {
     if (g > 65536) g = 65536;
     hipLaunchKernelGGL(k_int_direct, dim3((unsigned)g), dim3(256), 0, s, a);
     return hipGetLastError();
-}
-
-hipError_t launch_int_sums(const KArgs &a, int64_t a_rows, int64_t b_mats, int32_t *ra, int32_t *cb, hipStream_t s) {
-    if (ra && a_rows > 0) {
-        const int64_t g = (a_rows + 3) / 4;
-        if (g > 0x7fffffff) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_int_rowsum, dim3((unsigned)g), dim3(256), 0, s, (const uint8_t *)a.A, a_rows, a.K,
-                           a.flip_a, ra);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (cb && b_mats > 0 && a.N > 0) {
-        const int64_t n = b_mats * a.N;
-        hipLaunchKernelGGL(k_int_fill_zero, dim3((unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536)),
-                           dim3(256), 0, s, cb, n);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const int64_t gx = (a.N + 255) / 256, gy = (a.K + 255) / 256;
-        if (gx > 0x7fffffff || gy > 65535 || b_mats > 65535) return hipErrorInvalidValue;
-        if (gy > 0)
-            hipLaunchKernelGGL(k_int_colsum, dim3((unsigned)gx, (unsigned)gy, (unsigned)b_mats), dim3(256), 0, s,
-                               (const uint8_t *)a.B, a.K, a.N, a.flip_b, cb);
-        return hipGetLastError();
-    }
-    return hipSuccess;
 }
 
 static_assert(kNumTiles8 == 2, "launch switch must cover the INT8 tile table");

@@ -468,17 +468,11 @@ mm_status mm_int_plan_create(const int64_t *a_shape, int a_rank, const int64_t *
         delete p;
         return st;
     }
-    // Row sums of A' are needed when zb' can be non-zero, column sums of B'
-    // when za' can be (a UINT8 operand has a non-zero offset).
-    if (p->algo == MM_ALGO_GENERAL && p->K > 0) {
-        int64_t na = 1;
-        for (int i = 0; i < a_rank; ++i) na *= a_shape[i];
-        p->int_a_rows = na / p->K;
-        p->int_b_mats = p->N > 0 ? p->b_numel / (p->K * p->N) : 0;
-        p->need_ra = b_type == MM_UINT8 || b_zp_kind != MM_ZP_NONE;
-        p->need_cb = a_type == MM_UINT8 || a_zp_kind != MM_ZP_NONE;
-        p->workspace_bytes = 4 * ((p->need_ra ? p->int_a_rows : 0) + (p->need_cb ? p->int_b_mats * p->N : 0));
-    }
+    // The tiled kernel needs the row sums of A' when zb' can be non-zero and
+    // the column sums of B' when za' can be (a UINT8 operand has a non-zero
+    // offset); it forms them itself, so no workspace is needed.
+    p->need_ra = b_type == MM_UINT8 || b_zp_kind != MM_ZP_NONE;
+    p->need_cb = a_type == MM_UINT8 || a_zp_kind != MM_ZP_NONE;
     *out = p;
     return MM_OK;
 }

@@ -46,11 +46,10 @@ struct mm_plan_s {
     int64_t ldc = 0;
 
     // MatMulInteger (mm_int_plan_create): operand types, zero-point kinds and
-    // the row / column sum tables the zero points need (in the workspace).
+    // the row / column sums the zero points need (formed by the tiled kernel).
     bool is_int = false;
     int a_type = 0, b_type = 0;
     int zpa_kind = 0, zpb_kind = 0;
-    int64_t int_a_rows = 0, int_b_mats = 0;
     bool need_ra = false, need_cb = false;
 
     // Plan-owned constant B (mm_plan_set_constant_b).

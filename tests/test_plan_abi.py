@@ -398,23 +398,22 @@ def test_gemm_execute_checks_before_any_gpu_call():
     (mm.INT8, mm.INT8, mm.ZP_NONE, mm.ZP_VECTOR, True, False),
     (mm.UINT8, mm.UINT8, mm.ZP_VECTOR, mm.ZP_SCALAR, True, True),
 ])
-def test_int_plan_workspace(ta, tb, zka, zkb, ra, cb):
-    """Row sums of A (one per stored row) are kept only when zb' can be
-    non-zero, column sums of B (one per column of each stored B matrix) only
-    when za' can be."""
+def test_int_plan_shapes(ta, tb, zka, zkb, ra, cb):
+    """Every signedness / zero-point combination plans the tiled kernel with
+    no workspace (the kernel forms the row and column sums it needs)."""
     p = mm.IntPlan((4, 1, 64, 128), (3, 128, 96), ta, tb, zka, zkb)
     assert p.output_shape == (4, 3, 64, 96)
     inf = p.info()
     assert inf["dtype"] == mm.INT32 and inf["algo"] == mm.ALGO_GENERAL and not inf["folded"]
     assert inf["min_bytes"] == 4 * 64 * 128 + 3 * 128 * 96 + 4 * 4 * 3 * 64 * 96
-    assert p.workspace_bytes == 4 * ((4 * 64 if ra else 0) + (3 * 96 if cb else 0))
+    assert p.workspace_bytes == 0
 
 
 def test_int_plan_algorithms():
     u8, s8 = mm.UINT8, mm.INT8
     f = mm.IntPlan((8, 64, 256), (256, 128), u8, s8)
     assert f.info()["folded"] and f.info()["kernel_m"] == 512 and f.algo == mm.ALGO_GENERAL
-    assert f.workspace_bytes == 4 * 128  # column sums of the one shared B
+    assert f.workspace_bytes == 0
     assert mm.IntPlan((1, 4096), (4096, 4096), s8, s8).algo == mm.ALGO_GENERAL  # no skinny kernels
     assert mm.IntPlan((4096, 4096), (4096, 1), s8, s8).algo == mm.ALGO_GENERAL
     assert mm.IntPlan((8, 16), (16, 8), s8, s8).algo == mm.ALGO_DIRECT
