@@ -293,8 +293,10 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
 //   per-stage barrier.
 // ---------------------------------------------------------------------------
 
+// IFL (MatMulInteger only): bit 0 = A is UINT8, bit 1 = B is UINT8; those
+// operands' fragments are sign-flipped after every read.
 template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool SPLIT, bool TA, bool TB,
-          bool GEMM>
+          bool GEMM, int IFL = 0>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using E = Elem<DT>;
@@ -340,7 +342,12 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     auto aswz = [](int row) { return CA == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
     auto mswz = [](int k, int cpr) {  // k-row of cpr chunks
         if constexpr (ES == 4) return cpr >= 16 ? 8 * ((k >> 2) & 1) : 0;  // 8 chunks: no room to move
-        else if constexpr (ES == 1) return k & 7;  // a transposing 8-bit read covers 8 consecutive k-rows
+        // A transposing 8-bit read by 32 lanes covers 8 consecutive k-rows and
+        // two neighbouring chunks (c, c ^ 1): even shifts put the 16 pieces
+        // on 16 distinct chunk positions of the 256-byte bank window (for
+        // 8-chunk rows the window holds two rows, so rows of one parity
+        // take the four even shifts).
+        else if constexpr (ES == 1) return cpr >= 16 ? 2 * (k & 7) : 2 * ((k >> 1) & 3);
         else return cpr >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
     };
     static_assert(DT != MM_INT8 || (KG == 1 && !SPLIT), "INT8: no K groups, no split-K");
@@ -429,21 +436,34 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         }
     }
 
+    // Lanes whose rows / columns lie outside the output never load.
+#pragma unroll
+    for (int q = 0; q < A_INSTR; ++q)
+        if (!a_ok[q]) a_off[q] = kOutOfRange;
+#pragma unroll
+    for (int q = 0; q < B_INSTR; ++q)
+        if (!b_ok[q]) b_off[q] = kOutOfRange;
+
     auto issue_stage = [&](int st) {
         if (!producer) return;
         const uint32_t sbase = lds_base + (st % STAGES) * STAGE_BYTES;
         const int64_t k0 = kbeg + (int64_t)st * BK;
         const i32x4 ra = buffer_rsrc(Atile + (TA ? k0 * a.lda : k0) * ES);
-#pragma unroll
-        for (int q = 0; q < A_INSTR; ++q) {
-            const bool ok = a_ok[q] && k0 + a_k[q] < kend;
-            load_to_lds16(ra, sbase + (wave * A_INSTR + q) * 1024, ok ? a_off[q] : kOutOfRange);
-        }
         const i32x4 rb = buffer_rsrc(Btile + (TB ? k0 : k0 * a.ldb) * ES);
+        if (k0 + BK <= kend) {  // a whole stage: no K check per load
 #pragma unroll
-        for (int q = 0; q < B_INSTR; ++q) {
-            const bool ok = b_ok[q] && k0 + b_k[q] < kend;
-            load_to_lds16(rb, sbase + A_BYTES + (wave * B_INSTR + q) * 1024, ok ? b_off[q] : kOutOfRange);
+            for (int q = 0; q < A_INSTR; ++q) load_to_lds16(ra, sbase + (wave * A_INSTR + q) * 1024, a_off[q]);
+#pragma unroll
+            for (int q = 0; q < B_INSTR; ++q)
+                load_to_lds16(rb, sbase + A_BYTES + (wave * B_INSTR + q) * 1024, b_off[q]);
+        } else {
+            const int rem = (int)(kend - k0);  // 0 < rem < BK
+#pragma unroll
+            for (int q = 0; q < A_INSTR; ++q)
+                load_to_lds16(ra, sbase + (wave * A_INSTR + q) * 1024, a_k[q] < rem ? a_off[q] : kOutOfRange);
+#pragma unroll
+            for (int q = 0; q < B_INSTR; ++q)
+                load_to_lds16(rb, sbase + A_BYTES + (wave * B_INSTR + q) * 1024, b_k[q] < rem ? b_off[q] : kOutOfRange);
         }
     };
 
@@ -457,17 +477,24 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
     uint4 fa[2][FM], fb[2][FN];
-    // MatMulInteger: running row sums of A' (waves of column 0 hold every
-    // row of the tile) and column sums of B' (waves of row 0 hold every
-    // column), over the stages' K including the zero padding of the last.
+    // MatMulInteger: running row sums of A' and column sums of B' over the
+    // stages' K, including the zero padding of the last.  The WGN waves that
+    // share a row block take turns by MFMA step (step ks goes to the wave
+    // with wc == ks % WGN), as do the WGM waves that share a column block;
+    // their partial sums meet in LDS.
     constexpr int SA = DT == MM_INT8 ? FM : 1, SB = DT == MM_INT8 ? FN : 1;
     int32_t rs_acc[SA], cs_acc[SB];
 #pragma unroll
     for (int i = 0; i < SA; ++i) rs_acc[i] = 0;
 #pragma unroll
     for (int j = 0; j < SB; ++j) cs_acc[j] = 0;
-    const bool do_rs = DT == MM_INT8 && a.sum_a && wc == 0;
-    const bool do_cs = DT == MM_INT8 && a.sum_b && wr == 0;
+    const bool do_rs = DT == MM_INT8 && a.sum_a;
+    const bool do_cs = DT == MM_INT8 && a.sum_b;
+    __shared__ int32_t sums_lds[DT == MM_INT8 ? BM + BN : 1];
+    if constexpr (DT == MM_INT8) {
+        // Cleared before the main loop's first barrier, added to after it.
+        for (int x = tid; x < BM + BN; x += 64 * NW) sums_lds[x] = 0;
+    }
     // Fragment of K-contiguous rows: chunk c of row `row`.
     auto read_k = [&](const char *Xs, int row, int c) -> uint4 {
         return *(const uint4 *)(Xs + row * BKB + ((c ^ aswz(row)) * 16));
@@ -536,17 +563,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             else fb[slot][j] = read_mn(Bs, RBB, CPR, wc * WN + j * 32, ks, c);
         }
         if constexpr (DT == MM_INT8) {  // UINT8 operands: x - 128 in INT8
-            const uint32_t fa_x = a.flip_a, fb_x = a.flip_b;
+            constexpr uint32_t X = 0x80808080u;
+            if constexpr (IFL & 1) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                fa[slot][i].x ^= fa_x; fa[slot][i].y ^= fa_x; fa[slot][i].z ^= fa_x; fa[slot][i].w ^= fa_x;
+                for (int i = 0; i < FM; ++i) {
+                    fa[slot][i].x ^= X; fa[slot][i].y ^= X; fa[slot][i].z ^= X; fa[slot][i].w ^= X;
+                }
             }
+            if constexpr (IFL & 2) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                fb[slot][j].x ^= fb_x; fb[slot][j].y ^= fb_x; fb[slot][j].z ^= fb_x; fb[slot][j].w ^= fb_x;
+                for (int j = 0; j < FN; ++j) {
+                    fb[slot][j].x ^= X; fb[slot][j].y ^= X; fb[slot][j].z ^= X; fb[slot][j].w ^= X;
+                }
             }
             // Byte sums of the 16 k this lane holds: dot products with ones.
-            if (do_rs) {
+            if (do_rs && ks % WGN == wc) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
                     const uint4 &f = fa[slot][i];
@@ -557,7 +588,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
                     rs_acc[i] = __builtin_amdgcn_sdot4((int)f.w, 0x01010101, s, false);
                 }
             }
-            if (do_cs) {
+            if (do_cs && ks % WGM == wr) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     const uint4 &f = fb[slot][j];
@@ -650,21 +681,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     }
 
     // MatMulInteger sums: lanes l and l + 32 held the two 16-k halves of
-    // each step; the totals go to a small LDS table read by the store loop.
-    __shared__ int32_t sums_lds[DT == MM_INT8 ? BM + BN : 1];
+    // each step; the waves' partial totals are added into the LDS table the
+    // store loop reads (integer adds: the order does not matter).
     if constexpr (DT == MM_INT8) {
         if (do_rs) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int s = rs_acc[i] + __shfl_xor(rs_acc[i], 32);
-                if (lane < 32) sums_lds[wr * WM + i * 32 + lane] = s;
+                if (lane < 32) atomicAdd(&sums_lds[wr * WM + i * 32 + lane], s);
             }
         }
         if (do_cs) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int s = cs_acc[j] + __shfl_xor(cs_acc[j], 32);
-                if (lane < 32) sums_lds[BM + wc * WN + j * 32 + lane] = s;
+                if (lane < 32) atomicAdd(&sums_lds[BM + wc * WN + j * 32 + lane], s);
             }
         }
     }
@@ -868,8 +899,13 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
         // INT8 runs only this kernel, unsplit; the plan and execute layer
         // send other cases to the direct integer kernel.
         if (!(vec && fits) || split) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false>), g,
-                           dim3(64 * WGM * WGN * KG), 0, s, a);
+        const dim3 blk(64 * WGM * WGN * KG);
+        switch ((a.flip_a ? 1 : 0) | (a.flip_b ? 2 : 0)) {
+        case 0: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false, 0>), g, blk, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false, 1>), g, blk, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false, 2>), g, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false, 3>), g, blk, 0, s, a); break;
+        }
         return hipGetLastError();
     } else if (vec && fits) {
         const dim3 blk(64 * WGM * WGN * KG);

@@ -57,7 +57,7 @@ hipError_t launch_int_direct(const KArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-static_assert(kNumTiles8 == 2, "launch switch must cover the INT8 tile table");
+static_assert(kNumTiles8 == 3, "launch switch must cover the INT8 tile table");
 
 hipError_t launch_general_int(int tile, const KArgs &a, hipStream_t s) {
     switch (tile) {
@@ -67,6 +67,9 @@ hipError_t launch_general_int(int tile, const KArgs &a, hipStream_t s) {
     case 1:
         return launch_tile<MM_INT8, kTiles8[1].bm, kTiles8[1].bn, kTiles8[1].wgm, kTiles8[1].wgn, kTiles8[1].bkb,
                            kTiles8[1].stages, kTiles8[1].producers, kTiles8[1].kgroups>(true, false, a, s);
+    case 2:
+        return launch_tile<MM_INT8, kTiles8[2].bm, kTiles8[2].bn, kTiles8[2].wgm, kTiles8[2].wgn, kTiles8[2].bkb,
+                           kTiles8[2].stages, kTiles8[2].producers, kTiles8[2].kgroups>(true, false, a, s);
     }
     return hipErrorInvalidValue;
 }

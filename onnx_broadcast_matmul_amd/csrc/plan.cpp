@@ -66,7 +66,7 @@ static double tile_quality(int dtype, int index) {
     static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5};
     static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15};
     static const double q64[kNumTiles64] = {1.0, 0.8};
-    static const double q8[kNumTiles8] = {1.0, 0.75};
+    static const double q8[kNumTiles8] = {1.0, 0.75, 1.0};
     if (dtype == MM_DOUBLE) return q64[index];
     if (dtype == MM_INT32) return q8[index];
     return dtype == MM_FLOAT ? q32[index] : q16[index];
@@ -473,6 +473,10 @@ mm_status mm_int_plan_create(const int64_t *a_shape, int a_rank, const int64_t *
     // offset); it forms them itself, so no workspace is needed.
     p->need_ra = b_type == MM_UINT8 || b_zp_kind != MM_ZP_NONE;
     p->need_cb = a_type == MM_UINT8 || a_zp_kind != MM_ZP_NONE;
+    // The 256 x 256 tile in the wave layout that holds fewer fragments of
+    // the sign-flipped operand (entry 2: two A fragments per wave).
+    if (p->algo == MM_ALGO_GENERAL && !(opt && opt->tile > 0) && (p->tile == 0 || p->tile == 2))
+        p->tile = a_type == MM_UINT8 && b_type == MM_INT8 ? 2 : 0;
     *out = p;
     return MM_OK;
 }

@@ -53,9 +53,13 @@ constexpr int kTransTiles16[] = {0, 5, 4};
 constexpr int kTransTiles32[] = {4, 2};
 
 // INT8 entries (MatMulInteger; B rows need at least 128 bytes per stage row).
+// The two 256 x 256 entries differ in wave layout: 2 x 4 waves hold two B
+// fragments each, 4 x 2 waves two A fragments, so a UINT8 A (whose
+// fragments are sign-flipped after every read) takes the second.
 constexpr TileCfg kTiles8[] = {
     {256, 256, 2, 4, 128, 2, 4, 1},
     {128, 128, 2, 2, 128, 2, 4, 1},
+    {256, 256, 4, 2, 128, 2, 4, 1},
 };
 
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);

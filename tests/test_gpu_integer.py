@@ -92,7 +92,7 @@ def test_int_signedness_and_zero_points(ta, tb, zka, zkb, algo, dev):
     int_parity((2, 1, 200, 400), (3, 400, 272), ta, tb, zka, zkb, dev, algo=algo, seed=1)
 
 
-@pytest.mark.parametrize("tile", [1, 2])
+@pytest.mark.parametrize("tile", [1, 2, 3])
 @pytest.mark.parametrize("ta,tb", [("u8", "s8"), ("s8", "u8")], ids=lambda t: t)
 def test_int_every_tile(tile, ta, tb, dev):
     int_parity((700, 1024), (1024, 600), ta, tb, "vector", "vector", dev, algo=mm.ALGO_GENERAL, tile=tile, seed=2)

@@ -423,7 +423,11 @@ def test_int_plan_algorithms():
     assert d.algo == mm.ALGO_DIRECT and d.workspace_bytes == 0
     t = mm.IntPlan((512, 512), (512, 512), u8, u8, force_algo=mm.ALGO_GENERAL, tile=2)
     assert t.info()["tile"] == 2
-    assert mm.tile_configs(mm.INT8) == mm.tile_configs(mm.UINT8) == [(256, 256, 128), (128, 128, 128)]
+    assert mm.tile_configs(mm.INT8) == mm.tile_configs(mm.UINT8) == [(256, 256, 128), (128, 128, 128), (256, 256, 128)]
+    # the 256 x 256 entry whose waves hold fewer fragments of a sign-flipped A
+    assert mm.IntPlan((4096, 4096), (4096, 4096), u8, s8).info()["tile"] == 3
+    assert mm.IntPlan((4096, 4096), (4096, 4096), s8, u8).info()["tile"] == 1
+    assert mm.IntPlan((4096, 4096), (4096, 4096), u8, u8).info()["tile"] == 1
     assert mm.tile_configs(mm.INT32) == mm.tile_configs(mm.INT8)
 
 
@@ -434,7 +438,7 @@ def test_int_plan_algorithms():
     (dict(zkb=-1), mm.ERR_BAD_OPTION),
     (dict(force_algo=mm.ALGO_SKINNY_M), mm.ERR_BAD_OPTION),
     (dict(force_algo=mm.ALGO_SPLIT_K), mm.ERR_BAD_OPTION),
-    (dict(force_algo=mm.ALGO_GENERAL, tile=3), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_GENERAL, tile=4), mm.ERR_BAD_OPTION),
     (dict(sb=(100, 64)), mm.ERR_K_MISMATCH),
     (dict(sa=(3, 64, 128), sb=(2, 128, 64)), mm.ERR_BROADCAST),
 ])
