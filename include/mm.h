@@ -172,7 +172,9 @@ mm_status mm_execute(mm_plan_t plan, const void *A, const void *B, void *Y, void
  * hipStream_t; NULL = null stream), and returns once the copy has completed:
  * the caller may then reuse or free B.  Calling it again replaces the
  * contents.  Errors: MM_ERR_NULL_ARG (NULL plan, or NULL B with numel > 0),
- * MM_ERR_SIZE (numel differs from the planned B's element count),
+ * MM_ERR_BAD_OPTION (a Gemm or MatMulInteger plan: constant B serves
+ * mm_execute only), MM_ERR_SIZE (numel differs from the planned B's element
+ * count),
  * MM_ERR_ALLOC, MM_ERR_HIP (copy failed, or the plan already holds B on
  * another device).  The storage is freed by mm_plan_destroy.
  *

@@ -157,7 +157,8 @@ def torch_dtype_code(dt) -> int:
 def torch_dtype(code: int):
     import torch
 
-    return {FLOAT: torch.float32, FLOAT16: torch.float16, BFLOAT16: torch.bfloat16, DOUBLE: torch.float64}[code]
+    return {FLOAT: torch.float32, FLOAT16: torch.float16, BFLOAT16: torch.bfloat16, DOUBLE: torch.float64,
+            INT32: torch.int32, INT8: torch.int8, UINT8: torch.uint8}[code]
 
 
 def tile_configs(dtype: int):

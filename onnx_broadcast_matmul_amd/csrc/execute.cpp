@@ -216,6 +216,8 @@ mm_status mm_gemm_execute(mm_plan_t p, const void *A, const void *B, const void 
 mm_status mm_plan_set_constant_b(mm_plan_t p, const void *B, int64_t numel, void *stream) {
     clear_error();
     if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
+    if (p->is_gemm || p->is_int)
+        return fail(MM_ERR_BAD_OPTION, "constant B is for MatMul plans (it runs through mm_execute)");
     if (numel != p->b_numel)
         return fail(MM_ERR_SIZE, "constant B has %lld elements; the planned B has %lld", (long long)numel,
                     (long long)p->b_numel);

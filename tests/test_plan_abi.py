@@ -335,6 +335,11 @@ def test_constant_b_errors_before_any_gpu_call():
     assert L.mm_plan_has_constant_b(None) == 0
     assert L.mm_execute_constant_b(None, None, None, None) == mm.ERR_NULL_ARG
     assert not p.has_constant_b
+    # constant B serves mm_execute only: Gemm and MatMulInteger plans refuse it
+    for q in (mm.GemmPlan((64, 96), (96, 80), mm.FLOAT), mm.IntPlan((64, 96), (96, 80), mm.UINT8, mm.INT8)):
+        with pytest.raises(mm.MMError) as e:
+            q.set_constant_b_ptr(0, 96 * 80)
+        assert e.value.status == mm.ERR_BAD_OPTION and not q.has_constant_b
 
 
 # ---------------------------------------------------------------- Gemm
