@@ -163,7 +163,8 @@ static void plan_tail(mm_plan_s *p) {
     }
 }
 
-// Smallest-padding tile for split-K (its output is tiny by construction).
+// Smallest-padding tile for split-K (its output is tiny by construction);
+// among equally padded tiles, the one of higher relative throughput.
 static int choose_split_tile(int dtype, int64_t M, int64_t N, bool gemm = false) {
     int best = -1;
     double best_pad = -1.0;
@@ -171,7 +172,8 @@ static int choose_split_tile(int dtype, int64_t M, int64_t N, bool gemm = false)
         if (!tile_allowed(dtype, i, gemm)) continue;
         const TileCfg *t = tile_entry(dtype, i);
         double pad = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
-        if (pad > best_pad + 1e-9) {
+        const bool tie = best >= 0 && fabs(pad - best_pad) <= 1e-9;
+        if (pad > best_pad + 1e-9 || (tie && tile_quality(dtype, i) > tile_quality(dtype, best))) {
             best_pad = pad;
             best = i;
         }
