@@ -411,8 +411,8 @@ constexpr int kSkN8Rows = 16;  // rows per workgroup
 
 template <int DT>
 __global__ __launch_bounds__(512) void k_skinny_n8(KArgs a) {
-    constexpr int RB = 1;  // 16-row blocks per wave (two, with 32 rows per workgroup, measured 13 % slower)
 #if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int RB = 1;  // 16-row blocks per wave (two, with 32 rows per workgroup, measured 13 % slower)
     using E = Elem<DT>;
     using S = typename E::S;
     static_assert(sizeof(S) == 2, "16-bit element types");
