@@ -99,15 +99,19 @@ static mm_status execute_impl(mm_plan_s *p, const void *A, const void *B, const 
             e = launch_general_f64(p->tile, al, false, a, s);
         } else if (p->tail_col > 0) {
             // Columns [0, tail_col) in whole rounds of `tile`, then the rest
-            // with `tail_tile`; both read B and write Y with the full pitch N.
+            // with `tail_tile`; both read B and write Y (and a Gemm's C) with
+            // their full pitches.  Column c of B' is column c of B, or row c
+            // of a transposed B; a per-column or full C moves by c columns.
             KArgs m = a;
             m.N = p->tail_col;
             e = launch_general(p->dtype, p->tile, al, false, m, s);
             if (e == hipSuccess) {
                 KArgs r = a;
                 r.N = p->N - p->tail_col;
-                r.B = (const char *)B + p->tail_col * es;
+                r.B = (const char *)B + p->tail_col * (p->tb ? a.ldb : 1) * es;
                 r.Y = (char *)Y + p->tail_col * es;
+                if (p->is_gemm && (p->c_mode == kBiasRow || p->c_mode == kBiasFull))
+                    r.C = (const char *)C + p->tail_col * es;
                 Align ar = al;
                 ar.b = al.b && aligned16(r.B);
                 r.y_vec = al.y && aligned16(r.Y) && (r.N * es) % 16 == 0;

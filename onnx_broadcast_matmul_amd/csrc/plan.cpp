@@ -137,7 +137,7 @@ static int64_t gcd64(int64_t a, int64_t b) {
 static void plan_tail(mm_plan_s *p) {
     p->tail_col = 0;
     p->tail_tile = -1;
-    if (p->dtype == MM_DOUBLE || p->is_gemm || p->is_int) return;
+    if (p->dtype == MM_DOUBLE || p->is_int) return;
     const TileCfg *t = tile_entry(p->dtype, p->tile);
     if (tile_wgs_per_cu(t) != 1) return;
     const int64_t rows = p->batch * cdiv(p->kernel_m, t->bm);
@@ -149,7 +149,7 @@ static void plan_tail(mm_plan_s *p) {
     const int64_t c_main = ((tn - 1) / step) * step;  // whole rounds, at least one column left over
     if (c_main <= 0) return;
     const int64_t n_rem = p->N - c_main * t->bn;
-    const int rt = choose_tile(p->dtype, p->batch, p->kernel_m, n_rem);
+    const int rt = choose_tile(p->dtype, p->batch, p->kernel_m, n_rem, p->is_gemm);
     const TileCfg *r = tile_entry(p->dtype, rt);
     const int64_t T_rem = p->batch * cdiv(p->kernel_m, r->bm) * cdiv(n_rem, r->bn);
     const double without = (double)cdiv(T, kNumCUs);

@@ -80,9 +80,10 @@ def as_torch(storage: np.ndarray, dtype: int):
     """CPU torch tensor viewing the same bits with the element type."""
     import torch
 
+    shape = np.shape(storage)  # ascontiguousarray turns a 0-d array into 1-d
     if dtype == FLOAT or dtype == DOUBLE:
-        return torch.from_numpy(np.ascontiguousarray(storage))
-    t = torch.from_numpy(np.ascontiguousarray(storage).view(np.int16))
+        return torch.from_numpy(np.ascontiguousarray(storage)).reshape(shape)
+    t = torch.from_numpy(np.ascontiguousarray(storage).view(np.int16)).reshape(shape)
     return t.view(torch.float16 if dtype == FLOAT16 else torch.bfloat16)
 
 

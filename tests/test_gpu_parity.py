@@ -387,6 +387,50 @@ def test_gemm_exact_unaligned_and_zero_k(dt, ta, tb, dev):
     assert rep.ok, str(rep)
 
 
+@pytest.mark.parametrize("ta,tb,layout", [(0, 1, ("N",)), (1, 0, ("M", "N")), (1, 1, ("M", 1)), (0, 0, ())],
+                         ids=["t01-colbias", "t10-fullC", "t11-rowbias", "t00-scalar"])
+def test_gemm_tail_split(ta, tb, layout, dev):
+    """Last-round balancing for Gemm: columns [0, tail_col) run with the
+    plan's tile and the rest with the tail tile, with B (or the rows of a
+    transposed B) and a per-column or full C moved to the second launch's
+    first column.  Small-integer inputs and integer alpha / beta: the result
+    equals, bit for bit, each column range of a single launch forced to the
+    corresponding tile, and the oracle exactly on outputs around the
+    boundary."""
+    dt = mm.BFLOAT16
+    M, N, K = 8192, 11000, 128
+    sa = (K, M) if ta else (M, K)
+    sb = (N, K) if tb else (K, N)
+    cs = _cs(layout, M, N)
+    a = synth.generate(sa, dt, ("int",), [32, 0])
+    b = synth.generate(sb, dt, ("int",), [32, 1])
+    c = synth.generate(cs, dt, ("int",), [32, 2])
+    plan = mm.GemmPlan(sa, sb, dt, ta, tb, cs, 2.0, -1.0)
+    inf = plan.info()
+    assert plan.algo == mm.ALGO_GENERAL and inf["tail_col"] > 0, inf
+    cut = inf["tail_col"]
+    A, B, C = (synth.as_torch(x, dt).to(dev) for x in (a, b, c))
+
+    def run(p):
+        Y = _sentinel((M, N), dt, dev)
+        p.execute(A, B, Y, C)
+        torch.cuda.synchronize()
+        return synth.from_torch(Y)
+
+    y = run(plan)
+    ym = run(mm.GemmPlan(sa, sb, dt, ta, tb, cs, 2.0, -1.0, force_algo=mm.ALGO_GENERAL, tile=inf["tile"]))
+    yr = run(mm.GemmPlan(sa, sb, dt, ta, tb, cs, 2.0, -1.0, force_algo=mm.ALGO_GENERAL, tile=inf["tail_tile"]))
+    assert np.array_equal(y[:, :cut], ym[:, :cut])
+    assert np.array_equal(y[:, cut:], yr[:, cut:])
+    rng = np.random.default_rng(4)
+    rows = rng.integers(0, M, 400)
+    cols = np.concatenate([rng.integers(0, N, 200), rng.integers(cut - 8, min(N, cut + 8), 200)])
+    idx = np.unique(rows * N + cols)
+    o = oracle.gemm_at(a, b, dt, idx, bool(ta), bool(tb), c, 2.0, -1.0)
+    rep = check(y.reshape(-1)[idx], o, dt, K, abs_max(a, dt), abs_max(b, dt), exact=True)
+    assert rep.ok, str(rep)
+
+
 def test_gemm_linear_layer_full_size(dev):
     """The transformer projection as a linear layer: Y = X W^T + b with
     X [8192, 4096], W [11008, 4096] (stored [N, K]) and a per-column bias, in
