@@ -206,6 +206,24 @@ mm_status mm_int_execute(mm_plan_t p, const void *A, const void *B, const void *
     }
     a.sum_a = p->need_ra;
     a.sum_b = p->need_cb;
+    if (p->tail_col > 0) {
+        // Columns [0, tail_col) in whole rounds of `tile`, then the rest with
+        // `tail_tile` (B, Y and a per-column B zero point moved by tail_col
+        // columns; tail_col is a multiple of 256, so alignment holds).
+        KArgs m = a;
+        m.N = p->tail_col;
+        e = launch_general_int(p->tile, m, s);
+        if (e == hipSuccess) {
+            KArgs r = a;
+            r.N = p->N - p->tail_col;
+            r.B = (const uint8_t *)B + p->tail_col;
+            r.Y = (int32_t *)Y + p->tail_col;
+            if (p->zpb_kind == MM_ZP_VECTOR) r.zpb = (const uint8_t *)zb + p->tail_col;
+            r.y_vec = aligned16(r.Y) && (r.N * 4) % 16 == 0;
+            e = launch_general_int(p->tail_tile, r, s);
+        }
+        return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
+    }
     e = launch_general_int(p->tile, a, s);
     return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
 }

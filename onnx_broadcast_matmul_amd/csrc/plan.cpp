@@ -137,7 +137,7 @@ static int64_t gcd64(int64_t a, int64_t b) {
 static void plan_tail(mm_plan_s *p) {
     p->tail_col = 0;
     p->tail_tile = -1;
-    if (p->dtype == MM_DOUBLE || p->is_int) return;
+    if (p->dtype == MM_DOUBLE) return;
     const TileCfg *t = tile_entry(p->dtype, p->tile);
     if (tile_wgs_per_cu(t) != 1) return;
     const int64_t rows = p->batch * cdiv(p->kernel_m, t->bm);
@@ -476,7 +476,9 @@ mm_status mm_int_plan_create(const int64_t *a_shape, int a_rank, const int64_t *
     p->need_ra = b_type == MM_UINT8 || b_zp_kind != MM_ZP_NONE;
     p->need_cb = a_type == MM_UINT8 || a_zp_kind != MM_ZP_NONE;
     // The 256 x 256 tile in the wave layout that holds fewer fragments of
-    // the sign-flipped operand (entry 2: two A fragments per wave).
+    // the sign-flipped operand (entry 2: two A fragments per wave); the
+    // last-round balancing planned for entry 0 holds for entry 2 (same
+    // block tile).
     if (p->algo == MM_ALGO_GENERAL && !(opt && opt->tile > 0) && (p->tile == 0 || p->tile == 2))
         p->tile = a_type == MM_UINT8 && b_type == MM_INT8 ? 2 : 0;
     *out = p;

@@ -150,6 +150,36 @@ def test_int_wraps_modulo_2_32(dev):
     assert oracle.matmul_integer_at(a, b, [7])[0] == want and (y == want).all()
 
 
+@pytest.mark.parametrize("ta,tb,zka,zkb", [("u8", "s8", "scalar", "vector"), ("s8", "u8", "vector", "vector")],
+                         ids=["u8s8", "s8u8"])
+def test_int_tail_split(ta, tb, zka, zkb, dev):
+    """Last-round balancing: columns [0, tail_col) run with the plan's tile
+    and the rest with the tail tile, B, Y and a per-column B zero point
+    moved by tail_col columns.  The result equals single launches forced to
+    either tile and the oracle on outputs around the boundary."""
+    sa, sb = (16, 512, 256), (256, 11008)
+    sa_, sb_ = SIGN[ta], SIGN[tb]
+    a = synth.generate_int(sa, sa_, [33, 0])
+    b = synth.generate_int(sb, sb_, [33, 1])
+    za = _zero_point(zka, sa_, 512, [33, 2])
+    zb = _zero_point(zkb, sb_, 11008, [33, 3])
+    plan = mm.IntPlan(sa, sb, CODE[sa_], CODE[sb_], ZP[zka], ZP[zkb])
+    inf = plan.info()
+    assert plan.algo == mm.ALGO_GENERAL and inf["tail_col"] > 0, inf
+    cut = inf["tail_col"]
+    y = int_run(plan, a, b, za, zb, dev).reshape(-1, 11008)
+    for t in (inf["tile"], inf["tail_tile"]):
+        single = mm.IntPlan(sa, sb, CODE[sa_], CODE[sb_], ZP[zka], ZP[zkb], force_algo=mm.ALGO_GENERAL, tile=t)
+        ys = int_run(single, a, b, za, zb, dev).reshape(-1, 11008)
+        part = slice(0, cut) if t == inf["tile"] else slice(cut, None)
+        np.testing.assert_array_equal(y[:, part], ys[:, part])
+    rng = np.random.default_rng(5)
+    rows = rng.integers(0, 8192, 300)
+    cols = np.concatenate([rng.integers(0, 11008, 150), rng.integers(cut - 8, cut + 8, 150)])
+    idx = np.unique(rows * 11008 + cols)
+    np.testing.assert_array_equal(y.reshape(-1)[idx], oracle.matmul_integer_at(a, b, idx, za, zb))
+
+
 def test_int_full_size_projection(dev):
     """The quantized transformer projection at full size, in the
     configuration the benchmark times, on sampled outputs."""
