@@ -284,6 +284,13 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
 //   receives column i, i.e. four consecutive k of one column -- two such
 //   reads give the eight k values of a 32x32x16 operand.  FP32 B operands
 //   are plain 4-byte reads of one column per lane.
+// * MatMulInteger (INT8): a 128-byte stage is 128 k.  B operands come from
+//   ds_read_b64_tr_b8 (in each 16-lane group, lanes 2r and 2r + 1 address
+//   the two halves of row r of an 8 x 16 byte block, lane i receives column
+//   i; two reads give the 16 k of a 32x32x32 operand).  UINT8 fragments are
+//   sign-flipped into INT8, the waves form the row / column byte sums the
+//   zero points need, accumulation is INT32 (modulo 2^32), and the store
+//   loop applies the zero-point terms per output chunk.
 // * Only waves 0..PW-1 issue the direct loads.  Waves are dealt to the four
 //   SIMDs round-robin, so each SIMD pairs a producer with a wave that only
 //   computes: while a producer waits on a full memory queue, its partner
