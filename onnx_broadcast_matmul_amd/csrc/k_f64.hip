@@ -202,7 +202,19 @@ __global__ __launch_bounds__(256) void k_direct_f64(KArgs a) {
         const double *ap = A + oa + m * K;
         const double *bp = B + ob + n;
         double acc = 0.0;
-        for (int64_t k = 0; k < K; ++k) acc = fma(ap[k], bp[k * N], acc);
+        // Ascending k; the loads of 16 k are issued together (same order).
+        int64_t k = 0;
+        for (; k + 16 <= K; k += 16) {
+            double av[16], bv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                av[u] = ap[k + u];
+                bv[u] = bp[(k + u) * N];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) acc = fma(av[u], bv[u], acc);
+        }
+        for (; k < K; ++k) acc = fma(ap[k], bp[k * N], acc);
         Y[idx] = acc;
     }
 }

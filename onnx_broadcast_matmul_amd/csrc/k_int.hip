@@ -39,12 +39,25 @@ __global__ __launch_bounds__(256) void k_int_direct(KArgs a) {
         // zero points as raw values (int_zp subtracts the UINT8 offset, added back here)
         const uint32_t za = int_zp(a.zpa, a.zpa_mode, a.a_signed, m % a.zp_rows) + (a.a_signed ? 0u : 128u);
         const uint32_t zb = int_zp(a.zpb, a.zpb_mode, a.b_signed, n) + (a.b_signed ? 0u : 128u);
+        auto term = [&](uint8_t x, uint8_t y) {
+            const int32_t av = a.a_signed ? (int32_t)(int8_t)x : (int32_t)x;
+            const int32_t bv = a.b_signed ? (int32_t)(int8_t)y : (int32_t)y;
+            return ((uint32_t)av - za) * ((uint32_t)bv - zb);
+        };
+        // The loads of 16 k are issued together so their latencies overlap.
         uint32_t acc = 0;
-        for (int64_t k = 0; k < K; ++k) {
-            const int32_t av = a.a_signed ? (int32_t)(int8_t)ap[k] : (int32_t)ap[k];
-            const int32_t bv = a.b_signed ? (int32_t)(int8_t)bp[k * N] : (int32_t)bp[k * N];
-            acc += ((uint32_t)av - za) * ((uint32_t)bv - zb);
+        int64_t k = 0;
+        for (; k + 16 <= K; k += 16) {
+            uint8_t xv[16], yv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                xv[u] = ap[k + u];
+                yv[u] = bp[(k + u) * N];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) acc += term(xv[u], yv[u]);
         }
+        for (; k < K; ++k) acc += term(ap[k], bp[k * N]);
         ((int32_t *)a.Y)[idx] = (int32_t)acc;
     }
 }

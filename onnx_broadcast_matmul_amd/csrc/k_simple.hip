@@ -35,8 +35,21 @@ __global__ __launch_bounds__(256) void k_direct(KArgs a) {
         const S *ap = A + oa + (a.ta ? m : m * a.lda);
         const S *bp = B + ob + (a.tb ? n * a.ldb : n);
         const int64_t sak = a.ta ? a.lda : 1, sbk = a.tb ? 1 : a.ldb;
+        // Ascending k, one accumulator; the loads of 16 k are issued together
+        // so their latencies overlap (the summation order is unchanged).
         float acc = 0.0f;
-        for (int64_t k = 0; k < K; ++k) acc = fmaf(E::to_f32(ap[k * sak]), E::to_f32(bp[k * sbk]), acc);
+        int64_t k = 0;
+        for (; k + 16 <= K; k += 16) {
+            float av[16], bv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                av[u] = E::to_f32(ap[(k + u) * sak]);
+                bv[u] = E::to_f32(bp[(k + u) * sbk]);
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) acc = fmaf(av[u], bv[u], acc);
+        }
+        for (; k < K; ++k) acc = fmaf(E::to_f32(ap[k * sak]), E::to_f32(bp[k * sbk]), acc);
         if (a.gemm_epi) acc = gemm_epilogue<E>(a, acc, m, n);
         Y[idx] = E::from_f32(acc);
     }

@@ -354,7 +354,10 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         const TileCfg *small = tile_entry(p->dtype, tile_count(p->dtype) - 1);
         const int64_t small_tiles = p->batch * cdiv(M, small->bm) * cdiv(N, small->bn);
         (void)big_tiles;
-        if (flops <= 16777216.0 && K <= 512) {
+        const bool has_skinny = p->dtype != MM_DOUBLE && !p->is_gemm && !p->is_int;
+        if (has_skinny && N < 16 && N <= M && K >= 64) {
+            algo = MM_ALGO_SKINNY_N;  // few columns: the rows of A stream in parallel, K split over waves
+        } else if (flops <= 16777216.0 && K <= 512) {
             algo = MM_ALGO_DIRECT;  // tiny product with a short reduction: launch latency dominates
         } else if (N < 16 && N <= M) {
             algo = MM_ALGO_SKINNY_N;  // includes N == 1: never split-K

@@ -206,7 +206,9 @@ SELECTOR_CASES = [
     # workload products and the algorithm the selector must pick
     ((4, 64, 96), (96, 80), mm.FLOAT, "direct"),
     ((96,), (96, 80), mm.FLOAT, "direct"),
-    ((4, 64, 96), (96,), mm.FLOAT, "direct"),
+    ((4, 64, 96), (96,), mm.FLOAT, "skinny_n"),
+    ((8, 16), (16, 8), mm.FLOAT, "direct"),
+    ((4, 64, 96), (96,), mm.DOUBLE, "direct"),   # no skinny-N kernel for DOUBLE: tiny stays direct
     ((1024, 1024), (1024, 1024), mm.FLOAT, "general"),
     ((8, 1, 512, 512), (1, 6, 512, 512), mm.FLOAT, "general"),
     ((16, 512, 4096), (4096, 11008), mm.BFLOAT16, "general"),
