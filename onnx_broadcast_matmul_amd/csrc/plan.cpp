@@ -355,9 +355,16 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         const int64_t small_tiles = p->batch * cdiv(M, small->bm) * cdiv(N, small->bn);
         (void)big_tiles;
         const bool has_skinny = p->dtype != MM_DOUBLE && !p->is_gemm && !p->is_int;
+        // Direct-kernel limits (measured): for the 16-bit types the tiled
+        // MFMA kernel wins from K = 64 on, and from about 2^18 outputs at
+        // K = 16; for FP32 the direct kernel stays ahead of the FP32 tiles up
+        // to K = 512 and about 2^25 FLOPs.
+        const bool t16 = p->dtype == MM_FLOAT16 || p->dtype == MM_BFLOAT16;
+        const double direct_flops = p->dtype == MM_FLOAT && !p->is_gemm ? 33554432.0 : 16777216.0;
+        const int64_t direct_k = t16 ? (p->batch * M * N <= 262144 ? 32 : 0) : 512;
         if (has_skinny && N < 16 && N <= M && K >= 64) {
             algo = MM_ALGO_SKINNY_N;  // few columns: the rows of A stream in parallel, K split over waves
-        } else if (flops <= 16777216.0 && K <= 512) {
+        } else if (flops <= direct_flops && K <= direct_k) {
             algo = MM_ALGO_DIRECT;  // tiny product with a short reduction: launch latency dominates
         } else if (N < 16 && N <= M) {
             algo = MM_ALGO_SKINNY_N;  // includes N == 1: never split-K

@@ -209,6 +209,11 @@ SELECTOR_CASES = [
     ((4, 64, 96), (96,), mm.FLOAT, "skinny_n"),
     ((8, 16), (16, 8), mm.FLOAT, "direct"),
     ((4, 64, 96), (96,), mm.DOUBLE, "direct"),   # no skinny-N kernel for DOUBLE: tiny stays direct
+    ((32, 256), (256, 32), mm.BFLOAT16, "general"),  # 16-bit: MFMA tiles beat the direct loop from K = 64
+    ((32, 16), (16, 32), mm.BFLOAT16, "direct"),
+    ((8, 256, 16), (16, 256), mm.BFLOAT16, "general"),  # 2^19 outputs: the tiles win even at K = 16
+    ((256, 256), (256, 256), mm.FLOAT, "direct"),    # FP32: direct up to about 2^25 FLOPs
+    ((8, 128, 256), (256, 128), mm.FLOAT, "general"),
     ((1024, 1024), (1024, 1024), mm.FLOAT, "general"),
     ((8, 1, 512, 512), (1, 6, 512, 512), mm.FLOAT, "general"),
     ((16, 512, 4096), (4096, 11008), mm.BFLOAT16, "general"),
