@@ -32,7 +32,10 @@
  * the split-K algorithm, an FP32 (DOUBLE: double) workspace on the device of the first
  * execution (allocated by that first mm_execute, freed by mm_plan_destroy).
  * Because of that workspace, executions of one split-K plan must not overlap
- * on different streams; use one plan per stream.
+ * on different streams; use one plan per stream.  The allocation cannot
+ * happen while the stream is being captured into a HIP graph (the execute
+ * then fails with MM_ERR_ALLOC): execute a split-K plan once before
+ * capturing it.
  *
  * Threading: plans are immutable after creation apart from the lazily
  * allocated workspace, which is guarded; mm_last_error() is per thread.

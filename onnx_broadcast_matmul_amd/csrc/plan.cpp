@@ -349,11 +349,16 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
     int algo = opt ? opt->force_algo : MM_ALGO_AUTO;
     if (algo == MM_ALGO_AUTO) {
         const double flops = 2.0 * (double)p->batch * M * N * K;
-        const TileCfg *big = tile_entry(p->dtype, 0);
-        const int64_t big_tiles = p->batch * cdiv(M, big->bm) * cdiv(N, big->bn);
-        const TileCfg *small = tile_entry(p->dtype, tile_count(p->dtype) - 1);
-        const int64_t small_tiles = p->batch * cdiv(M, small->bm) * cdiv(N, small->bn);
-        (void)big_tiles;
+        // Tiles of the smallest block tile in the table: the most workgroups
+        // the tiled kernel can put on the GPU.
+        int64_t small_tiles = 0;
+        for (int i = 0; i < tile_count(p->dtype); ++i) {
+            const TileCfg *t = tile_entry(p->dtype, i);
+            small_tiles = std::max(small_tiles, p->batch * cdiv(M, t->bm) * cdiv(N, t->bn));
+        }
+        // Workgroups of the skinny-M kernel (one per 64 lanes x 16 bytes of
+        // columns per batch): with few of them the GEMV cannot fill the GPU.
+        const int64_t skm_wgs = p->batch * cdiv(N, 64 * (16 / elem_size(p->dtype)));
         const bool has_skinny = p->dtype != MM_DOUBLE && !p->is_gemm && !p->is_int;
         // Direct-kernel limits (measured): for the 16-bit types the tiled
         // MFMA kernel wins from K = 64 on, and from about 2^18 outputs at
@@ -362,15 +367,18 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         const bool t16 = p->dtype == MM_FLOAT16 || p->dtype == MM_BFLOAT16;
         const double direct_flops = p->dtype == MM_FLOAT && !p->is_gemm ? 33554432.0 : 16777216.0;
         const int64_t direct_k = t16 ? (p->batch * M * N <= 262144 ? 32 : 0) : 512;
-        if (has_skinny && N < 16 && N <= M && K >= 64) {
+        // The 16-bit eight-column skinny-N kernel gives each of its 8 waves
+        // 512 elements of K: below K = 1024 most waves idle and the tiles win.
+        const bool skn_short = t16 && N == 8 && K < 1024;
+        if (has_skinny && N < 16 && N <= M && K >= 64 && !skn_short) {
             algo = MM_ALGO_SKINNY_N;  // few columns: the rows of A stream in parallel, K split over waves
         } else if (flops <= direct_flops && K <= direct_k) {
             algo = MM_ALGO_DIRECT;  // tiny product with a short reduction: launch latency dominates
-        } else if (N < 16 && N <= M) {
+        } else if (N < 16 && N <= M && !skn_short) {
             algo = MM_ALGO_SKINNY_N;  // includes N == 1: never split-K
-        } else if (M < 16) {
-            algo = MM_ALGO_SKINNY_M;
-        } else if (small_tiles < kNumCUs / 2 && K >= 4096 && K >= 8 * std::max(M, N)) {
+        } else if (M < 16 && skm_wgs >= kNumCUs / 2) {
+            algo = MM_ALGO_SKINNY_M;  // GEMV over enough columns and batches to fill the GPU
+        } else if (small_tiles < kNumCUs / 2 && K >= 1024) {
             algo = MM_ALGO_SPLIT_K;  // tiles cannot fill the GPU; long K
         } else {
             algo = MM_ALGO_GENERAL;

@@ -212,6 +212,12 @@ SELECTOR_CASES = [
     ((32, 256), (256, 32), mm.BFLOAT16, "general"),  # 16-bit: MFMA tiles beat the direct loop from K = 64
     ((32, 16), (16, 32), mm.BFLOAT16, "direct"),
     ((8, 256, 16), (16, 256), mm.BFLOAT16, "general"),  # 2^19 outputs: the tiles win even at K = 16
+    ((1, 4096), (4096, 2048), mm.FLOAT, "split_k"),     # one GEMV of 8 column blocks cannot fill the GPU
+    ((15, 4096), (4096, 256), mm.BFLOAT16, "split_k"),
+    ((4, 256), (256, 2048), mm.BFLOAT16, "general"),   # short K: the tiles
+    ((256, 4096), (4096, 256), mm.FLOAT, "split_k"),
+    ((4096, 256), (256, 8), mm.BFLOAT16, "general"),   # eight 16-bit columns, short K: the tiles
+    ((4096, 256), (256, 4), mm.BFLOAT16, "skinny_n"),
     ((256, 256), (256, 256), mm.FLOAT, "direct"),    # FP32: direct up to about 2^25 FLOPs
     ((8, 128, 256), (256, 128), mm.FLOAT, "general"),
     ((1024, 1024), (1024, 1024), mm.FLOAT, "general"),
@@ -362,8 +368,10 @@ def test_gemm_plan_shapes(ta, tb):
     assert (inf["M"], inf["N"], inf["K"]) == (M, N, K) and inf["algo"] == mm.ALGO_GENERAL
     assert inf["tile"] - 1 in (0, 5, 4)  # Gemm: only the tiles instantiated with its epilogue
     assert inf["tail_col"] == 0
-    # skinny shapes of a Gemm take the tiled kernel
-    assert mm.GemmPlan((1, 4096), (4096, 4096), mm.FLOAT16).algo == mm.ALGO_GENERAL
+    # skinny shapes of a Gemm take the tiled kernels: split-K when one row
+    # of tiles cannot fill the GPU and K is long, else the general kernel
+    assert mm.GemmPlan((1, 4096), (4096, 4096), mm.FLOAT16).algo == mm.ALGO_SPLIT_K
+    assert mm.GemmPlan((1, 512), (512, 4096), mm.FLOAT16).algo == mm.ALGO_GENERAL
     assert mm.GemmPlan((4096, 64), (64, 0), mm.FLOAT16).algo == mm.ALGO_EMPTY
     assert mm.GemmPlan((64, 0), (0, 32), mm.FLOAT16, c_shape=(1,)).algo == mm.ALGO_DIRECT  # Y = beta * C
 
