@@ -374,20 +374,17 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             algo = MM_ALGO_SKINNY_N;  // few columns: the rows of A stream in parallel, K split over waves
         } else if (flops <= direct_flops && K <= direct_k) {
             algo = MM_ALGO_DIRECT;  // tiny product with a short reduction: launch latency dominates
-        } else if (N < 16 && N <= M && !skn_short) {
+        } else if (has_skinny && N < 16 && N <= M && !skn_short) {
             algo = MM_ALGO_SKINNY_N;  // includes N == 1: never split-K
-        } else if (M < 16 && skm_wgs >= kNumCUs / 2) {
+        } else if (has_skinny && M < 16 && skm_wgs >= kNumCUs / 2) {
             algo = MM_ALGO_SKINNY_M;  // GEMV over enough columns and batches to fill the GPU
         } else if (small_tiles < kNumCUs / 2 && K >= 1024) {
-            algo = MM_ALGO_SPLIT_K;  // tiles cannot fill the GPU; long K
+            // Tiles cannot fill the GPU and K is long.  Also the skinny
+            // shapes of DOUBLE and Gemm, which have no skinny kernels.
+            algo = MM_ALGO_SPLIT_K;
         } else {
             algo = MM_ALGO_GENERAL;
         }
-        // DOUBLE has no skinny kernels: its skinny shapes take the tiled
-        // FP64 kernel, which still reads the large operand once.
-        if (p->dtype == MM_DOUBLE && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N)) algo = MM_ALGO_GENERAL;
-        // Gemm (transposes, epilogue) runs on the direct, tiled and split-K kernels.
-        if (p->is_gemm && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N)) algo = MM_ALGO_GENERAL;
         // MatMulInteger runs on the direct and tiled INT8 kernels.
         if (p->is_int && algo != MM_ALGO_DIRECT) algo = MM_ALGO_GENERAL;
     }

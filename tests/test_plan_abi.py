@@ -218,6 +218,7 @@ SELECTOR_CASES = [
     ((256, 4096), (4096, 256), mm.FLOAT, "split_k"),
     ((4096, 256), (256, 8), mm.BFLOAT16, "general"),   # eight 16-bit columns, short K: the tiles
     ((4096, 256), (256, 4), mm.BFLOAT16, "skinny_n"),
+    ((256, 4096), (4096, 8), mm.DOUBLE, "split_k"),    # no skinny kernels: few tiles and long K take split-K
     ((256, 256), (256, 256), mm.FLOAT, "direct"),    # FP32: direct up to about 2^25 FLOPs
     ((8, 128, 256), (256, 128), mm.FLOAT, "general"),
     ((1024, 1024), (1024, 1024), mm.FLOAT, "general"),
