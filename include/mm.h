@@ -29,13 +29,14 @@
  *
  * Ownership: the caller owns A, B and Y and keeps them alive until the work
  * enqueued on the stream has completed.  The plan owns its metadata and, for
- * the split-K algorithm, an FP32 (DOUBLE: double) workspace on the device of the first
- * execution (allocated by that first mm_execute, freed by mm_plan_destroy).
- * Because of that workspace, executions of one split-K plan must not overlap
- * on different streams; use one plan per stream.  The allocation cannot
- * happen while the stream is being captured into a HIP graph (the execute
- * then fails with MM_ERR_ALLOC): execute a split-K plan once before
- * capturing it.
+ * the split-K algorithm and a skinny-M plan that cuts K (split_k > 1 in
+ * mm_plan_info), an FP32 (DOUBLE: double) workspace on the device of the
+ * first execution (allocated by that first mm_execute, freed by
+ * mm_plan_destroy; mm_plan_workspace_bytes() > 0 tells which plans have one).
+ * Because of that workspace, executions of such a plan must not overlap on
+ * different streams; use one plan per stream.  The allocation cannot happen
+ * while the stream is being captured into a HIP graph (the execute then
+ * fails with MM_ERR_ALLOC): execute such a plan once before capturing it.
  *
  * Threading: plans are immutable after creation apart from the lazily
  * allocated workspace, which is guarded; mm_last_error() is per thread.
@@ -92,7 +93,8 @@ typedef enum mm_algo {
     MM_ALGO_EMPTY = 1,     /* output has no element: nothing is launched */
     MM_ALGO_ZERO_FILL = 2, /* K == 0: the output is filled with zeros */
     MM_ALGO_DIRECT = 3,    /* tiny products: one thread per output */
-    MM_ALGO_SKINNY_M = 4,  /* small M (GEMV): B streamed once along N */
+    MM_ALGO_SKINNY_M = 4,  /* small M (GEMV): B streamed once along N; K may be cut
+                              into chunks (FP32 partials + ordered reduce) */
     MM_ALGO_SKINNY_N = 5,  /* small N: A streamed once along K */
     MM_ALGO_SPLIT_K = 6,   /* tiny output, long K: FP32 (DOUBLE: double) partials + ordered reduce */
     MM_ALGO_GENERAL = 7    /* tiled MFMA GEMM with LDS double buffering */
@@ -109,7 +111,9 @@ typedef struct mm_plan_options {
                            GENERAL/SPLIT_K tile table for the element type
                            (see mm_tile_config) */
     int32_t split_k;    /* 0 = plan's choice; >= 1 number of K partitions for
-                           SPLIT_K (clamped so every partition is non-empty) */
+                           SPLIT_K and SKINNY_M (clamped so every partition is
+                           non-empty; SKINNY_M partitions hold whole 64-row
+                           chunks of K) */
     int32_t reserved;   /* must be 0 */
 } mm_plan_options;
 
@@ -126,7 +130,7 @@ typedef struct mm_plan_info {
     int64_t a_batch_strides[MM_MAX_BATCH_DIMS]; /* elements; 0 = broadcast */
     int64_t b_batch_strides[MM_MAX_BATCH_DIMS]; /* elements; 0 = broadcast */
     int32_t tile;             /* tile table entry + 1 (0 if not a tiled algorithm) */
-    int32_t split_k;          /* K partitions (1 unless SPLIT_K) */
+    int32_t split_k;          /* K partitions (1 unless SPLIT_K or a split SKINNY_M) */
     int64_t k_chunk;          /* K elements per partition */
     int64_t workspace_bytes;  /* workspace the plan needs on the device (FP32 or double partials) */
     double flops;             /* 2 * batch * M * N * K of the un-folded problem */
@@ -273,7 +277,7 @@ int64_t mm_plan_output_numel(mm_plan_t plan);
 /* Selected algorithm (an mm_algo value), or -1 for a NULL plan. */
 int mm_plan_algo(mm_plan_t plan);
 
-/* Device workspace bytes the plan uses (0 unless SPLIT_K). */
+/* Device workspace bytes the plan uses (0 unless SPLIT_K or a split SKINNY_M). */
 size_t mm_plan_workspace_bytes(mm_plan_t plan);
 
 /* Fill *info with everything the plan resolved. */

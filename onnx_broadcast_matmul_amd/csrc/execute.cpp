@@ -89,7 +89,16 @@ static mm_status execute_impl(mm_plan_s *p, const void *A, const void *B, const 
         e = f64 ? launch_direct_f64(a, s) : launch_direct(p->dtype, a, s);
         break;
     case MM_ALGO_SKINNY_M:
-        e = launch_skinny_m(p->dtype, al, a, s);
+        if (p->split > 1) {
+            // K cut into chunks: FP32 partials, then the split-K reduction.
+            mm_status st = ensure_workspace(p);
+            if (st != MM_OK) return st;
+            a.W = (float *)p->ws;
+            e = launch_skinny_m(p->dtype, al, a, s);
+            if (e == hipSuccess) e = launch_splitk_reduce(p->dtype, a, s);
+        } else {
+            e = launch_skinny_m(p->dtype, al, a, s);
+        }
         break;
     case MM_ALGO_SKINNY_N:
         e = launch_skinny_n(p->dtype, al, a, s);

@@ -9,7 +9,10 @@
 // every B element is read exactly once from HBM with 16-byte coalesced
 // loads, and the next eight B rows are in flight while the current eight are
 // multiplied.  The per-wave partial sums meet in LDS and are added in wave
-// order.
+// order.  When the columns give too few workgroups to keep every CU
+// streaming, K is also cut into `split` chunks of whole workgroups; each
+// chunk writes FP32 partial sums, which the split-K reduction adds in chunk
+// order (the same fixed order on every run).
 //
 // Skinny-N: same page, same table (N == 1 or very small N: vectorize the K
 // reduction, no B packing) and roadmap PR06.2 (several partial accumulators
@@ -65,11 +68,14 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t ncb = (N + COLS - 1) / COLS;
     const int64_t nmg = (M + MT - 1) / MT;
+    const int64_t ns = a.split;
     int64_t id = blockIdx.x;
     const int64_t cb = id % ncb;
     id /= ncb;
     const int64_t mg = id % nmg;
-    const int64_t b = id / nmg;
+    id /= nmg;
+    const int64_t sidx = id % ns;
+    const int64_t b = id / ns;
 
     int64_t oa, ob;
     batch_offsets(a.bd, b, oa, ob);
@@ -79,10 +85,13 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
     const int64_t n = cb * COLS + (int64_t)lane * VE;
     const bool col_ok = n < N;
 
-    // Wave slab of K: a multiple of U rows (and of the A vector width).
-    const int64_t kper = ((K + kSkMWaves - 1) / kSkMWaves + U - 1) / U * U;
-    const int64_t klo = wave * kper;
-    const int64_t khi = (klo + kper) < K ? (klo + kper) : K;
+    // K chunk of this workgroup (a multiple of 64 rows), then the wave slab
+    // within it: a multiple of U rows (and of the A vector width).
+    const int64_t kb = sidx * a.kchunk;
+    const int64_t ke = (kb + a.kchunk) < K ? (kb + a.kchunk) : K;
+    const int64_t kper = ((ke - kb + kSkMWaves - 1) / kSkMWaves + U - 1) / U * U;
+    const int64_t klo = kb + wave * kper;
+    const int64_t khi = (klo + kper) < ke ? (klo + kper) : ke;
 
     float acc[MT][VE];
 #pragma unroll
@@ -135,8 +144,10 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
         }
     }
 
-    // Cross-wave reduction in wave order, one output row at a time.
+    // Cross-wave reduction in wave order, one output row at a time; with a
+    // K split the sums go to the chunk's FP32 partial rows.
     S *__restrict__ Y = (S *)a.Y + b * M * N;
+    float *__restrict__ P = ns > 1 ? a.W + (sidx * a.batch + b) * M * N : nullptr;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
@@ -147,7 +158,10 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
 #pragma unroll
             for (int w = 1; w < kSkMWaves; ++w) s += red[w][c];
             const int64_t col = cb * COLS + c;
-            if (m0 + m < M && col < N) Y[(m0 + m) * N + col] = E::from_f32(s);
+            if (m0 + m < M && col < N) {
+                if (ns > 1) P[(m0 + m) * N + col] = s;
+                else Y[(m0 + m) * N + col] = E::from_f32(s);
+            }
         }
         __syncthreads();
     }
@@ -156,7 +170,7 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
 template <int DT, int MT>
 static hipError_t launch_skm(bool vec, bool avec, const KArgs &a, hipStream_t s) {
     const int cols = 64 * (vec ? Elem<DT>::kVE : 1);
-    const int64_t blocks = a.batch * ((a.M + MT - 1) / MT) * ((a.N + cols - 1) / cols);
+    const int64_t blocks = a.batch * ((a.M + MT - 1) / MT) * ((a.N + cols - 1) / cols) * a.split;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 g((unsigned)blocks), blk(64 * kSkMWaves);

@@ -98,7 +98,28 @@ static bool tile_allowed(int dtype, int index, bool gemm) {
     return false;
 }
 
+// 16-bit entries for products of at most 64 rows (see choose_tile).
+constexpr int kT16Small2 = 8, kT16Small = 4, kT16Narrow = 3;
+static_assert(kTiles16[kT16Small2].bm == 64 && kTiles16[kT16Small2].bn == 64 && kTiles16[kT16Small2].kgroups == 2,
+              "64 x 64 entry with two K groups");
+static_assert(kTiles16[kT16Small].bm == 64 && kTiles16[kT16Small].bn == 64 && kTiles16[kT16Small].kgroups == 1,
+              "64 x 64 entry with one K group");
+static_assert(kTiles16[kT16Narrow].bm == 128 && kTiles16[kT16Narrow].bn == 64, "128 x 64 entry");
+static_assert(kTransTiles16[2] == kT16Small, "the 64 x 64 entry has a Gemm kernel");
+
 static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, bool gemm = false) {
+    if ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && M <= 64) {
+        // At most 64 rows: each tile is a K-long chain of B stages, not MFMA
+        // work, so the quality ranking above does not apply.  Measured for
+        // M = 1..64, K = 4096: up to one 64 x 64 tile per CU, the entry
+        // with two K groups (shorter chain) wins; up to 1.5 per CU, the
+        // single-group 64 x 64 entry; beyond, 128 x 64 tiles (one per CU).
+        // Gemm has the single-group 64 x 64 entry only.
+        const int64_t t64 = batch * cdiv(N, 64);
+        if (gemm) return kT16Small;
+        if (t64 <= kNumCUs) return kT16Small2;
+        return t64 <= 3 * kNumCUs / 2 ? kT16Small : kT16Narrow;
+    }
     int best = -1;
     double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
@@ -318,6 +339,34 @@ static void plan_split(mm_plan_s *p, int requested) {
     p->workspace_bytes = (int64_t)p->split * p->batch * p->kernel_m * p->N * part_bytes;
 }
 
+// K chunks of the skinny-M kernel.  Its workgroups each cover 64 lanes x 16
+// bytes of columns for one group of rows (the launcher's row groups: 1, 2,
+// 4, 8 or 16 rows); when those are fewer than one per CU, K is cut into
+// chunks of whole 64-row blocks so that the grid holds at most two
+// workgroups per CU (a third on some CUs would make a slow last round),
+// with at most kSkinnyMaxSplit chunks.  Measured over M = 1..8, K =
+// 1024..16384 and 1..120 column workgroups, that count is within 5 %
+// (geometric mean) of the best chunk count.  The FP32 partials (split x rows
+// x N) stay small next to B, which holds K rows of N.
+constexpr int64_t kSkinnyMaxSplit = 64;
+
+static void plan_skinny_split(mm_plan_s *p, int requested) {
+    const int64_t M = p->kernel_m, N = p->N, K = p->K;
+    const int64_t mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    const int64_t wgs = p->batch * cdiv(M, mt) * cdiv(N, 64 * (16 / elem_size(p->dtype)));
+    const int64_t kblocks = cdiv(K, 64);
+    int64_t s;
+    if (requested > 0) {
+        s = requested;
+    } else {
+        s = wgs >= kNumCUs ? 1 : std::min(2 * (int64_t)kNumCUs / std::max<int64_t>(wgs, 1), kSkinnyMaxSplit);
+    }
+    s = std::max<int64_t>(1, std::min(s, kblocks));
+    p->kchunk = cdiv(kblocks, s) * 64;
+    p->split = (int32_t)cdiv(K, p->kchunk);
+    p->workspace_bytes = p->split > 1 ? (int64_t)p->split * p->batch * M * N * 4 : 0;
+}
+
 static mm_status check_limits(const mm_plan_s *p) {
     const int64_t lim = INT32_MAX;
     if (p->kernel_m > lim || p->N > lim || p->K > lim || p->batch > lim)
@@ -370,6 +419,17 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         // The 16-bit eight-column skinny-N kernel gives each of its 8 waves
         // 512 elements of K: below K = 1024 most waves idle and the tiles win.
         const bool skn_short = t16 && N == 8 && K < 1024;
+        // Skinny-M with K cut over workgroups (measured against split-K and
+        // the tiles for M = 1..15, K = 1024..16384, N = 256..30720): FP32
+        // up to 8 rows wins everywhere (the tiles pad M to 64 rows of FP32
+        // MFMA work), by up to 3x, and up to 15 rows with K >= 8192 and
+        // N >= 4096; the 16-bit types, whose tiles run at the 16-bit MFMA
+        // rate, win only for up to 4 rows with a long K and a large B
+        // (K >= 8192, K * N >= 2^26).  Beyond that the kernel's per-row A
+        // loads make it latency-bound.
+        const bool skm_split = has_skinny && K >= 1024 &&
+                               ((p->dtype == MM_FLOAT && (M <= 8 || (K >= 8192 && N >= 4096))) ||
+                                (t16 && M <= 4 && K >= 8192 && (double)K * N >= 67108864.0));
         if (has_skinny && N < 16 && N <= M && K >= 64 && !skn_short) {
             algo = MM_ALGO_SKINNY_N;  // few columns: the rows of A stream in parallel, K split over waves
         } else if (flops <= direct_flops && K <= direct_k) {
@@ -378,9 +438,13 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             algo = MM_ALGO_SKINNY_N;  // includes N == 1: never split-K
         } else if (has_skinny && M < 16 && skm_wgs >= kNumCUs / 2) {
             algo = MM_ALGO_SKINNY_M;  // GEMV over enough columns and batches to fill the GPU
-        } else if (small_tiles < kNumCUs / 2 && K >= 1024) {
-            // Tiles cannot fill the GPU and K is long.  Also the skinny
-            // shapes of DOUBLE and Gemm, which have no skinny kernels.
+        } else if (skm_split) {
+            algo = MM_ALGO_SKINNY_M;  // GEMV over few columns: K cut into chunks
+        } else if ((small_tiles < kNumCUs / 2 && K >= 1024) || (small_tiles < 3 * kNumCUs / 4 && K >= 4096)) {
+            // Tiles cannot fill the GPU and K is long (with K >= 4096, up to
+            // three quarters of the CUs: a 64-stage reduction per tile
+            // outweighs the partials' round trip).  Also the skinny shapes of
+            // DOUBLE and Gemm, which have no skinny kernels.
             algo = MM_ALGO_SPLIT_K;
         } else {
             algo = MM_ALGO_GENERAL;
@@ -398,6 +462,14 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         return fail(MM_ERR_BAD_OPTION, "MatMulInteger runs on the direct and general kernels only");
     p->algo = algo;
 
+    if (algo == MM_ALGO_SKINNY_M) {
+        const int sreq = opt ? opt->split_k : 0;
+        if (sreq < 0) return fail(MM_ERR_BAD_OPTION, "split_k %d is negative", sreq);
+        plan_skinny_split(p, sreq);
+        const int64_t wgs = p->batch * cdiv(M, 16) * cdiv(N, 64);
+        if (wgs * p->split > INT32_MAX)
+            return fail(MM_ERR_TOO_LARGE, "too many workgroups (%lld x %d splits)", (long long)wgs, p->split);
+    }
     if (algo == MM_ALGO_GENERAL || algo == MM_ALGO_SPLIT_K) {
         int req = opt ? opt->tile : 0;
         if (req < 0 || req > tile_count(p->dtype))

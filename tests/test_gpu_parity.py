@@ -112,6 +112,21 @@ def test_split_counts(dt, split, dev):
 
 
 @pytest.mark.parametrize("dt", [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
+@pytest.mark.parametrize("split", [1, 2, 3, 7, 16, 64])
+def test_skinny_m_split_counts(dt, split, dev):
+    """Skinny-M with K cut into chunks over workgroups: a K that is not a
+    multiple of the 64-row chunk unit, a folded batch (rows in two row
+    groups), broadcast batches, unaligned columns (element-wise loads), and
+    small-integer exactness whatever the chunk count."""
+    cases = [((1, 4100), (4100, 300)), ((5, 2, 3, 1000), (1000, 520)),
+             ((3, 1, 4, 640), (2, 640, 136)), ((2, 1111), (1111, 77))]
+    for i, (sa, sb) in enumerate(cases):
+        plan, _, _ = parity(sa, sb, dt, dev, algo=mm.ALGO_SKINNY_M, split=split, seed=60 + i)
+        assert 1 <= plan.info()["split_k"] <= split
+        parity(sa, sb, dt, dev, algo=mm.ALGO_SKINNY_M, split=split, seed=60 + i, dist=("int",), exact=True)
+
+
+@pytest.mark.parametrize("dt", [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
 def test_skinny_n_eight_columns(dt, dev):
     """Eight output columns: ragged row counts, K from one chunk to the
     4096 limit of the register-slice kernel and past it, batched and

@@ -212,7 +212,16 @@ SELECTOR_CASES = [
     ((32, 256), (256, 32), mm.BFLOAT16, "general"),  # 16-bit: MFMA tiles beat the direct loop from K = 64
     ((32, 16), (16, 32), mm.BFLOAT16, "direct"),
     ((8, 256, 16), (16, 256), mm.BFLOAT16, "general"),  # 2^19 outputs: the tiles win even at K = 16
-    ((1, 4096), (4096, 2048), mm.FLOAT, "split_k"),     # one GEMV of 8 column blocks cannot fill the GPU
+    ((1, 4096), (4096, 2048), mm.FLOAT, "skinny_m"),    # FP32 GEMV over 8 column blocks: K cut into chunks
+    ((8, 1024), (1024, 30720), mm.FLOAT, "skinny_m"),
+    ((1, 16384), (16384, 8704), mm.BFLOAT16, "skinny_m"),  # 16-bit: up to 4 rows, long K, large B
+    ((4, 4096), (4096, 30720), mm.BFLOAT16, "general"),   # 16-bit, K < 8192: the tiles
+    ((8, 16384), (16384, 8704), mm.BFLOAT16, "split_k"),  # 16-bit, 8 rows: split-K over the tiles
+    ((1, 4096), (4096, 11008), mm.BFLOAT16, "split_k"),   # 172 tiles and K >= 4096
+    ((1, 1024), (1024, 11008), mm.BFLOAT16, "general"),   # 172 tiles, K < 4096
+    ((15, 4096), (4096, 8704), mm.FLOAT, "split_k"),
+    ((15, 16384), (16384, 8704), mm.FLOAT, "skinny_m"),   # FP32 9..15 rows: K >= 8192 and N >= 4096
+    ((15, 16384), (16384, 2048), mm.FLOAT, "split_k"),
     ((15, 4096), (4096, 256), mm.BFLOAT16, "split_k"),
     ((4, 256), (256, 2048), mm.BFLOAT16, "general"),   # short K: the tiles
     ((256, 4096), (4096, 256), mm.FLOAT, "split_k"),
@@ -239,6 +248,22 @@ SELECTOR_CASES = [
 @pytest.mark.parametrize("sa,sb,dt,algo", SELECTOR_CASES)
 def test_selector(sa, sb, dt, algo):
     assert mm.ALGO_NAMES[mm.Plan(sa, sb, dt).algo] == algo
+
+
+def test_small_m_tiles():
+    """16-bit products of at most 64 rows take 64 x 64 tiles with two K
+    groups up to one tile per CU, single-group 64 x 64 tiles up to 1.5 per
+    CU, then 128 x 64 tiles; Gemm takes its 64 x 64 entry."""
+    t16 = mm.tile_configs(mm.BFLOAT16)
+    for sa, sb, want in [((64, 1024), (1024, 15360), 9), ((1, 4096), (4096, 21760), 5),
+                         ((16, 4096), (4096, 30720), 4), ((2, 32, 1024), (2, 1024, 8192), 9)]:
+        inf = mm.Plan(sa, sb, mm.BFLOAT16).info()
+        assert mm.ALGO_NAMES[inf["algo"]] == "general" and inf["tile"] == want, (sa, sb, inf["tile"])
+    assert t16[8][:2] == (64, 64) and t16[4][:2] == (64, 64) and t16[3][:2] == (128, 64)
+    g = mm.GemmPlan((32, 4096), (21760, 4096), mm.FLOAT16, False, True, None, 1.0, 0.0)
+    assert g.algo == mm.ALGO_GENERAL and g.info()["tile"] == 5
+    # more rows: the quality-ranked choice
+    assert mm.Plan((65, 4096), (4096, 21760), mm.BFLOAT16).info()["tile"] not in (4, 5, 9)
 
 
 def test_tile_table():
@@ -279,7 +304,7 @@ def test_info_flops_bytes():
     ((4, 64, 96), (96, 80), mm.ALGO_DIRECT),
     ((1024, 1024), (1024, 1024), mm.ALGO_GENERAL),
     ((32, 1, 4096), (32, 4096, 4096), mm.ALGO_GENERAL),   # skinny-M shape: no FP64 skinny kernel
-    ((8192, 4096), (4096, 8), mm.ALGO_GENERAL),           # skinny-N shape
+    ((8192, 4096), (4096, 8), mm.ALGO_SPLIT_K),           # skinny-N shape: 128 tiles, long K
     ((64, 131072), (131072, 64), mm.ALGO_SPLIT_K),
 ])
 def test_double_plans(sa, sb, algo):
@@ -294,6 +319,33 @@ def test_double_plans(sa, sb, algo):
         assert inf["k_chunk"] % 16 == 0
     na = int(np.prod(sa)); nb = int(np.prod(sb))
     assert inf["min_bytes"] == 8.0 * (na + nb + plan.output_numel)
+
+
+def test_skinny_m_k_split_plans():
+    """Skinny-M cuts K into whole 64-row chunks (at most two workgroups per
+    CU, at most 64 chunks) when its column workgroups are fewer than two per
+    CU, and keeps one chunk, with no workspace, when they are not; a
+    requested count is clamped so that every chunk holds rows."""
+    p = mm.Plan((1, 4096), (4096, 2048), mm.BFLOAT16, force_algo=mm.ALGO_SKINNY_M)
+    inf = p.info()
+    # 2048 columns / 512 per workgroup = 4 workgroups -> 128 chunks wanted, at most 64
+    assert inf["split_k"] == 64 and inf["k_chunk"] == 64
+    assert inf["workspace_bytes"] == 64 * 1 * 1 * 2048 * 4 == p.workspace_bytes
+    mid = mm.Plan((8, 16384), (16384, 8704), mm.FLOAT, force_algo=mm.ALGO_SKINNY_M).info()
+    # 34 workgroups of 256 FP32 columns -> at most 512 / 34 = 15 chunks: 18 blocks of 64 rows each
+    assert (mid["split_k"], mid["k_chunk"]) == (15, 1152)
+    wide = mm.Plan((4, 4096), (4096, 131072), mm.FLOAT, force_algo=mm.ALGO_SKINNY_M).info()
+    assert wide["split_k"] == 1 and wide["k_chunk"] == 4096 and wide["workspace_bytes"] == 0
+    short = mm.Plan((1, 200), (200, 64), mm.FLOAT, force_algo=mm.ALGO_SKINNY_M).info()
+    assert (short["split_k"], short["k_chunk"]) == (4, 64) and short["workspace_bytes"] == 4 * 64 * 4
+    one = mm.Plan((1, 64), (64, 64), mm.FLOAT, force_algo=mm.ALGO_SKINNY_M).info()
+    assert one["split_k"] == 1 and one["workspace_bytes"] == 0
+    for req, want_chunk, want_split in [(1, 4160, 1), (7, 640, 7), (64, 128, 33), (500, 64, 65)]:
+        f = mm.Plan((3, 4100), (4100, 300), mm.FLOAT16, force_algo=mm.ALGO_SKINNY_M, split_k=req).info()
+        assert (f["k_chunk"], f["split_k"]) == (want_chunk, want_split)
+        assert f["k_chunk"] % 64 == 0 and (f["split_k"] - 1) * f["k_chunk"] < 4100 <= f["split_k"] * f["k_chunk"]
+        assert f["workspace_bytes"] == (0 if want_split == 1 else want_split * 3 * 300 * 4)
+    assert _try_plan((1, 64), (64, 64), mm.FLOAT, force_algo=mm.ALGO_SKINNY_M, split_k=-1)[1] == mm.ERR_BAD_OPTION
 
 
 @pytest.mark.parametrize("algo", [mm.ALGO_SKINNY_M, mm.ALGO_SKINNY_N])
