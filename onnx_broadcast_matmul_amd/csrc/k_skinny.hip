@@ -46,8 +46,14 @@ typedef __bf16 bfloat2_t __attribute__((ext_vector_type(2)));
 constexpr int kSkMWaves = 8;
 
 // B rows per pipeline step: deep for one or two output rows, shallower as the
-// MT x VE accumulators take the registers.
-constexpr int skm_unroll(int mt) { return mt <= 2 ? 16 : (mt <= 4 ? 8 : (mt <= 8 ? 4 : 2)); }
+// MT x VE accumulators take the registers, but never below the elements of
+// one 16-byte A load (av), so that A rows keep 16-byte loads: with fewer,
+// every row of a step costs one scalar A load per output row, and those
+// loads, not B, set the pace.
+constexpr int skm_unroll(int mt, int av) {
+    const int u = mt <= 2 ? 16 : (mt <= 4 ? 8 : (mt <= 8 ? 4 : 2));
+    return u > av ? u : av;
+}
 
 template <int DT, int MT, bool VEC, bool AVEC>
 __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
@@ -55,8 +61,8 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
     using S = typename E::S;
     constexpr int VE = VEC ? E::kVE : 1;  // columns per lane
     constexpr int COLS = 64 * VE;         // columns per workgroup
-    constexpr int U = skm_unroll(MT);
     constexpr int AV = 16 / (int)sizeof(S);  // A elements per 16-byte load
+    constexpr int U = skm_unroll(MT, AVEC ? AV : 1);
     // 16-byte A loads when rows allow them and each step covers whole chunks.
     constexpr bool AV_OK = AVEC && U % AV == 0;
 

@@ -219,9 +219,9 @@ SELECTOR_CASES = [
     ((8, 16384), (16384, 8704), mm.BFLOAT16, "split_k"),  # 16-bit, 8 rows: split-K over the tiles
     ((1, 4096), (4096, 11008), mm.BFLOAT16, "split_k"),   # 172 tiles and K >= 4096
     ((1, 1024), (1024, 11008), mm.BFLOAT16, "general"),   # 172 tiles, K < 4096
-    ((15, 4096), (4096, 8704), mm.FLOAT, "split_k"),
-    ((15, 16384), (16384, 8704), mm.FLOAT, "skinny_m"),   # FP32 9..15 rows: K >= 8192 and N >= 4096
+    ((15, 4096), (4096, 8704), mm.FLOAT, "skinny_m"),     # FP32 9..15 rows: K >= 4096 and N >= 4096
     ((15, 16384), (16384, 2048), mm.FLOAT, "split_k"),
+    ((15, 1024), (1024, 8704), mm.FLOAT, "general"),
     ((15, 4096), (4096, 256), mm.BFLOAT16, "split_k"),
     ((4, 256), (256, 2048), mm.BFLOAT16, "general"),   # short K: the tiles
     ((256, 4096), (4096, 256), mm.FLOAT, "split_k"),
