@@ -184,14 +184,18 @@ static void plan_tail(mm_plan_s *p) {
     }
 }
 
-// Smallest-padding tile for split-K (its output is tiny by construction);
-// among equally padded tiles, the one of higher relative throughput.
+// Smallest-padding tile for split-K (its output is small by construction);
+// among equally padded tiles, the one of higher relative throughput.  Tiles
+// above 128 x 128 are left out: with so few of them the plan would need
+// many short K chunks, whose FP32 partials (split x M x N x 4 bytes) can
+// outweigh the inputs.
 static int choose_split_tile(int dtype, int64_t M, int64_t N, bool gemm = false) {
     int best = -1;
     double best_pad = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
         if (!tile_allowed(dtype, i, gemm)) continue;
         const TileCfg *t = tile_entry(dtype, i);
+        if (t->bm * t->bn > 128 * 128) continue;
         double pad = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
         const bool tie = best >= 0 && fabs(pad - best_pad) <= 1e-9;
         if (pad > best_pad + 1e-9 || (tie && tile_quality(dtype, i) > tile_quality(dtype, best))) {
@@ -419,6 +423,11 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         // The 16-bit eight-column skinny-N kernel gives each of its 8 waves
         // 512 elements of K: below K = 1024 most waves idle and the tiles win.
         const bool skn_short = t16 && N == 8 && K < 1024;
+        // Workgroups of the tile the general path would choose.
+        auto general_tiles = [&]() -> int64_t {
+            const TileCfg *t = tile_entry(p->dtype, choose_tile(p->dtype, p->batch, M, N, p->is_gemm));
+            return p->batch * cdiv(M, t->bm) * cdiv(N, t->bn);
+        };
         // Skinny-M with K cut over workgroups (measured against split-K and
         // the tiles for M = 1..15, K = 1024..16384, N = 256..30720): FP32
         // up to 8 rows wins everywhere (the tiles pad M to 64 rows of FP32
@@ -428,7 +437,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         // (K >= 8192, K * N >= 2^26).  Beyond that the kernel's per-row A
         // loads make it latency-bound.
         const bool skm_split = has_skinny && K >= 1024 &&
-                               ((p->dtype == MM_FLOAT && (M <= 8 || (K >= 4096 && N >= 4096))) ||
+                               ((p->dtype == MM_FLOAT && (M <= 8 || (M < 16 && K >= 4096 && N >= 4096))) ||
                                 (t16 && M <= 4 && K >= 8192 && (double)K * N >= 67108864.0));
         if (has_skinny && N < 16 && N <= M && K >= 64 && !skn_short) {
             algo = MM_ALGO_SKINNY_N;  // few columns: the rows of A stream in parallel, K split over waves
@@ -440,11 +449,12 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             algo = MM_ALGO_SKINNY_M;  // GEMV over enough columns and batches to fill the GPU
         } else if (skm_split) {
             algo = MM_ALGO_SKINNY_M;  // GEMV over few columns: K cut into chunks
-        } else if ((small_tiles < kNumCUs / 2 && K >= 1024) || (small_tiles < 3 * kNumCUs / 4 && K >= 4096)) {
-            // Tiles cannot fill the GPU and K is long (with K >= 4096, up to
-            // three quarters of the CUs: a 64-stage reduction per tile
-            // outweighs the partials' round trip).  Also the skinny shapes of
-            // DOUBLE and Gemm, which have no skinny kernels.
+        } else if ((small_tiles < kNumCUs / 2 && K >= 1024) || (K >= 4096 && general_tiles() < 3 * kNumCUs / 4)) {
+            // Tiles cannot fill the GPU and K is long; with K >= 4096, also
+            // when the tile the general path would take leaves a quarter of
+            // the CUs idle (each of its tiles is then a chain of at least 64
+            // stages, which outweighs the partials' round trip).  Also the
+            // skinny shapes of DOUBLE and Gemm, which have no skinny kernels.
             algo = MM_ALGO_SPLIT_K;
         } else {
             algo = MM_ALGO_GENERAL;

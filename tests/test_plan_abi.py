@@ -222,6 +222,10 @@ SELECTOR_CASES = [
     ((15, 4096), (4096, 8704), mm.FLOAT, "skinny_m"),     # FP32 9..15 rows: K >= 4096 and N >= 4096
     ((15, 16384), (16384, 2048), mm.FLOAT, "split_k"),
     ((15, 1024), (1024, 8704), mm.FLOAT, "general"),
+    ((16, 4096), (4096, 8704), mm.FLOAT, "split_k"),      # 16 rows and more: never the K-split GEMV
+    ((128, 4096), (4096, 10880), mm.FLOAT, "split_k"),
+    ((128, 4096), (4096, 15360), mm.FLOAT, "general"),
+    ((32, 16384), (16384, 21760), mm.FLOAT, "general"),
     ((15, 4096), (4096, 256), mm.BFLOAT16, "split_k"),
     ((4, 256), (256, 2048), mm.BFLOAT16, "general"),   # short K: the tiles
     ((256, 4096), (4096, 256), mm.FLOAT, "split_k"),
