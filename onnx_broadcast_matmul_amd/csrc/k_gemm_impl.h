@@ -671,11 +671,36 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
         const int buf = kt % STAGES;
         if constexpr (KG == 1) {
+            // 16-bit types: the compiler, left alone, reuses one set of
+            // fragment registers and waits on each step's LDS reads right
+            // before its MFMAs.  Scheduling groups (mask 0x100: LDS reads,
+            // 0x008: MFMAs) keep the next step's reads ahead, in pairs
+            // between the step's first MFMAs, so that they land while the
+            // rest of the step's MFMAs run.  (Measured: no gain for FP32 or
+            // INT8, which keep the compiler's order.)
+            constexpr bool SCHED = DT == MM_FLOAT16 || DT == MM_BFLOAT16;
+            constexpr int RPA = TA ? 2 : 1;  // LDS reads per A fragment (transposing: two)
+            constexpr int RPB = TB ? 1 : 2;  // per B fragment
+            constexpr int RPS = FM * RPA + FN * RPB;
+            constexpr int MPS = FM * FN;     // MFMAs per step
             read_frags(buf, 0, 0);
+            if constexpr (SCHED) __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if (ks + 1 < KS) read_frags(buf, ks + 1, (ks + 1) & 1);
                 mfmas(ks & 1);
+                if constexpr (SCHED) {
+                    if (ks + 1 < KS) {
+#pragma unroll
+                        for (int q = 0; q < RPS / 2; ++q) {
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        }
+                        if constexpr (MPS > RPS / 2) __builtin_amdgcn_sched_group_barrier(0x008, MPS - RPS / 2, 0);
+                    } else {
+                        __builtin_amdgcn_sched_group_barrier(0x008, MPS, 0);
+                    }
+                }
             }
         } else {
             read_frags(buf, kg, 0);
