@@ -477,6 +477,56 @@ def _sample_indices(shape, n, rng):
     return np.unique(np.concatenate([idx, [0, total - 1]]))
 
 
+# Decode and prefill sizes for which the selector takes its newer paths:
+# (A shape, B shape [N, K] for the Gemm cases), element type, Gemm, and
+# the plan it must make (algorithm, tile entry + 1, K partitions).
+SELECTED_PATHS = [
+    ((1, 4096), (4096, 8704), mm.FLOAT, False, ("skinny_m", 0, 13)),      # FP32 GEMV, K in 13 chunks
+    ((15, 4096), (4096, 8704), mm.FLOAT, False, ("skinny_m", 0, 13)),
+    ((1, 16384), (16384, 8704), mm.BFLOAT16, False, ("skinny_m", 0, 29)),  # 16-bit GEMV, long K
+    ((64, 1024), (1024, 15360), mm.BFLOAT16, False, ("general", 9, 1)),    # <= 64 rows: two-group 64x64
+    ((1, 4096), (4096, 21760), mm.FLOAT16, False, ("general", 5, 1)),      # <= 64 rows, 340 tiles: 64x64
+    ((256, 4096), (4096, 4352), mm.BFLOAT16, False, ("split_k", 6, 4)),   # split-K tiles at most 128x128
+    ((32, 4096), (11008, 4096), mm.BFLOAT16, True, ("split_k", 5, 2)),    # Gemm decode: split-K
+    ((128, 16384), (8704, 16384), mm.FLOAT16, True, ("split_k", 6, 4)),
+]
+
+
+@pytest.mark.parametrize("sa,sb,dt,gemm,want", SELECTED_PATHS,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) and isinstance(v[0], int) else None)
+def test_selected_paths_full_size(sa, sb, dt, gemm, want, dev):
+    """The selector's plan for each shape, run at full size and checked on
+    sampled outputs against the oracle (Gemm: transposed B and a bias)."""
+    print(f"\n[selected] {sa} x {sb} {DT_IDS[dt]} gemm={gemm}", flush=True)
+    a = synth.generate(sa, dt, U1, [71, 0])
+    b = synth.generate(sb, dt, U1, [71, 1])
+    A = synth.as_torch(a, dt).to(dev)
+    B = synth.as_torch(b, dt).to(dev)
+    M, K = sa
+    N = sb[0] if gemm else sb[1]
+    rng = np.random.default_rng(71)
+    idx = _sample_indices((M, N), 2000, rng)
+    Y = _sentinel((M, N), dt, dev)
+    if gemm:
+        c = synth.generate((N,), dt, U1, [71, 2])
+        plan = mm.GemmPlan(sa, sb, dt, False, True, (N,), 1.0, 1.0)
+        plan.execute(A, B, Y, synth.as_torch(c, dt).to(dev))
+        o = oracle.gemm_at(a, b, dt, idx, False, True, c, 1.0, 1.0)
+        tol = gemm_tolerance(K, abs_max(a, dt), abs_max(b, dt), abs_max(c, dt), 1.0, 1.0)
+    else:
+        plan = mm.Plan(sa, sb, dt)
+        plan.execute(A, B, Y)
+        o = oracle.matmul_at(a, b, dt, idx)
+        tol = None
+    torch.cuda.synchronize()
+    inf = plan.info()
+    assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want
+    assert torch.isfinite(Y.float()).all().item()
+    y = synth.from_torch(Y).reshape(-1)[idx]
+    rep = check(y, o, dt, K, abs_max(a, dt), abs_max(b, dt), tol=tol)
+    assert rep.ok, f"{sa} x {sb} {DT_IDS[dt]} {want}: {rep}"
+
+
 @pytest.mark.parametrize("product", synth.all_products(), ids=lambda p: p.name)
 def test_workload_full_size(product, dev):
     """Each workload product at full size in the configuration the benchmark
