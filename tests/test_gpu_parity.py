@@ -112,6 +112,29 @@ def test_split_counts(dt, split, dev):
 
 
 @pytest.mark.parametrize("dt", [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
+@pytest.mark.parametrize("split", [64, 100])
+def test_gemm_split_reduction_epilogue(dt, split, dev):
+    """The wave-per-group reduction (64 or more partitions) applies the Gemm
+    epilogue (alpha, beta, per-column and full C) when it writes each
+    output."""
+    M, N, K = 64, 40, 19200
+    for i, layout in enumerate([("N",), ("M", "N")]):
+        cs = _cs(layout, M, N)
+        a = synth.generate((M, K), dt, U1, [80 + i, 0])
+        b = synth.generate((N, K), dt, U1, [80 + i, 1])
+        c = synth.generate(cs, dt, U1, [80 + i, 2])
+        plan = mm.GemmPlan((M, K), (N, K), dt, False, True, cs, 0.5, -2.0, force_algo=mm.ALGO_SPLIT_K, split_k=split)
+        assert plan.info()["split_k"] > 32
+        Y = _sentinel((M, N), dt, dev)
+        plan.execute(synth.as_torch(a, dt).to(dev), synth.as_torch(b, dt).to(dev), Y, synth.as_torch(c, dt).to(dev))
+        torch.cuda.synchronize()
+        o = oracle.gemm(a, b, dt, False, True, c, 0.5, -2.0)
+        tol = gemm_tolerance(K, abs_max(a, dt), abs_max(b, dt), abs_max(c, dt), 0.5, -2.0)
+        rep = check(synth.from_torch(Y), o, dt, K, abs_max(a, dt), abs_max(b, dt), tol=tol)
+        assert rep.ok, f"split {split} C={cs} {DT_IDS[dt]}: {rep}"
+
+
+@pytest.mark.parametrize("dt", [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
 @pytest.mark.parametrize("split", [1, 2, 3, 7, 16, 64])
 def test_skinny_m_split_counts(dt, split, dev):
     """Skinny-M with K cut into chunks over workgroups: a K that is not a
