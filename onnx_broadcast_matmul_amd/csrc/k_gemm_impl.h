@@ -668,7 +668,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         // After the barrier every wave's loads of stage kt have landed and every
         // wave has finished reading stage kt - 1, whose buffer is refilled next.
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
+        // INT8 issues the next stage's loads after its first MFMA step
+        // (measured 1.6 % faster); the other types right after the barrier.
+        constexpr bool LATE_ISSUE = DT == MM_INT8 && KG == 1;
+        if (!LATE_ISSUE && kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
         const int buf = kt % STAGES;
         if constexpr (KG == 1) {
             // 16-bit types: the compiler, left alone, reuses one set of
@@ -689,6 +692,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             for (int ks = 0; ks < KS; ++ks) {
                 if (ks + 1 < KS) read_frags(buf, ks + 1, (ks + 1) & 1);
                 mfmas(ks & 1);
+                if (LATE_ISSUE && ks == 0 && kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
                 if constexpr (SCHED) {
                     if (ks + 1 < KS) {
 #pragma unroll
