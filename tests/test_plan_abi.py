@@ -254,6 +254,17 @@ def test_selector(sa, sb, dt, algo):
     assert mm.ALGO_NAMES[mm.Plan(sa, sb, dt).algo] == algo
 
 
+@pytest.mark.parametrize("M,K,N,algo", [
+    (1, 4096, 15360, "split_k"),    # FP32 Gemm, <= 32 rows, fewer tiles than CUs
+    (32, 1024, 11008, "split_k"),
+    (32, 4096, 21760, "general"),   # 340 tiles: the tiles fill the GPU
+    (128, 4096, 15360, "general"),  # 128 rows: the tiles win
+])
+def test_fp32_gemm_few_rows(M, K, N, algo):
+    g = mm.GemmPlan((M, K), (N, K), mm.FLOAT, False, True, (N,), 1.0, 1.0)
+    assert mm.ALGO_NAMES[g.algo] == algo
+
+
 def test_small_m_tiles():
     """16-bit products of at most 64 rows take 64 x 64 tiles with two K
     groups up to one tile per CU, single-group 64 x 64 tiles up to 1.5 per
