@@ -332,6 +332,13 @@ static void plan_split(mm_plan_s *p, int requested) {
         // Aim for about one workgroup per CU, with at least 256 K elements
         // per partition (the partials then stay small next to the inputs).
         int64_t want = cdiv((int64_t)kNumCUs, std::max<int64_t>(tiles, 1));
+        // FP32 and DOUBLE: one partition fewer when that still fills three
+        // quarters of the CUs and the rounded-up count would put a second
+        // workgroup on a few of them (their long MFMA chains make that
+        // second one a slow last round; measured on 70 shapes, 0.64-0.89 of
+        // the time).  The 16-bit tiles gain nothing from it.
+        const bool long_chains = p->dtype == MM_FLOAT || p->dtype == MM_DOUBLE;
+        if (long_chains && want > 2 && tiles * want > kNumCUs && tiles * (want - 1) >= 3 * kNumCUs / 4) --want;
         int64_t max_s = std::max<int64_t>(1, p->K / 256);
         s = std::min(want, max_s);
     }
