@@ -106,7 +106,61 @@ __global__ __launch_bounds__(64 * kSkMWaves) void k_skinny_m(KArgs a) {
         for (int v = 0; v < VE; ++v) acc[m][v] = 0.0f;
 
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    for (int64_t k = klo; k < khi; k += U) {
+    // 16-bit types with 16-byte A and B rows: packed dot products.  The two
+    // B rows k + 2p and k + 2p + 1 are paired per column with byte selects
+    // (one select per column and pair of rows), and each output row takes
+    // a_{k+2p} b_{k+2p} + a_{k+2p+1} b_{k+2p+1} in one v_dot2_f32 (FP32
+    // accumulation), pairs in ascending k.  That halves the per-row vector
+    // work of the FP32 multiply-adds and drops the FP32 conversions.
+    constexpr bool DOT2 = (DT == MM_FLOAT16 || DT == MM_BFLOAT16) && VEC && AV_OK;
+    static_assert(!DOT2 || (U % 2 == 0 && VE == 8), "row pairs of eight-column chunks");
+    if constexpr (DOT2) {
+        for (int64_t k = klo; k < khi; k += U) {
+            uint32_t braw[U][4];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = col_ok && k + u < khi;
+                u32x4 raw = {0, 0, 0, 0};
+                if (ok) raw = __builtin_nontemporal_load((const u32x4 *)(Bb + (k + u) * N + n));
+#pragma unroll
+                for (int w = 0; w < 4; ++w) braw[u][w] = raw[w];
+            }
+            // bp[p][v]: (B[k+2p][n+v], B[k+2p+1][n+v]) as a packed pair.
+            uint32_t bp[U / 2][VE];
+#pragma unroll
+            for (int q = 0; q < U / 2; ++q)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t x = braw[2 * q][w], y = braw[2 * q + 1][w];
+                    bp[q][2 * w] = (x & 0xffffu) | (y << 16);
+                    bp[q][2 * w + 1] = (x >> 16) | (y & 0xffff0000u);
+                }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const bool row_ok = m0 + m < M;
+                uint32_t ap[U / 2];  // (A[m][k+2p], A[m][k+2p+1])
+#pragma unroll
+                for (int q = 0; q < U / AV; ++q) {
+                    uint4 raw = make_uint4(0, 0, 0, 0);
+                    if (row_ok && k + q * AV < khi) raw = *(const uint4 *)(Ab + (m0 + m) * K + k + q * AV);
+                    ap[4 * q] = raw.x; ap[4 * q + 1] = raw.y; ap[4 * q + 2] = raw.z; ap[4 * q + 3] = raw.w;
+                }
+#pragma unroll
+                for (int q = 0; q < U / 2; ++q)
+#pragma unroll
+                    for (int v = 0; v < VE; ++v) {
+                        if constexpr (DT == MM_FLOAT16)
+                            acc[m][v] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, ap[q]),
+                                                               __builtin_bit_cast(half2_t, bp[q][v]), acc[m][v], false);
+                        else
+                            acc[m][v] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfloat2_t, ap[q]),
+                                                                        __builtin_bit_cast(bfloat2_t, bp[q][v]),
+                                                                        acc[m][v], false);
+                    }
+            }
+        }
+    }
+    for (int64_t k = klo; k < (DOT2 ? klo : khi); k += U) {
         // B rows k .. k+U-1: streamed once, so loaded non-temporally.
         float bv[U][VE];
 #pragma unroll
