@@ -440,12 +440,13 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         // up to 8 rows wins everywhere (the tiles pad M to 64 rows of FP32
         // MFMA work), by up to 3x, and up to 15 rows with K >= 4096 and
         // N >= 4096; the 16-bit types, whose tiles run at the 16-bit MFMA
-        // rate, win only for up to 4 rows with a long K and a large B
-        // (K >= 8192, K * N >= 2^26).  Beyond that the kernel's per-row A
-        // loads make it latency-bound.
+        // rate, win for up to 4 rows with a long K and a large B (K >= 8192,
+        // K * N >= 2^26), and for up to 8 rows with K >= 16384 and
+        // N >= 8192 (packed dot products: 15-29 % faster than the tiles).
         const bool skm_split = has_skinny && K >= 1024 &&
                                ((p->dtype == MM_FLOAT && (M <= 8 || (M < 16 && K >= 4096 && N >= 4096))) ||
-                                (t16 && M <= 4 && K >= 8192 && (double)K * N >= 67108864.0));
+                                (t16 && M <= 4 && K >= 8192 && (double)K * N >= 67108864.0) ||
+                                (t16 && M <= 8 && K >= 16384 && N >= 8192));
         if (has_skinny && N < 16 && N <= M && K >= 64 && !skn_short) {
             algo = MM_ALGO_SKINNY_N;  // few columns: the rows of A stream in parallel, K split over waves
         } else if (flops <= direct_flops && K <= direct_k) {

@@ -216,7 +216,10 @@ SELECTOR_CASES = [
     ((8, 1024), (1024, 30720), mm.FLOAT, "skinny_m"),
     ((1, 16384), (16384, 8704), mm.BFLOAT16, "skinny_m"),  # 16-bit: up to 4 rows, long K, large B
     ((4, 4096), (4096, 30720), mm.BFLOAT16, "general"),   # 16-bit, K < 8192: the tiles
-    ((8, 16384), (16384, 8704), mm.BFLOAT16, "split_k"),  # 16-bit, 8 rows: split-K over the tiles
+    ((8, 16384), (16384, 8704), mm.BFLOAT16, "skinny_m"),  # 16-bit, 8 rows, K >= 16384, N >= 8192
+    ((8, 16384), (16384, 4352), mm.BFLOAT16, "split_k"),   # 16-bit, 8 rows, narrower B: the tiles
+    ((8, 4096), (4096, 30720), mm.FLOAT16, "general"),
+    ((15, 16384), (16384, 30720), mm.FLOAT16, "general"),
     ((1, 4096), (4096, 11008), mm.BFLOAT16, "split_k"),   # 172 tiles and K >= 4096
     ((1, 1024), (1024, 11008), mm.BFLOAT16, "general"),   # 172 tiles, K < 4096
     ((15, 4096), (4096, 8704), mm.FLOAT, "skinny_m"),     # FP32 9..15 rows: K >= 4096 and N >= 4096
