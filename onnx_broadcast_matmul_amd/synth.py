@@ -76,6 +76,45 @@ def generate(shape: Sequence[int], dtype: int, dist: Tuple, seed: Sequence[int])
     return to_storage(_draw(rng, n, dist, ft), dtype).reshape(tuple(shape))
 
 
+def generate_scaled_int(shape: Sequence[int], dtype: int, seed: Sequence[int], ints: Tuple[int, int],
+                        exps: Tuple[int, int], operand: str) -> np.ndarray:
+    """Storage array of ``shape`` whose values are i * 2^e: integers i uniform
+    over [ints[0], ints[1]] and exponents e uniform over [exps[0], exps[1]],
+    one exponent per row of an A operand (``operand="a"``: shared along the
+    last axis) or per column of a B operand (``operand="b"``: shared along
+    the second-to-last axis).  Every value is exactly representable in the
+    element type (checked); products of such operands are exact in FP32, and
+    with |i| small their sums are too, so results can be steered past a
+    type's largest finite value, into FP16 subnormals, or onto rounding ties
+    while staying bit-for-bit determined."""
+    shape = tuple(int(d) for d in shape)
+    rng = np.random.default_rng(list(seed))
+    n = int(np.prod(shape, dtype=np.int64)) if len(shape) else 1
+    iv = rng.integers(ints[0], ints[1] + 1, n).astype(np.float64).reshape(shape)
+    if len(shape) == 1:
+        eshape = (1,) if operand == "a" else shape
+    elif operand == "a":
+        eshape = shape[:-1] + (1,)
+    else:
+        eshape = shape[:-2] + (1,) + shape[-1:]
+    ev = rng.integers(exps[0], exps[1] + 1, int(np.prod(eshape, dtype=np.int64))).reshape(eshape)
+    x = np.ldexp(iv, ev)
+    ft = np.float64 if dtype == DOUBLE else np.float32
+    x32 = x.astype(ft)
+    if not np.array_equal(x32.astype(np.float64), x):
+        raise ValueError("scaled integers must be exact in the staging type")
+    st = to_storage(x32, dtype)
+    if dtype == FLOAT16:
+        back = st.view(np.float16).astype(np.float64)
+    elif dtype == BFLOAT16:
+        back = (st.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        back = st.astype(np.float64)
+    if not np.array_equal(back, x):
+        raise ValueError("scaled integers must be exact in the element type")
+    return st
+
+
 def as_torch(storage: np.ndarray, dtype: int):
     """CPU torch tensor viewing the same bits with the element type."""
     import torch

@@ -24,7 +24,10 @@ accumulation with final narrowing, page "MatMul Kernel Design", section
   max|C|)`` for the FP32 roundings of ``alpha * sum + beta * c`` (each term
   is at most that large).
 * Exact mode (small-integer-valued inputs): ``y == narrow(o)`` bit for bit.
-* NaN matches only NaN; an infinity matches only the same infinity.
+* Special values are judged against ``narrow(o)``, the oracle value rounded
+  once to the output type: NaN matches only NaN, and where ``narrow(o)`` is
+  an infinity (including a finite sum beyond the type's largest value) only
+  that same infinity matches; a finite reference needs a finite result.
 """
 from __future__ import annotations
 
@@ -87,20 +90,28 @@ class Report:
                 f"max_ulp={self.max_ulp} fp32_clause={self.n_fp32_clause} bad={self.n_bad} {self.detail}")
 
 
-def _special_mismatch(yv: np.ndarray, o: np.ndarray) -> np.ndarray:
-    """Elements where NaN/Inf status differs between result and oracle."""
-    nan_bad = np.isnan(yv) != np.isnan(o)
-    inf_o = np.isinf(o)
-    inf_y = np.isinf(yv)
-    inf_bad = (inf_o | inf_y) & ~(np.isnan(yv) | np.isnan(o)) & ~((inf_o & inf_y) & (np.sign(yv) == np.sign(o)))
-    return nan_bad | inf_bad
+def _special_mismatch(yv: np.ndarray, rv: np.ndarray) -> np.ndarray:
+    """Elements whose NaN / infinity status differs between the result ``yv``
+    and the reference ``rv`` -- the oracle value narrowed to the output type,
+    so a finite sum beyond the type's range is expected as that infinity.
+    NaN matches only NaN; an infinity matches only the same infinity."""
+    nan_bad = np.isnan(yv) != np.isnan(rv)
+    inf_y, inf_r = np.isinf(yv), np.isinf(rv)
+    inf_bad = (inf_y | inf_r) & ~(inf_y & inf_r & (np.sign(yv) == np.sign(rv)))
+    return nan_bad | (inf_bad & ~(np.isnan(yv) | np.isnan(rv)))
 
 
 def check(y: np.ndarray, o: np.ndarray, dtype: int, K: int, amax: float, bmax: float,
           exact: bool = False, tol: float = None) -> Report:
-    """Compare stored results ``y`` (float32 array, or uint16 bit patterns) with
-    fp64 oracle values ``o`` of the same shape.  ``tol`` overrides the
-    absolute rule (Gemm passes ``gemm_tolerance``)."""
+    """Compare stored results ``y`` (float32 / float64 arrays, or uint16 bit
+    patterns) with fp64 oracle values ``o`` of the same shape.  ``tol``
+    overrides the absolute rule (Gemm passes ``gemm_tolerance``).
+
+    Every status and distance is taken against ``narrow(o)``, the oracle
+    value rounded once to the output type: where that reference is an
+    infinity (a finite sum past the type's largest value) the result must be
+    the same infinity, and where it is finite the result must be finite and
+    within the tolerances; ulps are counted between finite bit patterns."""
     o = np.asarray(o, dtype=np.float64).reshape(-1)
     y = np.asarray(y).reshape(-1)
     if y.size != o.size:
@@ -113,29 +124,35 @@ def check(y: np.ndarray, o: np.ndarray, dtype: int, K: int, amax: float, bmax: f
         y_bits = y.view(np.uint16) if y.dtype != np.uint16 else y
         yv = decode(y_bits, dtype)
         ref = narrow(o, dtype)
-        special = _special_mismatch(yv, o)
-        finite = np.isfinite(yv) & np.isfinite(o)
-        err = np.where(finite, np.abs(yv - o), 0.0)
+        rv = decode(ref, dtype)
         if exact:
-            bad = (y_bits != ref) & ~(np.isnan(yv) & np.isnan(o))
+            bad = (y_bits != ref) & ~(np.isnan(yv) & np.isnan(rv))
+            finite = np.isfinite(yv) & np.isfinite(rv)
+            err = np.where(finite, np.abs(yv - o), 0.0)
             return Report(not bad.any(), int(y.size), float(err.max()), 0.0, n_bad=int(bad.sum()),
                           detail="exact")
+        special = _special_mismatch(yv, rv)
+        finite = np.isfinite(yv) & np.isfinite(rv)
+        err = np.where(finite, np.abs(yv - o), 0.0)
         ulp = np.where(finite, ulp_distance16(y_bits, ref), 0)
         ulp_ok = ulp <= 2
         tol_ok = err <= tol
-        bad = special | ~(ulp_ok | tol_ok)
+        bad = special | (finite & ~(ulp_ok | tol_ok))
         return Report(not bad.any(), int(y.size), float(err.max()), tol, max_ulp=int(ulp.max()),
-                      n_fp32_clause=int((~ulp_ok & tol_ok).sum()), n_bad=int(bad.sum()))
+                      n_fp32_clause=int((finite & ~ulp_ok & tol_ok).sum()), n_bad=int(bad.sum()))
     if dtype == FLOAT or dtype == DOUBLE:
         yv = y.astype(np.float64)
-        special = _special_mismatch(yv, o)
-        finite = np.isfinite(yv) & np.isfinite(o)
-        err = np.where(finite, np.abs(yv - o), 0.0)
+        ref = narrow(o, dtype)
+        rv = ref.astype(np.float64)
         if exact:
-            ref = narrow(o, dtype)
-            bad = (y != ref) & ~(np.isnan(yv) & np.isnan(o))
+            bad = (y.astype(ref.dtype) != ref) & ~(np.isnan(yv) & np.isnan(rv))
+            finite = np.isfinite(yv) & np.isfinite(rv)
+            err = np.where(finite, np.abs(yv - o), 0.0)
             return Report(not bad.any(), int(y.size), float(err.max()), 0.0, n_bad=int(bad.sum()),
                           detail="exact")
-        bad = special | (err > tol)
+        special = _special_mismatch(yv, rv)
+        finite = np.isfinite(yv) & np.isfinite(rv)
+        err = np.where(finite, np.abs(yv - o), 0.0)
+        bad = special | (finite & (err > tol))
         return Report(not bad.any(), int(y.size), float(err.max()), tol, n_bad=int(bad.sum()))
     raise ValueError(f"dtype {dtype}")

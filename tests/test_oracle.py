@@ -331,6 +331,134 @@ def test_comparator_ulp_rules():
     assert ulp_distance16(np.array([0x8001], np.uint16), np.array([0x0001], np.uint16))[0] == 2
 
 
+def test_comparator_judges_against_the_narrowed_reference():
+    """A finite oracle sum beyond the output type's largest value narrows to
+    infinity (round to nearest even), so the correct result is that infinity
+    and a saturated finite value is wrong; likewise a finite reference needs
+    a finite result.  Checked in tolerance and exact mode for every type."""
+    one = 1.0
+    # FP16: 70000 > 65504 -> +Inf (0x7C00); 65520 is the tie between 65504
+    # and 2^16 and rounds to the even pattern, which is +Inf; 65519 stays 65504.
+    o = np.array([70000.0, -70000.0, 65520.0, 65519.0, one])
+    good = np.array([0x7C00, 0xFC00, 0x7C00, 0x7BFF, 0x3C00], np.uint16)
+    assert np.array_equal(oracle.narrow(o, FLOAT16), good)
+    for exact in (False, True):
+        assert check(good, o, FLOAT16, 4, 1.0, 1.0, exact=exact).ok
+        for i, wrong in [(0, 0x7BFF), (1, 0xFBFF), (2, 0x7BFF), (3, 0x7C00), (1, 0x7C00)]:
+            y = good.copy()
+            y[i] = wrong
+            r = check(y, o, FLOAT16, 4, 1.0, 1.0, exact=exact)
+            assert not r.ok and r.n_bad == 1, (exact, i, hex(wrong))
+    # BF16: 2^128 and the tie (255.5 * 2^120) round up to +Inf; just below
+    # the tie stays at the largest finite value 0x7F7F.
+    big = np.array([2.0 ** 128, 255.5 * 2.0 ** 120, 255.25 * 2.0 ** 120, one])
+    good = np.array([0x7F80, 0x7F80, 0x7F7F, 0x3F80], np.uint16)
+    assert np.array_equal(oracle.narrow(big, BFLOAT16), good)
+    for exact in (False, True):
+        assert check(good, big, BFLOAT16, 4, 1.0, 1.0, exact=exact).ok
+        y = good.copy()
+        y[0] = 0x7F7F
+        assert not check(y, big, BFLOAT16, 4, 1.0, 1.0, exact=exact).ok
+    # FP32: 4e38 -> +Inf; FLT_MAX in its place is wrong, and +Inf where the
+    # reference is finite is wrong.
+    o = np.array([4e38, -4e38, one])
+    good = np.array([np.inf, -np.inf, 1.0], np.float32)
+    for exact in (False, True):
+        assert check(good, o, FLOAT, 4, 1.0, 1.0, exact=exact).ok
+        y = good.copy()
+        y[0] = np.finfo(np.float32).max
+        assert not check(y, o, FLOAT, 4, 1.0, 1.0, exact=exact).ok
+        y = good.copy()
+        y[2] = np.inf
+        assert not check(y, o, FLOAT, 4, 1.0, 1.0, exact=exact).ok
+    # NaN only matches NaN.
+    o = np.array([np.nan, one])
+    assert check(np.array([0x7E00, 0x3C00], np.uint16), o, FLOAT16, 4, 1.0, 1.0).ok
+    assert not check(np.array([0x7C00, 0x3C00], np.uint16), o, FLOAT16, 4, 1.0, 1.0).ok
+    assert not check(np.array([0x3C00, 0x7E00], np.uint16), o, FLOAT16, 4, 1.0, 1.0).ok
+    # FP16 subnormal: 2^-20 is 0x0010; flushing it to zero fails in exact mode.
+    o = np.array([2.0 ** -20])
+    assert oracle.narrow(o, FLOAT16)[0] == 0x0010
+    assert check(np.array([0x0010], np.uint16), o, FLOAT16, 4, 1.0, 1.0, exact=True).ok
+    assert not check(np.array([0x0000], np.uint16), o, FLOAT16, 4, 1.0, 1.0, exact=True).ok
+
+
+def _edge_classes(exact: np.ndarray, dtype: int):
+    """Counts of exact values whose narrowing overflows, lands in FP16
+    subnormals, or is a rounding tie (exactly halfway between neighbours)."""
+    p, emin = (11, -14) if dtype == FLOAT16 else (8, -126)
+    big = 65520.0 if dtype == FLOAT16 else 255.5 * 2.0 ** 120
+    ax = np.abs(exact)
+    fin = np.isfinite(ax) & (ax > 0)
+    e = np.floor(np.log2(np.where(fin, ax, 1.0)))
+    ulp = np.ldexp(1.0, (np.maximum(e, emin) - (p - 1)).astype(np.int64))
+    frac = np.where(fin, ax / ulp - np.floor(ax / ulp), 0.0)
+    return {
+        "overflow": int((ax >= big).sum()),
+        "subnormal": int((fin & (ax < 2.0 ** emin)).sum()),
+        "tie": int((fin & (ax < big) & (frac == 0.5)).sum()),
+    }
+
+
+@pytest.mark.parametrize("dtype,ints,exps", [
+    (FLOAT16, (-31, 31), (-14, 7)),    # overflow, subnormals, ties, underflow
+    (BFLOAT16, (-31, 31), (-20, 20)),  # ties
+    (BFLOAT16, (0, 31), (40, 60)),     # overflow (positive terms: FP32 sums never cancel)
+    (FLOAT, (0, 31), (40, 60)),        # FP32 overflow
+])
+def test_narrowing_edges_exact(dtype, ints, exps):
+    """Power-of-two-scaled integers: the exact product is the int64 product of
+    the integer parts times 2^(e_row + e_col), so the oracle's narrowed output
+    must equal numpy's float16 rounding (FP16), torch's bfloat16 rounding of
+    the exactly representable float32 value (BF16), or numpy's float32
+    rounding (FP32) of that exact value, bit for bit -- at overflow, in FP16
+    subnormals and on rounding ties, each of which the inputs must reach."""
+    import torch
+
+    shape_a, shape_b = (2, 40, 96), (96, 70)
+    a = synth.generate_scaled_int(shape_a, dtype, [31, 0, 0], ints, exps, "a")
+    b = synth.generate_scaled_int(shape_b, dtype, [31, 0, 1], ints, exps, "b")
+    av = oracle.decode(a, dtype) if dtype != FLOAT else a.astype(np.float64)
+    bv = oracle.decode(b, dtype) if dtype != FLOAT else b.astype(np.float64)
+
+    # Split each row of A (column of B) into integers times a common power of
+    # two, taken from the row's smallest non-zero magnitude.
+    def split(v, axis):
+        nz = np.where(v != 0, np.abs(v), np.inf)
+        lo = np.floor(np.log2(np.min(nz, axis=axis, keepdims=True)))
+        lo = np.where(np.isfinite(lo), lo, 0.0) - 5
+        ints_ = np.ldexp(v, (-lo).astype(np.int64))
+        assert np.array_equal(ints_, np.round(ints_))
+        return ints_.astype(np.int64), lo.astype(np.int64)
+
+    ia, sa = split(av, -1)
+    ib, sb = split(bv, -2)
+    S = np.matmul(ia, ib)                              # exact int64 sums
+    assert np.abs(S).max() < 2 ** 53
+    exact = np.ldexp(S.astype(np.float64), sa + sb)  # exact: |S| < 2^53, no underflow here
+    got = oracle.narrow(oracle.matmul(a, b, dtype), dtype)
+    with np.errstate(over="ignore"):
+        if dtype == FLOAT16:
+            want = exact.astype(np.float16).view(np.uint16)
+        elif dtype == BFLOAT16:
+            f32 = exact.astype(np.float32)
+            assert np.array_equal(f32.astype(np.float64)[np.isfinite(f32)], exact[np.isfinite(f32)])
+            want = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        else:
+            want = exact.astype(np.float32)
+    assert np.array_equal(got, want)
+    if dtype == FLOAT:
+        assert np.isinf(got).sum() > 50 and np.isfinite(got).sum() > 50
+        return
+    cls = _edge_classes(exact, dtype)
+    if ints[0] < 0:
+        assert cls["tie"] > 50, cls
+    if dtype == FLOAT16 or ints[0] >= 0:
+        assert cls["overflow"] > 50, cls
+    if dtype == FLOAT16:
+        assert cls["subnormal"] > 50, cls
+
+
 def test_comparator_fp32_rule():
     o = np.array([1.0, -2.0])
     K, amax, bmax = 100, 2.0, 3.0
