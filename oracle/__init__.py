@@ -45,7 +45,7 @@ class OracleError(RuntimeError):
 def build() -> str:
     """Compile oracle.c into liboracle.so with gcc (always recompiles)."""
     cmd = [
-        "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+        "gcc", "-O2", "-ftree-vectorize", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
         "-Wall", "-Wextra", SRC, "-o", LIB + ".tmp", "-lm",
     ]
     subprocess.run(cmd, check=True)

@@ -21,8 +21,14 @@
  *
  * Arithmetic: every stored element is decoded exactly to double (FP32, FP16
  * and BF16 all embed exactly in binary64); each output is the sum over k in
- * ascending order of a[m,k]*b[k,n] accumulated in double.  Nothing is blocked,
- * reordered or fused.  Build with -O2 -ffp-contract=off and no fast-math.
+ * ascending order of a[m,k]*b[k,n] accumulated in double.  Nothing is fused,
+ * and no output's summation order changes: the full product walks k in the
+ * outer loop over a handful of rows at a time (one double accumulator per
+ * output, each still receiving its terms in ascending k), which gives the
+ * same bits as the per-element loop that oracle_matmul_at keeps (a test pins
+ * the two against each other) while reading each row of B once per group of
+ * rows instead of once per output.  Build with -O2 -ffp-contract=off and no
+ * fast-math, so every product and every sum is rounded on its own.
  *
  * The narrowing helpers (double -> FP16 / BF16, round to nearest, ties to
  * even, single rounding) exist so the comparator can narrow the exact result
@@ -343,8 +349,15 @@ static double dot_one(const shapes_t *s, int dtype, const void *A, const void *B
     return acc;
 }
 
+/* Rows of one batch matrix that the full product carries at once. */
+#define OR_ROW_GROUP 16
+
 /* Full MatMul.  Y receives nbatch*M*N doubles in row-major order of the
- * output shape (squeezed axes have size 1, so the order is the same). */
+ * output shape (squeezed axes have size 1, so the order is the same).
+ * Work items are (batch, group of up to OR_ROW_GROUP rows); for each k in
+ * ascending order, row k of B is decoded once and a[m,k]*b[k,n] is added to
+ * the double accumulator of every output (m, n) of the group -- the same
+ * operations, in the same order per output, as dot_one. */
 int oracle_matmul(int dtype, const void *A, const int64_t *a_shape, int a_rank, const void *B,
                   const int64_t *b_shape, int b_rank, double *Y)
 {
@@ -353,17 +366,40 @@ int oracle_matmul(int dtype, const void *A, const int64_t *a_shape, int a_rank, 
     shapes_t s;
     int st = resolve(a_shape, a_rank, b_shape, b_rank, &s);
     if (st != OR_OK) return st;
-    int64_t rows = s.nbatch * s.M;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t r = 0; r < rows; ++r) {
-        int64_t bi = r / s.M, m = r % s.M;
-        int64_t offa, offb;
-        batch_offsets(&s, bi, &offa, &offb);
-        for (int64_t n = 0; n < s.N; ++n)
-            Y[r * s.N + n] = dot_one(&s, dtype, A, B, offa, offb, m, n);
+    const int64_t groups = (s.M + OR_ROW_GROUP - 1) / OR_ROW_GROUP;
+    const int64_t items = s.nbatch * groups;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *brow = (double *)malloc((size_t)(s.N > 0 ? s.N : 1) * sizeof(double));
+        double *acc = (double *)malloc((size_t)(s.N > 0 ? s.N : 1) * OR_ROW_GROUP * sizeof(double));
+        if (!brow || !acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < items; ++it) {
+            if (!brow || !acc) continue;
+            const int64_t bi = it / groups, m0 = (it % groups) * OR_ROW_GROUP;
+            const int64_t rows = (s.M - m0) < OR_ROW_GROUP ? (s.M - m0) : OR_ROW_GROUP;
+            int64_t offa, offb;
+            batch_offsets(&s, bi, &offa, &offb);
+            for (int64_t i = 0; i < rows * s.N; ++i) acc[i] = 0.0;
+            for (int64_t k = 0; k < s.K; ++k) {
+                for (int64_t n = 0; n < s.N; ++n) brow[n] = load_elem(B, dtype, offb + k * s.N + n);
+                for (int64_t r = 0; r < rows; ++r) {
+                    const double a = load_elem(A, dtype, offa + (m0 + r) * s.K + k);
+                    double *ar = acc + r * s.N;
+                    for (int64_t n = 0; n < s.N; ++n) ar[n] += a * brow[n];
+                }
+            }
+            memcpy(Y + (bi * s.M + m0) * s.N, acc, (size_t)(rows * s.N) * sizeof(double));
+        }
+        free(brow);
+        free(acc);
     }
     shapes_free(&s);
-    return OR_OK;
+    return failed ? OR_ERR_ALLOC : OR_OK;
 }
 
 /* Selected output elements, by flat row-major index into the output.  For

@@ -207,13 +207,21 @@ def test_rank1_equals_promoted():
     assert np.array_equal(oracle.matmul(A, b, FLOAT), oracle.matmul(A, b[:, None], FLOAT)[..., 0])
 
 
-def test_matmul_at_equals_full():
+@pytest.mark.parametrize("dtype", [FLOAT, FLOAT16, BFLOAT16, DOUBLE])
+def test_matmul_at_equals_full(dtype):
+    """The full product (k outer over groups of rows) and the per-element
+    loop of matmul_at sum every output in the same order: bitwise equal on
+    every output, over broadcast batches, several row groups with a ragged
+    last group, a single-row batch matrix and a rank-one B."""
     rng = np.random.default_rng(21)
-    A = synth.to_storage(rng.standard_normal((2, 1, 7, 33)).astype(np.float32), FLOAT16)
-    B = synth.to_storage(rng.standard_normal((3, 33, 5)).astype(np.float32), FLOAT16)
-    full = oracle.matmul(A, B, FLOAT16).reshape(-1)
-    idx = rng.choice(full.size, 40, replace=False)
-    assert np.array_equal(oracle.matmul_at(A, B, FLOAT16, idx), full[idx])
+    ft = np.float64 if dtype == DOUBLE else np.float32
+    for sa, sb in [((2, 1, 7, 33), (3, 33, 5)), ((3, 37, 50), (50, 41)), ((4, 1, 64), (4, 64, 9)),
+                   ((5, 19, 12), (12,))]:
+        A = synth.to_storage(rng.standard_normal(sa).astype(ft), dtype)
+        B = synth.to_storage(rng.standard_normal(sb).astype(ft), dtype)
+        full = oracle.matmul(A, B, dtype).reshape(-1)
+        idx = np.arange(full.size)
+        assert np.array_equal(oracle.matmul_at(A, B, dtype, idx), full), (sa, sb)
 
 
 # ---------------------------------------------------------------- decoding
