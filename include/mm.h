@@ -19,8 +19,9 @@
  * selection": the adapter takes DOUBLE with the same shape rules).
  *
  * Usage: create a plan once per (A shape, B shape, type); execute it any
- * number of times on device buffers; destroy it.  Plan creation touches no
- * GPU.  Every shape/type error is reported by plan creation, before compute.
+ * number of times on device buffers; destroy it.  Every shape/type error is
+ * reported by plan creation, before compute.  Plan creation makes no GPU
+ * call except for a plan that needs a workspace (below), which it allocates.
  *
  * Layout: A, B and Y are dense, contiguous, row-major device tensors with the
  * ONNX shapes given at plan creation (Y has the plan's output shape).
@@ -30,16 +31,22 @@
  * Ownership: the caller owns A, B and Y and keeps them alive until the work
  * enqueued on the stream has completed.  The plan owns its metadata and, for
  * the split-K algorithm and a skinny-M plan that cuts K (split_k > 1 in
- * mm_plan_info), an FP32 (DOUBLE: double) workspace on the device of the
- * first execution (allocated by that first mm_execute, freed by
- * mm_plan_destroy; mm_plan_workspace_bytes() > 0 tells which plans have one).
- * Because of that workspace, executions of such a plan must not overlap on
- * different streams; use one plan per stream.  The allocation cannot happen
- * while the stream is being captured into a HIP graph (the execute then
- * fails with MM_ERR_ALLOC): execute such a plan once before capturing it.
+ * mm_plan_info), an FP32 (DOUBLE: double) workspace of
+ * mm_plan_workspace_bytes() bytes, allocated by plan creation on the current
+ * device and freed by mm_plan_destroy (page "Gemm and MatMul Performance
+ * Roadmap", section "Planning once, computing many times": what the chosen
+ * algorithm and its parallel decomposition need is prepared with the plan,
+ * and execution only invokes it).  On a host where
+ * creation finds no GPU, the first execution allocates it instead.  Because
+ * of that workspace, executions of such a plan must not overlap on different
+ * streams; use one plan per stream.  A plan executes on the device that
+ * holds its workspace (another device gives MM_ERR_HIP).  Executions
+ * allocate nothing once the workspace exists, so a plan created before a
+ * HIP graph capture may be executed inside it.
  *
- * Threading: plans are immutable after creation apart from the lazily
- * allocated workspace, which is guarded; mm_last_error() is per thread.
+ * Threading: plans are immutable after creation apart from a workspace that
+ * the first execution allocates, which is guarded; mm_last_error() is per
+ * thread.
  */
 #ifndef MM_H
 #define MM_H
@@ -145,8 +152,10 @@ typedef struct mm_plan_info {
  * B of shape b_shape[0..b_rank), all of type `dtype`.  Validates ranks
  * (1..MM_MAX_RANK), dimensions (>= 0), the inner dimension, batch
  * broadcasting and the type; resolves the output shape, collapsed batch
- * strides and the algorithm.  Host only: no GPU call.  On error *out is set
- * to NULL and a status is returned (details: mm_last_error()). */
+ * strides and the algorithm.  A plan that needs a workspace allocates it on
+ * the current device (MM_ERR_ALLOC if that fails; skipped on a host without
+ * a GPU); no other GPU call is made.  On error *out is set to NULL and a
+ * status is returned (details: mm_last_error()). */
 mm_status mm_plan_create(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank,
                          int dtype, mm_plan_t *out);
 
@@ -277,7 +286,7 @@ int64_t mm_plan_output_numel(mm_plan_t plan);
 /* Selected algorithm (an mm_algo value), or -1 for a NULL plan. */
 int mm_plan_algo(mm_plan_t plan);
 
-/* Device workspace bytes the plan uses (0 unless SPLIT_K or a split SKINNY_M). */
+/* Device workspace bytes the plan owns (0 unless SPLIT_K or a split SKINNY_M). */
 size_t mm_plan_workspace_bytes(mm_plan_t plan);
 
 /* Fill *info with everything the plan resolved. */

@@ -243,7 +243,7 @@ class Plan:
         _check(lib().mm_execute(self._handle, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(Y),
                                 ctypes.c_void_p(stream)))
 
-    def execute(self, A, B, Y, stream=None) -> None:
+    def execute(self, A, B, Y, stream=None, _entry=None) -> None:
         """mm_execute on torch device tensors; ``stream`` is a torch.cuda.Stream
         (default: the current stream of Y's device)."""
         import torch
@@ -261,7 +261,7 @@ class Plan:
         if stream is None:
             stream = torch.cuda.current_stream(Y.device)
         with self._lock:
-            self.execute_ptr(A.data_ptr(), B.data_ptr(), Y.data_ptr(), stream.cuda_stream)
+            (_entry or self.execute_ptr)(A.data_ptr(), B.data_ptr(), Y.data_ptr(), stream.cuda_stream)
 
     # ---- plan-owned constant B
     def set_constant_b_ptr(self, B: int, numel: int, stream: int = 0) -> None:

@@ -59,6 +59,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
+    # The LDS-load asm writes M0 behind the compiler's back: refuse a build
+    # in which the compiler uses M0 in the same kernels.
+    from . import m0check
+
+    m0check.check_objects([o for o in objs if o.endswith(".hip.o")])
     tmp = LIB + ".tmp"
     _run([HIPCC, *DEVICE, "-shared", "-fPIC", *objs, "-o", tmp, f"-Wl,-rpath,{ROCM}/lib"])
     os.replace(tmp, LIB)

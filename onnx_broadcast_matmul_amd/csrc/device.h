@@ -106,9 +106,12 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void *base) {
 // 16 bytes per lane from global into LDS at lds_base + 16 * lane.  The
 // load takes its LDS address from M0.  The compiler reserves M0 and ignores
 // it in a clobber list, so the asm cannot declare the write; the kernels
-// that use this helper compile to code that uses M0 for nothing else (no
-// other M0 reference in their gfx950 ISA).  Saving and restoring M0 around
-// each load cost 2-3 % on the DMA-bound tiles.
+// that use this helper must compile to code that uses M0 for nothing else,
+// and the build disassembles every such kernel and fails if the compiler
+// writes or reads M0 anywhere in it (m0check.py).  Saving and restoring M0
+// around each load cost 2-3 % on the DMA-bound tiles; the compiler-owned
+// builtin for this load makes the compiler wait for all outstanding LDS
+// loads before the next LDS read, which serialises the stage pipeline.
 __device__ __forceinline__ void load_to_lds16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :

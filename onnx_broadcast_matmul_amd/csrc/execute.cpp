@@ -13,11 +13,25 @@ static mm_status hip_fail(hipError_t e, const char *what) {
     return fail(MM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Split-K workspace: allocated once, on the device of the first execution.
-static mm_status ensure_workspace(mm_plan_s *p) {
+namespace mm {
+
+// Split-K workspace: allocated once, on the current device, by plan creation
+// (at_create) or -- when creation found no GPU -- by the first execution.
+mm_status alloc_workspace(mm_plan_s *p, bool at_create) {
+    if (p->workspace_bytes <= 0) return MM_OK;
+    if (at_create) {
+        int count = 0;
+        if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+            (void)hipGetLastError();  // no GPU here: leave no error behind for later launches
+            return MM_OK;
+        }
+    }
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_fail(e, "hipGetDevice");
+    }
     std::lock_guard<std::mutex> lock(p->ws_mutex);
     if (p->ws) {
         if (p->ws_device != dev)
@@ -27,15 +41,25 @@ static mm_status ensure_workspace(mm_plan_s *p) {
     }
     void *ptr = nullptr;
     e = hipMalloc(&ptr, (size_t)p->workspace_bytes);
-    if (e != hipSuccess) return fail(MM_ERR_ALLOC, "hipMalloc of %lld workspace bytes: %s",
-                                     (long long)p->workspace_bytes, hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MM_ERR_ALLOC, "hipMalloc of %lld workspace bytes: %s", (long long)p->workspace_bytes,
+                    hipGetErrorString(e));
+    }
     p->ws = ptr;
     p->ws_device = dev;
     return MM_OK;
 }
 
-// Launches of a MatMul or Gemm plan (C: the Gemm bias, NULL if none).
-static mm_status execute_impl(mm_plan_s *p, const void *A, const void *B, const void *C, void *Y, void *stream) {
+}  // namespace mm
+
+static mm_status ensure_workspace(mm_plan_s *p) { return alloc_workspace(p, false); }
+
+// Launches of a MatMul or Gemm plan (C: the Gemm bias, NULL if none).  The
+// split partial sums go to `ws` when it is not NULL (at least the plan's
+// workspace_bytes, on the current device), else to the plan's workspace.
+mm_status mm::execute_plan(mm_plan_s *p, const void *A, const void *B, const void *C, void *Y, void *stream,
+                           void *ws) {
     if (p->algo == MM_ALGO_EMPTY) return MM_OK;
     if (!Y) return fail(MM_ERR_NULL_ARG, "Y is NULL for a non-empty output");
     hipStream_t s = (hipStream_t)stream;
@@ -91,9 +115,11 @@ static mm_status execute_impl(mm_plan_s *p, const void *A, const void *B, const 
     case MM_ALGO_SKINNY_M:
         if (p->split > 1) {
             // K cut into chunks: FP32 partials, then the split-K reduction.
-            mm_status st = ensure_workspace(p);
-            if (st != MM_OK) return st;
-            a.W = (float *)p->ws;
+            if (!ws) {
+                mm_status st = ensure_workspace(p);
+                if (st != MM_OK) return st;
+            }
+            a.W = (float *)(ws ? ws : p->ws);
             e = launch_skinny_m(p->dtype, al, a, s);
             if (e == hipSuccess) e = launch_splitk_reduce(p->dtype, a, s);
         } else {
@@ -131,9 +157,11 @@ static mm_status execute_impl(mm_plan_s *p, const void *A, const void *B, const 
         }
         break;
     case MM_ALGO_SPLIT_K: {
-        mm_status st = ensure_workspace(p);
-        if (st != MM_OK) return st;
-        a.W = (float *)p->ws;
+        if (!ws) {
+            mm_status st = ensure_workspace(p);
+            if (st != MM_OK) return st;
+        }
+        a.W = (float *)(ws ? ws : p->ws);
         if (f64) {
             e = launch_general_f64(p->tile, al, true, a, s);
             if (e == hipSuccess) e = launch_splitk_reduce_f64(a, s);
@@ -157,7 +185,7 @@ mm_status mm_execute(mm_plan_t p, const void *A, const void *B, void *Y, void *s
     if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
     if (p->is_gemm) return fail(MM_ERR_BAD_OPTION, "a Gemm plan runs through mm_gemm_execute");
     if (p->is_int) return fail(MM_ERR_BAD_OPTION, "a MatMulInteger plan runs through mm_int_execute");
-    return execute_impl(p, A, B, nullptr, Y, stream);
+    return execute_plan(p, A, B, nullptr, Y, stream, nullptr);
 }
 
 mm_status mm_int_execute(mm_plan_t p, const void *A, const void *B, const void *za, const void *zb, void *Y,
@@ -241,7 +269,7 @@ mm_status mm_gemm_execute(mm_plan_t p, const void *A, const void *B, const void 
     clear_error();
     if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
     if (!p->is_gemm) return fail(MM_ERR_BAD_OPTION, "not a Gemm plan");
-    return execute_impl(p, A, B, C, Y, stream);
+    return execute_plan(p, A, B, C, Y, stream, nullptr);
 }
 
 mm_status mm_plan_set_constant_b(mm_plan_t p, const void *B, int64_t numel, void *stream) {

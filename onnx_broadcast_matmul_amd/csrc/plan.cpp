@@ -1,6 +1,7 @@
 // plan.cpp -- host-side MatMul plan: shape resolution, broadcast strides,
-// batch collapsing/folding and algorithm selection.  No GPU call happens
-// here, so the whole layer is testable on a machine without a GPU.
+// batch collapsing/folding and algorithm selection.  The only GPU calls are
+// the device query and allocation of a split plan's workspace, and a host
+// without a GPU skips them, so the whole layer is testable there.
 //
 // Page "MatMul Kernel Design", section "Shape and plan model": the plan
 // resolves the complete output shape before execution (rank-one promotion and
@@ -442,11 +443,15 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         // N >= 4096; the 16-bit types, whose tiles run at the 16-bit MFMA
         // rate, win for up to 4 rows with a long K and a large B (K >= 8192,
         // K * N >= 2^26), and for up to 8 rows with K >= 16384 and
-        // N >= 8192 (packed dot products: 15-29 % faster than the tiles).
+        // N >= 8704 (packed dot products: 15-29 % faster than the tiles).
+        // The 16-bit wins come from the packed-dot kernel, which needs rows
+        // of A, B and Y in whole 16-byte chunks (K and N multiples of 8);
+        // other 16-bit shapes keep the tiles or split-K.
+        const bool rows16 = K % 8 == 0 && N % 8 == 0;
         const bool skm_split = has_skinny && K >= 1024 &&
                                ((p->dtype == MM_FLOAT && (M <= 8 || (M < 16 && K >= 4096 && N >= 4096))) ||
-                                (t16 && M <= 4 && K >= 8192 && (double)K * N >= 67108864.0) ||
-                                (t16 && M <= 8 && K >= 16384 && N >= 8192));
+                                (t16 && rows16 && M <= 4 && K >= 8192 && (double)K * N >= 67108864.0) ||
+                                (t16 && rows16 && M <= 8 && K >= 16384 && N >= 8704));
         if (has_skinny && N < 16 && N <= M && K >= 64 && !skn_short) {
             algo = MM_ALGO_SKINNY_N;  // few columns: the rows of A stream in parallel, K split over waves
         } else if (flops <= direct_flops && K <= direct_k) {
@@ -540,6 +545,7 @@ mm_status mm_plan_create_ex(const int64_t *a_shape, int a_rank, const int64_t *b
     p->dtype = dtype;
     mm_status st = resolve(a_shape, a_rank, b_shape, b_rank, p);
     if (st == MM_OK) st = select_algo(p, opt);
+    if (st == MM_OK) st = alloc_workspace(p, true);
     if (st != MM_OK) {
         delete p;
         return st;
@@ -654,8 +660,9 @@ mm_status mm_gemm_plan_create(const mm_gemm_desc *d, int dtype, const mm_plan_op
     p->kernel_m = M;
     p->folded = 0;
     mm_status st = select_algo(p, opt);
+    if (st == MM_OK) st = alloc_workspace(p, true);
     if (st != MM_OK) {
-        delete p;
+        mm_plan_destroy(p);
         return st;
     }
     *out = p;

@@ -33,7 +33,9 @@ struct mm_plan_s {
     int64_t kchunk = 0;
     int64_t workspace_bytes = 0;
 
-    // Device workspace for split-K, allocated on first execution.
+    // Device workspace for split-K and a split skinny-M, allocated by plan
+    // creation on the current device (by the first execution when creation
+    // found no GPU).
     std::mutex ws_mutex;
     void *ws = nullptr;
     int ws_device = -1;
@@ -61,6 +63,13 @@ struct mm_plan_s {
 };
 
 namespace mm {
+// Allocate the plan's split workspace on the current device (execute.cpp).
+// At creation a host without a GPU is not an error: the first execution
+// allocates instead.
+mm_status alloc_workspace(mm_plan_s *p, bool at_create);
+// Enqueue a MatMul or Gemm plan (C: the Gemm bias or NULL); split partial
+// sums go to `ws` when it is not NULL, else to the plan's workspace.
+mm_status execute_plan(mm_plan_s *p, const void *A, const void *B, const void *C, void *Y, void *stream, void *ws);
 mm_status fail(mm_status st, const char *fmt, ...);
 void clear_error();
 int elem_size(int dtype);

@@ -7,8 +7,8 @@ round their products); bit-exact on small-integer-valued inputs.  DOUBLE has
 no skinny kernels, so its cases skip the forced skinny algorithms.  Every
 algorithm is forced on every element type over shapes that span several
 tiles and ragged tails, plus broadcast, rank-one, empty, K == 0, unaligned
-and special-value cases, and the full-size workload products on sampled
-outputs.
+and special-value cases, and the full-size workload products on every
+output.
 """
 import numpy as np
 import pytest
@@ -141,8 +141,12 @@ def test_skinny_m_split_counts(dt, split, dev):
     multiple of the 64-row chunk unit, a folded batch (rows in two row
     groups), broadcast batches, unaligned columns (element-wise loads), and
     small-integer exactness whatever the chunk count."""
+    # The last two have K and N multiples of 8 (rows of 16-byte chunks): for
+    # the 16-bit types they run the packed-dot kernel's 2-row and 8-row
+    # instances.
     cases = [((1, 4100), (4100, 300)), ((5, 2, 3, 1000), (1000, 520)),
-             ((3, 1, 4, 640), (2, 640, 136)), ((2, 1111), (1111, 77))]
+             ((3, 1, 4, 640), (2, 640, 136)), ((2, 1111), (1111, 77)),
+             ((2, 4096), (4096, 264)), ((6, 2048), (2048, 136))]
     for i, (sa, sb) in enumerate(cases):
         plan, _, _ = parity(sa, sb, dt, dev, algo=mm.ALGO_SKINNY_M, split=split, seed=60 + i)
         assert 1 <= plan.info()["split_k"] <= split
@@ -507,6 +511,7 @@ SELECTED_PATHS = [
     ((1, 4096), (4096, 8704), mm.FLOAT, False, ("skinny_m", 0, 13)),      # FP32 GEMV, K in 13 chunks
     ((15, 4096), (4096, 8704), mm.FLOAT, False, ("skinny_m", 0, 13)),
     ((1, 16384), (16384, 8704), mm.BFLOAT16, False, ("skinny_m", 0, 29)),  # 16-bit GEMV, long K
+    ((8, 16384), (16384, 8704), mm.BFLOAT16, False, ("skinny_m", 0, 29)),  # 8 rows: packed-dot 8-row instance
     ((64, 1024), (1024, 15360), mm.BFLOAT16, False, ("general", 9, 1)),    # <= 64 rows: two-group 64x64
     ((1, 4096), (4096, 21760), mm.FLOAT16, False, ("general", 5, 1)),      # <= 64 rows, 340 tiles: 64x64
     ((256, 4096), (4096, 4352), mm.BFLOAT16, False, ("split_k", 6, 4)),   # split-K tiles at most 128x128
@@ -550,21 +555,70 @@ def test_selected_paths_full_size(sa, sb, dt, gemm, want, dev):
     assert rep.ok, f"{sa} x {sb} {DT_IDS[dt]} {want}: {rep}"
 
 
+def _leading_blocks(sa, sb):
+    """(A slice, B slice) pairs that cover the output in blocks along its
+    leading batch axis (one block when the output has no batch axis)."""
+    ra, rb = len(sa), len(sb)
+    nb = max(ra - 2 if ra > 1 else 0, rb - 2 if rb > 1 else 0)
+    if nb == 0:
+        return [(slice(None), slice(None))], None
+    da = sa[0] if ra - 2 == nb else 1
+    db = sb[0] if rb - 2 == nb else 1
+    n = max(da, db)
+    blocks = []
+    for i in range(n):
+        sla = slice(i, i + 1) if (ra - 2 == nb and da > 1) else slice(None)
+        slb = slice(i, i + 1) if (rb - 2 == nb and db > 1) else slice(None)
+        blocks.append((sla, slb))
+    return blocks, n
+
+
+def full_compare(a, b, dt, y, K, exact=False):
+    """Compare every output y (storage of the full output) with the oracle,
+    computed block by block along the leading batch axis to bound host
+    memory; returns (elements compared, worst report)."""
+    blocks, n = _leading_blocks(a.shape, b.shape)
+    amax, bmax = abs_max(a, dt), abs_max(b, dt)
+    compared, reps = 0, []
+    for i, (sla, slb) in enumerate(blocks):
+        ab = a[sla] if n else a
+        bb = b[slb] if n else b
+        o = oracle.matmul(np.ascontiguousarray(ab), np.ascontiguousarray(bb), dt)
+        yb = y[i:i + 1] if n else y
+        rep = check(yb.reshape(-1), o.reshape(-1), dt, K, amax, bmax, exact=exact)
+        assert rep.ok, f"block {i}: {rep}"
+        compared += o.size
+        reps.append(rep)
+    worst = max(reps, key=lambda r: (r.max_ulp, r.max_abs_err))
+    return compared, worst
+
+
 @pytest.mark.parametrize("product", synth.all_products(), ids=lambda p: p.name)
 def test_workload_full_size(product, dev):
     """Each workload product at full size in the configuration the benchmark
-    times (the plan's own choice), checked on sampled outputs against the
-    oracle and on every output for finiteness."""
+    times (the plan's own choice), every output compared with the oracle."""
     print(f"\n[full-size] {product.name} {product.a_shape} x {product.b_shape}", flush=True)
     a, b = product.make()
     dt = product.dtype
     plan = mm.Plan(product.a_shape, product.b_shape, dt)
     Y = run_plan(plan, a, b, dt, dev)
     y = synth.from_torch(Y)
-    assert torch.isfinite(Y.float()).all().item()
-    rng = np.random.default_rng(1234)
-    idx = _sample_indices(plan.output_shape, 3000, rng)
-    o = oracle.matmul_at(a, b, dt, idx)
-    rep = check(y.reshape(-1)[idx], o, dt, product.K, abs_max(a, dt), abs_max(b, dt))
-    print(f"[full-size] {product.name} algo={mm.ALGO_NAMES[plan.algo]} {rep}", flush=True)
-    assert rep.ok, str(rep)
+    del Y
+    n, rep = full_compare(a, b, dt, y, product.K)
+    print(f"[full-size] {product.name} algo={mm.ALGO_NAMES[plan.algo]} compared={n} worst block: {rep}", flush=True)
+    assert n == plan.output_numel
+
+
+@pytest.mark.parametrize("name", ["bf16_16x512x4096_by_4096x11008", "bf16_qk_4x32x2048x128_by_4x32x128x2048"])
+def test_workload_full_size_small_integers(name, dev):
+    """The projection and the attention-score product at full size on
+    small-integer inputs: every output equals the oracle's, bit for bit."""
+    product = [p for p in synth.all_products() if p.name == name][0]
+    print(f"\n[full-size exact] {product.name}", flush=True)
+    a, b = product.make(("int",))
+    dt = product.dtype
+    plan = mm.Plan(product.a_shape, product.b_shape, dt)
+    y = synth.from_torch(run_plan(plan, a, b, dt, dev))
+    n, rep = full_compare(a, b, dt, y, product.K, exact=True)
+    print(f"[full-size exact] {product.name} algo={mm.ALGO_NAMES[plan.algo]} compared={n}: {rep}", flush=True)
+    assert n == plan.output_numel

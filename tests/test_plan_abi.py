@@ -216,7 +216,11 @@ SELECTOR_CASES = [
     ((8, 1024), (1024, 30720), mm.FLOAT, "skinny_m"),
     ((1, 16384), (16384, 8704), mm.BFLOAT16, "skinny_m"),  # 16-bit: up to 4 rows, long K, large B
     ((4, 4096), (4096, 30720), mm.BFLOAT16, "general"),   # 16-bit, K < 8192: the tiles
-    ((8, 16384), (16384, 8704), mm.BFLOAT16, "skinny_m"),  # 16-bit, 8 rows, K >= 16384, N >= 8192
+    ((8, 16384), (16384, 8704), mm.BFLOAT16, "skinny_m"),  # 16-bit, 8 rows, K >= 16384, N >= 8704
+    ((8, 16384), (16384, 8192), mm.BFLOAT16, "split_k"),   # N below the measured 8704
+    ((8, 16384), (16384, 8705), mm.BFLOAT16, "split_k"),   # B / Y rows not whole 16-byte chunks
+    ((2, 16388), (16388, 8704), mm.FLOAT16, "split_k"),    # A rows not whole 16-byte chunks
+    ((4, 8192), (8192, 8196), mm.BFLOAT16, "split_k"),     # the 4-row rule needs aligned rows too
     ((8, 16384), (16384, 4352), mm.BFLOAT16, "split_k"),   # 16-bit, 8 rows, narrower B: the tiles
     ((8, 4096), (4096, 30720), mm.FLOAT16, "general"),
     ((15, 16384), (16384, 30720), mm.FLOAT16, "general"),
