@@ -177,6 +177,18 @@ void mm_plan_destroy(mm_plan_t plan);
  * vectorized kernels).  MM_ERR_HIP reports a failed launch or allocation. */
 mm_status mm_execute(mm_plan_t plan, const void *A, const void *B, void *Y, void *stream);
 
+/* mm_execute for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels, but a split plan's partial sums go to a fixed 16 MiB device
+ * array that the library holds on every device it runs on for the life of
+ * the process, instead of the plan's workspace; the call itself allocates
+ * nothing.  A plan whose workspace exceeds 16 MiB gives MM_ERR_TOO_LARGE
+ * (nothing is launched); plans without a workspace run exactly as with
+ * mm_execute.  All calls on one device share that array: calls that overlap
+ * on a device (other streams, other threads) race and must be serialised by
+ * the caller.  Other arguments and errors as for mm_execute. */
+mm_status mm_execute_noalloc(mm_plan_t plan, const void *A, const void *B, void *Y, void *stream);
+
 /* Constant B (page "MatMul Kernel Design": the reusable plan can own a
  * constant B, giving callers a lifetime independent of the source buffer;
  * that storage must hold exactly the planned matrix, and the B-less execute

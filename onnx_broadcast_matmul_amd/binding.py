@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.mm_plan_destroy.restype = None
         L.mm_execute.argtypes = [vp, vp, vp, vp, vp]
         L.mm_execute.restype = ctypes.c_int
+        L.mm_execute_noalloc.argtypes = [vp, vp, vp, vp, vp]
+        L.mm_execute_noalloc.restype = ctypes.c_int
         L.mm_plan_output_shape.argtypes = [vp, i64p, ctypes.POINTER(ctypes.c_int)]
         L.mm_plan_output_shape.restype = ctypes.c_int
         L.mm_plan_output_numel.argtypes = [vp]
@@ -242,6 +244,15 @@ class Plan:
         """mm_execute on raw device pointers and a raw hipStream_t."""
         _check(lib().mm_execute(self._handle, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(Y),
                                 ctypes.c_void_p(stream)))
+
+    def execute_noalloc_ptr(self, A: int, B: int, Y: int, stream: int = 0) -> None:
+        """mm_execute_noalloc on raw device pointers and a raw hipStream_t."""
+        _check(lib().mm_execute_noalloc(self._handle, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(Y),
+                                        ctypes.c_void_p(stream)))
+
+    def execute_noalloc(self, A, B, Y, stream=None) -> None:
+        """mm_execute_noalloc on torch device tensors (checked as in execute)."""
+        self.execute(A, B, Y, stream, _entry=self.execute_noalloc_ptr)
 
     def execute(self, A, B, Y, stream=None, _entry=None) -> None:
         """mm_execute on torch device tensors; ``stream`` is a torch.cuda.Stream
