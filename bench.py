@@ -10,7 +10,10 @@ Timing.  Every launch (one mm_execute) is bracketed by its own pair of HIP
 events recorded on the launch stream, so each launch is an individual
 sample.  Ahead of each batch of launches a bounded spin kernel occupies the
 GPU while the host enqueues, so the timed launches then run back to back and
-the host's enqueue cost is never inside an event pair.  The headline runs W
+the host's enqueue cost is never inside an event pair.  (The event between
+two launches keeps them from overlapping, so short kernels read a little
+slower than when they run back to back: each case also reports the mean of
+a batch of launches between a single event pair.)  The headline runs W
 untimed steps, then exactly K timed steps between device synchronisations;
 ``ms_per_step`` is the GPU time from the first step's start event to the
 last step's end event divided by K.
@@ -64,7 +67,9 @@ ROTATE_BYTES = 1 << 30  # rotate input/output copies until a rotation touches >=
 MAX_COPIES = 128
 CASE_PASSES = 5         # passes over the case list (order reversed on odd passes)
 CASE_LAUNCHES = 10      # individually timed launches per case and pass
-PAD_MS = 2.0            # spin ahead of each batch of timed launches
+PAD_MS = 2.0            # spin ahead of each batch of timed launches of the case table
+HEAD_PAD_MS = 0.3       # spin ahead of the headline's timed steps (covers the first enqueue only,
+                        # so the GPU does not idle long enough to leave its sustained clock)
 
 # Sources whose text fixes the tiled GEMM kernel's memory traffic; a traffic
 # record taken from hardware counters holds only while their hash matches.
@@ -342,7 +347,21 @@ def _ms(pairs):
     return [s.elapsed_time(e) for s, e in pairs]
 
 
-def case_report(c, samples_ms, oracle=None):
+def back_to_back(case, timer, n: int, offset: int) -> float:
+    """Mean time of n launches run back to back between one event pair (no
+    events between them, behind a spin kernel), in ms."""
+    E = timer.torch.cuda.Event
+    s, e = E(enable_timing=True), E(enable_timing=True)
+    timer.pad(PAD_MS)
+    s.record(timer.stream)
+    for i in range(n):
+        case.run(offset + i, timer.sp)
+    e.record(timer.stream)
+    timer.torch.cuda.synchronize()
+    return s.elapsed_time(e) / n
+
+
+def case_report(c, samples_ms, oracle=None, b2b_ms=None):
     d = np.array(samples_ms)
     med = float(np.median(d))
     tflops = c.flops / (med * 1e-3) / 1e12
@@ -362,6 +381,8 @@ def case_report(c, samples_ms, oracle=None):
         "flops": c.flops, "algorithmic_bytes": c.bytes,
         "us_samples": [round(x * 1e3, 3) for x in d.tolist()],
     }
+    if b2b_ms is not None:
+        r["us_back_to_back_mean"] = round(b2b_ms * 1e3, 3)
     if oracle is not None:
         f, t = oracle
         rate = f / t
@@ -541,7 +562,8 @@ def main():
         torch.cuda.synchronize()
         samples = time_case_table(cases, timer, CASE_PASSES, max(1, args.steps // CASE_PASSES))
         for c in cases:
-            print(json.dumps({"only": c.name, "case": case_report(c, samples[c.name])}), flush=True)
+            b2b = back_to_back(c, timer, max(1, args.steps // CASE_PASSES), 3)
+            print(json.dumps({"only": c.name, "case": case_report(c, samples[c.name], None, b2b)}), flush=True)
         return
 
     headline = synth.WORKLOADS[HEADLINE].products[0]
@@ -561,22 +583,16 @@ def main():
                 c.run(i, sp)
         torch.cuda.synchronize()
         samples = time_case_table(cases, timer, CASE_PASSES, CASE_LAUNCHES)
-        table = {}
-        for c in cases:
-            orc = None
-            if not args.no_cpu:
-                orc = c.oracle_sample(args.oracle_seconds)
-            table[c.name] = case_report(c, samples[c.name], orc)
-            r = table[c.name]
-            log(f"[bench]   {c.name}: {r['us_median']} us ({r['tflops']} TFLOP/s, {r['hbm_gbs']} GB/s, "
-                f"{r['roofline_frac']} of {r['roofline_unit']} peak)")
+        b2b = {c.name: back_to_back(c, timer, CASE_LAUNCHES, 7) for c in cases}
 
-    # Headline: W untimed steps, then exactly K timed steps.
+    # Headline: W untimed steps, then exactly K timed steps, right after the
+    # case table so that the GPU has not idled (an idle gap changes the clock
+    # for the next few hundred microseconds of MFMA work).
     for w in range(args.warmup):
         hc.run(w, sp)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    pairs = timer.launches(hc, args.steps, args.warmup, pad_ms=PAD_MS)
+    pairs = timer.launches(hc, args.steps, args.warmup, pad_ms=HEAD_PAD_MS)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = _ms(pairs)
@@ -585,6 +601,18 @@ def main():
     value = hc.flops / (ms * 1e-3) / 1e12
     same = check_against_eager(hc)
     log(f"[bench] {HEADLINE}: {ms:.4f} ms/step, {value:.2f} TFLOP/s")
+
+    # CPU work (the oracle) only after all GPU timing.
+    if not args.no_cases:
+        table = {}
+        for c in cases:
+            orc = None
+            if not args.no_cpu:
+                orc = c.oracle_sample(args.oracle_seconds)
+            table[c.name] = case_report(c, samples[c.name], orc, b2b[c.name])
+            r = table[c.name]
+            log(f"[bench]   {c.name}: {r['us_median']} us ({r['tflops']} TFLOP/s, {r['hbm_gbs']} GB/s, "
+                f"{r['roofline_frac']} of {r['roofline_unit']} peak)")
 
     mean_launch = float(np.mean(per))
     achieved = hc.flops / (mean_launch * 1e-3) / 1e12

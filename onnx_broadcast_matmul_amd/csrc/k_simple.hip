@@ -63,13 +63,15 @@ __global__ __launch_bounds__(256) void k_fill_zero(S *__restrict__ Y, int64_t n)
 
 // Y[i] = narrow(sum_{s=0}^{split-1} W[s][i]) for every output element i.
 //
-// Up to 32 partitions: a workgroup owns OG groups of four consecutive
-// outputs and SG partition lanes (SG = the split count rounded up to a power
-// of two, OG * SG = 256).  Partition lane g sums the partitions g, g + SG,
-// g + 2 SG, ... in ascending order; the SG lane sums are then combined by a
-// fixed pairwise tree in LDS.  The order depends only on the split count, so
-// results are bitwise reproducible.  Lanes that share a partition read
-// consecutive outputs, so each load instruction covers contiguous memory.
+// A workgroup owns OG groups of four consecutive outputs and SG partition
+// lanes (SG = the split count rounded up to a power of two, at most 32; OG *
+// SG = 256).  Partition lane g sums the partitions g, g + SG, g + 2 SG, ...
+// in ascending order; the SG lane sums are then combined by a fixed pairwise
+// tree in LDS.  The order depends only on the split count, so results are
+// bitwise reproducible.  Lanes that share a partition read consecutive
+// outputs, so each load instruction covers whole 128-byte lines (at SG = 32)
+// or more of each partition it touches, and a lane's loads (up to eight per
+// pass) are all in flight together.
 template <int DT, int SG, bool VEC>
 __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a) {
     using E = Elem<DT>;
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a) {
     if (o0 < total) {
         if constexpr (VEC) {
             // total is a multiple of 4: every group is whole and 16-byte aligned.
-#pragma unroll 4
+#pragma unroll 8
             for (int s = sg; s < a.split; s += SG) {
                 const float4 v = *(const float4 *)(W + (int64_t)s * total + o0);
                 acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
@@ -113,69 +115,6 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a) {
         for (int e = 0; e < 4; ++e)
             if (o0 + e < total) {
                 float v = red[0][og][e];
-                if (a.gemm_epi) v = gemm_epilogue<E>(a, v, (o0 + e) / a.N, (o0 + e) % a.N);
-                Y[o0 + e] = E::from_f32(v);
-            }
-    }
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float x) {
-    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over the 64 lanes in a fixed order: half-wave and row swaps (gfx950
-// permlane swaps of a register with itself), then DPP row mirror, half-row
-// mirror and two quad permutations.  Lane 0 holds the full sum.
-__device__ __forceinline__ float wave_sum(float v) {
-    {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    v = dpp_add<0x140>(v);  // row mirror
-    v = dpp_add<0x141>(v);  // half-row mirror
-    v = dpp_add<0x4E>(v);   // quad [2, 3, 0, 1]
-    v = dpp_add<0xB1>(v);   // quad [1, 0, 3, 2]
-    return v;
-}
-
-// The same sum for 64 or more partitions: one wave per group of four
-// outputs, lane g adding partitions g, g + 64, ... in ascending order, then
-// a fixed-order sum over the wave in registers (no LDS, no barrier).
-template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void k_splitk_reduce_wave(KArgs a) {
-    using E = Elem<DT>;
-    using S = typename E::S;
-    const int lane = threadIdx.x & 63;
-    const int64_t total = a.batch * a.M * a.N;
-    const int64_t o0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
-    if (o0 >= total) return;  // whole waves leave together
-    const float *__restrict__ W = a.W;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (VEC) {
-#pragma unroll 4
-        for (int s = lane; s < a.split; s += 64) {
-            const float4 v = *(const float4 *)(W + (int64_t)s * total + o0);
-            acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
-        }
-    } else {
-        for (int s = lane; s < a.split; s += 64)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (o0 + e < total) acc[e] += W[(int64_t)s * total + o0 + e];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = wave_sum(acc[e]);
-    if (lane == 0) {
-        S *__restrict__ Y = (S *)a.Y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (o0 + e < total) {
-                float v = acc[e];
                 if (a.gemm_epi) v = gemm_epilogue<E>(a, v, (o0 + e) / a.N, (o0 + e) % a.N);
                 Y[o0 + e] = E::from_f32(v);
             }
@@ -222,19 +161,13 @@ static hipError_t launch_reduce_sg(const KArgs &a, hipStream_t s) {
 
 template <int DT>
 static hipError_t launch_reduce_dt(const KArgs &a, hipStream_t s) {
-    // Partition lanes: the split count rounded up to a power of two, at most 64.
+    // Partition lanes: the split count rounded up to a power of two, at most 32.
     if (a.split <= 1) return launch_reduce_sg<DT, 1>(a, s);
     if (a.split <= 2) return launch_reduce_sg<DT, 2>(a, s);
     if (a.split <= 4) return launch_reduce_sg<DT, 4>(a, s);
     if (a.split <= 8) return launch_reduce_sg<DT, 8>(a, s);
     if (a.split <= 16) return launch_reduce_sg<DT, 16>(a, s);
-    if (a.split <= 32) return launch_reduce_sg<DT, 32>(a, s);
-    const int64_t total = a.batch * a.M * a.N;
-    const int64_t g = ((total + 3) / 4 + 3) / 4;  // four waves of four outputs per block
-    if (g > 0x7fffffff) return hipErrorInvalidValue;
-    if (total % 4 == 0) hipLaunchKernelGGL((k_splitk_reduce_wave<DT, true>), dim3((unsigned)g), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_splitk_reduce_wave<DT, false>), dim3((unsigned)g), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_reduce_sg<DT, 32>(a, s);
 }
 
 hipError_t launch_splitk_reduce(int dtype, const KArgs &a, hipStream_t s) {

@@ -114,9 +114,9 @@ def test_split_counts(dt, split, dev):
 @pytest.mark.parametrize("dt", [mm.FLOAT, mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
 @pytest.mark.parametrize("split", [64, 100])
 def test_gemm_split_reduction_epilogue(dt, split, dev):
-    """The wave-per-group reduction (64 or more partitions) applies the Gemm
-    epilogue (alpha, beta, per-column and full C) when it writes each
-    output."""
+    """The reduction over more partitions than partition lanes (each lane
+    then adds several partitions in order) applies the Gemm epilogue (alpha,
+    beta, per-column and full C) when it writes each output."""
     M, N, K = 64, 40, 19200
     for i, layout in enumerate([("N",), ("M", "N")]):
         cs = _cs(layout, M, N)
