@@ -145,7 +145,7 @@ typedef struct mm_plan_info {
     int64_t tail_col;         /* GENERAL: > 0 when output columns [tail_col, N) run as a
                                  second launch (last-round balancing), else 0 */
     int32_t tail_tile;        /* tile table entry + 1 of that second launch (0 if none) */
-    int32_t reserved_;
+    int32_t constant_b_packed; /* 1 if the plan holds a constant B also in the prepacked layout */
 } mm_plan_info;
 
 /* Create a plan for Y = MatMul(A, B) with A of shape a_shape[0..a_rank) and
@@ -206,10 +206,22 @@ mm_status mm_execute_noalloc(mm_plan_t plan, const void *A, const void *B, void 
  * MM_ERR_ALLOC, MM_ERR_HIP (copy failed, or the plan already holds B on
  * another device).  The storage is freed by mm_plan_destroy.
  *
- * mm_execute_constant_b is mm_execute with B taken from that storage.  It
- * gives MM_ERR_NO_CONSTANT_B when the plan owns no B, and MM_ERR_HIP when
- * called on a device other than the one holding it.  A plan with a constant
- * B may still be executed with an explicit B through mm_execute. */
+ * For a FLOAT16 / BFLOAT16 plan on the GENERAL algorithm with N a multiple
+ * of 8, mm_plan_set_constant_b also lays B out once in the tiled kernel's
+ * stage order (page "Gemm and MatMul Performance Roadmap", section "Target
+ * computation algorithm": a constant B prepacked once when its shape and
+ * layout are stable; section "Remaining pull-request sequence", PR06.4): for
+ * every tile column and K stage, that stage's B panel exactly as the kernel
+ * stages it in LDS, zero-padded past K and N (mm_plan_info
+ * constant_b_packed = 1).  This takes about as much device memory again as
+ * B and is rebuilt by every call.
+ *
+ * mm_execute_constant_b is mm_execute with B taken from that storage (the
+ * prepacked copy where the tiled kernel runs, the plain copy elsewhere; the
+ * results are the same bits).  It gives MM_ERR_NO_CONSTANT_B when the plan
+ * owns no B, and MM_ERR_HIP when called on a device other than the one
+ * holding it.  A plan with a constant B may still be executed with an
+ * explicit B through mm_execute. */
 mm_status mm_plan_set_constant_b(mm_plan_t plan, const void *B, int64_t numel, void *stream);
 
 /* 1 if the plan owns a constant B, 0 if not (or for a NULL plan). */

@@ -55,7 +55,7 @@ class PlanInfo(ctypes.Structure):
         ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
         ("k_chunk", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
         ("flops", ctypes.c_double), ("min_bytes", ctypes.c_double),
-        ("tail_col", ctypes.c_int64), ("tail_tile", ctypes.c_int32), ("reserved_", ctypes.c_int32),
+        ("tail_col", ctypes.c_int64), ("tail_tile", ctypes.c_int32), ("constant_b_packed", ctypes.c_int32),
     ]
 
 
@@ -237,7 +237,7 @@ class Plan:
             "a_batch_strides": tuple(inf.a_batch_strides[:nb]), "b_batch_strides": tuple(inf.b_batch_strides[:nb]),
             "tile": inf.tile, "split_k": inf.split_k, "k_chunk": inf.k_chunk,
             "workspace_bytes": inf.workspace_bytes, "flops": inf.flops, "min_bytes": inf.min_bytes,
-            "tail_col": inf.tail_col, "tail_tile": inf.tail_tile,
+            "tail_col": inf.tail_col, "tail_tile": inf.tail_tile, "constant_b_packed": inf.constant_b_packed,
         }
 
     def execute_ptr(self, A: int, B: int, Y: int, stream: int = 0) -> None:

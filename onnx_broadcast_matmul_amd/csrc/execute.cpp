@@ -59,7 +59,7 @@ static mm_status ensure_workspace(mm_plan_s *p) { return alloc_workspace(p, fals
 // split partial sums go to `ws` when it is not NULL (at least the plan's
 // workspace_bytes, on the current device), else to the plan's workspace.
 mm_status mm::execute_plan(mm_plan_s *p, const void *A, const void *B, const void *C, void *Y, void *stream,
-                           void *ws) {
+                           void *ws, bool packed_b) {
     if (p->algo == MM_ALGO_EMPTY) return MM_OK;
     if (!Y) return fail(MM_ERR_NULL_ARG, "Y is NULL for a non-empty output");
     hipStream_t s = (hipStream_t)stream;
@@ -137,11 +137,25 @@ mm_status mm::execute_plan(mm_plan_s *p, const void *A, const void *B, const voi
             // with `tail_tile`; both read B and write Y (and a Gemm's C) with
             // their full pitches.  Column c of B' is column c of B, or row c
             // of a transposed B; a per-column or full C moves by c columns.
+            // A prepacked constant B holds each launch's columns separately.
+            const int64_t nmat = packed_b ? p->b_numel / (p->K * p->N) : 0;
             KArgs m = a;
             m.N = p->tail_col;
+            if (packed_b) {
+                m.Bp = p->cbp;
+                m.bp_mat_bytes = p->cbp_main;
+                m.bp_mat_elems = p->K * p->N;
+                m.b_packed = 1;
+            }
             e = launch_general(p->dtype, p->tile, al, false, m, s);
             if (e == hipSuccess) {
                 KArgs r = a;
+                if (packed_b) {
+                    r.Bp = (const char *)p->cbp + nmat * p->cbp_main;
+                    r.bp_mat_bytes = p->cbp_tail;
+                    r.bp_mat_elems = p->K * p->N;
+                    r.b_packed = 1;
+                }
                 r.N = p->N - p->tail_col;
                 r.B = (const char *)B + p->tail_col * (p->tb ? a.ldb : 1) * es;
                 r.Y = (char *)Y + p->tail_col * es;
@@ -153,7 +167,14 @@ mm_status mm::execute_plan(mm_plan_s *p, const void *A, const void *B, const voi
                 e = launch_general(p->dtype, p->tail_tile, ar, false, r, s);
             }
         } else {
-            e = launch_general(p->dtype, p->tile, al, false, a, s);
+            KArgs m = a;
+            if (packed_b) {
+                m.Bp = p->cbp;
+                m.bp_mat_bytes = p->cbp_main;
+                m.bp_mat_elems = p->K * p->N;
+                m.b_packed = 1;
+            }
+            e = launch_general(p->dtype, p->tile, al, false, m, s);
         }
         break;
     case MM_ALGO_SPLIT_K: {
@@ -175,6 +196,50 @@ mm_status mm::execute_plan(mm_plan_s *p, const void *A, const void *B, const voi
         return fail(MM_ERR_BAD_OPTION, "plan has no executable algorithm (%d)", p->algo);
     }
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    return MM_OK;
+}
+
+// Page "Gemm and MatMul Performance Roadmap", section "Target computation
+// algorithm" (a constant B prepacked once, when its shape and layout are
+// stable) and section "Remaining pull-request sequence", PR06.4 (its panels
+// no longer re-derived on every run): a 16-bit plan on the tiled kernel also
+// keeps its constant B as the LDS image of every stage's B panel, so each
+// stage's B is one contiguous block and its loads need no per-lane address
+// or range arithmetic.  The row-major copy stays for the kernels that read
+// B as stored (unaligned A, other algorithms).
+static mm_status pack_constant_b(mm_plan_s *p, hipStream_t s) {
+    if (p->algo != MM_ALGO_GENERAL || (p->dtype != MM_FLOAT16 && p->dtype != MM_BFLOAT16)) return MM_OK;
+    if (p->K <= 0 || p->N <= 0 || p->N % 8 != 0 || p->tile < 0 || (p->tail_col > 0 && p->tail_tile < 0)) return MM_OK;
+    const TileCfg *t = tile_entry(p->dtype, p->tile);
+    const TileCfg *tt = p->tail_col > 0 ? tile_entry(p->dtype, p->tail_tile) : nullptr;
+    if (t->bkb != 128 || (tt && tt->bkb != 128)) return MM_OK;
+    const int64_t nmat = p->b_numel / (p->K * p->N);
+    const int64_t nmain = p->tail_col > 0 ? p->tail_col : p->N;
+    const int64_t main_b = packed_b_bytes(nmain, p->K, t->bn);
+    const int64_t tail_b = tt ? packed_b_bytes(p->N - p->tail_col, p->K, tt->bn) : 0;
+    const size_t bytes = (size_t)(nmat * (main_b + tail_b));
+    if (p->cbp && p->cbp_bytes != bytes) {
+        (void)hipFree(p->cbp);
+        p->cbp = nullptr;
+    }
+    if (!p->cbp) {
+        hipError_t e = hipMalloc(&p->cbp, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            p->cbp = nullptr;
+            return fail(MM_ERR_ALLOC, "hipMalloc of %zu prepacked constant-B bytes: %s", bytes, hipGetErrorString(e));
+        }
+        p->cbp_bytes = bytes;
+    }
+    hipError_t e = launch_pack_b(t->bn, p->cb, nmat, p->K * p->N, p->K, p->N, 0, nmain, p->cbp, s);
+    if (e == hipSuccess && tt)
+        e = launch_pack_b(tt->bn, p->cb, nmat, p->K * p->N, p->K, p->N, p->tail_col, p->N - p->tail_col,
+                          (char *)p->cbp + nmat * main_b, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "constant-B prepack");
+    p->cbp_main = main_b;
+    p->cbp_tail = tail_b;
+    p->cbp_ok = true;
     return MM_OK;
 }
 
@@ -289,6 +354,7 @@ mm_status mm_plan_set_constant_b(mm_plan_t p, const void *B, int64_t numel, void
         return fail(MM_ERR_HIP, "plan holds its constant B on device %d; setting it on device %d needs its own plan",
                     p->cb_device, dev);
     const size_t bytes = (size_t)numel * (size_t)elem_size(p->dtype);
+    p->cbp_ok = false;
     if (bytes > 0) {
         if (!p->cb) {
             void *ptr = nullptr;
@@ -302,6 +368,8 @@ mm_status mm_plan_set_constant_b(mm_plan_t p, const void *B, int64_t numel, void
         e = hipMemcpyAsync(p->cb, B, bytes, hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) return hip_fail(e, "constant-B copy");
+        mm_status st = pack_constant_b(p, s);
+        if (st != MM_OK) return st;
     }
     p->cb_set = true;
     return MM_OK;
@@ -317,6 +385,7 @@ mm_status mm_execute_constant_b(mm_plan_t p, const void *A, void *Y, void *strea
     clear_error();
     if (!p) return fail(MM_ERR_NULL_ARG, "plan is NULL");
     const void *B = nullptr;
+    bool packed = false;
     {
         std::lock_guard<std::mutex> lock(p->cb_mutex);
         if (!p->cb_set) return fail(MM_ERR_NO_CONSTANT_B, "the plan owns no constant B (mm_plan_set_constant_b)");
@@ -329,18 +398,24 @@ mm_status mm_execute_constant_b(mm_plan_t p, const void *A, void *Y, void *strea
                             p->cb_device, dev);
         }
         B = p->cb;
+        packed = p->cbp_ok;
     }
-    return mm_execute(p, A, B, Y, stream);
+    if (p->is_gemm || p->is_int) return fail(MM_ERR_BAD_OPTION, "constant B serves MatMul plans");
+    return execute_plan(p, A, B, nullptr, Y, stream, nullptr, packed);
 }
 
 void mm_plan_destroy(mm_plan_t p) {
     if (!p) return;
-    if (p->cb) {
+    if (p->cb || p->cbp) {
         int cur = -1;
         bool have_cur = hipGetDevice(&cur) == hipSuccess;
-        if (hipSetDevice(p->cb_device) == hipSuccess) (void)hipFree(p->cb);
+        if (hipSetDevice(p->cb_device) == hipSuccess) {
+            if (p->cb) (void)hipFree(p->cb);
+            if (p->cbp) (void)hipFree(p->cbp);
+        }
         if (have_cur) (void)hipSetDevice(cur);
         p->cb = nullptr;
+        p->cbp = nullptr;
     }
     if (p->ws) {
         int cur = -1;

@@ -70,6 +70,15 @@ struct KArgs {
     const void *zpb;
     int32_t sum_a, sum_b;
     int64_t zp_rows;  // rows of one A matrix: a per-row zero point is indexed by row % zp_rows
+    // Plan-owned constant B in the prepacked layout (b_packed = 1): for each
+    // B matrix (bp_mat_bytes apart; matrix i starts at element i * bp_mat_elems
+    // of the row-major B), for each tile column and K stage, the stage's B
+    // panel exactly as the tiled kernel lays it out in LDS, zero-padded past
+    // K and N.  Only the 16-bit MatMul tiles read it; other kernels read B.
+    const void *Bp;
+    int64_t bp_mat_bytes, bp_mat_elems;
+    int32_t b_packed;
+    int32_t pad1_;
 };
 
 // Layouts of the Gemm bias C, unidirectionally broadcast to (M, N).
@@ -106,6 +115,13 @@ hipError_t launch_general(int dtype, int tile, const Align &al, bool split, cons
 // kTransTiles entries.
 hipError_t launch_general_t(int dtype, int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);
 hipError_t launch_splitk_reduce(int dtype, const KArgs &a, hipStream_t s);
+// Prepack B columns [col0, col0 + ncols) of nmat row-major 16-bit [K][ldb]
+// matrices (matrix i at element i * mat_elems) into the layout KArgs::Bp
+// describes for a tile of bn columns (K stages of 64 elements); dst holds
+// nmat * packed_b_bytes(ncols, K, bn) bytes.
+hipError_t launch_pack_b(int bn, const void *B, int64_t nmat, int64_t mat_elems, int64_t K, int64_t ldb, int64_t col0,
+                         int64_t ncols, void *dst, hipStream_t s);
+int64_t packed_b_bytes(int64_t ncols, int64_t K, int bn);
 hipError_t launch_skinny_m(int dtype, const Align &al, const KArgs &a, hipStream_t s);
 hipError_t launch_skinny_n(int dtype, const Align &al, const KArgs &a, hipStream_t s);
 // MatMulInteger kernels (k_int.hip): the direct kernel, the row / column

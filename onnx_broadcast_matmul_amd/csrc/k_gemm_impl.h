@@ -40,6 +40,22 @@ namespace mm {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
 
+// Chunk position swizzle of a staged M/N-contiguous row (one k) of cpr
+// 16-byte chunks, for elements of ES bytes: chunk c of k-row k sits at
+// position c ^ kn_swizzle<ES>(k, cpr).  16-bit: a transposing read covers
+// k = 4 consecutive rows and n = 4 chunks per half-wave; FP32: the two
+// half-waves read rows k and k + 4; 8-bit: a transposing read by 32 lanes
+// covers 8 consecutive k-rows and two neighbouring chunks (c, c ^ 1), and
+// even shifts put the 16 pieces on 16 distinct chunk positions of the
+// 256-byte bank window (for 8-chunk rows the window holds two rows, so rows
+// of one parity take the four even shifts).
+template <int ES>
+__host__ __device__ __forceinline__ int kn_swizzle(int k, int cpr) {
+    if constexpr (ES == 4) return cpr >= 16 ? 8 * ((k >> 2) & 1) : 0;  // 8 chunks: no room to move
+    else if constexpr (ES == 1) return cpr >= 16 ? 2 * (k & 7) : 2 * ((k >> 1) & 3);
+    else return cpr >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+}
+
 template <int BYTES>
 struct RawVec;
 template <>
@@ -302,8 +318,10 @@ __global__ __launch_bounds__(256) void k_gemm_generic(KArgs a) {
 
 // IFL (MatMulInteger only): bit 0 = A is UINT8, bit 1 = B is UINT8; those
 // operands' fragments are sign-flipped after every read.
+// PACKB: B comes from the prepacked constant-B layout (KArgs::Bp): each
+// stage's B panel is one contiguous block in LDS order, copied verbatim.
 template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool SPLIT, bool TA, bool TB,
-          bool GEMM, int IFL = 0>
+          bool GEMM, int IFL = 0, bool PACKB = false>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using E = Elem<DT>;
@@ -344,20 +362,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     static_assert(TB || (CPR & (CPR - 1)) == 0, "B row chunks");
     static_assert(KG >= 1 && KS % KG == 0, "K groups split the MFMA steps of a stage");
     // 16-byte chunk position swizzles of A rows and B rows (see above).
-    // 16-bit B: a transposing read covers k = 4 consecutive rows and n = 4
-    // chunks per half-wave; FP32 B: the two half-waves read rows k and k + 4.
     auto aswz = [](int row) { return CA == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
-    auto mswz = [](int k, int cpr) {  // k-row of cpr chunks
-        if constexpr (ES == 4) return cpr >= 16 ? 8 * ((k >> 2) & 1) : 0;  // 8 chunks: no room to move
-        // A transposing 8-bit read by 32 lanes covers 8 consecutive k-rows and
-        // two neighbouring chunks (c, c ^ 1): even shifts put the 16 pieces
-        // on 16 distinct chunk positions of the 256-byte bank window (for
-        // 8-chunk rows the window holds two rows, so rows of one parity
-        // take the four even shifts).
-        else if constexpr (ES == 1) return cpr >= 16 ? 2 * (k & 7) : 2 * ((k >> 1) & 3);
-        else return cpr >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
-    };
+    auto mswz = [](int k, int cpr) { return kn_swizzle<ES>(k, cpr); };  // k-row of cpr chunks
     static_assert(DT != MM_INT8 || (KG == 1 && !SPLIT), "INT8: no K groups, no split-K");
+    static_assert(!PACKB || (ES == 2 && !SPLIT && !TA && !TB && !GEMM), "prepacked B: 16-bit MatMul tiles only");
     auto bswz = [&](int k) { return mswz(k, CPR); };
 
     __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
@@ -392,7 +400,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     // Tile origins (k = 0): row m0 of A (column m0 of a transposed A) and
     // column n0 of B (row n0 of a transposed B).
     const char *Atile = (const char *)((const S *)a.A + oa + (TA ? m0 : m0 * a.lda));
-    const char *Btile = (const char *)((const S *)a.B + ob + (TB ? n0 * a.ldb : n0));
+    // Prepacked B: this matrix's panels for tile column tn, one per K stage.
+    const char *Btile =
+        PACKB ? (const char *)a.Bp + (ob / a.bp_mat_elems) * a.bp_mat_bytes + tn * ((K + BK - 1) / BK) * B_BYTES
+              : (const char *)((const S *)a.B + ob + (TB ? n0 * a.ldb : n0));
 
     const int64_t kbeg = SPLIT ? sidx * a.kchunk : 0;
     const int64_t kend = SPLIT ? ((kbeg + a.kchunk) < K ? (kbeg + a.kchunk) : K) : K;
@@ -426,7 +437,11 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     bool b_ok[B_INSTR];
 #pragma unroll
     for (int q = 0; q < B_INSTR; ++q) {
-        if constexpr (!TB) {
+        if constexpr (PACKB) {
+            b_off[q] = (uint32_t)((wave * B_INSTR + q) * 1024 + lane * 16);
+            b_k[q] = 0;
+            b_ok[q] = true;
+        } else if constexpr (!TB) {
             const int row = (wave * B_INSTR + q) * B_RPB + lane / CPR;  // k within the stage
             const int p = lane % CPR;
             const int c = p ^ bswz(row);
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         const uint32_t sbase = lds_base + (st % STAGES) * STAGE_BYTES;
         const int64_t k0 = kbeg + (int64_t)st * BK;
         const i32x4 ra = buffer_rsrc(Atile + (TA ? k0 * a.lda : k0) * ES);
-        const i32x4 rb = buffer_rsrc(Btile + (TB ? k0 : k0 * a.ldb) * ES);
+        const i32x4 rb = buffer_rsrc(PACKB ? Btile + (int64_t)st * B_BYTES : Btile + (TB ? k0 : k0 * a.ldb) * ES);
         if (k0 + BK <= kend) {  // a whole stage: no K check per load
 #pragma unroll
             for (int q = 0; q < A_INSTR; ++q) load_to_lds16(ra, sbase + (wave * A_INSTR + q) * 1024, a_off[q]);
@@ -464,13 +479,16 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
             for (int q = 0; q < B_INSTR; ++q)
                 load_to_lds16(rb, sbase + A_BYTES + (wave * B_INSTR + q) * 1024, b_off[q]);
         } else {
+            // The last, partial stage: A (and an unpacked B) past kend read
+            // zeros; a prepacked panel is already zero past K.
             const int rem = (int)(kend - k0);  // 0 < rem < BK
 #pragma unroll
             for (int q = 0; q < A_INSTR; ++q)
                 load_to_lds16(ra, sbase + (wave * A_INSTR + q) * 1024, a_k[q] < rem ? a_off[q] : kOutOfRange);
 #pragma unroll
             for (int q = 0; q < B_INSTR; ++q)
-                load_to_lds16(rb, sbase + A_BYTES + (wave * B_INSTR + q) * 1024, b_k[q] < rem ? b_off[q] : kOutOfRange);
+                load_to_lds16(rb, sbase + A_BYTES + (wave * B_INSTR + q) * 1024,
+                              PACKB || b_k[q] < rem ? b_off[q] : kOutOfRange);
         }
     };
 
@@ -945,8 +963,12 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
         return hipGetLastError();
     } else if (vec && fits) {
         const dim3 blk(64 * WGM * WGN * KG);
+        constexpr bool kPackable = sizeof(typename Elem<DT>::S) == 2 && !TA && !TB && !GEMM;
         // Split-K partials take no epilogue (the reduction applies it).
         if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB, false>), g, blk, 0, s, a);
+        else if (kPackable && a.b_packed)
+            hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false, 0, kPackable>),
+                               g, blk, 0, s, a);
         else hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, GEMM>), g, blk, 0, s, a);
     } else {
         // The register-staged kernel needs at least 64 x 64 (2 x 2 waves of

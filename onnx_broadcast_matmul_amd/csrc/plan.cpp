@@ -705,6 +705,10 @@ mm_status mm_plan_get_info(mm_plan_t p, mm_plan_info *info) {
     info->workspace_bytes = p->workspace_bytes;
     info->tail_col = p->tail_col;
     info->tail_tile = p->tail_tile >= 0 ? p->tail_tile + 1 : 0;
+    {
+        std::lock_guard<std::mutex> lock(const_cast<mm_plan_s *>(p)->cb_mutex);
+        info->constant_b_packed = p->cb_set && p->cbp_ok ? 1 : 0;
+    }
     info->flops = 2.0 * (double)p->total_batch * (double)p->M * (double)p->N * (double)p->K;
     int64_t na = 1, nb = 1;
     for (int i = 0; i < p->a_rank; ++i) na *= p->a_shape[i];

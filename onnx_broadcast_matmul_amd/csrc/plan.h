@@ -60,6 +60,13 @@ struct mm_plan_s {
     void *cb = nullptr;
     int cb_device = -1;
     int64_t b_numel = 0;  // elements of the planned B tensor
+    // The same B prepacked for the tiled 16-bit kernel (see KArgs::Bp): the
+    // columns of `tile` (all of N, or [0, tail_col)) then those of
+    // `tail_tile`, cbp_main and cbp_tail bytes per B matrix.
+    void *cbp = nullptr;
+    size_t cbp_bytes = 0;
+    bool cbp_ok = false;
+    int64_t cbp_main = 0, cbp_tail = 0;
 };
 
 namespace mm {
@@ -69,7 +76,10 @@ namespace mm {
 mm_status alloc_workspace(mm_plan_s *p, bool at_create);
 // Enqueue a MatMul or Gemm plan (C: the Gemm bias or NULL); split partial
 // sums go to `ws` when it is not NULL, else to the plan's workspace.
-mm_status execute_plan(mm_plan_s *p, const void *A, const void *B, const void *C, void *Y, void *stream, void *ws);
+// packed_b: read B's prepacked copy (the plan's constant B) where the tiled
+// 16-bit kernel runs; B must then be the plan's row-major constant B.
+mm_status execute_plan(mm_plan_s *p, const void *A, const void *B, const void *C, void *Y, void *stream, void *ws,
+                       bool packed_b = false);
 mm_status fail(mm_status st, const char *fmt, ...);
 void clear_error();
 int elem_size(int dtype);

@@ -334,8 +334,42 @@ def test_constant_b(dt, algo, dev):
         assert rep.ok, str(rep)
 
 
+@pytest.mark.parametrize("dt", [mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
+def test_constant_b_prepacked(dt, dev):
+    """A 16-bit GENERAL plan keeps its constant B also prepacked in the tiled
+    kernel's stage order; for every tile of the table, over two B matrices,
+    ragged M, N (a multiple of 8) and a K that leaves the last stage partly
+    filled, mm_execute_constant_b equals mm_execute with the same B bit for
+    bit, and stays so after B is replaced."""
+    sa, sb = (2, 3, 70, 520), (2, 1, 520, 200)
+    a = synth.generate(sa, dt, U1, [45, 0])
+    b1 = synth.generate(sb, dt, U1, [45, 1])
+    b2 = synth.generate(sb, dt, U1, [45, 2])
+    A = synth.as_torch(a, dt).to(dev)
+    for t in range(1, len(mm.tile_configs(dt)) + 1):
+        plan = mm.Plan(sa, sb, dt, force_algo=mm.ALGO_GENERAL, tile=t)
+        for b in (b1, b2):
+            plan.set_constant_b(synth.as_torch(b, dt).to(dev))
+            assert plan.info()["constant_b_packed"] == 1
+            Yc = _sentinel(plan.output_shape, dt, dev)
+            plan.execute_constant_b(A, Yc)
+            Ye = run_plan(plan, a, b, dt, dev)
+            torch.cuda.synchronize()
+            assert np.array_equal(synth.from_torch(Yc), synth.from_torch(Ye)), f"tile {t}"
+        rep = check(synth.from_torch(Yc), oracle.matmul(a, b2, dt), dt, sa[-1], abs_max(a, dt), abs_max(b2, dt))
+        assert rep.ok, f"tile {t}: {rep}"
+    # not prepacked: N not a multiple of 8, and a non-GENERAL algorithm
+    p2 = mm.Plan((70, 520), (520, 90), dt, force_algo=mm.ALGO_GENERAL)
+    p2.set_constant_b(synth.as_torch(synth.generate((520, 90), dt, U1, [45, 3]), dt).to(dev))
+    assert p2.info()["constant_b_packed"] == 0
+    p3 = mm.Plan((70, 520), (520, 96), dt, force_algo=mm.ALGO_SPLIT_K)
+    p3.set_constant_b(synth.as_torch(synth.generate((520, 96), dt, U1, [45, 4]), dt).to(dev))
+    assert p3.info()["constant_b_packed"] == 0
+
+
 def test_constant_b_tail_split(dev):
-    """Constant B under the two-launch column split of a large BF16 product."""
+    """Constant B under the two-launch column split of a large BF16 product
+    (both column ranges prepacked, each for its own tile)."""
     dt = mm.BFLOAT16
     sa, sb = (16, 512, 64), (64, 11008)
     a = synth.generate(sa, dt, ("int",), [43, 0])
@@ -343,6 +377,7 @@ def test_constant_b_tail_split(dev):
     plan = mm.Plan(sa, sb, dt)
     assert plan.info()["tail_col"] > 0
     plan.set_constant_b(synth.as_torch(b, dt).to(dev))
+    assert plan.info()["constant_b_packed"] == 1
     Yc = _sentinel(plan.output_shape, dt, dev)
     plan.execute_constant_b(synth.as_torch(a, dt).to(dev), Yc)
     Ye = run_plan(plan, a, b, dt, dev)
