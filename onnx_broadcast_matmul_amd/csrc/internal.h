@@ -99,6 +99,8 @@ struct TileCfg {
     int stages;     // LDS stages
     int producers;  // waves that issue the global-to-LDS loads
     int kgroups;    // wave groups that split each stage's K steps (1: none)
+    int persistent; // 1: one workgroup per CU walks the tiles (16-bit MatMul,
+                    // two stages, one K group); other cases run the plain kernel
 };
 
 // Number of tile table entries and the entries, per element type.

@@ -7,7 +7,7 @@ namespace mm {
 #define MM_TILE_CASE(DT, T, IDX)                                                                          \
     case IDX:                                                                                             \
         return launch_tile<DT, T[IDX].bm, T[IDX].bn, T[IDX].wgm, T[IDX].wgn, T[IDX].bkb, T[IDX].stages, \
-                           T[IDX].producers, T[IDX].kgroups>(vec, split, a, s)
+                           T[IDX].producers, T[IDX].kgroups, false, false, false, T[IDX].persistent != 0>(vec, split, a, s)
 
 template <int DT>
 static hipError_t launch_16(int tile, bool vec, bool split, const KArgs &a, hipStream_t s) {
@@ -22,6 +22,7 @@ static hipError_t launch_16(int tile, bool vec, bool split, const KArgs &a, hipS
         MM_TILE_CASE(DT, kTiles16, 7);
         MM_TILE_CASE(DT, kTiles16, 8);
         MM_TILE_CASE(DT, kTiles16, 9);
+        MM_TILE_CASE(DT, kTiles16, 10);
     }
     return hipErrorInvalidValue;
 }
@@ -40,7 +41,7 @@ static hipError_t launch_32(int tile, bool vec, bool split, const KArgs &a, hipS
 }
 #undef MM_TILE_CASE
 
-static_assert(kNumTiles16 == 10 && kNumTiles32 == 7, "launch switch must cover the tile table");
+static_assert(kNumTiles16 == 11 && kNumTiles32 == 7, "launch switch must cover the tile table");
 
 // Prepacked constant B: the 16-byte chunk (piece, lane) of the panel of
 // matrix mi, tile column tn and K stage st is what lane `lane` of load

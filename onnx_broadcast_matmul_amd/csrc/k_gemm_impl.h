@@ -936,8 +936,295 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
 #endif
 }
 
+// Persistent variant for 16-bit MatMul with two LDS stages: one workgroup per
+// CU walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ... (in the same
+// XCD-aware order as the one-tile-per-workgroup grid), and the stage
+// pipeline runs on across tile boundaries: the first stage of the next tile
+// is loaded while the last stage of the current one is multiplied.  The
+// output leaves straight from the accumulators (8-byte stores, no LDS), so
+// the stage buffers never wait for an epilogue and the stores of one tile
+// drain while the next tile computes.  Per tile, the K order, the MFMA
+// sequence and the narrowing are those of k_gemm_lds_dma, so both give the
+// same bits.
+template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int PW>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_persist(KArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using E = Elem<DT>;
+    using S = typename E::S;
+    constexpr int ES = (int)sizeof(S);
+    static_assert(ES == 2, "16-bit element types");
+    constexpr int STAGES = 2;
+    constexpr int VE = 16 / ES;
+    constexpr int BK = BKB / ES;
+    constexpr int CA = BKB / 16;
+    constexpr int KS = BKB / 32;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int RBB = BN * ES;
+    constexpr int CPR = RBB / 16;
+    constexpr int A_BYTES = BM * BKB;
+    constexpr int B_BYTES = BK * RBB;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int A_INSTR = A_BYTES / 1024 / PW;
+    constexpr int B_INSTR = B_BYTES / 1024 / PW;
+    constexpr int A_RPB = 1024 / BKB;
+    constexpr int B_RPB = 1024 / RBB;
+    static_assert(CA == 8, "A rows are 128 bytes");
+    static_assert(FM >= 1 && FN >= 1 && PW >= 1 && PW <= WGM * WGN, "wave tile, producers");
+    static_assert(A_INSTR >= 1 && A_INSTR * PW * 1024 == A_BYTES, "A loads");
+    static_assert(B_INSTR >= 1 && B_INSTR * PW * 1024 == B_BYTES, "B loads");
+    static_assert(CPR >= 8 && RBB <= 1024 && (CPR & (CPR - 1)) == 0, "B rows");
+    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+    static_assert(FM * FN * 4 < 64, "stores counted by vmcnt");
+    auto aswz = [](int row) { return (row >> 1) & 7; };
+    auto bswz = [](int k) { return kn_swizzle<ES>(k, CPR); };
+
+    __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave / WGN, wc = wave % WGN;
+    // Tile counts, origins and batch indices fit in 32 bits (checked at
+    // launch); only element offsets are 64-bit.
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    const int per_batch = tiles_m * tiles_n;
+    const int total = (int)a.batch * per_batch;
+    const int G = (int)gridDim.x;
+    const int bid = (int)blockIdx.x;
+    const int ntiles = bid < total ? (total - 1 - bid) / G + 1 : 0;
+    const int nk = (int)((K + BK - 1) / BK);
+    if (ntiles == 0 || nk == 0) return;
+
+    // Tile j of this workgroup: batch, origin and operand panels.
+    struct Tile {
+        int b, m0, n0;
+        const char *At, *Bt;
+    };
+    auto tile_at = [&](int j) {
+        const int id = (int)xcd_remap(bid + j * G, total);
+        const int b = id / per_batch, t = id % per_batch;
+        constexpr int GM = 8;
+        const int group = t / (GM * tiles_n);
+        const int first_m = group * GM;
+        const int gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+        const int tm = first_m + (t % (GM * tiles_n)) % gsize;
+        const int tn = (t % (GM * tiles_n)) / gsize;
+        int64_t oa, ob;
+        batch_offsets(a.bd, b, oa, ob);
+        Tile T;
+        T.b = b;
+        T.m0 = tm * BM;
+        T.n0 = tn * BN;
+        T.At = (const char *)((const S *)a.A + oa + (int64_t)T.m0 * a.lda);
+        T.Bt = (const char *)((const S *)a.B + ob + T.n0);
+        return T;
+    };
+
+    // Stage st of tile T into LDS buffer buf (whole tiles and stages: M, N
+    // and K are multiples of BM, BN and BK).  Lane offsets are formed here
+    // rather than kept in registers across the loop.
+    const bool producer = wave < PW;
+    const uint32_t a_pitch = (uint32_t)(a.lda * ES), b_pitch = (uint32_t)(a.ldb * ES);
+    auto issue = [&](const Tile &T, int st, int buf) {
+        if (!producer) return;
+        const uint32_t sbase = lds_base + buf * STAGE_BYTES;
+        const int64_t k0 = (int64_t)st * BK;
+        const i32x4 ra = buffer_rsrc(T.At + k0 * ES);
+        const i32x4 rb = buffer_rsrc(T.Bt + k0 * a.ldb * ES);
+#pragma unroll
+        for (int q = 0; q < A_INSTR; ++q) {
+            const int row = (wave * A_INSTR + q) * A_RPB + lane / CA;
+            const int c = (lane % CA) ^ aswz(row);
+            load_to_lds16(ra, sbase + (wave * A_INSTR + q) * 1024, (uint32_t)row * a_pitch + c * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < B_INSTR; ++q) {
+            const int row = (wave * B_INSTR + q) * B_RPB + lane / CPR;
+            const int c = (lane % CPR) ^ bswz(row);
+            load_to_lds16(rb, sbase + A_BYTES + (wave * B_INSTR + q) * 1024, (uint32_t)row * b_pitch + c * 16);
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    uint4 fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, int ks, int slot) {
+        const char *As = lds + buf * STAGE_BYTES;
+        const char *Bs = As + A_BYTES;
+        const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wr * WM + i * 32 + (lane & 31);
+            fa[slot][i] = *(const uint4 *)(As + row * BKB + ((c ^ aswz(row)) * 16));
+        }
+        const int G4 = lane >> 4, jl = lane & 15;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = wc * WN + j * 32 + (G4 & 1) * 16 + (jl & 3) * 4;
+            uint2 h2[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = ks * 16 + (G4 >> 1) * 8 + h * 4 + (jl >> 2);
+                const int p = (n >> 3) ^ bswz(k);
+                const char *addr = Bs + k * RBB + p * 16 + ((n >> 2) & 1) * 8;
+                if constexpr (DT == MM_BFLOAT16)
+                    h2[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                          (__attribute__((address_space(3))) bf16x4 *)(addr)));
+                else
+                    h2[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                                          (__attribute__((address_space(3))) fp16x4 *)(addr)));
+            }
+            fb[slot][j] = make_uint4(h2[0].x, h2[0].y, h2[1].x, h2[1].y);
+        }
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (DT == MM_BFLOAT16)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fb[slot][j]),
+                                                                       __builtin_bit_cast(bf16x8, fa[slot][i]),
+                                                                       acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fb[slot][j]),
+                                                                      __builtin_bit_cast(f16x8, fa[slot][i]),
+                                                                      acc[i][j], 0, 0, 0);
+            }
+    };
+    // Epilogue through the stage buffer just consumed, in WGM passes of the
+    // WM rows of one row of waves.  Element r of a lane's accumulator block
+    // (i, j) is row lane % 32 and column 8 (r / 4) + 4 (lane / 32) + r % 4
+    // of the block, so r = 4q .. 4q + 3 are four consecutive columns of one
+    // row: one 8-byte LDS write.  Tile row r keeps its 16-byte chunk c at
+    // c ^ (r % OCPR); the workgroup then stores whole 16-byte chunks of
+    // output rows.  Every thread issues exactly NST stores per tile, so the
+    // wait for the next tile's first stage can count them.
+    constexpr int OCPR = BN * ES / 16;
+    constexpr int PASS_CHUNKS = WM * OCPR;
+    static_assert(PASS_CHUNKS % (64 * WGM * WGN) == 0 && WM * BN * ES <= STAGE_BYTES, "epilogue passes");
+    constexpr int NST = WGM * PASS_CHUNKS / (64 * WGM * WGN);
+    static_assert(NST < 64, "stores counted by vmcnt");
+    auto store_tile = [&](const Tile &T, int buf) {
+        typedef int i32x4v __attribute__((ext_vector_type(4)));
+        // An opaque zero keeps the tile-independent LDS and store offsets
+        // below from being hoisted out of the tile loop (where they would
+        // stay live in registers across the whole K loop).
+        int oz;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(oz));
+        char *tile = lds + buf * STAGE_BYTES + oz;
+        const S *Yt = (const S *)a.Y + ((int64_t)T.b * M + T.m0) * a.ldy + T.n0;
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void *)Yt, (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int pass = 0; pass < WGM; ++pass) {
+            if (pass > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (wr == pass) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int rl = i * 32 + (lane & 31);
+                    char *trow = tile + rl * (BN * ES);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int cl = wc * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+                            const int ch = (cl / VE) ^ (rl & (OCPR - 1));
+                            const f32x16 &v = acc[i][j];
+                            *(uint2 *)(trow + ch * 16 + (cl % VE) * ES) =
+                                make_uint2(E::pack2(v[4 * q], v[4 * q + 1]), E::pack2(v[4 * q + 2], v[4 * q + 3]));
+                        }
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+            for (int it = 0; it < PASS_CHUNKS / (64 * WGM * WGN); ++it) {
+                const int idx = it * 64 * WGM * WGN + tid;
+                const int rl = idx / OCPR, c = idx % OCPR;
+                const uint4 v = *(const uint4 *)(tile + rl * (BN * ES) + (c ^ (rl & (OCPR - 1))) * 16);
+                const int row = pass * WM + rl;
+                const uint32_t voff = (uint32_t)(((int64_t)row * a.ldy + c * VE) * ES) + (uint32_t)oz;
+                // aux 2: non-temporal
+                __builtin_amdgcn_raw_buffer_store_b128(i32x4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, ry, (int)voff, 0, 2);
+            }
+        }
+    };
+
+    Tile cur = tile_at(0);
+    Tile nxt = cur;
+    issue(cur, 0, 0);
+    const int total_gs = ntiles * nk;
+    int st = 0;
+    int j = 0;
+    bool stored = false;  // the previous step ended a tile (its NST stores follow this step's loads)
+    for (int gs = 0; gs < total_gs; ++gs) {
+        // This wave's loads of stage gs are complete once at most the stores
+        // issued after them are outstanding.
+        if (stored) wait_vmcnt<NST>();
+        else wait_vmcnt<0>();
+        stored = false;
+        // After the barrier every wave's loads of stage gs have landed and
+        // every wave has finished reading the other buffer, refilled next.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int buf = gs & 1;
+        if (gs + 1 < total_gs) {
+            if (st + 1 < nk) {
+                issue(cur, st + 1, buf ^ 1);
+            } else {
+                nxt = tile_at(j + 1);
+                issue(nxt, 0, buf ^ 1);
+            }
+        }
+        constexpr int RPS = FM + FN * 2;  // LDS reads per step
+        constexpr int MPS = FM * FN;      // MFMAs per step
+        read_frags(buf, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) read_frags(buf, ks + 1, (ks + 1) & 1);
+            mfmas(ks & 1);
+            if (ks + 1 < KS) {
+#pragma unroll
+                for (int q = 0; q < RPS / 2; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+                if constexpr (MPS > RPS / 2) __builtin_amdgcn_sched_group_barrier(0x008, MPS - RPS / 2, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, MPS, 0);
+            }
+        }
+        if (st + 1 < nk) {
+            ++st;
+            continue;
+        }
+        // Every wave has finished reading this stage's buffer before the
+        // epilogue reuses it.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        store_tile(cur, buf);
+        stored = true;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+        st = 0;
+        ++j;
+        cur = nxt;
+    }
+#endif
+}
+
 template <int DT, int BM, int BN, int WGM, int WGN, int BKB, int STAGES, int PW, int KG, bool TA = false, bool TB = false,
-          bool GEMM = false>
+          bool GEMM = false, bool PERS = false>
 static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t s) {
     const int64_t tiles = a.batch * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * (split ? a.split : 1);
     if (tiles <= 0) return hipSuccess;
@@ -964,6 +1251,19 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
     } else if (vec && fits) {
         const dim3 blk(64 * WGM * WGN * KG);
         constexpr bool kPackable = sizeof(typename Elem<DT>::S) == 2 && !TA && !TB && !GEMM;
+        constexpr bool kPersist = PERS && sizeof(typename Elem<DT>::S) == 2 && !TA && !TB && !GEMM && STAGES == 2 && KG == 1;
+        if constexpr (kPersist) {
+            // Whole tiles and stages, 32-bit tile origins, output rows of
+            // whole 16-byte chunks inside one buffer range.
+            const bool whole = a.M % BM == 0 && a.N % BN == 0 && a.K % (BKB / 2) == 0;
+            const bool small = a.M < 0x7fff0000LL && a.N < 0x7fff0000LL;
+            if (!split && !a.b_packed && a.y_vec && whole && small && (int64_t)BM * a.ldy * 2 < 0x7fff0000LL) {
+                constexpr int64_t kWgsPerCu = (160 * 1024) / (STAGES * (BM + BN) * BKB);
+                const int64_t grid = tiles < kNumCUs * kWgsPerCu ? tiles : kNumCUs * kWgsPerCu;
+                hipLaunchKernelGGL((k_gemm_persist<DT, BM, BN, WGM, WGN, BKB, PW>), dim3((unsigned)grid), blk, 0, s, a);
+                return hipGetLastError();
+            }
+        }
         // Split-K partials take no epilogue (the reduction applies it).
         if (split) hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB, false>), g, blk, 0, s, a);
         else if (kPackable && a.b_packed)

@@ -7,8 +7,11 @@
 // one wave's MFMAs cover the other's LDS and barrier waits.  The vectorized
 // kernel stages bkb bytes of K per row (64 elements of a 16-bit type, 32 of
 // FP32 for bkb = 128) in `stages` LDS buffers, filled by the first
-// `producers` waves.  The element-wise fallback kernel uses the block tile
-// only.  The selector picks an entry per shape; tests force each one.
+// `producers` waves.  An entry marked persistent runs one workgroup per CU
+// over many tiles (k_gemm_persist) where the shape allows it, and the
+// one-tile kernel of the same shape elsewhere.  The element-wise fallback
+// kernel uses the block tile only.  The selector picks an entry per shape;
+// tests force each one.
 #pragma once
 
 #include "internal.h"
@@ -27,6 +30,7 @@ constexpr TileCfg kTiles16[] = {
     {256, 128, 4, 2, 128, 2, 4, 1},
     {64, 64, 2, 2, 128, 3, 4, 2},
     {128, 128, 2, 2, 128, 2, 4, 2},
+    {256, 256, 2, 4, 128, 2, 4, 1, 1},
 };
 
 // FLOAT entries.

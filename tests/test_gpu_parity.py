@@ -346,11 +346,13 @@ def test_constant_b_prepacked(dt, dev):
     b1 = synth.generate(sb, dt, U1, [45, 1])
     b2 = synth.generate(sb, dt, U1, [45, 2])
     A = synth.as_torch(a, dt).to(dev)
-    for t in range(1, len(mm.tile_configs(dt)) + 1):
+    cfgs = mm.tile_configs(dt)
+    for t in range(1, len(cfgs) + 1):
         plan = mm.Plan(sa, sb, dt, force_algo=mm.ALGO_GENERAL, tile=t)
         for b in (b1, b2):
             plan.set_constant_b(synth.as_torch(b, dt).to(dev))
-            assert plan.info()["constant_b_packed"] == 1
+            # prepacked for the tiles that stage 64 elements of K
+            assert plan.info()["constant_b_packed"] == (1 if cfgs[t - 1][2] == 64 else 0)
             Yc = _sentinel(plan.output_shape, dt, dev)
             plan.execute_constant_b(A, Yc)
             Ye = run_plan(plan, a, b, dt, dev)
@@ -365,6 +367,29 @@ def test_constant_b_prepacked(dt, dev):
     p3 = mm.Plan((70, 520), (520, 96), dt, force_algo=mm.ALGO_SPLIT_K)
     p3.set_constant_b(synth.as_torch(synth.generate((520, 96), dt, U1, [45, 4]), dt).to(dev))
     assert p3.info()["constant_b_packed"] == 0
+
+
+@pytest.mark.parametrize("dt", [mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
+@pytest.mark.parametrize("sa,sb", [
+    ((16, 1024, 128), (16, 128, 2048)),  # 512 tiles: two per workgroup
+    ((1024, 64), (64, 1024)),            # one stage per tile
+    ((4, 512, 192), (192, 768)),         # broadcast B, three stages per tile
+    ((2, 3, 512, 256), (3, 256, 512)),   # broadcast A batch dimension
+], ids=lambda s: "x".join(map(str, s)))
+def test_persistent_tile(sa, sb, dt, dev):
+    """The persistent kernel (tile 11) on whole tiles and stages: the same
+    bits as the one-tile-per-workgroup 256 x 256 kernel (tile 1), and
+    within tolerance of the oracle on every output."""
+    a = synth.generate(sa, dt, U1, [47, 0])
+    b = synth.generate(sb, dt, U1, [47, 1])
+    outs = []
+    for t in (1, 11):
+        plan = mm.Plan(sa, sb, dt, force_algo=mm.ALGO_GENERAL, tile=t)
+        assert plan.info()["tile"] == t
+        outs.append(synth.from_torch(run_plan(plan, a, b, dt, dev)))
+    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+    rep = check(outs[1], oracle.matmul(a, b, dt), dt, sa[-1], abs_max(a, dt), abs_max(b, dt))
+    assert rep.ok, str(rep)
 
 
 def test_constant_b_tail_split(dev):

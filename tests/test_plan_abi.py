@@ -403,6 +403,28 @@ def test_tail_split_plans():
     assert forced.info()["tail_col"] == 0
 
 
+# 16-bit entry 10 (tile 11) is the persistent twin of the 256 x 256 entry.
+PERSIST_TILE = 11
+
+
+@pytest.mark.parametrize("sa,sb,dt,tile", [
+    ((4, 32, 2048, 128), (4, 32, 128, 2048), mm.BFLOAT16, PERSIST_TILE),  # QK^T: K = 128, 32 rounds
+    ((8192, 1024), (1024, 8192), mm.FLOAT16, PERSIST_TILE),               # K = 1024, 4 rounds
+    ((8192, 2048), (2048, 8192), mm.BFLOAT16, 1),                         # K = 2048: the plain kernel
+    ((16, 512, 4096), (4096, 11008), mm.BFLOAT16, 1),                      # long K (and a column split)
+    ((4, 32, 2000, 128), (4, 32, 128, 2048), mm.BFLOAT16, 1),             # rows not whole tiles
+    ((4, 32, 2048, 120), (4, 32, 120, 2048), mm.BFLOAT16, 1),             # K not whole stages
+    ((2048, 128), (128, 2048), mm.BFLOAT16, None),                        # 64 tiles: under two rounds
+])
+def test_persistent_selection(sa, sb, dt, tile):
+    """Short-K 16-bit products of whole 256 x 256 tiles and stages, with at
+    least two rounds of tiles, run the persistent kernel."""
+    assert mm.tile_configs(dt)[PERSIST_TILE - 1] == mm.tile_configs(dt)[0]
+    inf = mm.Plan(sa, sb, dt).info()
+    assert mm.ALGO_NAMES[inf["algo"]] == "general"
+    assert inf["tile"] == tile if tile is not None else inf["tile"] != PERSIST_TILE
+
+
 # ---------------------------------------------------------------- constant B
 
 def test_constant_b_errors_before_any_gpu_call():
