@@ -67,7 +67,9 @@ ROTATE_BYTES = 1 << 30  # rotate input/output copies until a rotation touches >=
 MAX_COPIES = 128
 CASE_PASSES = 5         # passes over the case list (order reversed on odd passes)
 CASE_LAUNCHES = 10      # individually timed launches per case and pass
-PAD_MS = 2.0            # spin ahead of each batch of timed launches of the case table
+PAD_MS = 0.3            # spin ahead of each batch of timed launches (covers the batch's enqueue)
+WARM_MS = 3.0           # untimed launches of the same case between the spin and a timed batch: the
+                        # clock climbs over the first milliseconds of sustained matrix-core load
 HEAD_PAD_MS = 0.3       # spin ahead of the headline's timed steps (covers the first enqueue only,
                         # so the GPU does not idle long enough to leave its sustained clock)
 
@@ -329,13 +331,16 @@ class Timer:
         # A bounded spin kernel (it ends after a fixed number of cycles).
         self.torch.cuda._sleep(int(self.cpm * ms))
 
-    def launches(self, case, n: int, offset: int, pad_ms: float = PAD_MS):
-        """Enqueue n launches of `case`, each between its own start and end
-        events; returns the event pairs (read them after synchronising)."""
+    def launches(self, case, n: int, offset: int, pad_ms: float = PAD_MS, warm: int = 0):
+        """Enqueue `warm` untimed launches of `case`, then n launches each
+        between its own start and end events; returns the event pairs (read
+        them after synchronising)."""
         E = self.torch.cuda.Event
         pairs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n)]
         if pad_ms > 0:
             self.pad(pad_ms)
+        for i in range(warm):
+            case.run(offset + n + i, self.sp)
         for i, (s, e) in enumerate(pairs):
             s.record(self.stream)
             case.run(offset + i, self.sp)
@@ -347,12 +352,27 @@ def _ms(pairs):
     return [s.elapsed_time(e) for s, e in pairs]
 
 
+def warm_count(case) -> int:
+    """Untimed launches of a case that make about WARM_MS of GPU work."""
+    return int(min(64, max(2, math.ceil(WARM_MS / max(getattr(case, "est_ms", WARM_MS), 1e-3)))))
+
+
+def calibrate(cases, timer) -> None:
+    """Rough per-launch time of every case (sets case.est_ms)."""
+    for c in cases:
+        pairs = timer.launches(c, 3, 0, warm=2)
+        timer.torch.cuda.synchronize()
+        c.est_ms = float(np.median(_ms(pairs)))
+
+
 def back_to_back(case, timer, n: int, offset: int) -> float:
     """Mean time of n launches run back to back between one event pair (no
-    events between them, behind a spin kernel), in ms."""
+    events between them, behind a spin kernel and warm-up launches), in ms."""
     E = timer.torch.cuda.Event
     s, e = E(enable_timing=True), E(enable_timing=True)
     timer.pad(PAD_MS)
+    for i in range(warm_count(case)):
+        case.run(offset + n + i, timer.sp)
     s.record(timer.stream)
     for i in range(n):
         case.run(offset + i, timer.sp)
@@ -392,14 +412,15 @@ def case_report(c, samples_ms, oracle=None, b2b_ms=None):
 
 
 def time_case_table(cases, timer, passes: int, per_pass: int):
-    """passes x per_pass individually timed launches of every case; the
+    """passes x per_pass individually timed launches of every case, each
+    batch behind about WARM_MS of untimed launches of the same case; the
     case order is reversed on every other pass."""
     samples = {c.name: [] for c in cases}
     offset = 0
     for p in range(passes):
         order = cases if p % 2 == 0 else list(reversed(cases))
         for c in order:
-            pairs = timer.launches(c, per_pass, offset)
+            pairs = timer.launches(c, per_pass, offset, warm=warm_count(c))
             timer.torch.cuda.synchronize()
             samples[c.name] += _ms(pairs)
             offset += per_pass
@@ -560,6 +581,7 @@ def main():
             for i in range(args.warmup):
                 c.run(i, sp)
         torch.cuda.synchronize()
+        calibrate(cases, timer)
         samples = time_case_table(cases, timer, CASE_PASSES, max(1, args.steps // CASE_PASSES))
         for c in cases:
             b2b = back_to_back(c, timer, max(1, args.steps // CASE_PASSES), 3)
@@ -582,6 +604,7 @@ def main():
             for i in range(3):
                 c.run(i, sp)
         torch.cuda.synchronize()
+        calibrate(cases, timer)
         samples = time_case_table(cases, timer, CASE_PASSES, CASE_LAUNCHES)
         b2b = {c.name: back_to_back(c, timer, CASE_LAUNCHES, 7) for c in cases}
 
@@ -643,6 +666,10 @@ def main():
         "repeat_matches_bitwise": same,
     }
     if table is not None:
+        out["cases_timing"] = (f"{CASE_PASSES} passes over the products (order reversed on odd passes); per pass "
+                               f"and product a {PAD_MS} ms spin, about {WARM_MS} ms of untimed launches of that "
+                               f"product, then {CASE_LAUNCHES} launches each between its own HIP events; "
+                               "us_back_to_back_mean: the same launches between one event pair")
         out["cases"] = table
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
