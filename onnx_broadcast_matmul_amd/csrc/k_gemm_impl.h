@@ -520,6 +520,22 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         // Cleared before the main loop's first barrier, added to after it.
         for (int x = tid; x < BM + BN; x += 64 * NW) sums_lds[x] = 0;
     }
+    // Gemm with a per-column or per-row C: the tile's BN (or BM) values of C,
+    // staged in LDS as FP32 before the main loop (visible after its first
+    // barrier), so the epilogue reads them from LDS instead of waiting on
+    // global loads at the end of the tile.  Positions outside the output hold
+    // zero.
+    constexpr bool EPI = GEMM && !SPLIT;
+    __shared__ __attribute__((aligned(16))) float ebias[EPI ? (BM > BN ? BM : BN) : 1];
+    if constexpr (EPI) {
+        if (a.gemm_epi && (a.c_mode == kBiasRow || a.c_mode == kBiasCol)) {
+            const S *Cp = (const S *)a.C;
+            const bool row = a.c_mode == kBiasRow;  // one C value per output column
+            const int len = row ? BN : BM;
+            const int64_t base = row ? n0 : m0, lim = row ? N : M;
+            for (int x = tid; x < len; x += 64 * NW) ebias[x] = base + x < lim ? E::to_f32(Cp[base + x]) : 0.0f;
+        }
+    }
     // Fragment of K-contiguous rows: chunk c of row `row`.
     auto read_k = [&](const char *Xs, int row, int c) -> uint4 {
         return *(const uint4 *)(Xs + row * BKB + ((c ^ aswz(row)) * 16));
@@ -804,38 +820,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
         }
     }
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    // Gemm bias values this lane needs, loaded once: per column (the lane's
-    // four columns of each (j, q) group), per row (one per row block i), or
-    // a single scalar.  A full C is read in the loop below.
-    // Only the Gemm instantiations carry the epilogue's registers and code.
-    constexpr bool EPI = GEMM && !SPLIT;
-    float bias_col[EPI ? FN : 1][4][4];
-    float bias_row[EPI ? FM : 1];
+    // Gemm: a scalar C is read once here; per-column and per-row C come from
+    // the LDS copy staged before the main loop; a full C is read per element
+    // below.  Only the Gemm instantiations carry the epilogue's code.
     float bias_one = 0.0f;
     int cmode = kBiasNone;
     if constexpr (EPI) {
         if (a.gemm_epi) {
             cmode = a.c_mode;
-            const S *Cp = (const S *)a.C;
-            if (cmode == kBiasScalar) bias_one = E::to_f32(Cp[0]);
-            if (cmode == kBiasRow) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int64_t gn = n0 + wc * WN + j * 32 + 8 * q + 4 * (lane >> 5) + e;
-                            bias_col[j][q][e] = gn < N ? E::to_f32(Cp[gn]) : 0.0f;
-                        }
-            }
-            if (cmode == kBiasCol) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    const int64_t gm = m0 + wr * WM + i * 32 + (lane & 31);
-                    bias_row[i] = gm < M ? E::to_f32(Cp[gm]) : 0.0f;
-                }
-            }
+            if (cmode == kBiasScalar) bias_one = E::to_f32(((const S *)a.C)[0]);
         }
     }
 #pragma unroll
@@ -866,17 +859,25 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
                         if constexpr (EPI) {
                             if (a.gemm_epi) {
                                 if (cmode == kBiasFull) {
+                                    // One row of C, four consecutive columns (C rows
+                                    // need not be 16-byte aligned: element loads).
                                     const int64_t gm = m0 + wr * WM + i * 32 + (lane & 31);
-#pragma unroll
-                                    for (int e = 0; e < 4; ++e) w[e] = gemm_epilogue<E>(a, w[e], gm, n0 + cl + e);
-                                } else {
+                                    const S *Cr = (const S *)a.C + (gm < M ? gm : 0) * a.ldc + n0 + cl;
 #pragma unroll
                                     for (int e = 0; e < 4; ++e) {
-                                        const float c = cmode == kBiasRow ? bias_col[j][q][e]
-                                                        : cmode == kBiasCol ? bias_row[i]
-                                                                            : bias_one;
-                                        w[e] = cmode == kBiasNone ? a.alpha * w[e] : a.alpha * w[e] + a.beta * c;
+                                        const float c = gm < M && n0 + cl + e < N ? E::to_f32(Cr[e]) : 0.0f;
+                                        w[e] = a.alpha * w[e] + a.beta * c;
                                     }
+                                } else if (cmode == kBiasRow) {
+                                    const float4 c4 = *(const float4 *)&ebias[cl];
+                                    const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) w[e] = a.alpha * w[e] + a.beta * c[e];
+                                } else {
+                                    const float c = cmode == kBiasCol ? ebias[wr * WM + i * 32 + (lane & 31)] : bias_one;
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e)
+                                        w[e] = cmode == kBiasNone ? a.alpha * w[e] : a.alpha * w[e] + a.beta * c;
                                 }
                             }
                         }
