@@ -148,6 +148,76 @@ static int64_t gcd64(int64_t a, int64_t b) {
     return a;
 }
 
+// Time model of the 16-bit tile entries, fitted (least squares on log time)
+// to the forced-tile timings of 48 BF16 products on one MI355X: M from 256
+// to 8192, K and N from 1024 to 14336, every entry.  A launch costs
+// kLaunchUs; each round of workgroups then costs, per 4096 of K, the
+// entry's round time at the occupancy of its busiest CU (1 up to the
+// workgroups one CU holds); a last round of at most one workgroup per CU
+// is cheaper in proportion to the idle CUs.  Root-mean-square error 7 %;
+// it ranks entries, its absolute values belong to that GPU.  The
+// quality ranking above mispriced the 128 x 128 entries against the
+// 256 x 256 one by up to 30 % (e.g. [2048,4096]x[4096,14336]: 272 against
+// 210 us).
+struct RoundCost {
+    double us[3];  // round time at occupancy 1, 2, 3 (levels past the entry's limit unused)
+};
+constexpr RoundCost kRound16[] = {
+    {{98.6, 0.0, 0.0}},   // 256 x 256, 2 stages (one workgroup per CU)
+    {{71.3, 0.0, 0.0}},   // 256 x 128, 3 stages
+    {{43.0, 0.0, 0.0}},   // 128 x 128, 3 stages
+    {{30.3, 49.7, 0.0}},  // 128 x 64, 3 stages (two per CU)
+    {{23.3, 36.5, 43.4}}, // 64 x 64, 3 stages (three per CU)
+    {{56.0, 68.8, 0.0}},  // 128 x 128, 2 stages (two per CU)
+    {{74.6, 0.0, 0.0}},   // 128 x 256, 2 stages
+    {{74.4, 0.0, 0.0}},   // 256 x 128 (4 x 2 waves), 2 stages
+    {{23.3, 37.2, 43.4}}, // 64 x 64, two K groups
+    {{56.5, 69.2, 0.0}},  // 128 x 128, two K groups
+    {{0.0, 0.0, 0.0}},    // persistent twin of entry 0: chosen by plan_persistent only
+};
+static_assert(sizeof(kRound16) / sizeof(kRound16[0]) == kNumTiles16, "one round cost per 16-bit entry");
+constexpr double kLaunchUs = 6.4, kPartialSlope = 0.12;
+
+static double est_us16(int index, int64_t tiles, int64_t K) {
+    const TileCfg *t = &kTiles16[index];
+    const int64_t w = std::min<int64_t>(tile_wgs_per_cu(t), 3);
+    const RoundCost &c = kRound16[index];
+    const int64_t slots = kNumCUs * w;
+    const int64_t full = tiles / slots, rem = tiles % slots;
+    double us = (double)full * c.us[w - 1];
+    if (rem > 0) {
+        const int64_t o = cdiv(rem, kNumCUs);
+        double r = c.us[o - 1];
+        if (o == 1) r *= 1.0 - kPartialSlope + kPartialSlope * (double)rem / kNumCUs;
+        us += r;
+    }
+    return kLaunchUs + us * (double)K / 4096.0;
+}
+
+// The 16-bit entry of least estimated time for a rectangle (more than 64
+// rows; smaller products keep choose_tile's measured rule).
+static int choose_tile16_timed(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm) {
+    int best = -1;
+    double best_us = 0.0;
+    for (int i = 0; i < kNumTiles16; ++i) {
+        if (!tile_allowed(dtype, i, gemm) || kTiles16[i].persistent) continue;
+        const TileCfg *t = &kTiles16[i];
+        const double us = est_us16(i, batch * cdiv(M, t->bm) * cdiv(N, t->bn), K);
+        if (best < 0 || us < best_us * (1.0 - 1e-9)) {
+            best = i;
+            best_us = us;
+        }
+    }
+    return best;
+}
+
+// The general path's entry: the time model for 16-bit products of more
+// than 64 rows, the quality ranking otherwise.
+static int choose_general_tile(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm) {
+    if ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && M > 64) return choose_tile16_timed(dtype, batch, M, N, K, gemm);
+    return choose_tile(dtype, batch, M, N, gemm);
+}
+
 // Last-round balancing for a large tile (one workgroup per CU).  When the
 // tiles leave the last round of workgroups less than half full, the leading
 // output columns are covered by whole rounds of the chosen tile and the
@@ -171,7 +241,7 @@ static void plan_tail(mm_plan_s *p) {
     const int64_t c_main = ((tn - 1) / step) * step;  // whole rounds, at least one column left over
     if (c_main <= 0) return;
     const int64_t n_rem = p->N - c_main * t->bn;
-    const int rt = choose_tile(p->dtype, p->batch, p->kernel_m, n_rem, p->is_gemm);
+    const int rt = choose_general_tile(p->dtype, p->batch, p->kernel_m, n_rem, p->K, p->is_gemm);
     const TileCfg *r = tile_entry(p->dtype, rt);
     const int64_t T_rem = p->batch * cdiv(p->kernel_m, r->bm) * cdiv(n_rem, r->bn);
     const double without = (double)cdiv(T, kNumCUs);
@@ -529,7 +599,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             if (!tile_allowed(p->dtype, p->tile, p->is_gemm))
                 return fail(MM_ERR_BAD_OPTION, "tile %d has no Gemm kernel", req);
         } else if (algo == MM_ALGO_GENERAL) {
-            p->tile = choose_tile(p->dtype, p->batch, M, N, p->is_gemm);
+            p->tile = choose_general_tile(p->dtype, p->batch, M, N, K, p->is_gemm);
         } else {
             p->tile = choose_split_tile(p->dtype, M, N, p->is_gemm);
         }

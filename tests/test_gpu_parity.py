@@ -275,15 +275,16 @@ def test_special_values(dt, algo, dev):
 
 
 @pytest.mark.parametrize("dt", [mm.FLOAT16, mm.BFLOAT16], ids=DT_IDS.get)
-@pytest.mark.parametrize("n", [11000, 11002])
-def test_tail_split(dt, n, dev):
+@pytest.mark.parametrize("m,n", [(8192, 11000), (8192, 11002), (2048, 11000), (2048, 9000)])
+def test_tail_split(dt, m, n, dev):
     """Last-round balancing: columns [0, tail_col) run with the plan's tile
     and the rest with the tail tile.  The result equals, bit for bit, each
     column range of a single launch forced to the corresponding tile (a
     tile's per-element summation order does not depend on N), and matches
     the oracle on sampled outputs around the boundary.  N = 11002 has rows
-    that are not whole 16-byte chunks (element-wise loads and stores)."""
-    sa, sb = (8192, 128), (128, n)
+    that are not whole 16-byte chunks (element-wise loads and stores); the
+    2048-row products take three-stage tail tiles (256 x 128, 128 x 64)."""
+    sa, sb = (m, 128), (128, n)
     a = synth.generate(sa, dt, ("int",), [31, 0])
     b = synth.generate(sb, dt, ("int",), [31, 1])
     plan = mm.Plan(sa, sb, dt)
@@ -577,6 +578,9 @@ SELECTED_PATHS = [
     ((256, 4096), (4096, 4352), mm.BFLOAT16, False, ("split_k", 6, 4)),   # split-K tiles at most 128x128
     ((32, 4096), (11008, 4096), mm.BFLOAT16, True, ("split_k", 5, 2)),    # Gemm decode: split-K
     ((128, 16384), (8704, 16384), mm.FLOAT16, True, ("split_k", 6, 4)),
+    ((1024, 4096), (4096, 11008), mm.BFLOAT16, False, ("general", 1, 1)),  # timed choice: 256x256, one round
+    ((768, 4096), (4096, 4096), mm.FLOAT16, False, ("general", 3, 1)),     # three-stage 128x128
+    ((512, 4096), (4096, 11008), mm.BFLOAT16, False, ("general", 2, 1)),   # 256x128
 ]
 
 

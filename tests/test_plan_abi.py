@@ -288,6 +288,24 @@ def test_small_m_tiles():
     assert mm.Plan((65, 4096), (4096, 21760), mm.BFLOAT16).info()["tile"] not in (4, 5, 9)
 
 
+@pytest.mark.parametrize("sa,sb,want", [
+    ((4096, 4096), (4096, 14336), 1),   # 3.5 rounds of 256 x 256 beat 7 rounds of 128 x 128
+    ((2048, 4096), (4096, 14336), 1),
+    ((1024, 4096), (4096, 11008), 1),   # 172 tiles of 256 x 256: one round
+    ((1024, 11008), (11008, 4096), 3),  # 256 tiles of 128 x 128: three stages, one per CU
+    ((768, 4096), (4096, 4096), 3),
+    ((512, 4096), (4096, 11008), 2),    # 172 tiles of 256 x 128
+    ((8192, 8192), (8192, 8192), 1),
+    ((8192, 4096), (4096, 1024), 6),    # 2 x 256 tiles of 128 x 128, two per CU
+])
+def test_timed_tile_selection(sa, sb, want):
+    """16-bit general plans of more than 64 rows take the tile entry of least
+    estimated time (a launch cost plus round times per occupancy level)."""
+    for dt in (mm.BFLOAT16, mm.FLOAT16):
+        inf = mm.Plan(sa, sb, dt).info()
+        assert mm.ALGO_NAMES[inf["algo"]] == "general" and inf["tile"] == want, (sa, sb, inf)
+
+
 def test_tile_table():
     t16 = mm.tile_configs(mm.BFLOAT16)
     t32 = mm.tile_configs(mm.FLOAT)
