@@ -148,17 +148,18 @@ static int64_t gcd64(int64_t a, int64_t b) {
     return a;
 }
 
-// Time model of the 16-bit tile entries, fitted (least squares on log time)
-// to the forced-tile timings of 48 BF16 products on one MI355X: M from 256
-// to 8192, K and N from 1024 to 14336, every entry.  A launch costs
-// kLaunchUs; each round of workgroups then costs, per 4096 of K, the
+// Time model of the tile entries of FLOAT16 / BFLOAT16 and of FLOAT, each
+// fitted (least squares on log time) to forced-tile timings on one MI355X:
+// every entry on 48 BF16 products (M 256-8192, K and N 1024-14336) and on
+// 35 FP32 products (M 256-4096, K and N 1024-11008).  A launch costs
+// launch_us; each round of workgroups then costs, per 4096 of K, the
 // entry's round time at the occupancy of its busiest CU (1 up to the
-// workgroups one CU holds); a last round of at most one workgroup per CU
-// is cheaper in proportion to the idle CUs.  Root-mean-square error 7 %;
-// it ranks entries, its absolute values belong to that GPU.  The
-// quality ranking above mispriced the 128 x 128 entries against the
-// 256 x 256 one by up to 30 % (e.g. [2048,4096]x[4096,14336]: 272 against
-// 210 us).
+// workgroups one CU holds); a last round of at most one workgroup per CU is
+// cheaper in proportion to the idle CUs (slope).  Root-mean-square error
+// 7 % (16-bit) and 2 % (FP32); the model ranks entries, its absolute values
+// belong to that GPU.  The quality ranking above mispriced the 16-bit
+// 128 x 128 entries against the 256 x 256 one by up to 30 % (e.g.
+// [2048,4096]x[4096,14336]: 272 against 210 us).
 struct RoundCost {
     double us[3];  // round time at occupancy 1, 2, 3 (levels past the entry's limit unused)
 };
@@ -175,34 +176,49 @@ constexpr RoundCost kRound16[] = {
     {{56.5, 69.2, 0.0}},  // 128 x 128, two K groups
     {{0.0, 0.0, 0.0}},    // persistent twin of entry 0: chosen by plan_persistent only
 };
+constexpr RoundCost kRound32[] = {
+    {{272.8, 0.0, 0.0}},    // 128 x 128, 3 stages (one workgroup per CU)
+    {{153.2, 260.6, 0.0}},  // 128 x 64, 3 stages (two per CU)
+    {{85.8, 150.9, 198.8}}, // 64 x 64, 3 stages (three per CU)
+    {{485.1, 0.0, 0.0}},    // 256 x 128, 3 stages
+    {{279.0, 495.5, 0.0}},  // 128 x 128, 2 stages (two per CU)
+    {{83.3, 155.9, 198.6}}, // 64 x 64, two K groups
+    {{254.8, 480.8, 0.0}},  // 128 x 128, two K groups
+};
 static_assert(sizeof(kRound16) / sizeof(kRound16[0]) == kNumTiles16, "one round cost per 16-bit entry");
-constexpr double kLaunchUs = 6.4, kPartialSlope = 0.12;
+static_assert(sizeof(kRound32) / sizeof(kRound32[0]) == kNumTiles32, "one round cost per FLOAT entry");
+struct TimeModel {
+    const RoundCost *round;
+    double launch_us, slope;
+};
+constexpr TimeModel kModel16 = {kRound16, 6.4, 0.12}, kModel32 = {kRound32, 6.7, 0.054};
 
-static double est_us16(int index, int64_t tiles, int64_t K) {
-    const TileCfg *t = &kTiles16[index];
+static double est_us(int dtype, int index, int64_t tiles, int64_t K) {
+    const TimeModel &m = dtype == MM_FLOAT ? kModel32 : kModel16;
+    const TileCfg *t = tile_entry(dtype, index);
     const int64_t w = std::min<int64_t>(tile_wgs_per_cu(t), 3);
-    const RoundCost &c = kRound16[index];
+    const RoundCost &c = m.round[index];
     const int64_t slots = kNumCUs * w;
     const int64_t full = tiles / slots, rem = tiles % slots;
     double us = (double)full * c.us[w - 1];
     if (rem > 0) {
         const int64_t o = cdiv(rem, kNumCUs);
         double r = c.us[o - 1];
-        if (o == 1) r *= 1.0 - kPartialSlope + kPartialSlope * (double)rem / kNumCUs;
+        if (o == 1) r *= 1.0 - m.slope + m.slope * (double)rem / kNumCUs;
         us += r;
     }
-    return kLaunchUs + us * (double)K / 4096.0;
+    return m.launch_us + us * (double)K / 4096.0;
 }
 
-// The 16-bit entry of least estimated time for a rectangle (more than 64
-// rows; smaller products keep choose_tile's measured rule).
-static int choose_tile16_timed(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm) {
+// The entry of least estimated time for a rectangle (FLOAT16, BFLOAT16 or
+// FLOAT; persistent entries are left to plan_persistent).
+static int choose_tile_timed(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm) {
     int best = -1;
     double best_us = 0.0;
-    for (int i = 0; i < kNumTiles16; ++i) {
-        if (!tile_allowed(dtype, i, gemm) || kTiles16[i].persistent) continue;
-        const TileCfg *t = &kTiles16[i];
-        const double us = est_us16(i, batch * cdiv(M, t->bm) * cdiv(N, t->bn), K);
+    for (int i = 0; i < tile_count(dtype); ++i) {
+        const TileCfg *t = tile_entry(dtype, i);
+        if (!tile_allowed(dtype, i, gemm) || t->persistent) continue;
+        const double us = est_us(dtype, i, batch * cdiv(M, t->bm) * cdiv(N, t->bn), K);
         if (best < 0 || us < best_us * (1.0 - 1e-9)) {
             best = i;
             best_us = us;
@@ -211,10 +227,12 @@ static int choose_tile16_timed(int dtype, int64_t batch, int64_t M, int64_t N, i
     return best;
 }
 
-// The general path's entry: the time model for 16-bit products of more
-// than 64 rows, the quality ranking otherwise.
+// The general path's entry: the time model for FLOAT and for 16-bit
+// products of more than 64 rows (smaller ones keep choose_tile's measured
+// rule), the quality ranking for DOUBLE and INT8.
 static int choose_general_tile(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm) {
-    if ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && M > 64) return choose_tile16_timed(dtype, batch, M, N, K, gemm);
+    if (dtype == MM_FLOAT || ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && M > 64))
+        return choose_tile_timed(dtype, batch, M, N, K, gemm);
     return choose_tile(dtype, batch, M, N, gemm);
 }
 
@@ -278,22 +296,35 @@ static void plan_persistent(mm_plan_s *p) {
     if (tiles >= 2 * kNumCUs) p->tile = kT16Persist;
 }
 
-// Smallest-padding tile for split-K (its output is small by construction);
-// among equally padded tiles, the one of higher relative throughput.  Tiles
-// above 128 x 128 are left out: with so few of them the plan would need
-// many short K chunks, whose FP32 partials (split x M x N x 4 bytes) can
-// outweigh the inputs.
-static int choose_split_tile(int dtype, int64_t M, int64_t N, bool gemm = false) {
+// Tile for split-K (its output is small by construction): the smallest
+// edge padding, and among equally padded tiles the one of higher relative
+// throughput.  Tiles above 128 x 128 are left out: with so few of them the
+// plan would need many short K chunks, whose FP32 partials (split x M x N x
+// 4 bytes) can outweigh the inputs.  FLOAT MatMul uses its two-K-group
+// entries, and weighs the padding by the share of the CUs the split
+// fills: plan_split aims at one workgroup per
+// CU with at least 256 K elements per chunk, so a large tile over a small
+// output can leave most CUs idle (e.g. [128,2048]x[2048,2048]: 128 x 128
+// tiles in 8 chunks fill 128 CUs, 29.7 us; 64 x 64 tiles in 4 chunks fill
+// 256, 20.2 us).
+static int choose_split_tile(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm = false) {
     int best = -1;
-    double best_pad = -1.0;
+    double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
         if (!tile_allowed(dtype, i, gemm)) continue;
         const TileCfg *t = tile_entry(dtype, i);
         if (t->bm * t->bn > 128 * 128) continue;
-        double pad = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
-        const bool tie = best >= 0 && fabs(pad - best_pad) <= 1e-9;
-        if (pad > best_pad + 1e-9 || (tie && tile_quality(dtype, i) > tile_quality(dtype, best))) {
-            best_pad = pad;
+        // FLOAT MatMul: the two-K-group entries (the measured split tiles).
+        if (dtype == MM_FLOAT && !gemm && t->kgroups != 2) continue;
+        double score = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
+        if (dtype == MM_FLOAT) {
+            const int64_t tiles = batch * cdiv(M, t->bm) * cdiv(N, t->bn);
+            const int64_t s = std::min<int64_t>(cdiv(kNumCUs, tiles), std::max<int64_t>(1, K / 256));
+            score *= (double)std::min<int64_t>(kNumCUs, tiles * s) / kNumCUs;
+        }
+        const bool tie = best >= 0 && fabs(score - best_s) <= 1e-9;
+        if (score > best_s + 1e-9 || (tie && tile_quality(dtype, i) > tile_quality(dtype, best))) {
+            best_s = score;
             best = i;
         }
     }
@@ -526,7 +557,11 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         const bool skn_short = t16 && N == 8 && K < 1024;
         // Workgroups of the tile the general path would choose.
         auto general_tiles = [&]() -> int64_t {
-            const TileCfg *t = tile_entry(p->dtype, choose_tile(p->dtype, p->batch, M, N, p->is_gemm));
+            // FLOAT: the entry the general path would run; the 16-bit
+            // thresholds below were measured with the quality ranking.
+            const int gt = p->dtype == MM_FLOAT ? choose_general_tile(p->dtype, p->batch, M, N, K, p->is_gemm)
+                                                : choose_tile(p->dtype, p->batch, M, N, p->is_gemm);
+            const TileCfg *t = tile_entry(p->dtype, gt);
             return p->batch * cdiv(M, t->bm) * cdiv(N, t->bn);
         };
         // Skinny-M with K cut over workgroups (measured against split-K and
@@ -601,7 +636,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         } else if (algo == MM_ALGO_GENERAL) {
             p->tile = choose_general_tile(p->dtype, p->batch, M, N, K, p->is_gemm);
         } else {
-            p->tile = choose_split_tile(p->dtype, M, N, p->is_gemm);
+            p->tile = choose_split_tile(p->dtype, p->batch, M, N, K, p->is_gemm);
         }
         if (algo == MM_ALGO_GENERAL && req == 0) {
             plan_tail(p);

@@ -581,6 +581,8 @@ SELECTED_PATHS = [
     ((1024, 4096), (4096, 11008), mm.BFLOAT16, False, ("general", 1, 1)),  # timed choice: 256x256, one round
     ((768, 4096), (4096, 4096), mm.FLOAT16, False, ("general", 3, 1)),     # three-stage 128x128
     ((512, 4096), (4096, 11008), mm.BFLOAT16, False, ("general", 2, 1)),   # 256x128
+    ((128, 2048), (2048, 2048), mm.FLOAT, False, ("split_k", 6, 4)),       # FP32 split tile filling the CUs
+    ((256, 4096), (4096, 11008), mm.FLOAT, False, ("general", 6, 1)),      # FP32 timed choice: no split
 ]
 
 

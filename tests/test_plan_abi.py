@@ -306,6 +306,20 @@ def test_timed_tile_selection(sa, sb, want):
         assert mm.ALGO_NAMES[inf["algo"]] == "general" and inf["tile"] == want, (sa, sb, inf)
 
 
+@pytest.mark.parametrize("sa,sb,want", [
+    ((128, 2048), (2048, 2048), ("split_k", 6, 4)),   # 64 x 64 tiles in 4 chunks fill the CUs
+    ((128, 1024), (1024, 1024), ("split_k", 6, 4)),
+    ((128, 4096), (4096, 4096), ("split_k", 7, 8)),   # 128 x 128 tiles in 8 chunks fill them too
+    ((256, 4096), (4096, 11008), ("general", 6, 1)),  # 688 tiles of 64 x 64: no split
+    ((64, 131072), (131072, 64), ("split_k", 6, 256)),
+])
+def test_fp32_split_tiles(sa, sb, want):
+    """FLOAT split-K takes the two-K-group tile whose chunks fill the most
+    CUs, and the split-K occupancy test counts the general path's own tiles."""
+    inf = mm.Plan(sa, sb, mm.FLOAT).info()
+    assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
+
+
 def test_tile_table():
     t16 = mm.tile_configs(mm.BFLOAT16)
     t32 = mm.tile_configs(mm.FLOAT)
