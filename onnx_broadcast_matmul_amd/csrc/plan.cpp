@@ -236,6 +236,32 @@ static int choose_general_tile(int dtype, int64_t batch, int64_t M, int64_t N, i
     return choose_tile(dtype, batch, M, N, gemm);
 }
 
+constexpr int kT16Large = 0, kT16Persist = 10;  // the 256 x 256 entry and its persistent twin
+// Split-K on the 256 x 256 entry for a 16-bit product the general path
+// would run in at most half a round of that entry with a long K: the K
+// chunks fill one round, and the FP32 partials they write and the reduction
+// reads cost about kSplitUsPerMB per MB of partials (measured on 18 BF16
+// products of 2-8 M outputs and K 4096-14336: about 35 us for 67 MB).
+// Returns the split count, or 0 when the estimate does not gain 5 % over
+// the general plan's.  E.g. [2048,14336]x[14336,4096]: general 256 us,
+// two chunks of 256 x 256 tiles 218 us; [2048,4096]x[4096,4096]: general
+// 77 us, split 90 us.
+constexpr double kSplitUsPerMB = 0.55;
+static int large_tile_split16(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm) {
+    if (!(dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) || M <= 64 || !tile_allowed(dtype, kT16Large, gemm)) return 0;
+    const TileCfg *t0 = tile_entry(dtype, kT16Large);
+    const int64_t n0 = batch * cdiv(M, t0->bm) * cdiv(N, t0->bn);
+    if (n0 > kNumCUs / 2) return 0;
+    const int64_t s = std::min<int64_t>(kNumCUs / n0, K / 1024);
+    if (s < 2) return 0;
+    const int gt = choose_general_tile(dtype, batch, M, N, K, gemm);
+    const TileCfg *g = tile_entry(dtype, gt);
+    const double t_gen = est_us(dtype, gt, batch * cdiv(M, g->bm) * cdiv(N, g->bn), K);
+    const double part_mb = (double)s * batch * M * N * 4.0 / 1e6;
+    const double t_split = est_us(dtype, kT16Large, n0 * s, cdiv(K, s)) + kSplitUsPerMB * part_mb;
+    return t_split < 0.95 * t_gen ? (int)s : 0;
+}
+
 // Last-round balancing for a large tile (one workgroup per CU).  When the
 // tiles leave the last round of workgroups less than half full, the leading
 // output columns are covered by whole rounds of the chosen tile and the
@@ -281,7 +307,6 @@ static void plan_tail(mm_plan_s *p) {
 // of tiles 18 % faster, K = 256 8 %, K = 512 5 %, K = 1024 4 %, K = 2048
 // even, K = 4096 5 % slower -- so short K with at least two rounds.  The
 // kernel takes whole tiles and stages only.
-constexpr int kT16Large = 0, kT16Persist = 10;
 static_assert(kTiles16[kT16Persist].persistent == 1 && kTiles16[kT16Large].persistent == 0 &&
                   kTiles16[kT16Persist].bm == kTiles16[kT16Large].bm && kTiles16[kT16Persist].bn == kTiles16[kT16Large].bn &&
                   kTiles16[kT16Persist].bkb == kTiles16[kT16Large].bkb,
@@ -532,6 +557,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
     if (st != MM_OK) return st;
 
     int algo = opt ? opt->force_algo : MM_ALGO_AUTO;
+    int large_split = 0;  // > 0: split-K on the 256 x 256 entry in this many chunks
     if (algo == MM_ALGO_AUTO) {
         const double flops = 2.0 * (double)p->batch * M * N * K;
         // Tiles of the smallest block tile in the table: the most workgroups
@@ -601,6 +627,8 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             // whose FP32 MFMA chains are four times as long as the 16-bit
             // ones (measured 10-20 % faster split).
             algo = MM_ALGO_SPLIT_K;
+        } else if ((large_split = large_tile_split16(p->dtype, p->batch, M, N, K, p->is_gemm)) > 0) {
+            algo = MM_ALGO_SPLIT_K;  // a long K over at most half a round of large tiles
         } else {
             algo = MM_ALGO_GENERAL;
         }
@@ -635,6 +663,8 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
                 return fail(MM_ERR_BAD_OPTION, "tile %d has no Gemm kernel", req);
         } else if (algo == MM_ALGO_GENERAL) {
             p->tile = choose_general_tile(p->dtype, p->batch, M, N, K, p->is_gemm);
+        } else if (large_split > 0) {
+            p->tile = kT16Large;
         } else {
             p->tile = choose_split_tile(p->dtype, p->batch, M, N, K, p->is_gemm);
         }
@@ -647,7 +677,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         if (algo == MM_ALGO_SPLIT_K) {
             int sreq = opt ? opt->split_k : 0;
             if (sreq < 0) return fail(MM_ERR_BAD_OPTION, "split_k %d is negative", sreq);
-            plan_split(p, sreq);
+            plan_split(p, sreq > 0 ? sreq : large_split);
         }
         if (tiles * p->split > INT32_MAX)
             return fail(MM_ERR_TOO_LARGE, "too many workgroups (%lld tiles x %d splits)", (long long)tiles,

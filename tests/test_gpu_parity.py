@@ -583,6 +583,8 @@ SELECTED_PATHS = [
     ((512, 4096), (4096, 11008), mm.BFLOAT16, False, ("general", 2, 1)),   # 256x128
     ((128, 2048), (2048, 2048), mm.FLOAT, False, ("split_k", 6, 4)),       # FP32 split tile filling the CUs
     ((256, 4096), (4096, 11008), mm.FLOAT, False, ("general", 6, 1)),      # FP32 timed choice: no split
+    ((2048, 14336), (14336, 4096), mm.BFLOAT16, False, ("split_k", 1, 2)),  # long K on 256x256 tiles
+    ((1024, 14336), (4096, 14336), mm.FLOAT16, True, ("split_k", 1, 4)),    # the same for a Gemm (B transposed)
 ]
 
 

@@ -292,7 +292,7 @@ def test_small_m_tiles():
     ((4096, 4096), (4096, 14336), 1),   # 3.5 rounds of 256 x 256 beat 7 rounds of 128 x 128
     ((2048, 4096), (4096, 14336), 1),
     ((1024, 4096), (4096, 11008), 1),   # 172 tiles of 256 x 256: one round
-    ((1024, 11008), (11008, 4096), 3),  # 256 tiles of 128 x 128: three stages, one per CU
+    ((1024, 4096), (4096, 4096), 3),    # 256 tiles of 128 x 128: three stages, one per CU
     ((768, 4096), (4096, 4096), 3),
     ((512, 4096), (4096, 11008), 2),    # 172 tiles of 256 x 128
     ((8192, 8192), (8192, 8192), 1),
@@ -304,6 +304,26 @@ def test_timed_tile_selection(sa, sb, want):
     for dt in (mm.BFLOAT16, mm.FLOAT16):
         inf = mm.Plan(sa, sb, dt).info()
         assert mm.ALGO_NAMES[inf["algo"]] == "general" and inf["tile"] == want, (sa, sb, inf)
+
+
+@pytest.mark.parametrize("sa,sb,want", [
+    ((2048, 14336), (14336, 4096), ("split_k", 1, 2)),  # 128 tiles of 256 x 256, K 14336: two chunks
+    ((1024, 14336), (14336, 4096), ("split_k", 1, 4)),  # 64 tiles: four chunks
+    ((2048, 11008), (11008, 4096), ("split_k", 1, 2)),
+    ((2048, 4096), (4096, 4096), ("general", 6, 1)),    # K 4096: the partials' round trip does not pay
+    ((2048, 8192), (8192, 4096), ("general", 6, 1)),
+    ((4096, 14336), (14336, 4096), ("general", 1, 1)),  # a full round of large tiles
+])
+def test_large_tile_split(sa, sb, want):
+    """A 16-bit product that fills at most half a round of 256 x 256 tiles
+    with a long K splits K on that tile when the time estimate (chunks
+    filling one round plus the partials' round trip) gains 5 %."""
+    for dt in (mm.BFLOAT16, mm.FLOAT16):
+        inf = mm.Plan(sa, sb, dt).info()
+        assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
+    # Gemm with a transposed B takes the same rule (its 256 x 256 entry has a split-K kernel)
+    g = mm.GemmPlan((2048, 14336), (4096, 14336), mm.BFLOAT16, False, True, None, 1.0, 0.0)
+    assert (g.algo, g.info()["tile"], g.info()["split_k"]) == (mm.ALGO_SPLIT_K, 1, 2)
 
 
 @pytest.mark.parametrize("sa,sb,want", [
