@@ -423,16 +423,18 @@ def _cs(layout, M, N):
 
 
 def gemm_parity(M, N, K, dt, ta, tb, layout, dev, algo=0, alpha=0.75, beta=-1.5, dist=U1, seed=0, exact=False,
-                offset=0):
+                offset=0, tile=0):
     sa = (K, M) if ta else (M, K)
     sb = (N, K) if tb else (K, N)
     cs = _cs(layout, M, N)
     a = synth.generate(sa, dt, dist, [seed, 0])
     b = synth.generate(sb, dt, dist, [seed, 1])
     c = None if cs is None else synth.generate(cs, dt, dist, [seed, 2])
-    plan = mm.GemmPlan(sa, sb, dt, ta, tb, cs, alpha, beta, force_algo=algo)
+    plan = mm.GemmPlan(sa, sb, dt, ta, tb, cs, alpha, beta, force_algo=algo, tile=tile)
     if algo:
         assert plan.algo == algo
+    if tile:
+        assert plan.info()["tile"] == tile
 
     def dev_tensor(x, shape):
         # `offset` elements past the allocation start: unaligned operands
@@ -461,6 +463,28 @@ def test_gemm(dt, ta, tb, algo, dev):
     per column, per row, full) and each algorithm, on ragged sizes."""
     for i, layout in enumerate(GEMM_LAYOUTS):
         gemm_parity(300, 200, 520, dt, ta, tb, layout, dev, algo=algo, seed=60 + i)
+
+
+@pytest.mark.parametrize("dt", GEMM_DTYPES, ids=DT_IDS.get)
+@pytest.mark.parametrize("ta,tb", GEMM_TRANS, ids=lambda t: f"t{t}")
+def test_gemm_every_tile(dt, ta, tb, dev):
+    """Every tile entry that has Gemm kernels, general and split-K, bit-exact
+    on small-integer inputs with integer alpha / beta and a per-column C;
+    the other entries are refused at plan creation."""
+    n_tiles = len(mm.tile_configs(dt))
+    ran = 0
+    for tile in range(1, n_tiles + 1):
+        try:
+            mm.GemmPlan((130, 1000), (1000, 70), dt, False, False, (70,), 1.0, 1.0, force_algo=mm.ALGO_GENERAL, tile=tile)
+        except mm.MMError as e:
+            assert e.status == mm.ERR_BAD_OPTION
+            continue
+        gemm_parity(130, 70, 1000, dt, ta, tb, ("N",), dev, algo=mm.ALGO_GENERAL, tile=tile, alpha=2.0, beta=-3.0,
+                    dist=("int",), exact=True, seed=80 + tile)
+        gemm_parity(130, 70, 1000, dt, ta, tb, ("N",), dev, algo=mm.ALGO_SPLIT_K, tile=tile, alpha=2.0, beta=-3.0,
+                    dist=("int",), exact=True, seed=90 + tile)
+        ran += 1
+    assert ran == (5 if dt != mm.FLOAT else 2)
 
 
 @pytest.mark.parametrize("dt", GEMM_DTYPES, ids=DT_IDS.get)

@@ -515,7 +515,7 @@ def test_gemm_plan_shapes(ta, tb):
     assert p.output_shape == (M, N) and p.output_numel == M * N
     inf = p.info()
     assert (inf["M"], inf["N"], inf["K"]) == (M, N, K) and inf["algo"] == mm.ALGO_GENERAL
-    assert inf["tile"] - 1 in (0, 5, 4)  # Gemm: only the tiles instantiated with its epilogue
+    assert inf["tile"] - 1 in (0, 5, 4, 2, 1)  # Gemm: only the tiles instantiated with its epilogue
     assert inf["tail_col"] == 0
     # skinny shapes of a Gemm take the tiled kernels: split-K when one row
     # of tiles cannot fill the GPU and K is long, else the general kernel
@@ -534,7 +534,7 @@ def test_gemm_plan_shapes(ta, tb):
     (dict(sa=(4, 3), sb=(3, 5), c_shape=(-1,)), mm.ERR_NEG_DIM),
     (dict(sa=(4, 3), sb=(3, 5), dtype=mm.DOUBLE), mm.ERR_DTYPE),
     (dict(sa=(64, 64), sb=(64, 8), force_algo=mm.ALGO_SKINNY_N), mm.ERR_BAD_OPTION),
-    (dict(sa=(64, 64), sb=(64, 64), trans_a=1, force_algo=mm.ALGO_GENERAL, tile=2), mm.ERR_BAD_OPTION),
+    (dict(sa=(64, 64), sb=(64, 64), trans_a=1, force_algo=mm.ALGO_GENERAL, tile=4), mm.ERR_BAD_OPTION),
 ])
 def test_gemm_plan_errors(kw, status):
     kw = dict(kw)
