@@ -325,8 +325,8 @@ static void plan_persistent(mm_plan_s *p) {
 // edge padding, and among equally padded tiles the one of higher relative
 // throughput.  Tiles above 128 x 128 are left out: with so few of them the
 // plan would need many short K chunks, whose FP32 partials (split x M x N x
-// 4 bytes) can outweigh the inputs.  FLOAT MatMul uses its two-K-group
-// entries, and weighs the padding by the share of the CUs the split
+// 4 bytes) can outweigh the inputs.  FLOAT uses its two-K-group entries,
+// and weighs the padding by the share of the CUs the split
 // fills: plan_split aims at one workgroup per
 // CU with at least 256 K elements per chunk, so a large tile over a small
 // output can leave most CUs idle (e.g. [128,2048]x[2048,2048]: 128 x 128
@@ -339,8 +339,8 @@ static int choose_split_tile(int dtype, int64_t batch, int64_t M, int64_t N, int
         if (!tile_allowed(dtype, i, gemm)) continue;
         const TileCfg *t = tile_entry(dtype, i);
         if (t->bm * t->bn > 128 * 128) continue;
-        // FLOAT MatMul: the two-K-group entries (the measured split tiles).
-        if (dtype == MM_FLOAT && !gemm && t->kgroups != 2) continue;
+        // FLOAT: the two-K-group entries (the measured split tiles).
+        if (dtype == MM_FLOAT && t->kgroups != 2) continue;
         double score = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
         if (dtype == MM_FLOAT) {
             const int64_t tiles = batch * cdiv(M, t->bm) * cdiv(N, t->bn);
