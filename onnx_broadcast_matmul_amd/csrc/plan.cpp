@@ -249,6 +249,9 @@ constexpr int kT16Large = 0, kT16Persist = 10;  // the 256 x 256 entry and its p
 constexpr double kSplitUsPerMB = 0.55;
 static int large_tile_split16(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm) {
     if (!(dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) || M <= 64 || !tile_allowed(dtype, kT16Large, gemm)) return 0;
+    // Measured gains start at K = 8192; below it the estimate can pick a
+    // split that loses ([1296,6464]x[6464,4480]: 105 against 93.5 us).
+    if (K < 8192) return 0;
     const TileCfg *t0 = tile_entry(dtype, kT16Large);
     const int64_t n0 = batch * cdiv(M, t0->bm) * cdiv(N, t0->bn);
     if (n0 > kNumCUs / 2) return 0;
