@@ -23,6 +23,9 @@ static hipError_t launch_16(int tile, bool vec, bool split, const KArgs &a, hipS
         MM_TILE_CASE(DT, kTiles16, 8);
         MM_TILE_CASE(DT, kTiles16, 9);
         MM_TILE_CASE(DT, kTiles16, 10);
+        MM_TILE_CASE(DT, kTiles16, 11);
+        MM_TILE_CASE(DT, kTiles16, 12);
+        MM_TILE_CASE(DT, kTiles16, 13);
     }
     return hipErrorInvalidValue;
 }
@@ -41,7 +44,7 @@ static hipError_t launch_32(int tile, bool vec, bool split, const KArgs &a, hipS
 }
 #undef MM_TILE_CASE
 
-static_assert(kNumTiles16 == 11 && kNumTiles32 == 7, "launch switch must cover the tile table");
+static_assert(kNumTiles16 == 14 && kNumTiles32 == 7, "launch switch must cover the tile table");
 
 // Prepacked constant B: the 16-byte chunk (piece, lane) of the panel of
 // matrix mi, tile column tn and K stage st is what lane `lane` of load

@@ -64,7 +64,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Relative per-CU throughput of a tile entry (bigger tiles reuse each LDS
 // byte more often); used only to rank entries against each other.
 static double tile_quality(int dtype, int index) {
-    static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5, 0.0};
+    static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5, 0.0, 0.0, 0.0, 0.0};
     static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15};
     static const double q64[kNumTiles64] = {1.0, 0.8};
     static const double q8[kNumTiles8] = {1.0, 0.75, 1.0};
@@ -99,32 +99,49 @@ static bool tile_allowed(int dtype, int index, bool gemm) {
     return false;
 }
 
-// 16-bit entries for products of at most 64 rows (see choose_tile).
-constexpr int kT16Small2 = 8, kT16Small = 4, kT16Narrow = 3;
+// 16-bit entries for products of at most 64 rows (see choose_tile).  The
+// last three entries of the table serve such products only: the selector
+// takes them by the rules below, never by ranking or time estimate.
+constexpr int kT16Small2 = 8, kT16Small = 4, kT16Row32 = 11, kT16Row32Wide = 12, kT16Row64 = 13;
 static_assert(kTiles16[kT16Small2].bm == 64 && kTiles16[kT16Small2].bn == 64 && kTiles16[kT16Small2].kgroups == 2,
               "64 x 64 entry with two K groups");
 static_assert(kTiles16[kT16Small].bm == 64 && kTiles16[kT16Small].bn == 64 && kTiles16[kT16Small].kgroups == 1,
               "64 x 64 entry with one K group");
-static_assert(kTiles16[kT16Narrow].bm == 128 && kTiles16[kT16Narrow].bn == 64, "128 x 64 entry");
+static_assert(kTiles16[kT16Row32].bm == 32 && kTiles16[kT16Row32].bn == 128 && kTiles16[kT16Row32Wide].bm == 32 &&
+                  kTiles16[kT16Row32Wide].bn == 256 && kTiles16[kT16Row64].bm == 64 && kTiles16[kT16Row64].bn == 128 &&
+                  kNumTiles16 == kT16Row64 + 1 && kT16Row32Wide == kT16Row32 + 1 && kT16Row64 == kT16Row32 + 2,
+              "the small-row entries close the 16-bit table");
 static_assert(kTransTiles16[2] == kT16Small, "the 64 x 64 entry has a Gemm kernel");
+
+static bool small_m_entry(int dtype, int index) {
+    return (dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && index >= kT16Row32;
+}
 
 static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, bool gemm = false) {
     if ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && M <= 64) {
         // At most 64 rows: each tile is a K-long chain of B stages, not MFMA
         // work, so the quality ranking above does not apply.  Measured for
         // M = 1..64, K = 4096: up to one 64 x 64 tile per CU, the entry
-        // with two K groups (shorter chain) wins; up to 1.5 per CU, the
-        // single-group 64 x 64 entry; beyond, 128 x 64 tiles (one per CU).
+        // with two K groups (shorter chain) wins.  Beyond that, tiles one
+        // row tile high and 128 columns wide (32 rows for M <= 32, else 64)
+        // stream B 6-27 % faster than the 64 x 64 and 128 x 64 tiles
+        // (BF16, M = 16..64, K = 2048..8192, N = 20480..128256); for
+        // M <= 32, 256-column tiles (one per CU) gain another 4-15 % when
+        // every round fills at least three quarters of the CUs (N = 49152,
+        // 65536, 128256), and lose up to 45 % when a round is less full.
         // Gemm has the single-group 64 x 64 entry only.
         const int64_t t64 = batch * cdiv(N, 64);
         if (gemm) return kT16Small;
         if (t64 <= kNumCUs) return kT16Small2;
-        return t64 <= 3 * kNumCUs / 2 ? kT16Small : kT16Narrow;
+        if (M > 32) return kT16Row64;
+        const int64_t t256 = batch * cdiv(N, 256), last = t256 % kNumCUs;
+        if (t256 >= 3 * kNumCUs / 4 && (last == 0 || last >= 3 * kNumCUs / 4)) return kT16Row32Wide;
+        return kT16Row32;
     }
     int best = -1;
     double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
-        if (!tile_allowed(dtype, i, gemm)) continue;
+        if (!tile_allowed(dtype, i, gemm) || small_m_entry(dtype, i)) continue;
         double s = tile_score(dtype, i, batch, M, N);
         if (s > best_s + 1e-9) {
             best_s = s;
@@ -175,6 +192,9 @@ constexpr RoundCost kRound16[] = {
     {{23.3, 37.2, 43.4}}, // 64 x 64, two K groups
     {{56.5, 69.2, 0.0}},  // 128 x 128, two K groups
     {{0.0, 0.0, 0.0}},    // persistent twin of entry 0: chosen by plan_persistent only
+    {{0.0, 0.0, 0.0}},    // 32 x 128, 32 x 256, 64 x 128: products of at most 64 rows,
+    {{0.0, 0.0, 0.0}},    // chosen by choose_tile and choose_split_tile
+    {{0.0, 0.0, 0.0}},
 };
 constexpr RoundCost kRound32[] = {
     {{272.8, 0.0, 0.0}},    // 128 x 128, 3 stages (one workgroup per CU)
@@ -217,7 +237,7 @@ static int choose_tile_timed(int dtype, int64_t batch, int64_t M, int64_t N, int
     double best_us = 0.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
         const TileCfg *t = tile_entry(dtype, i);
-        if (!tile_allowed(dtype, i, gemm) || t->persistent) continue;
+        if (!tile_allowed(dtype, i, gemm) || t->persistent || small_m_entry(dtype, i)) continue;
         const double us = est_us(dtype, i, batch * cdiv(M, t->bm) * cdiv(N, t->bn), K);
         if (best < 0 || us < best_us * (1.0 - 1e-9)) {
             best = i;
@@ -276,7 +296,9 @@ static int large_tile_split16(int dtype, int64_t batch, int64_t M, int64_t N, in
 static void plan_tail(mm_plan_s *p) {
     p->tail_col = 0;
     p->tail_tile = -1;
-    if (p->dtype == MM_DOUBLE) return;
+    // The small-row entries span M in one row tile: choose_tile already
+    // balanced their rounds.
+    if (p->dtype == MM_DOUBLE || small_m_entry(p->dtype, p->tile)) return;
     const TileCfg *t = tile_entry(p->dtype, p->tile);
     if (tile_wgs_per_cu(t) != 1) return;
     const int64_t rows = p->batch * cdiv(p->kernel_m, t->bm);
@@ -336,10 +358,24 @@ static void plan_persistent(mm_plan_s *p) {
 // tiles in 8 chunks fill 128 CUs, 29.7 us; 64 x 64 tiles in 4 chunks fill
 // 256, 20.2 us).
 static int choose_split_tile(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K, bool gemm = false) {
+    if ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && M <= 64 && !gemm) {
+        // At most 64 rows: the 64 x 64 tiles in cdiv(CUs, tiles) chunks,
+        // unless those chunks overfill the CUs or stay K-long (>= 3072);
+        // then the 128-column tiles one row tile high, whose chunks
+        // plan_split keeps to one workgroup per CU.  Measured on 28 BF16
+        // products (M = 16..64, K = 1024..14336, N = 2048..11008): within
+        // 0.9 % of the best tile and chunk count tried (geometric mean),
+        // against 6.9 % for the 64 x 64 tiles alone; e.g.
+        // [64,4096]x[4096,11008] 33.4 -> 27.6 us, [16,14336]x[14336,4096]
+        // 32.0 -> 29.1 us.
+        const int64_t t64 = batch * cdiv(N, 64);
+        const int64_t s64 = std::min<int64_t>(cdiv(kNumCUs, t64), std::max<int64_t>(1, K / 256));
+        if (t64 * s64 > kNumCUs || K / s64 >= 3072) return M <= 32 ? kT16Row32 : kT16Row64;
+    }
     int best = -1;
     double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {
-        if (!tile_allowed(dtype, i, gemm)) continue;
+        if (!tile_allowed(dtype, i, gemm) || small_m_entry(dtype, i)) continue;
         const TileCfg *t = tile_entry(dtype, i);
         if (t->bm * t->bn > 128 * 128) continue;
         // FLOAT: the two-K-group entries (the measured split tiles).
@@ -485,6 +521,10 @@ static void plan_split(mm_plan_s *p, int requested) {
         // Aim for about one workgroup per CU, with at least 256 K elements
         // per partition (the partials then stay small next to the inputs).
         int64_t want = cdiv((int64_t)kNumCUs, std::max<int64_t>(tiles, 1));
+        // The entries for at most 64 rows: never more workgroups than CUs
+        // (BF16 [48,4096]x[4096,11008] on 64 x 128 tiles: 2 chunks 26.5
+        // us, 3 chunks -- two workgroups on two CUs -- 32.1 us).
+        if (small_m_entry(p->dtype, p->tile)) want = std::max<int64_t>(1, kNumCUs / std::max<int64_t>(tiles, 1));
         // FP32 and DOUBLE: one partition fewer when that still fills three
         // quarters of the CUs and the rounded-up count would put a second
         // workgroup on a few of them (their long MFMA chains make that
@@ -564,10 +604,12 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
     if (algo == MM_ALGO_AUTO) {
         const double flops = 2.0 * (double)p->batch * M * N * K;
         // Tiles of the smallest block tile in the table: the most workgroups
-        // the tiled kernel can put on the GPU.
+        // the tiled kernel can put on the GPU (64-row tiles: the 32-row
+        // entries serve at most 32 rows, where they count the same).
         int64_t small_tiles = 0;
         for (int i = 0; i < tile_count(p->dtype); ++i) {
             const TileCfg *t = tile_entry(p->dtype, i);
+            if (t->bm < 64) continue;
             small_tiles = std::max(small_tiles, p->batch * cdiv(M, t->bm) * cdiv(N, t->bn));
         }
         // Workgroups of the skinny-M kernel (one per 64 lanes x 16 bytes of
@@ -587,7 +629,9 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         // Workgroups of the tile the general path would choose.
         auto general_tiles = [&]() -> int64_t {
             // FLOAT: the entry the general path would run; the 16-bit
-            // thresholds below were measured with the quality ranking.
+            // thresholds below were measured with the quality ranking, and
+            // for at most 64 rows with the 64-column tiles of that time.
+            if (t16 && M <= 64) return p->batch * cdiv(N, 64);
             const int gt = p->dtype == MM_FLOAT ? choose_general_tile(p->dtype, p->batch, M, N, K, p->is_gemm)
                                                 : choose_tile(p->dtype, p->batch, M, N, p->is_gemm);
             const TileCfg *t = tile_entry(p->dtype, gt);

@@ -31,6 +31,12 @@ constexpr TileCfg kTiles16[] = {
     {64, 64, 2, 2, 128, 3, 4, 2},
     {128, 128, 2, 2, 128, 2, 4, 2},
     {256, 256, 2, 4, 128, 2, 4, 1, 1},
+    // Entries for products of at most 64 rows, where one row tile spans M
+    // and the kernel streams B: 128 or 256 columns per tile give each wave
+    // longer contiguous B rows per stage than the 64-column tiles.
+    {32, 128, 1, 4, 128, 3, 4, 1},
+    {32, 256, 1, 4, 128, 3, 4, 1},
+    {64, 128, 2, 2, 128, 3, 4, 1},
 };
 
 // FLOAT entries.

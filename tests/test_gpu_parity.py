@@ -598,7 +598,11 @@ SELECTED_PATHS = [
     ((1, 16384), (16384, 8704), mm.BFLOAT16, False, ("skinny_m", 0, 29)),  # 16-bit GEMV, long K
     ((8, 16384), (16384, 8704), mm.BFLOAT16, False, ("skinny_m", 0, 29)),  # 8 rows: packed-dot 8-row instance
     ((64, 1024), (1024, 15360), mm.BFLOAT16, False, ("general", 9, 1)),    # <= 64 rows: two-group 64x64
-    ((1, 4096), (4096, 21760), mm.FLOAT16, False, ("general", 5, 1)),      # <= 64 rows, 340 tiles: 64x64
+    ((1, 4096), (4096, 21760), mm.FLOAT16, False, ("general", 12, 1)),     # <= 32 rows, 170 tiles of 32x128
+    ((48, 4096), (4096, 28672), mm.BFLOAT16, False, ("general", 14, 1)),   # <= 64 rows: 64x128
+    ((16, 4096), (4096, 65536), mm.FLOAT16, False, ("general", 13, 1)),    # one full round of 32x256
+    ((64, 4096), (4096, 11008), mm.BFLOAT16, False, ("split_k", 14, 2)),   # 64x128 chunks, one per CU
+    ((16, 14336), (14336, 4096), mm.FLOAT16, False, ("split_k", 12, 8)),   # 32x128 chunks of a long K
     ((256, 4096), (4096, 4352), mm.BFLOAT16, False, ("split_k", 6, 4)),   # split-K tiles at most 128x128
     ((32, 4096), (11008, 4096), mm.BFLOAT16, True, ("split_k", 5, 2)),    # Gemm decode: split-K
     ((128, 16384), (8704, 16384), mm.FLOAT16, True, ("split_k", 6, 4)),

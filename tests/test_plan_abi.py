@@ -274,18 +274,61 @@ def test_fp32_gemm_few_rows(M, K, N, algo):
 
 def test_small_m_tiles():
     """16-bit products of at most 64 rows take 64 x 64 tiles with two K
-    groups up to one tile per CU, single-group 64 x 64 tiles up to 1.5 per
-    CU, then 128 x 64 tiles; Gemm takes its 64 x 64 entry."""
+    groups up to one tile per CU; beyond that, 128-column tiles one row tile
+    high (32 x 128 up to 32 rows, else 64 x 128), and for at most 32 rows
+    32 x 256 tiles when every round of them fills three quarters of the
+    CUs.  Gemm takes its 64 x 64 entry."""
     t16 = mm.tile_configs(mm.BFLOAT16)
-    for sa, sb, want in [((64, 1024), (1024, 15360), 9), ((1, 4096), (4096, 21760), 5),
-                         ((16, 4096), (4096, 30720), 4), ((2, 32, 1024), (2, 1024, 8192), 9)]:
+    assert t16[8][:2] == (64, 64) and t16[4][:2] == (64, 64)
+    assert [c[:2] for c in t16[11:]] == [(32, 128), (32, 256), (64, 128)]
+    for sa, sb, want in [((64, 1024), (1024, 15360), 9), ((2, 32, 1024), (2, 1024, 8192), 9),
+                         ((1, 4096), (4096, 21760), 12), ((16, 4096), (4096, 30720), 12),
+                         ((33, 4096), (4096, 30720), 14), ((64, 2048), (2048, 128256), 14),
+                         ((16, 4096), (4096, 49152), 13),    # 192 tiles of 32 x 256: one round at 3/4
+                         ((32, 4096), (4096, 65536), 13),    # 256: one full round
+                         ((16, 4096), (4096, 98304), 12),    # 384: a last round of 128 tiles
+                         ((16, 4096), (4096, 128256), 13),   # 501: a last round of 245
+                         ((2, 16, 2048), (2, 2048, 32768), 13)]:
         inf = mm.Plan(sa, sb, mm.BFLOAT16).info()
         assert mm.ALGO_NAMES[inf["algo"]] == "general" and inf["tile"] == want, (sa, sb, inf["tile"])
-    assert t16[8][:2] == (64, 64) and t16[4][:2] == (64, 64) and t16[3][:2] == (128, 64)
+        assert inf["tail_col"] == 0
     g = mm.GemmPlan((32, 4096), (21760, 4096), mm.FLOAT16, False, True, None, 1.0, 0.0)
     assert g.algo == mm.ALGO_GENERAL and g.info()["tile"] == 5
-    # more rows: the quality-ranked choice
-    assert mm.Plan((65, 4096), (4096, 21760), mm.BFLOAT16).info()["tile"] not in (4, 5, 9)
+    # more rows: the time model, which leaves the small-row entries out
+    for sa, sb in [((65, 4096), (4096, 21760)), ((96, 4096), (4096, 65536)), ((128, 2048), (2048, 40000))]:
+        assert mm.Plan(sa, sb, mm.BFLOAT16).info()["tile"] not in (4, 5, 9, 12, 13, 14)
+
+
+@pytest.mark.parametrize("sa,sb,want", [
+    ((16, 4096), (4096, 11008), ("split_k", 12, 2)),   # 64 x 64 chunks would put 344 workgroups on 256 CUs
+    ((48, 8192), (8192, 11008), ("split_k", 14, 2)),   # 86 tiles of 64 x 128: 2 chunks, not 3
+    ((16, 14336), (14336, 4096), ("split_k", 12, 8)),  # 64 x 64 chunks of 3584: K-long
+    ((64, 14336), (14336, 4096), ("split_k", 14, 8)),
+    ((32, 4096), (4096, 4096), ("split_k", 5, 4)),     # 64 x 64 in 4 chunks of 1024 fill the CUs
+    ((64, 8192), (8192, 4096), ("split_k", 5, 4)),
+    ((16, 1024), (1024, 4096), ("split_k", 5, 4)),
+])
+def test_small_m_split_tiles(sa, sb, want):
+    """16-bit split-K of at most 64 rows: the 64 x 64 tiles unless their
+    chunks overfill the CUs or stay long, then the 128-column small-row
+    tile with at most one workgroup per CU."""
+    for dt in (mm.BFLOAT16, mm.FLOAT16):
+        inf = mm.Plan(sa, sb, dt).info()
+        assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
+
+
+def test_small_m_entries_left_out_of_larger_products():
+    """The split-K tile of a product of more than 64 rows, and the forced
+    small-row tiles on any shape, work as before."""
+    for sa, sb in [((96, 4096), (4096, 4096)), ((128, 8192), (8192, 2048)), ((200, 14336), (14336, 1024))]:
+        inf = mm.Plan(sa, sb, mm.BFLOAT16).info()
+        if mm.ALGO_NAMES[inf["algo"]] == "split_k":
+            assert inf["tile"] not in (12, 13, 14), (sa, sb, inf)
+    for t in (12, 13, 14):
+        inf = mm.Plan((300, 520), (520, 200), mm.BFLOAT16, force_algo=mm.ALGO_GENERAL, tile=t).info()
+        assert inf["tile"] == t and inf["tail_col"] == 0
+        inf = mm.Plan((100, 4096), (4096, 300), mm.FLOAT16, force_algo=mm.ALGO_SPLIT_K, tile=t).info()
+        assert inf["tile"] == t and inf["split_k"] >= 2
 
 
 @pytest.mark.parametrize("sa,sb,want", [
