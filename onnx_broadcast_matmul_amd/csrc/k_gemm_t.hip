@@ -19,8 +19,8 @@ static hipError_t launch_t_tile(bool vec, bool split, const KArgs &a, hipStream_
     return launch_tile<DT, c.bm, c.bn, c.wgm, c.wgn, c.bkb, c.stages, c.producers, c.kgroups, false, false, true>(vec, split, a, s);
 }
 
-static_assert(sizeof(kTransTiles16) / sizeof(int) == 5 && kTransTiles16[0] == 0 && kTransTiles16[1] == 5 &&
-                  kTransTiles16[2] == 4 && kTransTiles16[3] == 2 && kTransTiles16[4] == 1,
+static_assert(sizeof(kTransTiles16) / sizeof(int) == 6 && kTransTiles16[0] == 0 && kTransTiles16[1] == 5 &&
+                  kTransTiles16[2] == 4 && kTransTiles16[3] == 2 && kTransTiles16[4] == 1 && kTransTiles16[5] == 13,
               "launch switch must cover the transposed tile subset");
 static_assert(sizeof(kTransTiles32) / sizeof(int) == 4 && kTransTiles32[0] == 4 && kTransTiles32[1] == 2 &&
                   kTransTiles32[2] == 6 && kTransTiles32[3] == 5,
@@ -34,6 +34,7 @@ static hipError_t launch_t16(int tile, bool vec, bool split, const KArgs &a, hip
     case 4: return launch_t_tile<DT, kTiles16, 4>(vec, split, a, s);
     case 2: return launch_t_tile<DT, kTiles16, 2>(vec, split, a, s);
     case 1: return launch_t_tile<DT, kTiles16, 1>(vec, split, a, s);
+    case 13: return launch_t_tile<DT, kTiles16, 13>(vec, split, a, s);
     }
     return hipErrorInvalidValue;
 }

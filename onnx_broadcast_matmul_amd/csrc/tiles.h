@@ -59,7 +59,7 @@ constexpr TileCfg kTiles64[] = {
 };
 
 // Entries instantiated for Gemm (its epilogue and transA / transB).
-constexpr int kTransTiles16[] = {0, 5, 4, 2, 1};
+constexpr int kTransTiles16[] = {0, 5, 4, 2, 1, 13};
 constexpr int kTransTiles32[] = {4, 2, 6, 5};
 
 // INT8 entries (MatMulInteger; B rows need at least 128 bytes per stage row).

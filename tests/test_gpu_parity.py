@@ -484,7 +484,7 @@ def test_gemm_every_tile(dt, ta, tb, dev):
         gemm_parity(130, 70, 1000, dt, ta, tb, ("N",), dev, algo=mm.ALGO_SPLIT_K, tile=tile, alpha=2.0, beta=-3.0,
                     dist=("int",), exact=True, seed=90 + tile)
         ran += 1
-    assert ran == (5 if dt != mm.FLOAT else 4)
+    assert ran == (6 if dt != mm.FLOAT else 4)
 
 
 @pytest.mark.parametrize("dt", GEMM_DTYPES, ids=DT_IDS.get)
@@ -604,7 +604,8 @@ SELECTED_PATHS = [
     ((64, 4096), (4096, 11008), mm.BFLOAT16, False, ("split_k", 14, 2)),   # 64x128 chunks, one per CU
     ((16, 14336), (14336, 4096), mm.FLOAT16, False, ("split_k", 12, 8)),   # 32x128 chunks of a long K
     ((256, 4096), (4096, 4352), mm.BFLOAT16, False, ("split_k", 6, 4)),   # split-K tiles at most 128x128
-    ((32, 4096), (11008, 4096), mm.BFLOAT16, True, ("split_k", 5, 2)),    # Gemm decode: split-K
+    ((32, 4096), (11008, 4096), mm.BFLOAT16, True, ("split_k", 14, 4)),   # Gemm decode: 64x128 chunks
+    ((16, 14336), (4096, 14336), mm.FLOAT16, True, ("split_k", 14, 8)),
     ((128, 16384), (8704, 16384), mm.FLOAT16, True, ("split_k", 6, 4)),
     ((1024, 4096), (4096, 11008), mm.BFLOAT16, False, ("general", 1, 1)),  # timed choice: 256x256, one round
     ((768, 4096), (4096, 4096), mm.FLOAT16, False, ("general", 3, 1)),     # three-stage 128x128

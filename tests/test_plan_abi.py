@@ -520,6 +520,35 @@ def test_persistent_selection(sa, sb, dt, tile):
     assert inf["tile"] == tile if tile is not None else inf["tile"] != PERSIST_TILE
 
 
+@pytest.mark.parametrize("M,K,N,want", [
+    (16, 4096, 4096, ("split_k", 14, 8)),     # 32 tiles of 64 x 128: 8 chunks, at most 2 per CU
+    (32, 4096, 11008, ("split_k", 14, 4)),    # 86 tiles: 4 chunks
+    (16, 4096, 12288, ("split_k", 14, 4)),
+    (64, 14336, 4096, ("split_k", 14, 8)),    # chunks capped at 8
+    (16, 2048, 8192, ("split_k", 14, 4)),     # chunks at least 512 long
+    (16, 4096, 2048, ("split_k", 5, 8)),      # 16 tiles x 8 chunks leave CUs idle: the earlier rule
+    (16, 1024, 4096, ("split_k", 5, 4)),
+    (16, 4096, 28672, ("general", 5, 1)),     # more than half a round of tiles
+    (65, 4096, 4096, None),                   # more rows
+])
+def test_gemm_linear_split(M, K, N, want):
+    """A 16-bit Gemm with B transposed (a linear layer) over at most 64 rows
+    splits K on the 64 x 128 entry, in the largest power-of-two chunk count
+    with at most two workgroups per CU (capped at K / 512 and 8), when
+    the chunks give every CU a workgroup."""
+    for dt in (mm.BFLOAT16, mm.FLOAT16):
+        inf = mm.GemmPlan((M, K), (N, K), dt, False, True, (N,), 1.0, 1.0).info()
+        got = (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"])
+        if want is None:
+            assert got[1] != 14, got
+        else:
+            assert got == want, (M, K, N, got)
+    # B not transposed, A transposed, or FP32: the rule does not apply
+    assert mm.GemmPlan((16, 4096), (4096, 4096), mm.BFLOAT16, False, False).info()["tile"] != 14
+    assert mm.GemmPlan((4096, 16), (4096, 4096), mm.BFLOAT16, True, True).info()["tile"] != 14
+    assert mm.GemmPlan((16, 4096), (4096, 4096), mm.FLOAT, False, True).info()["tile"] != 14
+
+
 # ---------------------------------------------------------------- constant B
 
 def test_constant_b_errors_before_any_gpu_call():
@@ -558,7 +587,7 @@ def test_gemm_plan_shapes(ta, tb):
     assert p.output_shape == (M, N) and p.output_numel == M * N
     inf = p.info()
     assert (inf["M"], inf["N"], inf["K"]) == (M, N, K) and inf["algo"] == mm.ALGO_GENERAL
-    assert inf["tile"] - 1 in (0, 5, 4, 2, 1)  # Gemm: only the tiles instantiated with its epilogue
+    assert inf["tile"] - 1 in (0, 5, 4, 2, 1, 13)  # Gemm: only the tiles instantiated with its epilogue
     assert inf["tail_col"] == 0
     # skinny shapes of a Gemm take the tiled kernels: split-K when one row
     # of tiles cannot fill the GPU and K is long, else the general kernel
