@@ -692,6 +692,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             algo = MM_ALGO_SPLIT_K;  // a linear layer over few rows: B streamed by 64 x 128 chunks
             rule_tile = kT16Row64;
         } else if ((small_tiles < kNumCUs / 2 && K >= 1024) || (K >= 4096 && general_tiles() < 3 * kNumCUs / 4) ||
+                   (t16 && !p->is_gemm && M <= 32 && K >= 4096 && general_tiles() <= kNumCUs) ||
                    (p->is_gemm && p->dtype == MM_FLOAT && M <= 32 && K >= 1024 && general_tiles() < kNumCUs)) {
             // Tiles cannot fill the GPU and K is long; with K >= 4096, also
             // when the tile the general path would take leaves a quarter of
@@ -700,7 +701,11 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             // skinny shapes of DOUBLE and Gemm, which have no skinny kernels,
             // and FP32 Gemm with at most 32 rows on fewer tiles than CUs,
             // whose FP32 MFMA chains are four times as long as the 16-bit
-            // ones (measured 10-20 % faster split).
+            // ones (measured 10-20 % faster split).  16-bit MatMul of at
+            // most 32 rows splits up to one 64-column tile per CU: two
+            // chunks of 32 x 128 tiles stream B faster than one K-long
+            // chain per 64 x 64 tile ([16,4096]x[4096,14336] BF16: 31.2
+            // against 27.4 us; at 16384 columns 31.6 against 30.1 us).
             algo = MM_ALGO_SPLIT_K;
         } else if ((rule_split = large_tile_split16(p->dtype, p->batch, M, N, K, p->is_gemm)) > 0) {
             algo = MM_ALGO_SPLIT_K;  // a long K over at most half a round of large tiles

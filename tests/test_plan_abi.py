@@ -307,6 +307,10 @@ def test_small_m_tiles():
     ((32, 4096), (4096, 4096), ("split_k", 5, 4)),     # 64 x 64 in 4 chunks of 1024 fill the CUs
     ((64, 8192), (8192, 4096), ("split_k", 5, 4)),
     ((16, 1024), (1024, 4096), ("split_k", 5, 4)),
+    ((16, 4096), (4096, 14336), ("split_k", 12, 2)),   # <= 32 rows, up to one 64-column tile per CU: split
+    ((1, 4096), (4096, 16384), ("split_k", 12, 2)),
+    ((33, 4096), (4096, 14336), ("general", 9, 1)),    # more rows: the two-group 64 x 64 tiles
+    ((16, 2048), (2048, 14336), ("general", 9, 1)),    # K < 4096
 ])
 def test_small_m_split_tiles(sa, sb, want):
     """16-bit split-K of at most 64 rows: the 64 x 64 tiles unless their
