@@ -39,12 +39,13 @@ static hipError_t launch_32(int tile, bool vec, bool split, const KArgs &a, hipS
         MM_TILE_CASE(MM_FLOAT, kTiles32, 4);
         MM_TILE_CASE(MM_FLOAT, kTiles32, 5);
         MM_TILE_CASE(MM_FLOAT, kTiles32, 6);
+        MM_TILE_CASE(MM_FLOAT, kTiles32, 7);
     }
     return hipErrorInvalidValue;
 }
 #undef MM_TILE_CASE
 
-static_assert(kNumTiles16 == 14 && kNumTiles32 == 7, "launch switch must cover the tile table");
+static_assert(kNumTiles16 == 14 && kNumTiles32 == 8, "launch switch must cover the tile table");
 
 // Prepacked constant B: the 16-byte chunk (piece, lane) of the panel of
 // matrix mi, tile column tn and K stage st is what lane `lane` of load

@@ -65,7 +65,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // byte more often); used only to rank entries against each other.
 static double tile_quality(int dtype, int index) {
     static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5, 0.0, 0.0, 0.0, 0.0};
-    static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15};
+    static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15, 0.0};
     static const double q64[kNumTiles64] = {1.0, 0.8};
     static const double q8[kNumTiles8] = {1.0, 0.75, 1.0};
     if (dtype == MM_DOUBLE) return q64[index];
@@ -113,8 +113,14 @@ static_assert(kTiles16[kT16Row32].bm == 32 && kTiles16[kT16Row32].bn == 128 && k
               "the small-row entries close the 16-bit table");
 static_assert(kTransTiles16[2] == kT16Small, "the 64 x 64 entry has a Gemm kernel");
 
+constexpr int kT32Row32 = 7;  // FLOAT 32 x 128, two K groups (see float_small_rows)
+static_assert(kTiles32[kT32Row32].bm == 32 && kTiles32[kT32Row32].bn == 128 && kTiles32[kT32Row32].kgroups == 2 &&
+                  kNumTiles32 == kT32Row32 + 1,
+              "the FLOAT small-row entry closes its table");
+
 static bool small_m_entry(int dtype, int index) {
-    return (dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && index >= kT16Row32;
+    return ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && index >= kT16Row32) ||
+           (dtype == MM_FLOAT && index == kT32Row32);
 }
 
 static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, bool gemm = false) {
@@ -204,6 +210,7 @@ constexpr RoundCost kRound32[] = {
     {{279.0, 495.5, 0.0}},  // 128 x 128, 2 stages (two per CU)
     {{83.3, 155.9, 198.6}}, // 64 x 64, two K groups
     {{254.8, 480.8, 0.0}},  // 128 x 128, two K groups
+    {{0.0, 0.0, 0.0}},      // 32 x 128, two K groups: at most 32 rows, chosen by float_small_rows
 };
 static_assert(sizeof(kRound16) / sizeof(kRound16[0]) == kNumTiles16, "one round cost per 16-bit entry");
 static_assert(sizeof(kRound32) / sizeof(kRound32[0]) == kNumTiles32, "one round cost per FLOAT entry");
@@ -310,6 +317,28 @@ static int gemm_linear_split16(const mm_plan_s *p, int64_t M, int64_t N, int64_t
     return (int)s;
 }
 
+// FP32 MatMul over at most 32 rows (where skinny-M does not take it): the
+// 32 x 128 entry with two K groups.  With 64-row tiles the FP32 matrix
+// cores did twice or more the useful work; one 32-row tile per column block
+// halves that and leaves B's stream as the bound.  Up to one tile per CU
+// the plan splits K in s chunks, s the largest power of two (at least 2)
+// with at most one workgroup per CU beyond the first two chunks, and at
+// most K / 256; past one tile per CU it runs the tiles whole.  Measured on
+// FP32 products of 16 and 32 rows (K 1024-11008, N 2048-28672), forced
+// tiles and chunk counts: [16,4096]x[4096,11008] 76.5 -> 47.2 us,
+// [16,8192]x[8192,8192] 86.4 -> 58.4 us, [32,11008]x[11008,4096] 62.5 ->
+// 43.4 us, [16,4096]x[4096,28672] 147.7 -> 94.7 us.  Returns the chunk
+// count (1: the general path on this entry), or 0 when the rule does not
+// apply.
+static int float_small_rows(const mm_plan_s *p, int64_t M, int64_t N, int64_t K) {
+    if (p->dtype != MM_FLOAT || p->is_gemm || M > 32) return 0;
+    const int64_t tiles = p->batch * cdiv(N, kTiles32[kT32Row32].bn);
+    if (tiles > kNumCUs) return 1;
+    int64_t s = 2;
+    while (2 * s * tiles <= kNumCUs) s *= 2;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(s, K / 256));
+}
+
 // Last-round balancing for a large tile (one workgroup per CU).  When the
 // tiles leave the last round of workgroups less than half full, the leading
 // output columns are covered by whole rounds of the chosen tile and the
@@ -404,7 +433,7 @@ static int choose_split_tile(int dtype, int64_t batch, int64_t M, int64_t N, int
         const TileCfg *t = tile_entry(dtype, i);
         if (t->bm * t->bn > 128 * 128) continue;
         // FLOAT: the two-K-group entries (the measured split tiles).
-        if (dtype == MM_FLOAT && t->kgroups != 2) continue;
+        if (dtype == MM_FLOAT && (t->kgroups != 2 || small_m_entry(dtype, i))) continue;
         double score = ((double)M * N) / ((double)cdiv(M, t->bm) * t->bm * (double)cdiv(N, t->bn) * t->bn);
         if (dtype == MM_FLOAT) {
             const int64_t tiles = batch * cdiv(M, t->bm) * cdiv(N, t->bn);
@@ -625,7 +654,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
     if (st != MM_OK) return st;
 
     int algo = opt ? opt->force_algo : MM_ALGO_AUTO;
-    int rule_split = 0, rule_tile = -1;  // a split-K plan fixed by a rule below: chunks and tile
+    int rule_split = 0, rule_tile = -1;  // a plan fixed by a rule below: split chunks (1: none) and tile
     if (algo == MM_ALGO_AUTO) {
         const double flops = 2.0 * (double)p->batch * M * N * K;
         // Tiles of the smallest block tile in the table: the most workgroups
@@ -688,6 +717,9 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             algo = MM_ALGO_SKINNY_M;  // GEMV over enough columns and batches to fill the GPU
         } else if (skm_split) {
             algo = MM_ALGO_SKINNY_M;  // GEMV over few columns: K cut into chunks
+        } else if ((rule_split = float_small_rows(p, M, N, K)) > 0) {
+            algo = rule_split > 1 ? MM_ALGO_SPLIT_K : MM_ALGO_GENERAL;  // FP32 over few rows: 32-row tiles
+            rule_tile = kT32Row32;
         } else if ((rule_split = gemm_linear_split16(p, M, N, K)) > 0) {
             algo = MM_ALGO_SPLIT_K;  // a linear layer over few rows: B streamed by 64 x 128 chunks
             rule_tile = kT16Row64;
@@ -742,10 +774,10 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
             p->tile = req - 1;
             if (!tile_allowed(p->dtype, p->tile, p->is_gemm))
                 return fail(MM_ERR_BAD_OPTION, "tile %d has no Gemm kernel", req);
+        } else if (rule_tile >= 0) {
+            p->tile = rule_tile;
         } else if (algo == MM_ALGO_GENERAL) {
             p->tile = choose_general_tile(p->dtype, p->batch, M, N, K, p->is_gemm);
-        } else if (rule_split > 0) {
-            p->tile = rule_tile;
         } else {
             p->tile = choose_split_tile(p->dtype, p->batch, M, N, K, p->is_gemm);
         }

@@ -48,6 +48,9 @@ constexpr TileCfg kTiles32[] = {
     {128, 128, 2, 2, 128, 2, 4, 1},
     {64, 64, 2, 2, 128, 3, 4, 2},
     {128, 128, 2, 2, 128, 2, 4, 2},
+    // For products of at most 32 rows: one row tile spans M, so the FP32
+    // matrix-core work is not padded to 64 rows.
+    {32, 128, 1, 4, 128, 3, 4, 2},
 };
 
 // DOUBLE entries (k_f64.hip: 4 waves, 16 doubles of K per stage, two

@@ -604,6 +604,8 @@ SELECTED_PATHS = [
     ((64, 4096), (4096, 11008), mm.BFLOAT16, False, ("split_k", 14, 2)),   # 64x128 chunks, one per CU
     ((16, 14336), (14336, 4096), mm.FLOAT16, False, ("split_k", 12, 8)),   # 32x128 chunks of a long K
     ((8, 5120), (5120, 13824), mm.BFLOAT16, False, ("split_k", 12, 2)),    # <= 32 rows, 216 64-col tiles
+    ((16, 4096), (4096, 11008), mm.FLOAT, False, ("split_k", 8, 2)),       # FP32 <= 32 rows: 32x128 tiles
+    ((32, 4096), (4096, 40000), mm.FLOAT, False, ("general", 8, 1)),
     ((256, 4096), (4096, 4352), mm.BFLOAT16, False, ("split_k", 6, 4)),   # split-K tiles at most 128x128
     ((32, 4096), (11008, 4096), mm.BFLOAT16, True, ("split_k", 14, 4)),   # Gemm decode: 64x128 chunks
     ((16, 14336), (4096, 14336), mm.FLOAT16, True, ("split_k", 14, 8)),

@@ -228,11 +228,12 @@ SELECTOR_CASES = [
     ((1, 1024), (1024, 11008), mm.BFLOAT16, "general"),   # 172 tiles, K < 4096
     ((15, 4096), (4096, 8704), mm.FLOAT, "skinny_m"),     # FP32 9..15 rows: K >= 4096 and N >= 4096
     ((15, 16384), (16384, 2048), mm.FLOAT, "split_k"),
-    ((15, 1024), (1024, 8704), mm.FLOAT, "general"),
+    ((15, 1024), (1024, 8704), mm.FLOAT, "split_k"),      # FP32 <= 32 rows: 32-row tiles, K in chunks
     ((16, 4096), (4096, 8704), mm.FLOAT, "split_k"),      # 16 rows and more: never the K-split GEMV
     ((128, 4096), (4096, 10880), mm.FLOAT, "split_k"),
     ((128, 4096), (4096, 15360), mm.FLOAT, "general"),
-    ((32, 16384), (16384, 21760), mm.FLOAT, "general"),
+    ((32, 16384), (16384, 21760), mm.FLOAT, "split_k"),   # 170 tiles of 32x128: two chunks
+    ((32, 4096), (4096, 40000), mm.FLOAT, "general"),     # past one tile per CU: whole tiles
     ((15, 4096), (4096, 256), mm.BFLOAT16, "split_k"),
     ((4, 256), (256, 2048), mm.BFLOAT16, "general"),   # short K: the tiles
     ((256, 4096), (4096, 256), mm.FLOAT, "split_k"),
@@ -551,6 +552,30 @@ def test_gemm_linear_split(M, K, N, want):
     assert mm.GemmPlan((16, 4096), (4096, 4096), mm.BFLOAT16, False, False).info()["tile"] != 14
     assert mm.GemmPlan((4096, 16), (4096, 4096), mm.BFLOAT16, True, True).info()["tile"] != 14
     assert mm.GemmPlan((16, 4096), (4096, 4096), mm.FLOAT, False, True).info()["tile"] != 14
+
+
+@pytest.mark.parametrize("M,K,N,want", [
+    (16, 4096, 4096, ("split_k", 8, 8)),      # 32 tiles of 32 x 128: 8 chunks, one workgroup per CU
+    (32, 4096, 11008, ("split_k", 8, 2)),     # 86 tiles: 2 chunks, not 3 (258 workgroups)
+    (16, 8192, 8192, ("split_k", 8, 4)),
+    (16, 2048, 2048, ("split_k", 8, 8)),      # 16 tiles: at most K / 256 chunks
+    (16, 1024, 4096, ("split_k", 8, 4)),
+    (16, 4096, 28672, ("split_k", 8, 2)),     # up to one tile per CU: at least 2 chunks
+    (32, 4096, 40000, ("general", 8, 1)),     # past one tile per CU
+])
+def test_float_small_rows(M, K, N, want):
+    """FP32 MatMul of at most 32 rows (where skinny-M does not take it) runs
+    on the 32 x 128 entry with two K groups, splitting K up to one tile per
+    CU."""
+    assert mm.tile_configs(mm.FLOAT)[7] == (32, 128, 32)
+    inf = mm.Plan((M, K), (K, N), mm.FLOAT).info()
+    assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
+    # more rows, the 16-bit types and Gemm keep their rules
+    assert mm.Plan((33, 4096), (4096, 11008), mm.FLOAT).info()["tile"] != 8
+    assert mm.Plan((15, 4096), (4096, 8704), mm.FLOAT).algo == mm.ALGO_SKINNY_M
+    assert mm.GemmPlan((16, 4096), (11008, 4096), mm.FLOAT, False, True).info()["tile"] != 8
+    with pytest.raises(mm.MMError):
+        mm.GemmPlan((16, 4096), (11008, 4096), mm.FLOAT, False, True, force_algo=mm.ALGO_GENERAL, tile=8)
 
 
 # ---------------------------------------------------------------- constant B
