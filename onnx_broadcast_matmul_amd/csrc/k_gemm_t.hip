@@ -22,8 +22,8 @@ static hipError_t launch_t_tile(bool vec, bool split, const KArgs &a, hipStream_
 static_assert(sizeof(kTransTiles16) / sizeof(int) == 6 && kTransTiles16[0] == 0 && kTransTiles16[1] == 5 &&
                   kTransTiles16[2] == 4 && kTransTiles16[3] == 2 && kTransTiles16[4] == 1 && kTransTiles16[5] == 13,
               "launch switch must cover the transposed tile subset");
-static_assert(sizeof(kTransTiles32) / sizeof(int) == 4 && kTransTiles32[0] == 4 && kTransTiles32[1] == 2 &&
-                  kTransTiles32[2] == 6 && kTransTiles32[3] == 5,
+static_assert(sizeof(kTransTiles32) / sizeof(int) == 5 && kTransTiles32[0] == 4 && kTransTiles32[1] == 2 &&
+                  kTransTiles32[2] == 6 && kTransTiles32[3] == 5 && kTransTiles32[4] == 7,
               "launch switch must cover the transposed tile subset");
 
 template <int DT>
@@ -45,6 +45,7 @@ static hipError_t launch_t32(int tile, bool vec, bool split, const KArgs &a, hip
     case 2: return launch_t_tile<MM_FLOAT, kTiles32, 2>(vec, split, a, s);
     case 6: return launch_t_tile<MM_FLOAT, kTiles32, 6>(vec, split, a, s);
     case 5: return launch_t_tile<MM_FLOAT, kTiles32, 5>(vec, split, a, s);
+    case 7: return launch_t_tile<MM_FLOAT, kTiles32, 7>(vec, split, a, s);
     }
     return hipErrorInvalidValue;
 }

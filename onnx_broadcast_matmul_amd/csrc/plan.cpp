@@ -317,10 +317,10 @@ static int gemm_linear_split16(const mm_plan_s *p, int64_t M, int64_t N, int64_t
     return (int)s;
 }
 
-// FP32 MatMul over at most 32 rows (where skinny-M does not take it): the
-// 32 x 128 entry with two K groups.  With 64-row tiles the FP32 matrix
-// cores did twice or more the useful work; one 32-row tile per column block
-// halves that and leaves B's stream as the bound.  Up to one tile per CU
+// FP32 MatMul and Gemm over at most 32 rows (where skinny-M does not take
+// a MatMul): the 32 x 128 entry with two K groups.  With 64-row tiles the
+// FP32 matrix cores did twice or more the useful work; one 32-row tile per
+// column block halves that and leaves B's stream as the bound.  Up to one tile per CU
 // the plan splits K in s chunks, s the largest power of two (at least 2)
 // with at most one workgroup per CU beyond the first two chunks, and at
 // most K / 256; past one tile per CU it runs the tiles whole.  Measured on
@@ -331,7 +331,7 @@ static int gemm_linear_split16(const mm_plan_s *p, int64_t M, int64_t N, int64_t
 // count (1: the general path on this entry), or 0 when the rule does not
 // apply.
 static int float_small_rows(const mm_plan_s *p, int64_t M, int64_t N, int64_t K) {
-    if (p->dtype != MM_FLOAT || p->is_gemm || M > 32) return 0;
+    if (p->dtype != MM_FLOAT || M > 32) return 0;
     const int64_t tiles = p->batch * cdiv(N, kTiles32[kT32Row32].bn);
     if (tiles > kNumCUs) return 1;
     int64_t s = 2;

@@ -63,7 +63,7 @@ constexpr TileCfg kTiles64[] = {
 
 // Entries instantiated for Gemm (its epilogue and transA / transB).
 constexpr int kTransTiles16[] = {0, 5, 4, 2, 1, 13};
-constexpr int kTransTiles32[] = {4, 2, 6, 5};
+constexpr int kTransTiles32[] = {4, 2, 6, 5, 7};
 
 // INT8 entries (MatMulInteger; B rows need at least 128 bytes per stage row).
 // The two 256 x 256 entries differ in wave layout: 2 x 4 waves hold two B

@@ -484,7 +484,7 @@ def test_gemm_every_tile(dt, ta, tb, dev):
         gemm_parity(130, 70, 1000, dt, ta, tb, ("N",), dev, algo=mm.ALGO_SPLIT_K, tile=tile, alpha=2.0, beta=-3.0,
                     dist=("int",), exact=True, seed=90 + tile)
         ran += 1
-    assert ran == (6 if dt != mm.FLOAT else 4)
+    assert ran == (6 if dt != mm.FLOAT else 5)
 
 
 @pytest.mark.parametrize("dt", GEMM_DTYPES, ids=DT_IDS.get)
@@ -606,6 +606,7 @@ SELECTED_PATHS = [
     ((8, 5120), (5120, 13824), mm.BFLOAT16, False, ("split_k", 12, 2)),    # <= 32 rows, 216 64-col tiles
     ((16, 4096), (4096, 11008), mm.FLOAT, False, ("split_k", 8, 2)),       # FP32 <= 32 rows: 32x128 tiles
     ((32, 4096), (4096, 40000), mm.FLOAT, False, ("general", 8, 1)),
+    ((24, 4096), (11008, 4096), mm.FLOAT, True, ("split_k", 8, 2)),        # FP32 linear layer, 24 rows
     ((256, 4096), (4096, 4352), mm.BFLOAT16, False, ("split_k", 6, 4)),   # split-K tiles at most 128x128
     ((32, 4096), (11008, 4096), mm.BFLOAT16, True, ("split_k", 14, 4)),   # Gemm decode: 64x128 chunks
     ((16, 14336), (4096, 14336), mm.FLOAT16, True, ("split_k", 14, 8)),

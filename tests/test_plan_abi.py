@@ -263,9 +263,10 @@ def test_selector(sa, sb, dt, algo):
 
 
 @pytest.mark.parametrize("M,K,N,algo", [
-    (1, 4096, 15360, "split_k"),    # FP32 Gemm, <= 32 rows, fewer tiles than CUs
+    (1, 4096, 15360, "split_k"),    # FP32 Gemm, <= 32 rows: 32-row tiles, K in chunks
     (32, 1024, 11008, "split_k"),
-    (32, 4096, 21760, "general"),   # 340 tiles: the tiles fill the GPU
+    (32, 4096, 21760, "split_k"),   # 170 tiles of 32 x 128: two chunks
+    (32, 4096, 40000, "general"),   # past one tile per CU
     (128, 4096, 15360, "general"),  # 128 rows: the tiles win
 ])
 def test_fp32_gemm_few_rows(M, K, N, algo):
@@ -564,18 +565,20 @@ def test_gemm_linear_split(M, K, N, want):
     (32, 4096, 40000, ("general", 8, 1)),     # past one tile per CU
 ])
 def test_float_small_rows(M, K, N, want):
-    """FP32 MatMul of at most 32 rows (where skinny-M does not take it) runs
-    on the 32 x 128 entry with two K groups, splitting K up to one tile per
-    CU."""
+    """FP32 MatMul (where skinny-M does not take it) and Gemm of at most 32
+    rows run on the 32 x 128 entry with two K groups, splitting K up to one
+    tile per CU."""
     assert mm.tile_configs(mm.FLOAT)[7] == (32, 128, 32)
     inf = mm.Plan((M, K), (K, N), mm.FLOAT).info()
     assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
-    # more rows, the 16-bit types and Gemm keep their rules
+    for ta, tb in ((0, 0), (0, 1), (1, 0), (1, 1)):
+        sa = (K, M) if ta else (M, K)
+        sb = (N, K) if tb else (K, N)
+        g = mm.GemmPlan(sa, sb, mm.FLOAT, ta, tb, (N,), 1.0, 1.0).info()
+        assert (mm.ALGO_NAMES[g["algo"]], g["tile"], g["split_k"]) == want, (ta, tb, g)
+    # more rows keep the other rules; few-row MatMul keeps skinny-M where it wins
     assert mm.Plan((33, 4096), (4096, 11008), mm.FLOAT).info()["tile"] != 8
     assert mm.Plan((15, 4096), (4096, 8704), mm.FLOAT).algo == mm.ALGO_SKINNY_M
-    assert mm.GemmPlan((16, 4096), (11008, 4096), mm.FLOAT, False, True).info()["tile"] != 8
-    with pytest.raises(mm.MMError):
-        mm.GemmPlan((16, 4096), (11008, 4096), mm.FLOAT, False, True, force_algo=mm.ALGO_GENERAL, tile=8)
 
 
 # ---------------------------------------------------------------- constant B
