@@ -339,6 +339,47 @@ static int float_small_rows(const mm_plan_s *p, int64_t M, int64_t N, int64_t K)
     return (int)std::max<int64_t>(1, std::min<int64_t>(s, K / 256));
 }
 
+// FP32 products of 33-512 rows: split-K when the time model says it pays.
+// Each candidate is priced by est_us: the general path's timed tile run
+// whole, or a two-K-group entry (64 x 64 or 128 x 128) in 2, 3 or a power
+// of two up to 256 chunks of at least 256, plus kSplitUsPerMB per MB of
+// FP32 partials and kReduceLaunchUs for the reduction's launch.  The
+// cheapest is taken.  Without the launch cost the estimate took three
+// chunks over [512,2048]x[2048,2048] for a 1 % gain (measured 48.4 against
+// 44.3 us).  Measured on 24 FP32 products (M 64-512; K, N 1024-11008),
+// forced tiles and chunk counts: the choice is within 1.4 % of the best
+// tried (geometric mean), where the occupancy rules before it were 9.4 %
+// off.  E.g. [128,4096]x[4096,11008] 176 -> 122 us (two chunks of 64 x 64
+// tiles, not three chunks of 128 x 128 ones that put 258 workgroups on 256
+// CUs), [256,2048]x[2048,2048] 44.2 -> 30.8 us, [512,11008]x[11008,4096]
+// 396 -> 356 us.  Returns the chunk count (the entry in *tile), or 0 for
+// the general path.
+constexpr double kReduceLaunchUs = 3.0;
+static int float_timed_split(const mm_plan_s *p, int64_t M, int64_t N, int64_t K, int *tile) {
+    const int gt = choose_general_tile(MM_FLOAT, p->batch, M, N, K, p->is_gemm);
+    const TileCfg *g = tile_entry(MM_FLOAT, gt);
+    double best = est_us(MM_FLOAT, gt, p->batch * cdiv(M, g->bm) * cdiv(N, g->bn), K);
+    int best_s = 0;
+    const int bk = stage_k(MM_FLOAT);
+    for (int i = 0; i < kNumTiles32; ++i) {
+        const TileCfg *t = tile_entry(MM_FLOAT, i);
+        if (t->kgroups != 2 || small_m_entry(MM_FLOAT, i) || !tile_allowed(MM_FLOAT, i, p->is_gemm)) continue;
+        const int64_t tiles = p->batch * cdiv(M, t->bm) * cdiv(N, t->bn);
+        for (int s : {2, 3, 4, 8, 16, 32, 64, 128, 256}) {
+            if (K / s < 256) break;
+            const int64_t kc = cdiv(cdiv(K, bk), s) * bk;
+            const double part_mb = (double)s * p->batch * M * N * 4.0 / 1e6;
+            const double us = est_us(MM_FLOAT, i, tiles * s, kc) + kSplitUsPerMB * part_mb + kReduceLaunchUs;
+            if (us < best) {
+                best = us;
+                best_s = s;
+                *tile = i;
+            }
+        }
+    }
+    return best_s;
+}
+
 // Last-round balancing for a large tile (one workgroup per CU).  When the
 // tiles leave the last round of workgroups less than half full, the leading
 // output columns are covered by whole rounds of the chosen tile and the
@@ -720,20 +761,21 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         } else if ((rule_split = float_small_rows(p, M, N, K)) > 0) {
             algo = rule_split > 1 ? MM_ALGO_SPLIT_K : MM_ALGO_GENERAL;  // FP32 over few rows: 32-row tiles
             rule_tile = kT32Row32;
+        } else if (p->dtype == MM_FLOAT && M > 32 && M <= 512) {
+            // FP32 of 33-512 rows: split-K or general by the time model
+            rule_split = float_timed_split(p, M, N, K, &rule_tile);
+            algo = rule_split > 0 ? MM_ALGO_SPLIT_K : MM_ALGO_GENERAL;
         } else if ((rule_split = gemm_linear_split16(p, M, N, K)) > 0) {
             algo = MM_ALGO_SPLIT_K;  // a linear layer over few rows: B streamed by 64 x 128 chunks
             rule_tile = kT16Row64;
         } else if ((small_tiles < kNumCUs / 2 && K >= 1024) || (K >= 4096 && general_tiles() < 3 * kNumCUs / 4) ||
-                   (t16 && !p->is_gemm && M <= 32 && K >= 4096 && general_tiles() <= kNumCUs) ||
-                   (p->is_gemm && p->dtype == MM_FLOAT && M <= 32 && K >= 1024 && general_tiles() < kNumCUs)) {
+                   (t16 && !p->is_gemm && M <= 32 && K >= 4096 && general_tiles() <= kNumCUs)) {
             // Tiles cannot fill the GPU and K is long; with K >= 4096, also
             // when the tile the general path would take leaves a quarter of
             // the CUs idle (each of its tiles is then a chain of at least 64
             // stages, which outweighs the partials' round trip).  Also the
-            // skinny shapes of DOUBLE and Gemm, which have no skinny kernels,
-            // and FP32 Gemm with at most 32 rows on fewer tiles than CUs,
-            // whose FP32 MFMA chains are four times as long as the 16-bit
-            // ones (measured 10-20 % faster split).  16-bit MatMul of at
+            // skinny shapes of DOUBLE and Gemm, which have no skinny kernels.
+            // 16-bit MatMul of at
             // most 32 rows splits up to one 64-column tile per CU: two
             // chunks of 32 x 128 tiles stream B faster than one K-long
             // chain per 64 x 64 tile ([16,4096]x[4096,14336] BF16: 31.2

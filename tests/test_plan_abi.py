@@ -231,7 +231,7 @@ SELECTOR_CASES = [
     ((15, 1024), (1024, 8704), mm.FLOAT, "split_k"),      # FP32 <= 32 rows: 32-row tiles, K in chunks
     ((16, 4096), (4096, 8704), mm.FLOAT, "split_k"),      # 16 rows and more: never the K-split GEMV
     ((128, 4096), (4096, 10880), mm.FLOAT, "split_k"),
-    ((128, 4096), (4096, 15360), mm.FLOAT, "general"),
+    ((128, 4096), (4096, 15360), mm.FLOAT, "split_k"),  # FP32 33-512 rows: the time model splits
     ((32, 16384), (16384, 21760), mm.FLOAT, "split_k"),   # 170 tiles of 32x128: two chunks
     ((32, 4096), (4096, 40000), mm.FLOAT, "general"),     # past one tile per CU: whole tiles
     ((15, 4096), (4096, 256), mm.BFLOAT16, "split_k"),
@@ -267,7 +267,8 @@ def test_selector(sa, sb, dt, algo):
     (32, 1024, 11008, "split_k"),
     (32, 4096, 21760, "split_k"),   # 170 tiles of 32 x 128: two chunks
     (32, 4096, 40000, "general"),   # past one tile per CU
-    (128, 4096, 15360, "general"),  # 128 rows: the tiles win
+    (128, 4096, 15360, "split_k"),  # 128 rows: the time model (two chunks of 128 x 128)
+    (512, 2048, 2048, "general"),   # the split's gain does not cover the reduction
 ])
 def test_fp32_gemm_few_rows(M, K, N, algo):
     g = mm.GemmPlan((M, K), (N, K), mm.FLOAT, False, True, (N,), 1.0, 1.0)
@@ -579,6 +580,24 @@ def test_float_small_rows(M, K, N, want):
     # more rows keep the other rules; few-row MatMul keeps skinny-M where it wins
     assert mm.Plan((33, 4096), (4096, 11008), mm.FLOAT).info()["tile"] != 8
     assert mm.Plan((15, 4096), (4096, 8704), mm.FLOAT).algo == mm.ALGO_SKINNY_M
+
+
+@pytest.mark.parametrize("sa,sb,want", [
+    ((128, 4096), (4096, 11008), ("split_k", 6, 2)),   # 2 chunks of 64 x 64, not 3 of 128 x 128 (258 workgroups)
+    ((256, 2048), (2048, 2048), ("split_k", 6, 2)),
+    ((512, 11008), (11008, 4096), ("split_k", 7, 4)),
+    ((128, 8192), (8192, 8192), ("split_k", 7, 4)),
+    ((512, 2048), (2048, 2048), ("general", 6, 1)),    # a 1 % estimated gain does not pay the reduction
+    ((512, 8192), (8192, 8192), ("split_k", 7, 2)),
+    ((1024, 8192), (8192, 8192), ("general", 7, 1)),   # more rows: the earlier rules
+    ((64, 131072), (131072, 64), ("split_k", 6, 256)),  # one tile: 256 chunks of 512
+])
+def test_float_timed_split(sa, sb, want):
+    """FP32 products of 33-512 rows split K when the time model's estimate
+    of the chunks, their partials and the reduction beats the general
+    plan's."""
+    inf = mm.Plan(sa, sb, mm.FLOAT).info()
+    assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
 
 
 # ---------------------------------------------------------------- constant B
