@@ -514,6 +514,33 @@ def all_cases():
     return prods, synth.GEMM_PRODUCTS, synth.INT_PRODUCTS
 
 
+_SHAPE_DTYPES = {"bf16": mm.BFLOAT16, "fp16": mm.FLOAT16, "fp32": mm.FLOAT, "fp64": mm.DOUBLE}
+
+
+def parse_shapes(spec: str):
+    """Products named on the command line, for timing and profiling shapes
+    outside the workload list: comma-separated items, each either
+    ``<type>:<A dims>/<B dims>`` (MatMul, dims joined by ``x``) or
+    ``<type>:linear:<M>x<K>x<N>`` (Gemm X W^T + b, W stored [N, K]), with
+    <type> one of bf16, fp16, fp32, fp64; inputs normal(0, 0.02), seed 7."""
+    out = []
+    for item in spec.split(","):
+        parts = item.split(":")
+        if len(parts) < 2 or parts[0] not in _SHAPE_DTYPES:
+            raise ValueError(f"bad product spec {item!r}")
+        dt = _SHAPE_DTYPES[parts[0]]
+        if parts[1] == "linear":
+            M, K, N = (int(v) for v in parts[2].split("x"))
+            out.append(synth.GemmProduct(f"{parts[0]}_linear_{M}x{K}_by_{N}x{K}T_bias", M, N, K, False, True, (N,),
+                                         1.0, 1.0, dt, ("normal", 0.02), 7))
+        else:
+            sa, sb = parts[1].split("/")
+            a = tuple(int(v) for v in sa.split("x"))
+            b = tuple(int(v) for v in sb.split("x"))
+            out.append(synth.Product(f"{parts[0]}_{sa}_by_{sb}", a, b, dt, ("normal", 0.02), 7))
+    return out
+
+
 def make_case(p, dev):
     if isinstance(p, synth.IntProduct):
         return IntCase(p, dev)
@@ -532,8 +559,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--oracle-seconds", type=float, default=0.5, help="oracle sample per case")
     ap.add_argument("--only", default=None, help="time only these products (comma-separated names)")
+    ap.add_argument("--shapes", default=None,
+                    help="time only these products given by shape (see parse_shapes); like --only")
     ap.add_argument("--eager", type=int, default=0,
-                    help="with --only: run this many plain launches of each product and exit (counter passes)")
+                    help="with --only or --shapes: run this many plain launches of each product and exit "
+                         "(counter passes)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run three plain device copies of this many MiB and exit (counter calibration)")
     args = ap.parse_args()
@@ -562,11 +592,15 @@ def main():
 
     prods, gprods, iprods = all_cases()
     everything = prods + gprods + iprods
-    if args.only:
-        names = args.only.split(",")
-        sel = [p for p in everything if p.name in names]
-        if len(sel) != len(names):
-            sys.exit(f"unknown product in {args.only}")
+    if args.only or args.shapes:
+        sel = []
+        if args.only:
+            names = args.only.split(",")
+            sel = [p for p in everything if p.name in names]
+            if len(sel) != len(names):
+                sys.exit(f"unknown product in {args.only}")
+        if args.shapes:
+            sel += parse_shapes(args.shapes)
         cases = [make_case(p, dev) for p in sel]
         timer = Timer()
         sp = timer.sp
