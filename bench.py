@@ -515,6 +515,7 @@ def all_cases():
 
 
 _SHAPE_DTYPES = {"bf16": mm.BFLOAT16, "fp16": mm.FLOAT16, "fp32": mm.FLOAT, "fp64": mm.DOUBLE}
+_SHAPE_INT = {"u8s8": (False, True), "s8s8": (True, True), "u8u8": (False, False), "s8u8": (True, False)}
 
 
 def parse_shapes(spec: str):
@@ -522,10 +523,19 @@ def parse_shapes(spec: str):
     outside the workload list: comma-separated items, each either
     ``<type>:<A dims>/<B dims>`` (MatMul, dims joined by ``x``) or
     ``<type>:linear:<M>x<K>x<N>`` (Gemm X W^T + b, W stored [N, K]), with
-    <type> one of bf16, fp16, fp32, fp64; inputs normal(0, 0.02), seed 7."""
+    <type> one of bf16, fp16, fp32, fp64 (inputs normal(0, 0.02), seed 7),
+    or u8s8, s8s8, u8u8, s8u8 for MatMulInteger without zero points (A's and
+    B's types; inputs uniform over the type)."""
     out = []
     for item in spec.split(","):
         parts = item.split(":")
+        if len(parts) == 2 and parts[0] in _SHAPE_INT:
+            sa, sb = parts[1].split("/")
+            a = tuple(int(v) for v in sa.split("x"))
+            b = tuple(int(v) for v in sb.split("x"))
+            sgn = _SHAPE_INT[parts[0]]
+            out.append(synth.IntProduct(f"{parts[0]}_{sa}_by_{sb}", a, b, sgn[0], sgn[1], 0, 0, 7))
+            continue
         if len(parts) < 2 or parts[0] not in _SHAPE_DTYPES:
             raise ValueError(f"bad product spec {item!r}")
         dt = _SHAPE_DTYPES[parts[0]]

@@ -281,11 +281,15 @@ mm_status mm_gemm_execute(mm_plan_t plan, const void *A, const void *B, const vo
  * a_type / b_type: MM_UINT8 or MM_INT8.  Zero points (same type as their
  * operand): MM_ZP_NONE (0), MM_ZP_SCALAR (one value) or MM_ZP_VECTOR (A: one
  * value per row, [M]; B: one value per column, [N]; shared by every batch).
- * Y is INT32 of the MatMul output shape.  MatMulInteger plans own no
- * workspace and may run on several streams at once.  Errors as for
- * mm_plan_create, plus MM_ERR_DTYPE for other types
- * and MM_ERR_BAD_OPTION for an unknown zero-point kind or an option other
- * than DIRECT / GENERAL with an INT8 tile. */
+ * Y is INT32 of the MatMul output shape.  A plan whose tiles cannot fill
+ * the GPU over a long K (few rows) splits K: INT32 partials in a workspace
+ * the plan allocates at creation (mm_plan_workspace_bytes), summed modulo
+ * 2^32 by a second kernel; such a plan's executions must not overlap, as
+ * for a MatMul split plan.  Other MatMulInteger plans own no workspace and
+ * may run on several streams at once.  Errors as for mm_plan_create, plus
+ * MM_ERR_DTYPE for other types and MM_ERR_BAD_OPTION for an unknown
+ * zero-point kind or an option other than DIRECT, GENERAL with an INT8 tile,
+ * or SPLIT_K on the 128 x 128 INT8 tile (entry 2). */
 enum { MM_ZP_NONE = 0, MM_ZP_SCALAR = 1, MM_ZP_VECTOR = 2 };
 
 mm_status mm_int_plan_create(const int64_t *a_shape, int a_rank, const int64_t *b_shape, int b_rank, int a_type,

@@ -379,7 +379,7 @@ class IntPlan(Plan):
     output modulo 2^32)."""
 
     def __init__(self, a_shape, b_shape, a_type: int, b_type: int, a_zp: int = ZP_NONE, b_zp: int = ZP_NONE,
-                 force_algo: int = 0, tile: int = 0):
+                 force_algo: int = 0, tile: int = 0, split_k: int = 0):
         L = lib()
         self._handle = ctypes.c_void_p()
         self.a_shape = tuple(int(d) for d in a_shape)
@@ -387,7 +387,7 @@ class IntPlan(Plan):
         self.a_type, self.b_type = int(a_type), int(b_type)
         self.a_zp, self.b_zp = int(a_zp), int(b_zp)
         self.dtype = INT32
-        opt = PlanOptions(force_algo, tile, 0, 0)
+        opt = PlanOptions(force_algo, tile, split_k, 0)
         _check(L.mm_int_plan_create(_shape(self.a_shape), len(self.a_shape), _shape(self.b_shape), len(self.b_shape),
                                     self.a_type, self.b_type, self.a_zp, self.b_zp, ctypes.byref(opt),
                                     ctypes.byref(self._handle)))

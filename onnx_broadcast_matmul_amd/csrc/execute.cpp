@@ -294,7 +294,7 @@ mm_status mm_int_execute(mm_plan_t p, const void *A, const void *B, const void *
     a.zpb = zb;
     a.zp_rows = p->M > 0 ? p->M : 1;
     a.y_vec = aligned16(Y) && (p->N * 4) % 16 == 0;
-    bool tiled = p->algo == MM_ALGO_GENERAL;
+    bool tiled = p->algo == MM_ALGO_GENERAL || p->algo == MM_ALGO_SPLIT_K;
     if (tiled) {
         // The tiled kernel streams 16-byte chunks of A rows and B rows, with
         // 32-bit offsets within one tile of A rows and one stage of B rows.
@@ -314,7 +314,7 @@ mm_status mm_int_execute(mm_plan_t p, const void *A, const void *B, const void *
         // columns; tail_col is a multiple of 256, so alignment holds).
         KArgs m = a;
         m.N = p->tail_col;
-        e = launch_general_int(p->tile, m, s);
+        e = launch_general_int(p->tile, false, m, s);
         if (e == hipSuccess) {
             KArgs r = a;
             r.N = p->N - p->tail_col;
@@ -322,11 +322,28 @@ mm_status mm_int_execute(mm_plan_t p, const void *A, const void *B, const void *
             r.Y = (int32_t *)Y + p->tail_col;
             if (p->zpb_kind == MM_ZP_VECTOR) r.zpb = (const uint8_t *)zb + p->tail_col;
             r.y_vec = aligned16(r.Y) && (r.N * 4) % 16 == 0;
-            e = launch_general_int(p->tail_tile, r, s);
+            e = launch_general_int(p->tail_tile, false, r, s);
         }
         return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
     }
-    e = launch_general_int(p->tile, a, s);
+    if (p->algo == MM_ALGO_SPLIT_K) {
+        // K in partitions: INT32 partials in the plan's workspace (rows of N),
+        // then their sum modulo 2^32.
+        mm_status st = ensure_workspace(p);
+        if (st != MM_OK) return st;
+        a.W = (float *)p->ws;
+        a.split = p->split;
+        a.kchunk = p->kchunk;
+        a.y_vec = (p->N * 4) % 16 == 0;
+        e = launch_general_int(p->tile, true, a, s);
+        if (e == hipSuccess) {
+            KArgs r = a;
+            r.y_vec = aligned16(Y);
+            e = launch_splitk_reduce_i32(r, s);
+        }
+        return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
+    }
+    e = launch_general_int(p->tile, false, a, s);
     return e == hipSuccess ? MM_OK : hip_fail(e, "kernel launch");
 }
 

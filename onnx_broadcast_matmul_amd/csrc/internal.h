@@ -130,7 +130,8 @@ hipError_t launch_skinny_n(int dtype, const Align &al, const KArgs &a, hipStream
 // sum passes (ra over a_rows rows of A, cb over b_mats B matrices; either
 // may be NULL) and the INT8 tiled kernel for the kTiles8 entries.
 hipError_t launch_int_direct(const KArgs &a, hipStream_t s);
-hipError_t launch_general_int(int tile, const KArgs &a, hipStream_t s);
+hipError_t launch_general_int(int tile, bool split, const KArgs &a, hipStream_t s);
+hipError_t launch_splitk_reduce_i32(const KArgs &a, hipStream_t s);
 // DOUBLE kernels (k_f64.hip); W holds double partials for split-K.
 hipError_t launch_direct_f64(const KArgs &a, hipStream_t s);
 hipError_t launch_general_f64(int tile, const Align &al, bool split, const KArgs &a, hipStream_t s);

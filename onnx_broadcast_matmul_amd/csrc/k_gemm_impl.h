@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     // 16-byte chunk position swizzles of A rows and B rows (see above).
     auto aswz = [](int row) { return CA == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
     auto mswz = [](int k, int cpr) { return kn_swizzle<ES>(k, cpr); };  // k-row of cpr chunks
-    static_assert(DT != MM_INT8 || (KG == 1 && !SPLIT), "INT8: no K groups, no split-K");
+    static_assert(DT != MM_INT8 || KG == 1, "INT8: no K groups");
     static_assert(!PACKB || (ES == 2 && !SPLIT && !TA && !TB && !GEMM), "prepacked B: 16-bit MatMul tiles only");
     auto bswz = [&](int k) { return mswz(k, CPR); };
 
@@ -778,7 +778,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
     // which spreads the 32 rows of one write over distinct chunks; the
     // workgroup then writes whole 16-byte chunks of output rows.  Tiles larger
     // than the stage buffers go in row passes.
-    using O = typename std::conditional<SPLIT, float, typename std::conditional<DT == MM_INT8, int32_t, S>::type>::type;
+    // Split-K partials: FP32, or INT32 for MatMulInteger (added modulo 2^32).
+    using O = typename std::conditional<DT == MM_INT8, int32_t, typename std::conditional<SPLIT, float, S>::type>::type;
     constexpr int OS = (int)sizeof(O);
     constexpr int OV = 16 / OS;            // output elements per chunk
     constexpr int OCPR = BN * OS / 16;     // output chunks per tile row
@@ -905,7 +906,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_gemm_lds_dma(KArgs a) {
                     // zero-point period are below 2^31.
                     const uint32_t za = int_zp(a.zpa, a.zpa_mode, a.a_signed, (uint32_t)row % (uint32_t)a.zp_rows);
                     const uint32_t za_raw = za + (a.a_signed ? 0u : 128u);
-                    const uint32_t kp = (uint32_t)((int64_t)nk * BK), pad = kp - (uint32_t)K;
+                    // (K is this partition's length under split-K: each
+                    // partition's terms are those of its own K range, and
+                    // their sum is the whole product's.)
+                    const uint32_t kp = (uint32_t)((int64_t)nk * BK), pad = kp - (uint32_t)(kend - kbeg);
                     const uint32_t rsum = a.sum_a ? (uint32_t)sums_lds[pass * PR + rl] : 0u;
                     uint32_t y[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -1238,10 +1242,23 @@ static hipError_t launch_tile(bool vec, bool split, const KArgs &a, hipStream_t 
     const int64_t b_span = TB ? (int64_t)BN * a.ldb : (int64_t)(BKB / ES) * a.ldb;
     const bool fits = a_span * ES < 0x7fff0000LL && b_span * ES < 0x7fff0000LL;
     if constexpr (DT == MM_INT8) {
-        // INT8 runs only this kernel, unsplit; the plan and execute layer
-        // send other cases to the direct integer kernel.
-        if (!(vec && fits) || split) return hipErrorInvalidValue;
+        // INT8 runs only this kernel (split-K on the 128 x 128 entry); the
+        // plan and execute layer send other cases to the direct integer kernel.
+        if (!(vec && fits)) return hipErrorInvalidValue;
         const dim3 blk(64 * WGM * WGN * KG);
+        if (split) {
+            if constexpr (BM * BN <= 128 * 128) {
+                switch ((a.flip_a ? 1 : 0) | (a.flip_b ? 2 : 0)) {
+                case 0: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB, false, 0>), g, blk, 0, s, a); break;
+                case 1: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB, false, 1>), g, blk, 0, s, a); break;
+                case 2: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB, false, 2>), g, blk, 0, s, a); break;
+                default: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, true, TA, TB, false, 3>), g, blk, 0, s, a); break;
+                }
+                return hipGetLastError();
+            } else {
+                return hipErrorInvalidValue;
+            }
+        }
         switch ((a.flip_a ? 1 : 0) | (a.flip_b ? 2 : 0)) {
         case 0: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false, 0>), g, blk, 0, s, a); break;
         case 1: hipLaunchKernelGGL((k_gemm_lds_dma<DT, BM, BN, WGM, WGN, BKB, STAGES, PW, KG, false, TA, TB, false, 1>), g, blk, 0, s, a); break;

@@ -72,19 +72,58 @@ hipError_t launch_int_direct(const KArgs &a, hipStream_t s) {
 
 static_assert(kNumTiles8 == 3, "launch switch must cover the INT8 tile table");
 
-hipError_t launch_general_int(int tile, const KArgs &a, hipStream_t s) {
+hipError_t launch_general_int(int tile, bool split, const KArgs &a, hipStream_t s) {
     switch (tile) {
     case 0:
         return launch_tile<MM_INT8, kTiles8[0].bm, kTiles8[0].bn, kTiles8[0].wgm, kTiles8[0].wgn, kTiles8[0].bkb,
-                           kTiles8[0].stages, kTiles8[0].producers, kTiles8[0].kgroups>(true, false, a, s);
+                           kTiles8[0].stages, kTiles8[0].producers, kTiles8[0].kgroups>(true, split, a, s);
     case 1:
         return launch_tile<MM_INT8, kTiles8[1].bm, kTiles8[1].bn, kTiles8[1].wgm, kTiles8[1].wgn, kTiles8[1].bkb,
-                           kTiles8[1].stages, kTiles8[1].producers, kTiles8[1].kgroups>(true, false, a, s);
+                           kTiles8[1].stages, kTiles8[1].producers, kTiles8[1].kgroups>(true, split, a, s);
     case 2:
         return launch_tile<MM_INT8, kTiles8[2].bm, kTiles8[2].bn, kTiles8[2].wgm, kTiles8[2].wgn, kTiles8[2].bkb,
-                           kTiles8[2].stages, kTiles8[2].producers, kTiles8[2].kgroups>(true, false, a, s);
+                           kTiles8[2].stages, kTiles8[2].producers, kTiles8[2].kgroups>(true, split, a, s);
     }
     return hipErrorInvalidValue;
+}
+
+// MatMulInteger split-K phase 2: Y = the sum of the partitions' INT32
+// partials modulo 2^32 (integer adds: any order gives the same value).  A
+// thread owns four consecutive outputs.
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_splitk_reduce_i32(KArgs a) {
+    const int64_t total = a.batch * a.M * a.N;
+    const int64_t o0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (o0 >= total) return;
+    const uint32_t *__restrict__ W = (const uint32_t *)a.W;
+    uint32_t acc[4] = {0u, 0u, 0u, 0u};
+    if constexpr (VEC) {
+        // total is a multiple of 4: every group is whole and 16-byte aligned.
+        for (int s = 0; s < a.split; ++s) {
+            const uint4 v = *(const uint4 *)(W + (int64_t)s * total + o0);
+            acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+        }
+        *(uint4 *)((uint32_t *)a.Y + o0) = make_uint4(acc[0], acc[1], acc[2], acc[3]);
+    } else {
+        for (int s = 0; s < a.split; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (o0 + e < total) acc[e] += W[(int64_t)s * total + o0 + e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (o0 + e < total) ((uint32_t *)a.Y)[o0 + e] = acc[e];
+    }
+}
+
+hipError_t launch_splitk_reduce_i32(const KArgs &a, hipStream_t s) {
+    const int64_t total = a.batch * a.M * a.N;
+    const int64_t g = ((total + 3) / 4 + 255) / 256;
+    if (g > 0x7fffffff) return hipErrorInvalidValue;
+    if (g <= 0) return hipSuccess;
+    // Vector stores need Y 16-byte aligned as well.
+    if (total % 4 == 0 && a.y_vec) hipLaunchKernelGGL(k_splitk_reduce_i32<true>, dim3((unsigned)g), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_splitk_reduce_i32<false>, dim3((unsigned)g), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace mm

@@ -787,8 +787,11 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         } else {
             algo = MM_ALGO_GENERAL;
         }
-        // MatMulInteger runs on the direct and tiled INT8 kernels.
-        if (p->is_int && algo != MM_ALGO_DIRECT) algo = MM_ALGO_GENERAL;
+        // MatMulInteger runs on the direct and tiled INT8 kernels; split-K
+        // (INT32 partials) where the rules above split and the tiled kernel
+        // can take the shape (K and N whole 16-byte chunks).
+        if (p->is_int && algo != MM_ALGO_DIRECT)
+            algo = algo == MM_ALGO_SPLIT_K && K % 16 == 0 && N % 16 == 0 ? MM_ALGO_SPLIT_K : MM_ALGO_GENERAL;
     }
     if (algo < MM_ALGO_DIRECT || algo > MM_ALGO_GENERAL)
         return fail(MM_ERR_BAD_OPTION, "force_algo %d is not a forcible algorithm", algo);
@@ -796,8 +799,8 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         return fail(MM_ERR_BAD_OPTION, "DOUBLE has no skinny-M / skinny-N kernel (force GENERAL or DIRECT)");
     if (p->is_gemm && (algo == MM_ALGO_SKINNY_M || algo == MM_ALGO_SKINNY_N))
         return fail(MM_ERR_BAD_OPTION, "Gemm runs on the direct, general and split-K kernels only");
-    if (p->is_int && algo != MM_ALGO_DIRECT && algo != MM_ALGO_GENERAL)
-        return fail(MM_ERR_BAD_OPTION, "MatMulInteger runs on the direct and general kernels only");
+    if (p->is_int && algo != MM_ALGO_DIRECT && algo != MM_ALGO_GENERAL && algo != MM_ALGO_SPLIT_K)
+        return fail(MM_ERR_BAD_OPTION, "MatMulInteger runs on the direct, general and split-K kernels only");
     p->algo = algo;
 
     if (algo == MM_ALGO_SKINNY_M) {
@@ -912,6 +915,15 @@ mm_status mm_int_plan_create(const int64_t *a_shape, int a_rank, const int64_t *
     // block tile).
     if (p->algo == MM_ALGO_GENERAL && !(opt && opt->tile > 0) && (p->tile == 0 || p->tile == 2))
         p->tile = a_type == MM_UINT8 && b_type == MM_INT8 ? 2 : 0;
+    if (p->algo == MM_ALGO_SPLIT_K && tile_entry(MM_INT32, p->tile)->bm * tile_entry(MM_INT32, p->tile)->bn > 128 * 128) {
+        delete p;
+        return fail(MM_ERR_BAD_OPTION, "MatMulInteger split-K runs on the 128 x 128 tile only");
+    }
+    st = alloc_workspace(p, true);
+    if (st != MM_OK) {
+        delete p;
+        return st;
+    }
     *out = p;
     return MM_OK;
 }

@@ -82,7 +82,10 @@ constexpr int kNumTiles8 = sizeof(kTiles8) / sizeof(kTiles8[0]);
 
 // K granularity of split-K partitions: 128 bytes of K, a whole number of
 // LDS stages of every tile entry.
-inline int stage_k(int dtype) { return dtype == MM_DOUBLE ? 16 : dtype == MM_FLOAT ? 32 : 64; }
+inline int stage_k(int dtype) {
+    if (dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) return 128;  // MatMulInteger
+    return dtype == MM_DOUBLE ? 16 : dtype == MM_FLOAT ? 32 : 64;
+}
 constexpr bool stages_divide_128() {
     for (const TileCfg &t : kTiles16)
         if (128 % t.bkb != 0) return false;

@@ -14,6 +14,9 @@ def test_parse_shapes():
     assert isinstance(g, synth.GemmProduct) and (g.M, g.K, g.N) == (16, 4096, 11008)
     assert g.trans_b and not g.trans_a and g.c_shape == (11008,) and g.dtype == mm.FLOAT
     assert p[2].a_shape == (2, 16, 2048) and p[2].dtype == mm.FLOAT16
+    (q,) = bench.parse_shapes("u8s8:16x4096/4096x11008")
+    assert isinstance(q, synth.IntProduct) and q.a_shape == (16, 4096) and not q.a_signed and q.b_signed
+    assert q.a_zp == 0 and q.b_zp == 0
 
 
 @pytest.mark.parametrize("bad", ["int8:4x4/4x4", "bf16", "bf16:4x4"])

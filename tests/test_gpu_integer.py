@@ -58,7 +58,7 @@ def int_run(plan, a, b, za, zb, dev, a_off=0, b_off=0):
     return Y.cpu().numpy()
 
 
-def int_parity(sa, sb, ta, tb, zka, zkb, dev, algo=0, tile=0, seed=0, a_off=0, b_off=0):
+def int_parity(sa, sb, ta, tb, zka, zkb, dev, algo=0, tile=0, seed=0, a_off=0, b_off=0, split=0):
     sa_, sb_ = SIGN[ta], SIGN[tb]
     a = synth.generate_int(sa, sa_, [seed, 0])
     b = synth.generate_int(sb, sb_, [seed, 1])
@@ -66,7 +66,7 @@ def int_parity(sa, sb, ta, tb, zka, zkb, dev, algo=0, tile=0, seed=0, a_off=0, b
     n = 1 if len(sb) == 1 else sb[-1]
     za = _zero_point(zka, sa_, m, [seed, 2])
     zb = _zero_point(zkb, sb_, n, [seed, 3])
-    plan = mm.IntPlan(sa, sb, CODE[sa_], CODE[sb_], ZP[zka], ZP[zkb], force_algo=algo, tile=tile)
+    plan = mm.IntPlan(sa, sb, CODE[sa_], CODE[sb_], ZP[zka], ZP[zkb], force_algo=algo, tile=tile, split_k=split)
     if algo:
         assert plan.algo == algo
     y = int_run(plan, a, b, za, zb, dev, a_off, b_off)
@@ -130,24 +130,51 @@ def test_int_rank_one_empty_zero_k(dev):
         int_parity(sa, sb, "u8", "s8", "scalar", "scalar", dev, seed=9)
 
 
-def test_int_wraps_modulo_2_32(dev):
+@pytest.mark.parametrize("algo", [mm.ALGO_GENERAL, mm.ALGO_SPLIT_K], ids=lambda a: mm.ALGO_NAMES[a])
+def test_int_wraps_modulo_2_32(algo, dev):
     """Sums beyond the INT32 range wrap: 16384 * 2^18 = 2^32 gives 0 in the
-    matrix-core accumulator itself; 255 * 255 * 40000 - 2^32 comes from the
-    UINT8 corrections."""
+    matrix-core accumulator itself (split-K: in the partials' sum);
+    255 * 255 * 40000 - 2^32 comes from the UINT8 corrections."""
     K = 1 << 18
     a = np.full((64, K), -128, np.int8)
     b = np.full((K, 64), -128, np.int8)
-    plan = mm.IntPlan(a.shape, b.shape, mm.INT8, mm.INT8)
-    assert plan.algo == mm.ALGO_GENERAL
+    plan = mm.IntPlan(a.shape, b.shape, mm.INT8, mm.INT8, force_algo=algo)
+    assert plan.algo == algo
     y = int_run(plan, a, b, None, None, dev)
     assert oracle.matmul_integer_at(a, b, [0, 4095])[0] == 0 and not y.any()
     K = 40000
     a = np.full((64, K), 255, np.uint8)
     b = np.full((K, 64), 255, np.uint8)
-    plan = mm.IntPlan(a.shape, b.shape, mm.UINT8, mm.UINT8)
+    plan = mm.IntPlan(a.shape, b.shape, mm.UINT8, mm.UINT8, force_algo=algo)
     y = int_run(plan, a, b, None, None, dev)
     want = 255 * 255 * K - 2**32
     assert oracle.matmul_integer_at(a, b, [7])[0] == want and (y == want).all()
+
+
+@pytest.mark.parametrize("ta,tb", TYPES, ids=lambda t: t)
+@pytest.mark.parametrize("zka,zkb", ZPS, ids=lambda z: z)
+def test_int_split_k(ta, tb, zka, zkb, dev):
+    """Split-K (INT32 partials, summed modulo 2^32): each partition applies
+    the zero-point and sign-flip terms of its own K range, the last one with
+    a partly padded 128-byte stage; broadcast batches, ragged M and N."""
+    p = int_parity((2, 1, 200, 1040), (3, 1040, 272), ta, tb, zka, zkb, dev, algo=mm.ALGO_SPLIT_K, split=3, seed=11)
+    assert p.info()["split_k"] == 3 and p.info()["tile"] == 2
+
+
+@pytest.mark.parametrize("split", [2, 5, 8, 16, 31])
+def test_int_split_counts(split, dev):
+    p = int_parity((37, 4096), (4096, 272), "u8", "s8", "vector", "vector", dev, algo=mm.ALGO_SPLIT_K, split=split,
+                   seed=12 + split)
+    assert split // 2 < p.info()["split_k"] <= split
+
+
+@pytest.mark.parametrize("sa,sb", [((16, 4096), (4096, 11008)), ((1, 11008), (11008, 4096)),
+                                   ((2, 8, 4096), (2, 4096, 2048))])
+def test_int_few_rows_split(sa, sb, dev):
+    """The plans' own split for few-row quantized layers, every output
+    compared."""
+    p = int_parity(sa, sb, "u8", "s8", "scalar", "vector", dev, seed=13)
+    assert p.algo == mm.ALGO_SPLIT_K
 
 
 @pytest.mark.parametrize("ta,tb,zka,zkb", [("u8", "s8", "scalar", "vector"), ("s8", "u8", "vector", "vector")],

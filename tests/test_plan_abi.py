@@ -706,7 +706,8 @@ def test_int_plan_algorithms():
     f = mm.IntPlan((8, 64, 256), (256, 128), u8, s8)
     assert f.info()["folded"] and f.info()["kernel_m"] == 512 and f.algo == mm.ALGO_GENERAL
     assert f.workspace_bytes == 0
-    assert mm.IntPlan((1, 4096), (4096, 4096), s8, s8).algo == mm.ALGO_GENERAL  # no skinny kernels
+    # no skinny kernels: few tiles over a long K split K (INT32 partials)
+    assert mm.IntPlan((1, 4096), (4096, 4096), s8, s8).algo == mm.ALGO_SPLIT_K
     assert mm.IntPlan((4096, 4096), (4096, 1), s8, s8).algo == mm.ALGO_GENERAL
     assert mm.IntPlan((8, 16), (16, 8), s8, s8).algo == mm.ALGO_DIRECT
     assert mm.IntPlan((64, 0), (0, 32), s8, u8).algo == mm.ALGO_ZERO_FILL
@@ -729,7 +730,7 @@ def test_int_plan_algorithms():
     (dict(zka=3), mm.ERR_BAD_OPTION),
     (dict(zkb=-1), mm.ERR_BAD_OPTION),
     (dict(force_algo=mm.ALGO_SKINNY_M), mm.ERR_BAD_OPTION),
-    (dict(force_algo=mm.ALGO_SPLIT_K), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_SPLIT_K, tile=1), mm.ERR_BAD_OPTION),  # split-K: the 128 x 128 entry only
     (dict(force_algo=mm.ALGO_GENERAL, tile=4), mm.ERR_BAD_OPTION),
     (dict(sb=(100, 64)), mm.ERR_K_MISMATCH),
     (dict(sa=(3, 64, 128), sb=(2, 128, 64)), mm.ERR_BROADCAST),
@@ -741,6 +742,28 @@ def test_int_plan_errors(kw, status):
     with pytest.raises(mm.MMError) as e:
         mm.IntPlan(sa, sb, *args, **kw)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("sa,sb,want", [
+    ((16, 4096), (4096, 11008), ("split_k", 2, 3)),   # 86 tiles of 128 x 128: 3 chunks
+    ((16, 11008), (11008, 4096), ("split_k", 2, 8)),
+    ((2, 8, 4096), (2, 4096, 2048), ("split_k", 2, 8)),  # batched: 2 x 16 tiles
+    ((64, 4096), (4096, 28672), ("general", 2, 1)),   # 224 tiles: no split
+    ((16, 4100), (4100, 4096), ("general", 2, 1)),    # K not whole 16-byte chunks: the tiled kernel's limit
+    ((16, 512, 4096), (4096, 11008), ("general", 3, 1)),
+])
+def test_int_split_plans(sa, sb, want):
+    """MatMulInteger splits K where the other types' rules split (few tiles,
+    long K) and the tiled kernel takes the shape, on the 128 x 128 entry,
+    with INT32 partials in a workspace of split x rows x N x 4 bytes."""
+    p = mm.IntPlan(sa, sb, mm.UINT8, mm.INT8, mm.ZP_SCALAR, mm.ZP_VECTOR)
+    inf = p.info()
+    assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
+    if want[0] == "split_k":
+        assert inf["k_chunk"] % 128 == 0  # partitions hold whole 128-byte stages
+        assert p.workspace_bytes == inf["split_k"] * inf["batch"] * inf["kernel_m"] * inf["N"] * 4
+    f = mm.IntPlan((16, 1000), (1000, 256), mm.INT8, mm.INT8, force_algo=mm.ALGO_SPLIT_K, split_k=3)
+    assert (f.algo, f.info()["tile"], f.info()["split_k"]) == (mm.ALGO_SPLIT_K, 2, 3)
 
 
 def test_int_execute_checks_before_any_gpu_call():
