@@ -70,7 +70,7 @@ hipError_t launch_int_direct(const KArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-static_assert(kNumTiles8 == 3, "launch switch must cover the INT8 tile table");
+static_assert(kNumTiles8 == 4, "launch switch must cover the INT8 tile table");
 
 hipError_t launch_general_int(int tile, bool split, const KArgs &a, hipStream_t s) {
     switch (tile) {
@@ -83,6 +83,9 @@ hipError_t launch_general_int(int tile, bool split, const KArgs &a, hipStream_t 
     case 2:
         return launch_tile<MM_INT8, kTiles8[2].bm, kTiles8[2].bn, kTiles8[2].wgm, kTiles8[2].wgn, kTiles8[2].bkb,
                            kTiles8[2].stages, kTiles8[2].producers, kTiles8[2].kgroups>(true, split, a, s);
+    case 3:
+        return launch_tile<MM_INT8, kTiles8[3].bm, kTiles8[3].bn, kTiles8[3].wgm, kTiles8[3].wgn, kTiles8[3].bkb,
+                           kTiles8[3].stages, kTiles8[3].producers, kTiles8[3].kgroups>(true, split, a, s);
     }
     return hipErrorInvalidValue;
 }

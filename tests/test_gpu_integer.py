@@ -92,7 +92,7 @@ def test_int_signedness_and_zero_points(ta, tb, zka, zkb, algo, dev):
     int_parity((2, 1, 200, 400), (3, 400, 272), ta, tb, zka, zkb, dev, algo=algo, seed=1)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
 @pytest.mark.parametrize("ta,tb", [("u8", "s8"), ("s8", "u8")], ids=lambda t: t)
 def test_int_every_tile(tile, ta, tb, dev):
     int_parity((700, 1024), (1024, 600), ta, tb, "vector", "vector", dev, algo=mm.ALGO_GENERAL, tile=tile, seed=2)
@@ -159,6 +159,9 @@ def test_int_split_k(ta, tb, zka, zkb, dev):
     a partly padded 128-byte stage; broadcast batches, ragged M and N."""
     p = int_parity((2, 1, 200, 1040), (3, 1040, 272), ta, tb, zka, zkb, dev, algo=mm.ALGO_SPLIT_K, split=3, seed=11)
     assert p.info()["split_k"] == 3 and p.info()["tile"] == 2
+    # at most 64 rows: the three-stage 64 x 128 entry
+    p = int_parity((2, 1, 40, 1040), (3, 1040, 272), ta, tb, zka, zkb, dev, algo=mm.ALGO_SPLIT_K, split=3, seed=12)
+    assert p.info()["split_k"] == 3 and p.info()["tile"] == 4
 
 
 @pytest.mark.parametrize("split", [2, 5, 8, 16, 31])

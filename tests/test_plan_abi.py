@@ -716,7 +716,8 @@ def test_int_plan_algorithms():
     assert d.algo == mm.ALGO_DIRECT and d.workspace_bytes == 0
     t = mm.IntPlan((512, 512), (512, 512), u8, u8, force_algo=mm.ALGO_GENERAL, tile=2)
     assert t.info()["tile"] == 2
-    assert mm.tile_configs(mm.INT8) == mm.tile_configs(mm.UINT8) == [(256, 256, 128), (128, 128, 128), (256, 256, 128)]
+    assert mm.tile_configs(mm.INT8) == mm.tile_configs(mm.UINT8) == [(256, 256, 128), (128, 128, 128), (256, 256, 128),
+                                                                      (64, 128, 128)]
     # the 256 x 256 entry whose waves hold fewer fragments of a sign-flipped A
     assert mm.IntPlan((4096, 4096), (4096, 4096), u8, s8).info()["tile"] == 3
     assert mm.IntPlan((4096, 4096), (4096, 4096), s8, u8).info()["tile"] == 1
@@ -731,7 +732,7 @@ def test_int_plan_algorithms():
     (dict(zkb=-1), mm.ERR_BAD_OPTION),
     (dict(force_algo=mm.ALGO_SKINNY_M), mm.ERR_BAD_OPTION),
     (dict(force_algo=mm.ALGO_SPLIT_K, tile=1), mm.ERR_BAD_OPTION),  # split-K: the 128 x 128 entry only
-    (dict(force_algo=mm.ALGO_GENERAL, tile=4), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_GENERAL, tile=5), mm.ERR_BAD_OPTION),
     (dict(sb=(100, 64)), mm.ERR_K_MISMATCH),
     (dict(sa=(3, 64, 128), sb=(2, 128, 64)), mm.ERR_BROADCAST),
 ])
@@ -745,17 +746,19 @@ def test_int_plan_errors(kw, status):
 
 
 @pytest.mark.parametrize("sa,sb,want", [
-    ((16, 4096), (4096, 11008), ("split_k", 2, 3)),   # 86 tiles of 128 x 128: 3 chunks
-    ((16, 11008), (11008, 4096), ("split_k", 2, 8)),
-    ((2, 8, 4096), (2, 4096, 2048), ("split_k", 2, 8)),  # batched: 2 x 16 tiles
+    ((16, 4096), (4096, 11008), ("split_k", 4, 3)),   # 86 tiles of 64 x 128 (three stages): 3 chunks
+    ((16, 11008), (11008, 4096), ("split_k", 4, 8)),
+    ((2, 8, 4096), (2, 4096, 2048), ("split_k", 4, 8)),  # batched: 2 x 16 tiles
+    ((96, 4096), (4096, 4096), ("split_k", 2, 8)),    # more rows: the 128 x 128 entry
     ((64, 4096), (4096, 28672), ("general", 2, 1)),   # 224 tiles: no split
     ((16, 4100), (4100, 4096), ("general", 2, 1)),    # K not whole 16-byte chunks: the tiled kernel's limit
     ((16, 512, 4096), (4096, 11008), ("general", 3, 1)),
 ])
 def test_int_split_plans(sa, sb, want):
     """MatMulInteger splits K where the other types' rules split (few tiles,
-    long K) and the tiled kernel takes the shape, on the 128 x 128 entry,
-    with INT32 partials in a workspace of split x rows x N x 4 bytes."""
+    long K) and the tiled kernel takes the shape, on the three-stage 64 x 128
+    entry up to 64 rows and the 128 x 128 one beyond, with INT32 partials in
+    a workspace of split x rows x N x 4 bytes."""
     p = mm.IntPlan(sa, sb, mm.UINT8, mm.INT8, mm.ZP_SCALAR, mm.ZP_VECTOR)
     inf = p.info()
     assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
@@ -763,7 +766,7 @@ def test_int_split_plans(sa, sb, want):
         assert inf["k_chunk"] % 128 == 0  # partitions hold whole 128-byte stages
         assert p.workspace_bytes == inf["split_k"] * inf["batch"] * inf["kernel_m"] * inf["N"] * 4
     f = mm.IntPlan((16, 1000), (1000, 256), mm.INT8, mm.INT8, force_algo=mm.ALGO_SPLIT_K, split_k=3)
-    assert (f.algo, f.info()["tile"], f.info()["split_k"]) == (mm.ALGO_SPLIT_K, 2, 3)
+    assert (f.algo, f.info()["tile"], f.info()["split_k"]) == (mm.ALGO_SPLIT_K, 4, 3)
 
 
 def test_int_execute_checks_before_any_gpu_call():
