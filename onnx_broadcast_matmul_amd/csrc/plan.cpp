@@ -114,9 +114,9 @@ static_assert(kTiles16[kT16Row32].bm == 32 && kTiles16[kT16Row32].bn == 128 && k
 static_assert(kTransTiles16[2] == kT16Small, "the 64 x 64 entry has a Gemm kernel");
 
 constexpr int kT32Row32 = 7;  // FLOAT 32 x 128, two K groups (see float_small_rows)
-constexpr int kT8Split64 = 3;  // INT8 64 x 128, three stages (MatMulInteger split-K over at most 64 rows)
-static_assert(kTiles8[kT8Split64].bm == 64 && kTiles8[kT8Split64].bn == 128 && kTiles8[kT8Split64].stages == 3 &&
-                  kNumTiles8 == kT8Split64 + 1,
+constexpr int kT8Row64 = 3;  // INT8 64 x 128, three stages (MatMulInteger over at most 64 rows)
+static_assert(kTiles8[kT8Row64].bm == 64 && kTiles8[kT8Row64].bn == 128 && kTiles8[kT8Row64].stages == 3 &&
+                  kNumTiles8 == kT8Row64 + 1,
               "the INT8 split entry closes its table");
 static_assert(kTiles32[kT32Row32].bm == 32 && kTiles32[kT32Row32].bn == 128 && kTiles32[kT32Row32].kgroups == 2 &&
                   kNumTiles32 == kT32Row32 + 1,
@@ -125,10 +125,16 @@ static_assert(kTiles32[kT32Row32].bm == 32 && kTiles32[kT32Row32].bn == 128 && k
 static bool small_m_entry(int dtype, int index) {
     return ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && index >= kT16Row32) ||
            (dtype == MM_FLOAT && index == kT32Row32) ||
-           ((dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) && index == kT8Split64);
+           ((dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) && index == kT8Row64);
 }
 
 static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, bool gemm = false) {
+    // MatMulInteger over at most 64 rows, up to one 128-column tile per CU:
+    // the three-stage 64 x 128 INT8 entry, 37-41 % faster than the two-stage
+    // 128 x 128 one the ranking picks (UINT8 x INT8, M = 1..64, N = 28672,
+    // K = 4096 and 8192: [16,8192]x[8192,28672] 85.6 -> 51.7 us).  Past
+    // one round (N = 65536) the 128 x 128 entry stays ahead.
+    if (dtype == MM_INT32 && M <= 64 && batch * cdiv(N, kTiles8[kT8Row64].bn) <= kNumCUs) return kT8Row64;
     if ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && M <= 64) {
         // At most 64 rows: each tile is a K-long chain of B stages, not MFMA
         // work, so the quality ranking above does not apply.  Measured for
@@ -477,7 +483,7 @@ static int choose_split_tile(int dtype, int64_t batch, int64_t M, int64_t N, int
     // than on the two-stage 128 x 128 entry (UINT8 x INT8, M = 1..64, K
     // 4096-11008): [16,8192]x[8192,8192] 31.7 -> 23.9 us, [16,4096]x
     // [4096,11008] 23.6 -> 20.2 us.
-    if (dtype == MM_INT32 && M <= 64) return kT8Split64;
+    if (dtype == MM_INT32 && M <= 64) return kT8Row64;
     int best = -1;
     double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {

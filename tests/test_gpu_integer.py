@@ -171,13 +171,17 @@ def test_int_split_counts(split, dev):
     assert split // 2 < p.info()["split_k"] <= split
 
 
-@pytest.mark.parametrize("sa,sb", [((16, 4096), (4096, 11008)), ((1, 11008), (11008, 4096)),
-                                   ((2, 8, 4096), (2, 4096, 2048))])
-def test_int_few_rows_split(sa, sb, dev):
-    """The plans' own split for few-row quantized layers, every output
+@pytest.mark.parametrize("sa,sb,algo,tile", [
+    ((16, 4096), (4096, 11008), mm.ALGO_SPLIT_K, 4),
+    ((1, 11008), (11008, 4096), mm.ALGO_SPLIT_K, 4),
+    ((2, 8, 4096), (2, 4096, 2048), mm.ALGO_SPLIT_K, 4),
+    ((48, 4096), (4096, 28672), mm.ALGO_GENERAL, 4),   # one round of 64 x 128 tiles, whole
+])
+def test_int_few_rows(sa, sb, algo, tile, dev):
+    """The plans' own choices for few-row quantized layers, every output
     compared."""
     p = int_parity(sa, sb, "u8", "s8", "scalar", "vector", dev, seed=13)
-    assert p.algo == mm.ALGO_SPLIT_K
+    assert p.algo == algo and p.info()["tile"] == tile
 
 
 @pytest.mark.parametrize("ta,tb,zka,zkb", [("u8", "s8", "scalar", "vector"), ("s8", "u8", "vector", "vector")],

@@ -750,8 +750,9 @@ def test_int_plan_errors(kw, status):
     ((16, 11008), (11008, 4096), ("split_k", 4, 8)),
     ((2, 8, 4096), (2, 4096, 2048), ("split_k", 4, 8)),  # batched: 2 x 16 tiles
     ((96, 4096), (4096, 4096), ("split_k", 2, 8)),    # more rows: the 128 x 128 entry
-    ((64, 4096), (4096, 28672), ("general", 2, 1)),   # 224 tiles: no split
-    ((16, 4100), (4100, 4096), ("general", 2, 1)),    # K not whole 16-byte chunks: the tiled kernel's limit
+    ((64, 4096), (4096, 28672), ("general", 4, 1)),   # 224 tiles: no split, the 64 x 128 entry whole
+    ((16, 4096), (4096, 65536), ("general", 2, 1)),   # past one round of 128-column tiles: 128 x 128
+    ((16, 4100), (4100, 4096), ("general", 4, 1)),    # K not whole 16-byte chunks: no split (the tiled kernel's limit)
     ((16, 512, 4096), (4096, 11008), ("general", 3, 1)),
 ])
 def test_int_split_plans(sa, sb, want):
