@@ -246,8 +246,9 @@ static hipError_t launch_f64_tile(bool vec, bool split, const KArgs &a, hipStrea
     return hipGetLastError();
 }
 
-static_assert(kNumTiles64 == 2 && kTiles64[0].bm == 128 && kTiles64[0].bn == 128 && kTiles64[1].bm == 64 &&
-                  kTiles64[1].bn == 64 && kTiles64[0].bkb == kF64BK * 8 && kTiles64[1].bkb == kF64BK * 8,
+static_assert(kNumTiles64 == 3 && kTiles64[0].bm == 128 && kTiles64[0].bn == 128 && kTiles64[1].bm == 64 &&
+                  kTiles64[1].bn == 64 && kTiles64[2].bm == 32 && kTiles64[2].bn == 128 &&
+                  kTiles64[0].bkb == kF64BK * 8 && kTiles64[1].bkb == kF64BK * 8 && kTiles64[2].bkb == kF64BK * 8,
               "launch switch must cover the FP64 tile table");
 
 hipError_t launch_general_f64(int tile, const Align &al, bool split, const KArgs &a, hipStream_t s) {
@@ -255,6 +256,7 @@ hipError_t launch_general_f64(int tile, const Align &al, bool split, const KArgs
     switch (tile) {
     case 0: return launch_f64_tile<128, 128>(vec, split, a, s);
     case 1: return launch_f64_tile<64, 64>(vec, split, a, s);
+    case 2: return launch_f64_tile<32, 128>(vec, split, a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -66,7 +66,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static double tile_quality(int dtype, int index) {
     static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5, 0.0, 0.0, 0.0, 0.0};
     static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15, 0.0};
-    static const double q64[kNumTiles64] = {1.0, 0.8};
+    static const double q64[kNumTiles64] = {1.0, 0.8, 0.0};
     static const double q8[kNumTiles8] = {1.0, 0.75, 1.0, 0.0};
     if (dtype == MM_DOUBLE) return q64[index];
     if (dtype == MM_INT32) return q8[index];
@@ -115,6 +115,9 @@ static_assert(kTransTiles16[2] == kT16Small, "the 64 x 64 entry has a Gemm kerne
 
 constexpr int kT32Row32 = 7;  // FLOAT 32 x 128, two K groups (see float_small_rows)
 constexpr int kT8Row64 = 3;  // INT8 64 x 128, three stages (MatMulInteger over at most 64 rows)
+constexpr int kT64Row32 = 2;  // DOUBLE 32 x 128 (see double_small_rows)
+static_assert(kTiles64[kT64Row32].bm == 32 && kTiles64[kT64Row32].bn == 128 && kNumTiles64 == kT64Row32 + 1,
+              "the DOUBLE small-row entry closes its table");
 static_assert(kTiles8[kT8Row64].bm == 64 && kTiles8[kT8Row64].bn == 128 && kTiles8[kT8Row64].stages == 3 &&
                   kNumTiles8 == kT8Row64 + 1,
               "the INT8 split entry closes its table");
@@ -125,7 +128,8 @@ static_assert(kTiles32[kT32Row32].bm == 32 && kTiles32[kT32Row32].bn == 128 && k
 static bool small_m_entry(int dtype, int index) {
     return ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && index >= kT16Row32) ||
            (dtype == MM_FLOAT && index == kT32Row32) ||
-           ((dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) && index == kT8Row64);
+           ((dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) && index == kT8Row64) ||
+           (dtype == MM_DOUBLE && index == kT64Row32);
 }
 
 static int choose_tile(int dtype, int64_t batch, int64_t M, int64_t N, bool gemm = false) {
@@ -348,6 +352,25 @@ static int float_small_rows(const mm_plan_s *p, int64_t M, int64_t N, int64_t K)
     int64_t s = 2;
     while (2 * s * tiles <= kNumCUs) s *= 2;
     return (int)std::max<int64_t>(1, std::min<int64_t>(s, K / 256));
+}
+
+// DOUBLE over at most 32 rows (DOUBLE has no skinny kernels): the 32 x 128
+// entry, which halves the FP64 matrix-core work that 64-row tiles pad in.
+// Up to one tile per CU it splits K in s chunks, s the largest power of two
+// (at least 2) with at most three workgroups per CU (the FP64 kernel's
+// small LDS footprint holds several), at most K / 512 and at most 8; past
+// one tile per CU it runs the tiles whole.  Forced tiles and chunk counts
+// on 12 products (M = 1..32; K, N 4096-28672): [16,4096]x[4096,11008]
+// 175.6 -> 81.0 us (8 chunks), [16,11008]x[11008,4096] 150.1 -> 91.8 us,
+// [16,4096]x[4096,28672] 345 -> 204 us (2 chunks).  Returns the chunk
+// count (1: the general path on this entry), or 0.
+static int double_small_rows(const mm_plan_s *p, int64_t M, int64_t N, int64_t K) {
+    if (p->dtype != MM_DOUBLE || M > 32) return 0;
+    const int64_t tiles = p->batch * cdiv(N, kTiles64[kT64Row32].bn);
+    if (tiles > kNumCUs) return 1;
+    int64_t s = 2;
+    while (2 * s * tiles <= 3 * kNumCUs) s *= 2;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(s, 8), K / 512));
 }
 
 // FP32 products of 33-512 rows: split-K when the time model says it pays.
@@ -781,6 +804,9 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         } else if ((rule_split = float_small_rows(p, M, N, K)) > 0) {
             algo = rule_split > 1 ? MM_ALGO_SPLIT_K : MM_ALGO_GENERAL;  // FP32 over few rows: 32-row tiles
             rule_tile = kT32Row32;
+        } else if ((rule_split = double_small_rows(p, M, N, K)) > 0) {
+            algo = rule_split > 1 ? MM_ALGO_SPLIT_K : MM_ALGO_GENERAL;  // DOUBLE over few rows: 32-row tiles
+            rule_tile = kT64Row32;
         } else if (p->dtype == MM_FLOAT && M > 32 && M <= 512) {
             // FP32 of 33-512 rows: split-K or general by the time model
             rule_split = float_timed_split(p, M, N, K, &rule_tile);

@@ -59,6 +59,7 @@ constexpr TileCfg kTiles32[] = {
 constexpr TileCfg kTiles64[] = {
     {128, 128, 2, 2, 128, 2, 4, 1},
     {64, 64, 2, 2, 128, 2, 4, 1},
+    {32, 128, 2, 2, 128, 2, 4, 1},  // products of at most 32 rows
 };
 
 // Entries instantiated for Gemm (its epilogue and transA / transB).

@@ -607,6 +607,7 @@ SELECTED_PATHS = [
     ((16, 4096), (4096, 11008), mm.FLOAT, False, ("split_k", 8, 2)),       # FP32 <= 32 rows: 32x128 tiles
     ((32, 4096), (4096, 40000), mm.FLOAT, False, ("general", 8, 1)),
     ((24, 4096), (11008, 4096), mm.FLOAT, True, ("split_k", 8, 2)),        # FP32 linear layer, 24 rows
+    ((16, 4096), (4096, 11008), mm.DOUBLE, False, ("split_k", 3, 8)),      # DOUBLE few rows: 32x128 tiles
     ((256, 4096), (4096, 4352), mm.BFLOAT16, False, ("split_k", 6, 4)),   # split-K tiles at most 128x128
     ((32, 4096), (11008, 4096), mm.BFLOAT16, True, ("split_k", 14, 4)),   # Gemm decode: 64x128 chunks
     ((16, 14336), (4096, 14336), mm.FLOAT16, True, ("split_k", 14, 8)),

@@ -479,8 +479,23 @@ def test_double_rejects_forced_skinny(algo):
 
 
 def test_double_tile_table():
-    assert mm.lib().mm_tile_count(mm.DOUBLE) == 2
-    assert mm.tile_configs(mm.DOUBLE) == [(128, 128, 16), (64, 64, 16)]
+    assert mm.lib().mm_tile_count(mm.DOUBLE) == 3
+    assert mm.tile_configs(mm.DOUBLE) == [(128, 128, 16), (64, 64, 16), (32, 128, 16)]
+
+
+@pytest.mark.parametrize("sa,sb,want", [
+    ((16, 4096), (4096, 11008), ("split_k", 3, 8)),   # 86 tiles of 32 x 128: 8 chunks (688 workgroups)
+    ((1, 4096), (4096, 4096), ("split_k", 3, 8)),     # at most 8 chunks
+    ((16, 2048), (2048, 4096), ("split_k", 3, 4)),    # at most K / 512 chunks
+    ((16, 4096), (4096, 28672), ("split_k", 3, 2)),   # 224 tiles: 2 chunks
+    ((16, 4096), (4096, 65536), ("general", 3, 1)),   # past one tile per CU: whole tiles
+    ((33, 4096), (4096, 11008), ("split_k", 2, 2)),   # more rows: the earlier rules
+])
+def test_double_small_rows(sa, sb, want):
+    """DOUBLE over at most 32 rows runs on the 32 x 128 entry, splitting K
+    up to one tile per CU."""
+    inf = mm.Plan(sa, sb, mm.DOUBLE).info()
+    assert (mm.ALGO_NAMES[inf["algo"]], inf["tile"], inf["split_k"]) == want, inf
 
 
 # ---------------------------------------------------------------- last-round balancing
