@@ -70,7 +70,7 @@ hipError_t launch_int_direct(const KArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-static_assert(kNumTiles8 == 4, "launch switch must cover the INT8 tile table");
+static_assert(kNumTiles8 == 5, "launch switch must cover the INT8 tile table");
 
 hipError_t launch_general_int(int tile, bool split, const KArgs &a, hipStream_t s) {
     switch (tile) {
@@ -86,6 +86,9 @@ hipError_t launch_general_int(int tile, bool split, const KArgs &a, hipStream_t 
     case 3:
         return launch_tile<MM_INT8, kTiles8[3].bm, kTiles8[3].bn, kTiles8[3].wgm, kTiles8[3].wgn, kTiles8[3].bkb,
                            kTiles8[3].stages, kTiles8[3].producers, kTiles8[3].kgroups>(true, split, a, s);
+    case 4:
+        return launch_tile<MM_INT8, kTiles8[4].bm, kTiles8[4].bn, kTiles8[4].wgm, kTiles8[4].wgn, kTiles8[4].bkb,
+                           kTiles8[4].stages, kTiles8[4].producers, kTiles8[4].kgroups>(true, split, a, s);
     }
     return hipErrorInvalidValue;
 }

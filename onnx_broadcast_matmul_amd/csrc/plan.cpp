@@ -67,7 +67,7 @@ static double tile_quality(int dtype, int index) {
     static const double q16[kNumTiles16] = {1.0, 0.85, 0.7, 0.55, 0.4, 0.9, 0.8, 0.8, 0.35, 0.5, 0.0, 0.0, 0.0, 0.0};
     static const double q32[kNumTiles32] = {0.95, 1.0, 0.8, 1.0, 1.1, 0.85, 1.15, 0.0};
     static const double q64[kNumTiles64] = {1.0, 0.8, 0.0};
-    static const double q8[kNumTiles8] = {1.0, 0.75, 1.0, 0.0};
+    static const double q8[kNumTiles8] = {1.0, 0.75, 1.0, 0.0, 0.0};
     if (dtype == MM_DOUBLE) return q64[index];
     if (dtype == MM_INT32) return q8[index];
     return dtype == MM_FLOAT ? q32[index] : q16[index];
@@ -114,13 +114,15 @@ static_assert(kTiles16[kT16Row32].bm == 32 && kTiles16[kT16Row32].bn == 128 && k
 static_assert(kTransTiles16[2] == kT16Small, "the 64 x 64 entry has a Gemm kernel");
 
 constexpr int kT32Row32 = 7;  // FLOAT 32 x 128, two K groups (see float_small_rows)
-constexpr int kT8Row64 = 3;  // INT8 64 x 128, three stages (MatMulInteger over at most 64 rows)
+constexpr int kT8Row64 = 3;    // INT8 64 x 128, three stages (MatMulInteger over at most 64 rows)
+constexpr int kT8Deep128 = 4;  // INT8 128 x 128, three stages (split-K that fills the CUs exactly)
 constexpr int kT64Row32 = 2;  // DOUBLE 32 x 128 (see double_small_rows)
 static_assert(kTiles64[kT64Row32].bm == 32 && kTiles64[kT64Row32].bn == 128 && kNumTiles64 == kT64Row32 + 1,
               "the DOUBLE small-row entry closes its table");
 static_assert(kTiles8[kT8Row64].bm == 64 && kTiles8[kT8Row64].bn == 128 && kTiles8[kT8Row64].stages == 3 &&
-                  kNumTiles8 == kT8Row64 + 1,
-              "the INT8 split entry closes its table");
+                  kTiles8[kT8Deep128].bm == 128 && kTiles8[kT8Deep128].bn == 128 &&
+                  kTiles8[kT8Deep128].stages == 3 && kNumTiles8 == kT8Deep128 + 1,
+              "the INT8 split entries close their table");
 static_assert(kTiles32[kT32Row32].bm == 32 && kTiles32[kT32Row32].bn == 128 && kTiles32[kT32Row32].kgroups == 2 &&
                   kNumTiles32 == kT32Row32 + 1,
               "the FLOAT small-row entry closes its table");
@@ -128,7 +130,7 @@ static_assert(kTiles32[kT32Row32].bm == 32 && kTiles32[kT32Row32].bn == 128 && k
 static bool small_m_entry(int dtype, int index) {
     return ((dtype == MM_FLOAT16 || dtype == MM_BFLOAT16) && index >= kT16Row32) ||
            (dtype == MM_FLOAT && index == kT32Row32) ||
-           ((dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) && index == kT8Row64) ||
+           ((dtype == MM_INT8 || dtype == MM_UINT8 || dtype == MM_INT32) && index >= kT8Row64) ||
            (dtype == MM_DOUBLE && index == kT64Row32);
 }
 
@@ -507,6 +509,18 @@ static int choose_split_tile(int dtype, int64_t batch, int64_t M, int64_t N, int
     // 4096-11008): [16,8192]x[8192,8192] 31.7 -> 23.9 us, [16,4096]x
     // [4096,11008] 23.6 -> 20.2 us.
     if (dtype == MM_INT32 && M <= 64) return kT8Row64;
+    // More rows: the three-stage 128 x 128 entry (one workgroup per CU)
+    // when the rounded-up chunk count fills the CUs exactly (the tile count
+    // divides them): 16-22 % faster than the two-stage entry on the K-long
+    // products of 96-256 rows measured (e.g. [128,8192]x[8192,8192] 42.4
+    // -> 33.8 us).  Otherwise a 257th workgroup would start a second round
+    // on one CU, and the two-stage entry (two per CU) stays ([128,4096]x
+    // [4096,11008], 86 tiles: 40.8 us or more on three-stage chunks,
+    // against 32.1 us).
+    if (dtype == MM_INT32) {
+        const int64_t tiles = batch * cdiv(M, kTiles8[kT8Deep128].bm) * cdiv(N, kTiles8[kT8Deep128].bn);
+        if (tiles <= kNumCUs && kNumCUs % tiles == 0) return kT8Deep128;
+    }
     int best = -1;
     double best_s = -1.0;
     for (int i = 0; i < tile_count(dtype); ++i) {

@@ -74,8 +74,9 @@ constexpr TileCfg kTiles8[] = {
     {256, 256, 2, 4, 128, 2, 4, 1},
     {128, 128, 2, 2, 128, 2, 4, 1},
     {256, 256, 4, 2, 128, 2, 4, 1},
-    // Split-K over at most 64 rows: three stages deep for short K chunks.
+    // Split-K (and few-row) entries: three stages deep for short K chunks.
     {64, 128, 2, 2, 128, 3, 4, 1},
+    {128, 128, 2, 2, 128, 3, 4, 1},
 };
 
 constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);

@@ -92,7 +92,7 @@ def test_int_signedness_and_zero_points(ta, tb, zka, zkb, algo, dev):
     int_parity((2, 1, 200, 400), (3, 400, 272), ta, tb, zka, zkb, dev, algo=algo, seed=1)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("ta,tb", [("u8", "s8"), ("s8", "u8")], ids=lambda t: t)
 def test_int_every_tile(tile, ta, tb, dev):
     int_parity((700, 1024), (1024, 600), ta, tb, "vector", "vector", dev, algo=mm.ALGO_GENERAL, tile=tile, seed=2)
@@ -176,6 +176,7 @@ def test_int_split_counts(split, dev):
     ((1, 11008), (11008, 4096), mm.ALGO_SPLIT_K, 4),
     ((2, 8, 4096), (2, 4096, 2048), mm.ALGO_SPLIT_K, 4),
     ((48, 4096), (4096, 28672), mm.ALGO_GENERAL, 4),   # one round of 64 x 128 tiles, whole
+    ((128, 8192), (8192, 8192), mm.ALGO_SPLIT_K, 5),   # 64 tiles x 4 chunks: the three-stage 128 x 128 entry
 ])
 def test_int_few_rows(sa, sb, algo, tile, dev):
     """The plans' own choices for few-row quantized layers, every output

@@ -732,7 +732,7 @@ def test_int_plan_algorithms():
     t = mm.IntPlan((512, 512), (512, 512), u8, u8, force_algo=mm.ALGO_GENERAL, tile=2)
     assert t.info()["tile"] == 2
     assert mm.tile_configs(mm.INT8) == mm.tile_configs(mm.UINT8) == [(256, 256, 128), (128, 128, 128), (256, 256, 128),
-                                                                      (64, 128, 128)]
+                                                                      (64, 128, 128), (128, 128, 128)]
     # the 256 x 256 entry whose waves hold fewer fragments of a sign-flipped A
     assert mm.IntPlan((4096, 4096), (4096, 4096), u8, s8).info()["tile"] == 3
     assert mm.IntPlan((4096, 4096), (4096, 4096), s8, u8).info()["tile"] == 1
@@ -747,7 +747,7 @@ def test_int_plan_algorithms():
     (dict(zkb=-1), mm.ERR_BAD_OPTION),
     (dict(force_algo=mm.ALGO_SKINNY_M), mm.ERR_BAD_OPTION),
     (dict(force_algo=mm.ALGO_SPLIT_K, tile=1), mm.ERR_BAD_OPTION),  # split-K: the 128 x 128 entry only
-    (dict(force_algo=mm.ALGO_GENERAL, tile=5), mm.ERR_BAD_OPTION),
+    (dict(force_algo=mm.ALGO_GENERAL, tile=6), mm.ERR_BAD_OPTION),
     (dict(sb=(100, 64)), mm.ERR_K_MISMATCH),
     (dict(sa=(3, 64, 128), sb=(2, 128, 64)), mm.ERR_BROADCAST),
 ])
@@ -764,7 +764,8 @@ def test_int_plan_errors(kw, status):
     ((16, 4096), (4096, 11008), ("split_k", 4, 3)),   # 86 tiles of 64 x 128 (three stages): 3 chunks
     ((16, 11008), (11008, 4096), ("split_k", 4, 8)),
     ((2, 8, 4096), (2, 4096, 2048), ("split_k", 4, 8)),  # batched: 2 x 16 tiles
-    ((96, 4096), (4096, 4096), ("split_k", 2, 8)),    # more rows: the 128 x 128 entry
+    ((96, 4096), (4096, 4096), ("split_k", 5, 8)),    # more rows, 32 tiles x 8 chunks fill the CUs: three stages
+    ((128, 4096), (4096, 11008), ("split_k", 2, 3)),  # 86 tiles x 3 chunks overflow them: two-stage 128 x 128
     ((64, 4096), (4096, 28672), ("general", 4, 1)),   # 224 tiles: no split, the 64 x 128 entry whole
     ((16, 4096), (4096, 65536), ("general", 2, 1)),   # past one round of 128-column tiles: 128 x 128
     ((16, 4100), (4100, 4096), ("general", 4, 1)),    # K not whole 16-byte chunks: no split (the tiled kernel's limit)
