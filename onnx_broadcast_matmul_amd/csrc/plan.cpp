@@ -791,9 +791,12 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         };
         // Skinny-M with K cut over workgroups (measured against split-K and
         // the tiles for M = 1..15, K = 1024..16384, N = 256..30720): FP32
-        // up to 8 rows wins everywhere (the tiles pad M to 64 rows of FP32
-        // MFMA work), by up to 3x, and up to 15 rows with K >= 4096 and
-        // N >= 4096; the 16-bit types, whose tiles run at the 16-bit MFMA
+        // up to 8 rows wins everywhere (64-row tiles padded M to 64 rows of
+        // FP32 MFMA work), by up to 3x.  It also won for 9-15 rows with
+        // K >= 4096 and N >= 4096 until the 32-row FP32 entry: split on that
+        // entry, 12 and 15 rows run 1.11-1.37x faster than skinny-M on 10
+        // products (K, N 4096-28672), so float_small_rows takes them.  The
+        // 16-bit types, whose tiles run at the 16-bit MFMA
         // rate, win for up to 4 rows with a long K and a large B (K >= 8192,
         // K * N >= 2^26), and for up to 8 rows with K >= 16384 and
         // N >= 8704 (packed dot products: 15-29 % faster than the tiles).
@@ -802,7 +805,7 @@ static mm_status select_algo(mm_plan_s *p, const mm_plan_options *opt) {
         // other 16-bit shapes keep the tiles or split-K.
         const bool rows16 = K % 8 == 0 && N % 8 == 0;
         const bool skm_split = has_skinny && K >= 1024 &&
-                               ((p->dtype == MM_FLOAT && (M <= 8 || (M < 16 && K >= 4096 && N >= 4096))) ||
+                               ((p->dtype == MM_FLOAT && M <= 8) ||
                                 (t16 && rows16 && M <= 4 && K >= 8192 && (double)K * N >= 67108864.0) ||
                                 (t16 && rows16 && M <= 8 && K >= 16384 && N >= 8704));
         if (has_skinny && N < 16 && N <= M && K >= 64 && !skn_short) {

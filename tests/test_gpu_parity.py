@@ -594,7 +594,7 @@ def _sample_indices(shape, n, rng):
 # the plan it must make (algorithm, tile entry + 1, K partitions).
 SELECTED_PATHS = [
     ((1, 4096), (4096, 8704), mm.FLOAT, False, ("skinny_m", 0, 13)),      # FP32 GEMV, K in 13 chunks
-    ((15, 4096), (4096, 8704), mm.FLOAT, False, ("skinny_m", 0, 13)),
+    ((15, 4096), (4096, 8704), mm.FLOAT, False, ("split_k", 8, 2)),       # FP32 9..15 rows: 32-row tiles
     ((1, 16384), (16384, 8704), mm.BFLOAT16, False, ("skinny_m", 0, 29)),  # 16-bit GEMV, long K
     ((8, 16384), (16384, 8704), mm.BFLOAT16, False, ("skinny_m", 0, 29)),  # 8 rows: packed-dot 8-row instance
     ((64, 1024), (1024, 15360), mm.BFLOAT16, False, ("general", 9, 1)),    # <= 64 rows: two-group 64x64

@@ -226,7 +226,8 @@ SELECTOR_CASES = [
     ((15, 16384), (16384, 30720), mm.FLOAT16, "general"),
     ((1, 4096), (4096, 11008), mm.BFLOAT16, "split_k"),   # 172 tiles and K >= 4096
     ((1, 1024), (1024, 11008), mm.BFLOAT16, "general"),   # 172 tiles, K < 4096
-    ((15, 4096), (4096, 8704), mm.FLOAT, "skinny_m"),     # FP32 9..15 rows: K >= 4096 and N >= 4096
+    ((15, 4096), (4096, 8704), mm.FLOAT, "split_k"),      # FP32 9..15 rows: 32-row tiles, K in chunks
+    ((8, 4096), (4096, 8704), mm.FLOAT, "skinny_m"),      # FP32 up to 8 rows: the K-split GEMV
     ((15, 16384), (16384, 2048), mm.FLOAT, "split_k"),
     ((15, 1024), (1024, 8704), mm.FLOAT, "split_k"),      # FP32 <= 32 rows: 32-row tiles, K in chunks
     ((16, 4096), (4096, 8704), mm.FLOAT, "split_k"),      # 16 rows and more: never the K-split GEMV
@@ -594,7 +595,8 @@ def test_float_small_rows(M, K, N, want):
         assert (mm.ALGO_NAMES[g["algo"]], g["tile"], g["split_k"]) == want, (ta, tb, g)
     # more rows keep the other rules; few-row MatMul keeps skinny-M where it wins
     assert mm.Plan((33, 4096), (4096, 11008), mm.FLOAT).info()["tile"] != 8
-    assert mm.Plan((15, 4096), (4096, 8704), mm.FLOAT).algo == mm.ALGO_SKINNY_M
+    assert mm.Plan((8, 4096), (4096, 8704), mm.FLOAT).algo == mm.ALGO_SKINNY_M
+    assert mm.Plan((15, 4096), (4096, 8704), mm.FLOAT).info()["tile"] == 8
 
 
 @pytest.mark.parametrize("sa,sb,want", [
